@@ -1,0 +1,263 @@
+"""MI355X-native Q4_0 Mixture-of-Experts expert FFN (libmoe_q4.so binding).
+
+Thin Python layer over the C ABI of include/moe_q4.h: the functions below
+have the ABI's names and only marshal arguments (device pointers of torch
+tensors, the current HIP stream, workspace buffers).  Every step of the
+computation runs in the library's HIP kernels; torch only owns device memory
+and streams.  If the library is not built, every call raises.
+
+    layer = MoELayer.from_float(w_router, gate, up, down, top_k=8, s_gate=..)
+    r = moe_q4_route(layer, x_bf16)             # router, top-k, permutation
+    y = moe_q4_prefill(layer, x_bf16, r)        # grouped 4-bit GEMM prefill
+    y1 = moe_q4_decode(layer, x_f32)            # one-token W4A8 decode
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "q4_packed_bytes", "q4_pack", "q8_quantize", "MoELayer", "Routing",
+    "moe_q4_route_workspace_bytes", "moe_q4_route",
+    "moe_q4_prefill_workspace_bytes", "moe_q4_prefill",
+    "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
+    "moe_q4_w4a8_gemv", "moe_q4_rmsnorm", "library_path",
+]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+# ------------------------------------------------------------------ helpers
+def q4_packed_bytes(rows: int, K: int) -> int:
+    return int(_lib.lib().q4_packed_bytes(rows, K))
+
+
+def q4_pack(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fp32 [..., rows, K] device tensor -> uint8 [..., rows, K/32*18] Q4_0 blocks."""
+    _dev(w, "w")
+    K = w.shape[-1]
+    rows = w.numel() // K
+    if out is None:
+        out = torch.empty(w.shape[:-1] + (K // 32 * 18,), dtype=torch.uint8, device=w.device)
+    _lib.check(_lib.lib().q4_pack(_p(w), rows, K, _p(out), _s(stream)), "q4_pack")
+    return out
+
+
+def q8_quantize(x: torch.Tensor, stream=None):
+    """fp32 [..., K] -> (int8 [..., K], fp32 scales [..., K/32])."""
+    _dev(x, "x")
+    K = x.shape[-1]
+    rows = x.numel() // K
+    q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    d = torch.empty(x.shape[:-1] + (K // 32,), dtype=torch.float32, device=x.device)
+    _lib.check(_lib.lib().q8_quantize(_p(x), rows, K, _p(q), _p(d), _s(stream)), "q8_quantize")
+    return q, d
+
+
+# ------------------------------------------------------------------ layer
+class MoELayer:
+    """Device-resident packed layer (moe_q4_layer).
+
+    w_router fp32 [H, E]; gate/up uint8 [E, I, H/32*18]; down uint8
+    [E, H, I/32*18]; optional router_bias fp32 [E] and shared expert
+    s_gate/s_up uint8 [I, H/32*18], s_down uint8 [H, I/32*18].
+    """
+
+    def __init__(self, w_router, gate, up, down, top_k, router_bias=None,
+                 s_gate=None, s_up=None, s_down=None):
+        for n, t in (("w_router", w_router), ("gate", gate), ("up", up), ("down", down),
+                     ("router_bias", router_bias), ("s_gate", s_gate), ("s_up", s_up),
+                     ("s_down", s_down)):
+            _dev(t, n)
+        self.w_router, self.router_bias = w_router, router_bias
+        self.gate, self.up, self.down = gate, up, down
+        self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
+        self.hidden, self.n_experts = int(w_router.shape[0]), int(w_router.shape[1])
+        self.inter = int(gate.shape[1])
+        self.top_k = int(top_k)
+        self.has_shared = s_gate is not None
+        st = _lib.Layer()
+        st.hidden, st.inter, st.n_experts, st.top_k = self.hidden, self.inter, self.n_experts, self.top_k
+        st.has_shared = 1 if self.has_shared else 0
+        st.w_router, st.router_bias = _p(w_router), _p(router_bias)
+        st.w_gate, st.w_up, st.w_down = _p(gate), _p(up), _p(down)
+        st.s_gate, st.s_up, st.s_down = _p(s_gate), _p(s_up), _p(s_down)
+        self._c = st
+
+    @classmethod
+    def from_float(cls, w_router, gate, up, down, top_k, router_bias=None,
+                   s_gate=None, s_up=None, s_down=None, stream=None):
+        """Pack fp32 device weights with the library's q4_pack kernel."""
+        pk = lambda t: None if t is None else q4_pack(t, stream=stream)  # noqa: E731
+        return cls(w_router, pk(gate), pk(up), pk(down), top_k, router_bias,
+                   pk(s_gate), pk(s_up), pk(s_down))
+
+    def struct_ptr(self):
+        return C.byref(self._c)
+
+
+@dataclass
+class Routing:
+    """Device buffers of moe_q4_routing for a T-token batch."""
+    topk_ids: torch.Tensor      # int32 [T, k]
+    topk_w: torch.Tensor        # fp32  [T, k]
+    expert_offsets: torch.Tensor  # int32 [E+1]
+    perm: torch.Tensor          # int32 [T*k]
+    inv_perm: torch.Tensor      # int32 [T*k]
+    logits: torch.Tensor | None = None
+
+    @classmethod
+    def empty(cls, T, k, E, device, logits=False):
+        i32 = dict(dtype=torch.int32, device=device)
+        return cls(torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=device),
+                   torch.empty(E + 1, **i32), torch.empty(T * k, **i32), torch.empty(T * k, **i32),
+                   torch.empty((T, E), dtype=torch.float32, device=device) if logits else None)
+
+    def cstruct(self):
+        r = _lib.Routing()
+        r.topk_ids, r.topk_w = _p(self.topk_ids), _p(self.topk_w)
+        r.expert_offsets, r.perm, r.inv_perm = _p(self.expert_offsets), _p(self.perm), _p(self.inv_perm)
+        return r
+
+
+def _ws(nbytes, device, ws):
+    if ws is not None:
+        return ws
+    # 256-byte aligned by the caching allocator
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ prefill
+def moe_q4_route_workspace_bytes(layer: MoELayer, T: int) -> int:
+    return int(_lib.lib().moe_q4_route_workspace_bytes(layer.struct_ptr(), T))
+
+
+def moe_q4_route(layer: MoELayer, x: torch.Tensor, out: Routing | None = None,
+                 logits: bool = False, ws: torch.Tensor | None = None, stream=None) -> Routing:
+    """Router + top-k + permutation of x [T, H] (fp32 or bf16)."""
+    _dev(x, "x")
+    T = int(x.shape[0])
+    if x.dtype == torch.bfloat16:
+        dt = _lib.MOE_Q4_BF16
+    elif x.dtype == torch.float32:
+        dt = _lib.MOE_Q4_F32
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    if out is None:
+        out = Routing.empty(T, layer.top_k, layer.n_experts, x.device, logits=logits)
+    nb = moe_q4_route_workspace_bytes(layer, T)
+    w = _ws(nb, x.device, ws)
+    rs = out.cstruct()
+    _lib.check(_lib.lib().moe_q4_route(layer.struct_ptr(), _p(x), dt, T, C.byref(rs), _p(out.logits),
+                                       _p(w), w.numel(), _s(stream)), "moe_q4_route")
+    return out
+
+
+def moe_q4_prefill_workspace_bytes(layer: MoELayer, T: int) -> int:
+    return int(_lib.lib().moe_q4_prefill_workspace_bytes(layer.struct_ptr(), T))
+
+
+def moe_q4_prefill(layer: MoELayer, x_bf16: torch.Tensor, routing: Routing,
+                   y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """Grouped 4-bit GEMM prefill: y [T, H] fp32."""
+    _dev(x_bf16, "x_bf16")
+    if x_bf16.dtype != torch.bfloat16:
+        raise ValueError("x_bf16 must be bfloat16")
+    T = int(x_bf16.shape[0])
+    if y is None:
+        y = torch.empty((T, layer.hidden), dtype=torch.float32, device=x_bf16.device)
+    nb = moe_q4_prefill_workspace_bytes(layer, T)
+    w = _ws(nb, x_bf16.device, ws)
+    rs = routing.cstruct()
+    _lib.check(_lib.lib().moe_q4_prefill(layer.struct_ptr(), _p(x_bf16), T, C.byref(rs), _p(y),
+                                         _p(w), w.numel(), _s(stream)), "moe_q4_prefill")
+    return y
+
+
+# ------------------------------------------------------------------ decode
+def moe_q4_decode_workspace_bytes(layer: MoELayer) -> int:
+    return int(_lib.lib().moe_q4_decode_workspace_bytes(layer.struct_ptr()))
+
+
+def decode_workspace(layer: MoELayer, device=None) -> torch.Tensor:
+    """A zero-filled decode workspace (must be zero before its first use)."""
+    dev = device if device is not None else layer.w_router.device
+    return torch.zeros(max(moe_q4_decode_workspace_bytes(layer), 1), dtype=torch.uint8, device=dev)
+
+
+def moe_q4_decode(layer: MoELayer, x: torch.Tensor, y: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None, trace: bool = False, stream=None):
+    """One-token W4A8 decode: x [H] fp32 -> y [H] fp32 (and the trace dict)."""
+    _dev(x, "x")
+    if x.dtype != torch.float32:
+        raise ValueError("x must be float32")
+    if y is None:
+        y = torch.empty(layer.hidden, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = decode_workspace(layer, x.device)
+    tr, tc = None, None
+    if trace:
+        H, I, k = layer.hidden, layer.inter, layer.top_k
+        ns = k + (1 if layer.has_shared else 0)
+        d = x.device
+        tr = dict(logits=torch.empty(layer.n_experts, dtype=torch.float32, device=d),
+                  ids=torch.empty(k, dtype=torch.int32, device=d),
+                  w=torch.empty(k, dtype=torch.float32, device=d),
+                  qx=torch.empty(H, dtype=torch.int8, device=d),
+                  dx=torch.empty(H // 32, dtype=torch.float32, device=d),
+                  qh=torch.empty((ns, I), dtype=torch.int8, device=d),
+                  dh=torch.empty((ns, I // 32), dtype=torch.float32, device=d))
+        tc = _lib.DecodeTrace(**{k_: _p(v) for k_, v in tr.items()})
+    _lib.check(_lib.lib().moe_q4_decode(layer.struct_ptr(), _p(x), _p(y),
+                                        C.byref(tc) if tc is not None else None,
+                                        _p(ws), ws.numel(), _s(stream)), "moe_q4_decode")
+    return (y, tr) if trace else y
+
+
+def moe_q4_w4a8_gemv(W: torch.Tensor, N: int, K: int, qa: torch.Tensor, da: torch.Tensor,
+                     with_dots: bool = True, stream=None):
+    """The decode row program on one packed matrix -> (dots int32 [N, K/32] | None, out fp32 [N])."""
+    for n, t in (("W", W), ("qa", qa), ("da", da)):
+        _dev(t, n)
+    dots = torch.empty((N, K // 32), dtype=torch.int32, device=W.device) if with_dots else None
+    out = torch.empty(N, dtype=torch.float32, device=W.device)
+    _lib.check(_lib.lib().moe_q4_w4a8_gemv(_p(W), N, K, _p(qa), _p(da), _p(dots), _p(out), _s(stream)),
+               "moe_q4_w4a8_gemv")
+    return dots, out
+
+
+def moe_q4_rmsnorm(y: torch.Tensor, eps: float = 1e-6, f32: bool = True, bf16: bool = False,
+                   stream=None):
+    """Unit-gain RMSNorm of y [T, H] fp32 -> (fp32 | None, bf16 | None)."""
+    _dev(y, "y")
+    T, H = int(y.shape[0]), int(y.shape[1])
+    o32 = torch.empty_like(y) if f32 else None
+    o16 = torch.empty((T, H), dtype=torch.bfloat16, device=y.device) if bf16 else None
+    _lib.check(_lib.lib().moe_q4_rmsnorm(_p(y), T, H, float(eps), _p(o32), _p(o16), _s(stream)),
+               "moe_q4_rmsnorm")
+    return o32, o16

@@ -1,0 +1,78 @@
+"""Build libmoe_q4.so (HIP for gfx950) in-tree with hipcc.
+
+    python -m bit_quantized_moe_q4_amd.build
+
+Every source under csrc/ is compiled to an object in _build/ (in parallel),
+then linked into bit_quantized_moe_q4_amd/libmoe_q4.so.  Flags:
+  --offload-arch=gfx950          MI355X only
+  -ffp-contract=off              the fixed fp32 programs need every a*b+c to
+                                 stay two roundings unless an fma is written
+  -packed-fp32-ops disabled      no packed fp32 VALU instructions are emitted
+  (no fast-math; fp32 '/' and sqrtf stay correctly rounded, denormals kept)
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libmoe_q4.so")
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+SOURCES = ["abi.cpp", "pack.hip", "router.hip", "gemm.hip", "decode.hip", "rmsnorm.hip"]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd[1:1] = ["-x", "hip"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr[-6000:]))
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libmoe_q4.so (always recompiles)."""
+    if not os.path.exists(HIPCC):
+        raise RuntimeError("hipcc not found at %s" % HIPCC)
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s" % r.stderr[-4000:])
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+def clean() -> None:
+    shutil.rmtree(BUILD, ignore_errors=True)
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

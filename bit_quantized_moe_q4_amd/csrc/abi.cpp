@@ -1,0 +1,319 @@
+// abi.cpp -- the extern "C" entry points of libmoe_q4.so (declared and
+// documented in include/moe_q4.h): argument checks, workspace layout and the
+// launch sequence of each call.  No device memory is allocated here.
+#include "moe_q4.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_Q4_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxDim = 16384;
+
+int check_layer(const moe_q4_layer* L) {
+  if (!L) return fail(MOE_Q4_EINVAL, "layer is NULL");
+  if (L->hidden <= 0 || L->hidden % 32 || L->hidden > kMaxDim)
+    return fail(MOE_Q4_EINVAL, "hidden=%d must be a positive multiple of 32 <= %d", L->hidden, kMaxDim);
+  if (L->inter <= 0 || L->inter % 32 || L->inter > kMaxDim)
+    return fail(MOE_Q4_EINVAL, "inter=%d must be a positive multiple of 32 <= %d", L->inter, kMaxDim);
+  if (L->n_experts < 1 || L->n_experts > kMaxExperts)
+    return fail(MOE_Q4_EINVAL, "n_experts=%d must be in [1, %d]", L->n_experts, kMaxExperts);
+  if (L->top_k < 1 || L->top_k > L->n_experts || L->top_k > kMaxTopK)
+    return fail(MOE_Q4_EINVAL, "top_k=%d must be in [1, min(n_experts, %d)]", L->top_k, kMaxTopK);
+  if (L->has_shared != 0 && L->has_shared != 1)
+    return fail(MOE_Q4_EINVAL, "has_shared=%d must be 0 or 1", L->has_shared);
+  if (!L->w_router || !L->w_gate || !L->w_up || !L->w_down)
+    return fail(MOE_Q4_EINVAL, "w_router, w_gate, w_up and w_down must be non-NULL");
+  if (L->has_shared && (!L->s_gate || !L->s_up || !L->s_down))
+    return fail(MOE_Q4_EINVAL, "has_shared=1 needs s_gate, s_up and s_down");
+  if (!aligned(L->w_router, 16) || !aligned(L->w_gate, 16) || !aligned(L->w_up, 16) ||
+      !aligned(L->w_down, 16) || (L->router_bias && !aligned(L->router_bias, 4)))
+    return fail(MOE_Q4_EINVAL, "layer pointers must be 16-byte aligned (router_bias 4-byte)");
+  if (L->has_shared && (!aligned(L->s_gate, 16) || !aligned(L->s_up, 16) || !aligned(L->s_down, 16)))
+    return fail(MOE_Q4_EINVAL, "shared expert pointers must be 16-byte aligned");
+  return MOE_Q4_OK;
+}
+
+struct RouteWs {
+  size_t partials, counts, rank, total;
+};
+RouteWs route_ws(const moe_q4_layer* L, int32_t T, const moeq4::RouterSplit& sp) {
+  RouteWs w;
+  const size_t tiles = ((size_t)T + moeq4::kTopkTokensPerBlock - 1) / moeq4::kTopkTokensPerBlock;
+  w.partials = 0;
+  w.counts = w.partials + up256((size_t)sp.nsplit * T * L->n_experts * sizeof(float));
+  w.rank = w.counts + up256(tiles * L->n_experts * sizeof(int32_t));
+  w.total = w.rank + up256((size_t)T * L->top_k * sizeof(int32_t));
+  return w;
+}
+
+struct PrefillWs {
+  size_t h, o, total;
+};
+PrefillWs prefill_ws(const moe_q4_layer* L, int32_t T) {
+  PrefillWs w;
+  const size_t rows = (size_t)T * L->top_k + (L->has_shared ? (size_t)T : 0);
+  w.h = 0;
+  w.o = w.h + up256(rows * L->inter * 2);
+  w.total = w.o + up256((size_t)T * L->top_k * L->hidden * 2);
+  return w;
+}
+
+struct DecodeWs {
+  size_t ticket, partials, ids, w, qx, dx, sx, qh, dh, sh, total;
+};
+DecodeWs decode_ws(const moe_q4_layer* L, const moeq4::RouterSplit& sp) {
+  DecodeWs w;
+  const size_t ns = (size_t)L->top_k + (L->has_shared ? 1 : 0);
+  const size_t H = L->hidden, I = L->inter;
+  w.ticket = 0;
+  w.partials = 256;
+  w.ids = w.partials + up256((size_t)sp.nsplit * L->n_experts * 4);
+  w.w = w.ids + up256((size_t)L->top_k * 4);
+  w.qx = w.w + up256((size_t)L->top_k * 4);
+  w.dx = w.qx + up256(H);
+  w.sx = w.dx + up256(H / 32 * 4);
+  w.qh = w.sx + up256(H / 32 * 4);
+  w.dh = w.qh + up256(ns * I);
+  w.sh = w.dh + up256(ns * I / 32 * 4);
+  w.total = w.sh + up256(ns * I / 32 * 4);
+  return w;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MOE_Q4_OK;
+  if (!ws) return fail(MOE_Q4_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, 256)) return fail(MOE_Q4_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MOE_Q4_EWORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return MOE_Q4_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_q4_last_error(void) { return g_err; }
+
+size_t q4_packed_bytes(int64_t rows, int64_t K) {
+  if (rows < 0 || K <= 0 || K % 32) return 0;
+  return (size_t)rows * (size_t)(K / 32) * 18;
+}
+
+int q4_pack(const float* w, int64_t rows, int64_t K, void* packed, hipStream_t stream) {
+  if (rows < 0 || K <= 0 || K % 32) return fail(MOE_Q4_EINVAL, "q4_pack: rows=%lld K=%lld (K %% 32 == 0)", (long long)rows, (long long)K);
+  if (rows == 0) return MOE_Q4_OK;
+  if (!w || !packed) return fail(MOE_Q4_EINVAL, "q4_pack: NULL pointer");
+  if (!aligned(w, 16) || !aligned(packed, 2)) return fail(MOE_Q4_EINVAL, "q4_pack: w must be 16-byte and packed 2-byte aligned");
+  if (rows * (K / 32) > ((int64_t)1 << 40)) return fail(MOE_Q4_EINVAL, "q4_pack: too many blocks");
+  hipError_t e = moeq4::launch_q4_pack(w, rows, K, packed, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "q4_pack");
+}
+
+int q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d, hipStream_t stream) {
+  if (rows < 0 || K <= 0 || K % 32) return fail(MOE_Q4_EINVAL, "q8_quantize: rows=%lld K=%lld (K %% 32 == 0)", (long long)rows, (long long)K);
+  if (rows == 0) return MOE_Q4_OK;
+  if (!x || !q || !d) return fail(MOE_Q4_EINVAL, "q8_quantize: NULL pointer");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(d, 4)) return fail(MOE_Q4_EINVAL, "q8_quantize: x and q must be 16-byte aligned");
+  hipError_t e = moeq4::launch_q8_quantize(x, rows, K, q, d, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "q8_quantize");
+}
+
+size_t moe_q4_route_workspace_bytes(const moe_q4_layer* L, int32_t T) {
+  if (check_layer(L) != MOE_Q4_OK || T < 0) return 0;
+  return route_ws(L, T, moeq4::prefill_router_split(L->hidden)).total;
+}
+
+int moe_q4_route(const moe_q4_layer* L, const void* x, int32_t x_dtype, int32_t T,
+                 const moe_q4_routing* out, float* logits, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_Q4_EINVAL, "moe_q4_route: T=%d < 0", T);
+  if (x_dtype != MOE_Q4_F32 && x_dtype != MOE_Q4_BF16) return fail(MOE_Q4_EINVAL, "moe_q4_route: bad x_dtype %d", x_dtype);
+  if ((int64_t)T * L->top_k > 0x7fffffff) return fail(MOE_Q4_EINVAL, "moe_q4_route: T*k exceeds int32");
+  if (!out) return fail(MOE_Q4_EINVAL, "moe_q4_route: routing is NULL");
+  if (T == 0) {
+    // only the offsets have content: all zero (the scan over no tiles)
+    if (!out->expert_offsets) return fail(MOE_Q4_EINVAL, "moe_q4_route: expert_offsets is NULL");
+    hipError_t e = moeq4::launch_route_scan(nullptr, 0, L->n_experts, 0, out->expert_offsets, stream);
+    return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_route");
+  }
+  if (!x || !out->topk_ids || !out->topk_w || !out->expert_offsets || !out->perm || !out->inv_perm)
+    return fail(MOE_Q4_EINVAL, "moe_q4_route: NULL pointer");
+  if (!aligned(x, 16)) return fail(MOE_Q4_EINVAL, "moe_q4_route: x must be 16-byte aligned");
+  const moeq4::RouterSplit sp = moeq4::prefill_router_split(L->hidden);
+  const RouteWs W = route_ws(L, T, sp);
+  rc = check_ws(ws, ws_bytes, W.total);
+  if (rc) return rc;
+  float* partials = at<float>(ws, W.partials);
+  int32_t* counts = at<int32_t>(ws, W.counts);
+  int32_t* rank = at<int32_t>(ws, W.rank);
+  const int E = L->n_experts, k = L->top_k;
+  hipError_t e = moeq4::launch_router_partials(x, x_dtype == MOE_Q4_BF16, T, L->hidden, L->w_router, E, sp,
+                                               partials, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_q4_route/router");
+  e = moeq4::launch_topk_hist(partials, sp, L->router_bias, T, E, k, logits, out->topk_ids, out->topk_w,
+                              counts, rank, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_q4_route/topk");
+  const int tiles = (T + moeq4::kTopkTokensPerBlock - 1) / moeq4::kTopkTokensPerBlock;
+  e = moeq4::launch_route_scan(counts, tiles, E, T * k, out->expert_offsets, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_q4_route/scan");
+  e = moeq4::launch_route_scatter(out->topk_ids, rank, counts, T, k, E, out->perm, out->inv_perm, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_q4_route/scatter");
+  return MOE_Q4_OK;
+}
+
+size_t moe_q4_prefill_workspace_bytes(const moe_q4_layer* L, int32_t T) {
+  if (check_layer(L) != MOE_Q4_OK || T < 0) return 0;
+  return prefill_ws(L, T).total;
+}
+
+int moe_q4_prefill(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T,
+                   const moe_q4_routing* routing, float* y, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_Q4_EINVAL, "moe_q4_prefill: T=%d < 0", T);
+  if ((int64_t)T * L->top_k > 0x7fffffff) return fail(MOE_Q4_EINVAL, "moe_q4_prefill: T*k exceeds int32");
+  if (T == 0) return MOE_Q4_OK;
+  if (!x_bf16 || !routing || !y || !routing->topk_w || !routing->expert_offsets || !routing->perm ||
+      !routing->inv_perm)
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill: NULL pointer");
+  if (!aligned(x_bf16, 16) || !aligned(y, 16)) return fail(MOE_Q4_EINVAL, "moe_q4_prefill: x_bf16 and y must be 16-byte aligned");
+  const PrefillWs W = prefill_ws(L, T);
+  rc = check_ws(ws, ws_bytes, W.total);
+  if (rc) return rc;
+  moeq4::PrefillArgs a;
+  a.x = x_bf16;
+  a.T = T;
+  a.H = L->hidden;
+  a.I = L->inter;
+  a.E = L->n_experts;
+  a.k = L->top_k;
+  a.has_shared = L->has_shared;
+  a.perm = routing->perm;
+  a.offsets = routing->expert_offsets;
+  a.inv_perm = routing->inv_perm;
+  a.topk_w = routing->topk_w;
+  a.w_gate = static_cast<const uint8_t*>(L->w_gate);
+  a.w_up = static_cast<const uint8_t*>(L->w_up);
+  a.w_down = static_cast<const uint8_t*>(L->w_down);
+  a.s_gate = static_cast<const uint8_t*>(L->s_gate);
+  a.s_up = static_cast<const uint8_t*>(L->s_up);
+  a.s_down = static_cast<const uint8_t*>(L->s_down);
+  a.h = at<uint16_t>(ws, W.h);
+  a.o_perm = at<uint16_t>(ws, W.o);
+  a.y = y;
+  hipError_t e = moeq4::launch_prefill(a, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_prefill");
+}
+
+size_t moe_q4_decode_workspace_bytes(const moe_q4_layer* L) {
+  if (check_layer(L) != MOE_Q4_OK) return 0;
+  return decode_ws(L, moeq4::decode_router_split(L->hidden, L->n_experts)).total;
+}
+
+int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_decode_trace* tr,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!x || !y) return fail(MOE_Q4_EINVAL, "moe_q4_decode: NULL pointer");
+  if (!aligned(x, 16) || !aligned(y, 4)) return fail(MOE_Q4_EINVAL, "moe_q4_decode: x must be 16-byte aligned");
+  const moeq4::RouterSplit sp = moeq4::decode_router_split(L->hidden, L->n_experts);
+  if ((size_t)sp.cw * L->n_experts > 1024)
+    return fail(MOE_Q4_EINVAL, "moe_q4_decode: hidden=%d with n_experts=%d exceeds the router block", L->hidden, L->n_experts);
+  const DecodeWs W = decode_ws(L, sp);
+  rc = check_ws(ws, ws_bytes, W.total);
+  if (rc) return rc;
+  if (tr && ((tr->qx && !aligned(tr->qx, 16))))
+    return fail(MOE_Q4_EINVAL, "moe_q4_decode: trace qx must be 16-byte aligned");
+  moeq4::DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x;
+  a.y = y;
+  a.H = L->hidden;
+  a.I = L->inter;
+  a.E = L->n_experts;
+  a.k = L->top_k;
+  a.has_shared = L->has_shared;
+  a.w_router = L->w_router;
+  a.bias = L->router_bias;
+  a.w_gate = static_cast<const uint8_t*>(L->w_gate);
+  a.w_up = static_cast<const uint8_t*>(L->w_up);
+  a.w_down = static_cast<const uint8_t*>(L->w_down);
+  a.s_gate = static_cast<const uint8_t*>(L->s_gate);
+  a.s_up = static_cast<const uint8_t*>(L->s_up);
+  a.s_down = static_cast<const uint8_t*>(L->s_down);
+  a.ticket = at<uint32_t>(ws, W.ticket);
+  a.partials = at<float>(ws, W.partials);
+  a.ids = at<int32_t>(ws, W.ids);
+  a.w = at<float>(ws, W.w);
+  a.qx = at<int8_t>(ws, W.qx);
+  a.dx = at<float>(ws, W.dx);
+  a.sx = at<int32_t>(ws, W.sx);
+  a.qh = at<int8_t>(ws, W.qh);
+  a.dh = at<float>(ws, W.dh);
+  a.sh = at<int32_t>(ws, W.sh);
+  if (tr) {
+    a.t_logits = tr->logits;
+    a.t_ids = tr->ids;
+    a.t_w = tr->w;
+    a.t_qx = tr->qx;
+    a.t_dx = tr->dx;
+    a.t_qh = tr->qh;
+    a.t_dh = tr->dh;
+  }
+  hipError_t e = moeq4::launch_decode(a, sp, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_decode");
+}
+
+int moe_q4_w4a8_gemv(const void* W, int32_t N, int32_t K, const int8_t* qa, const float* da,
+                     int32_t* dots, float* out, hipStream_t stream) {
+  if (N < 0 || K <= 0 || K % 32 || K > kMaxDim)
+    return fail(MOE_Q4_EINVAL, "moe_q4_w4a8_gemv: N=%d K=%d (K a multiple of 32 <= %d)", N, K, kMaxDim);
+  if (N == 0) return MOE_Q4_OK;
+  if (!W || !qa || !da || !out) return fail(MOE_Q4_EINVAL, "moe_q4_w4a8_gemv: NULL pointer");
+  if (!aligned(W, 2) || !aligned(qa, 4) || !aligned(da, 4))
+    return fail(MOE_Q4_EINVAL, "moe_q4_w4a8_gemv: W 2-byte, qa/da 4-byte alignment");
+  hipError_t e = moeq4::launch_w4a8_gemv(static_cast<const uint8_t*>(W), N, K, qa, da, dots, out, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_w4a8_gemv");
+}
+
+int moe_q4_rmsnorm(const float* y, int32_t T, int32_t H, float eps, float* out_f32,
+                   uint16_t* out_bf16, hipStream_t stream) {
+  if (T < 0 || H <= 0 || H % 32 || H > kMaxDim)
+    return fail(MOE_Q4_EINVAL, "moe_q4_rmsnorm: T=%d H=%d (H a multiple of 32 <= %d)", T, H, kMaxDim);
+  if (T == 0) return MOE_Q4_OK;
+  if (!y || (!out_f32 && !out_bf16)) return fail(MOE_Q4_EINVAL, "moe_q4_rmsnorm: NULL pointer");
+  if (!aligned(y, 16)) return fail(MOE_Q4_EINVAL, "moe_q4_rmsnorm: y must be 16-byte aligned");
+  hipError_t e = moeq4::launch_rmsnorm(y, T, H, eps, out_f32, out_bf16, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_rmsnorm");
+}
+
+}  // extern "C"

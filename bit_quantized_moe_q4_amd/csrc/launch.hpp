@@ -1,0 +1,97 @@
+// launch.hpp -- host-side launchers of the HIP kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeq4 {
+
+hipError_t launch_q4_pack(const float* w, int64_t rows, int64_t K, void* packed,
+                          hipStream_t stream);
+hipError_t launch_q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d,
+                              hipStream_t stream);
+
+// Router split geometry: the chunk tree (nc = H/32 leaves padded to the power
+// of two m) is cut into nsplit aligned subtrees of cw leaves each.
+struct RouterSplit {
+  int nc, m, cw, nsplit;
+};
+RouterSplit prefill_router_split(int H);
+RouterSplit decode_router_split(int H, int E);
+
+// Prefill routing.
+hipError_t launch_router_partials(const void* x, int x_bf16, int T, int H, const float* w_router,
+                                  int E, const RouterSplit& sp, float* partials,
+                                  hipStream_t stream);
+hipError_t launch_topk_hist(const float* partials, const RouterSplit& sp, const float* bias,
+                            int T, int E, int k, float* logits_out, int32_t* ids, float* w,
+                            int32_t* counts_w, int32_t* rank, hipStream_t stream);
+hipError_t launch_route_scan(int32_t* counts_w, int n_tiles, int E, int total,
+                             int32_t* offsets, hipStream_t stream);
+hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* base_w,
+                                int T, int k, int E, int32_t* perm, int32_t* inv_perm,
+                                hipStream_t stream);
+constexpr int kTopkTokensPerBlock = 64;
+
+// Prefill expert FFN.
+struct PrefillArgs {
+  const uint16_t* x;        // [T][H] bf16
+  int T, H, I, E, k, has_shared;
+  const int32_t* perm;      // [T*k]
+  const int32_t* offsets;   // [E+1]
+  const int32_t* inv_perm;  // [T*k]
+  const float* topk_w;      // [T][k]
+  const uint8_t* w_gate;    // [E][I][H/32*18]
+  const uint8_t* w_up;
+  const uint8_t* w_down;    // [E][H][I/32*18]
+  const uint8_t* s_gate;
+  const uint8_t* s_up;
+  const uint8_t* s_down;
+  uint16_t* h;              // [(T*k + T*S)][I] bf16
+  uint16_t* o_perm;         // [T*k][H] bf16
+  float* y;                 // [T][H] fp32
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Decode.
+struct DecodeArgs {
+  const float* x;           // [H]
+  float* y;                 // [H]
+  int H, I, E, k, has_shared;
+  const float* w_router;
+  const float* bias;
+  const uint8_t* w_gate;
+  const uint8_t* w_up;
+  const uint8_t* w_down;
+  const uint8_t* s_gate;
+  const uint8_t* s_up;
+  const uint8_t* s_down;
+  // workspace pieces
+  float* partials;          // [nsplit][E]
+  uint32_t* ticket;         // one counter, zero between calls
+  int32_t* ids;             // [k]
+  float* w;                 // [k]
+  int8_t* qx;               // [H]
+  float* dx;                // [H/32]
+  int32_t* sx;              // [H/32] sum of the int8 codes of each block
+  int8_t* qh;               // [k+S][I]
+  float* dh;                // [k+S][I/32]
+  int32_t* sh;              // [k+S][I/32]
+  // optional trace
+  float* t_logits;
+  int32_t* t_ids;
+  float* t_w;
+  int8_t* t_qx;
+  float* t_dx;
+  int8_t* t_qh;
+  float* t_dh;
+};
+hipError_t launch_decode(const DecodeArgs& a, const RouterSplit& sp, hipStream_t stream);
+
+hipError_t launch_w4a8_gemv(const uint8_t* W, int N, int K, const int8_t* qa, const float* da,
+                            int32_t* dots, float* out, hipStream_t stream);
+
+hipError_t launch_rmsnorm(const float* y, int T, int H, float eps, float* out_f32,
+                          uint16_t* out_bf16, hipStream_t stream);
+
+}  // namespace moeq4

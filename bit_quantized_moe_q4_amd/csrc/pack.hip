@@ -1,0 +1,103 @@
+// pack.hip -- Q4_0 weight packing and 8-bit activation quantisation.
+//
+// Formats ("A 35B Hybrid-Attention Mixture-of-Experts Model on a 6GB 2011
+// GPU", technical summary, Methodology 2: group-wise symmetric 4-bit Q4_0
+// weights, 8-bit activations on the decode path); the exact block layout and
+// rounding rules are the ones stated in moe_q4.h.
+//
+// Both kernels are one thread per 32-element block: packing runs once per
+// weight load and activation quantisation of a decode step is 64 blocks, so
+// neither is on a bandwidth-critical path.
+#include "launch.hpp"
+#include "device_math.hpp"
+
+namespace moeq4 {
+
+__global__ void __launch_bounds__(256) q4_pack_kernel(const float* __restrict__ w, int64_t nblocks,
+                                                      uint16_t* __restrict__ out) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nblocks) return;
+  const float4* src = reinterpret_cast<const float4*>(w + i * BLK);
+  float v[BLK];
+#pragma unroll
+  for (int c = 0; c < BLK / 4; c++) {
+    float4 t = src[c];
+    v[4 * c] = t.x; v[4 * c + 1] = t.y; v[4 * c + 2] = t.z; v[4 * c + 3] = t.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < BLK; j++) amax = fmaxf(amax, fabsf(v[j]));
+  uint16_t dh = f32_to_f16_bits(amax / 7.0f);
+  float df = f16_bits_to_f32(dh);
+  uint32_t q[BLK];
+#pragma unroll
+  for (int j = 0; j < BLK; j++) {
+    float t = roundf(v[j] / df);
+    t = fminf(fmaxf(t, -8.0f), 7.0f);
+    q[j] = (df == 0.0f) ? 8u : (uint32_t)((int)t + 8);
+  }
+  // 18 bytes = 9 little-endian halfwords: d, then bytes (q_j | q_{j+16} << 4)
+  uint16_t* dst = out + i * (Q4B / 2);
+  dst[0] = dh;
+#pragma unroll
+  for (int p = 0; p < 8; p++) {
+    uint32_t lo = q[2 * p] | (q[2 * p + 16] << 4);
+    uint32_t hi = q[2 * p + 1] | (q[2 * p + 17] << 4);
+    dst[1 + p] = (uint16_t)(lo | (hi << 8));
+  }
+}
+
+__global__ void __launch_bounds__(256) q8_quantize_kernel(const float* __restrict__ x,
+                                                          int64_t nblocks, int8_t* __restrict__ q,
+                                                          float* __restrict__ d) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nblocks) return;
+  const float4* src = reinterpret_cast<const float4*>(x + i * BLK);
+  float v[BLK];
+#pragma unroll
+  for (int c = 0; c < BLK / 4; c++) {
+    float4 t = src[c];
+    v[4 * c] = t.x; v[4 * c + 1] = t.y; v[4 * c + 2] = t.z; v[4 * c + 3] = t.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < BLK; j++) amax = fmaxf(amax, fabsf(v[j]));
+  float dd = amax / 127.0f;
+  d[i] = dd;
+  uint32_t packed[BLK / 4];
+#pragma unroll
+  for (int c = 0; c < BLK / 4; c++) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      int qi = (dd == 0.0f) ? 0 : (int)roundf(v[4 * c + b] / dd);
+      word |= ((uint32_t)qi & 0xffu) << (8 * b);
+    }
+    packed[c] = word;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(q + i * BLK);
+  dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+}
+
+hipError_t launch_q4_pack(const float* w, int64_t rows, int64_t K, void* packed,
+                          hipStream_t stream) {
+  int64_t nblocks = rows * (K / BLK);
+  if (nblocks == 0) return hipSuccess;
+  int64_t grid = (nblocks + 255) / 256;
+  hipLaunchKernelGGL(q4_pack_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, w, nblocks,
+                     static_cast<uint16_t*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d,
+                              hipStream_t stream) {
+  int64_t nblocks = rows * (K / BLK);
+  if (nblocks == 0) return hipSuccess;
+  int64_t grid = (nblocks + 255) / 256;
+  hipLaunchKernelGGL(q8_quantize_kernel, dim3((uint32_t)grid), dim3(256), 0, stream, x, nblocks,
+                     q, d);
+  return hipGetLastError();
+}
+
+}  // namespace moeq4

@@ -1,0 +1,430 @@
+// router.hip -- prefill routing: router logits, top-k + softmax weights,
+// expert histogram, segment offsets and the token permutation.
+//
+// The pages route each prompt token to experts before the grouped 4-bit GEMM
+// ("A 35B Hybrid-Attention Mixture-of-Experts Model on a 6GB 2011 GPU",
+// technical summary, Methodology 1) and give no routing arithmetic; the
+// library's fp32 programs (moe_q4.h) are reproduced here bit for bit:
+//   logit = pairwise tree over 32-wide chunks of a sequential FMA chain,
+//   then + bias; top-k by (logit desc, index asc); weights by the fixed exp.
+// The companion report ("A Modern Multimodal Assistant on a 6 GB 2011 GPU",
+// abstract) is the reason every tie and summation order is pinned.
+//
+// Kernels (one stream, no host round trip):
+//   router_partials  tiled fp32 VALU product, 64 tokens x 64 experts per
+//                    block, one aligned subtree of cw chunks per grid z
+//   topk_hist        finishes the chunk tree, top-k, weights, and a
+//                    wavefront-ballot histogram of the block's 64 tokens with
+//                    each assignment's stable rank inside the block
+//   route_scan       per-expert prefix over blocks -> segment bases, offsets
+//   route_scatter    perm / inv_perm
+#include "launch.hpp"
+#include "device_math.hpp"
+
+namespace moeq4 {
+
+RouterSplit prefill_router_split(int H) {
+  RouterSplit s;
+  s.nc = H / BLK;
+  s.m = 1;
+  while (s.m < s.nc) s.m <<= 1;
+  s.cw = s.m < 8 ? s.m : 8;
+  s.nsplit = s.m / s.cw;
+  return s;
+}
+
+// ---------------------------------------------------------------- partials
+constexpr int RT = 64;   // tokens per block
+constexpr int RE = 64;   // experts per block
+
+template <int CW>
+struct Log2 { static constexpr int v = 1 + Log2<CW / 2>::v; };
+template <>
+struct Log2<1> { static constexpr int v = 0; };
+
+template <bool BF16, int CW>
+__global__ void __launch_bounds__(256) router_partials_kernel(const void* __restrict__ xv, int T,
+                                                              int H, const float* __restrict__ Wr,
+                                                              int E, int nc,
+                                                              float* __restrict__ partials) {
+  constexpr int L = Log2<CW>::v;
+  __shared__ float xs[BLK][RT + 4];   // [h][token], rows 16-byte aligned
+  __shared__ float wsh[BLK][RE + 4];  // [h][expert]
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  const int e0 = blockIdx.x * RE, t0 = blockIdx.y * RT, split = blockIdx.z;
+  const bool vecw = (E % 4) == 0;
+
+  // global -> register staging of one chunk: 8 x values and 8 W values per thread
+  const int xt = tid / 4, xh = (tid % 4) * 8;      // token row, h offset
+  const int wr = tid / 8, we = (tid % 8) * 8;      // W row, expert offset
+  float px[8], pw[8];
+  auto fetch = [&](int c) {
+    const int h0 = c * BLK;
+    const int t = t0 + xt;
+    if (t < T) {
+      if (BF16) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(
+            static_cast<const uint16_t*>(xv) + (size_t)t * H + h0 + xh);
+        const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          px[2 * i] = bf16_bits_to_f32(r[i] & 0xffffu);
+          px[2 * i + 1] = bf16_bits_to_f32(r[i] >> 16);
+        }
+      } else {
+        const float* src = static_cast<const float*>(xv) + (size_t)t * H + h0 + xh;
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 b = *reinterpret_cast<const float4*>(src + 4);
+        px[0] = a.x; px[1] = a.y; px[2] = a.z; px[3] = a.w;
+        px[4] = b.x; px[5] = b.y; px[6] = b.z; px[7] = b.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) px[i] = 0.0f;
+    }
+    const float* wsrc = Wr + (size_t)(h0 + wr) * E;
+    const int e = e0 + we;
+    if (vecw && e + 8 <= E) {
+      const float4 a = *reinterpret_cast<const float4*>(wsrc + e);
+      const float4 b = *reinterpret_cast<const float4*>(wsrc + e + 4);
+      pw[0] = a.x; pw[1] = a.y; pw[2] = a.z; pw[3] = a.w;
+      pw[4] = b.x; pw[5] = b.y; pw[6] = b.z; pw[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) pw[i] = (e + i < E) ? wsrc[e + i] : 0.0f;
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; i++) xs[xh + i][xt] = px[i];
+    *reinterpret_cast<float4*>(&wsh[wr][we]) = make_float4(pw[0], pw[1], pw[2], pw[3]);
+    *reinterpret_cast<float4*>(&wsh[wr][we + 4]) = make_float4(pw[4], pw[5], pw[6], pw[7]);
+  };
+
+  float st[L + 1][16];
+  const int cbase = split * CW;
+  if (cbase < nc) fetch(cbase);
+#pragma unroll
+  for (int cl = 0; cl < CW; cl++) {
+    const int c = cbase + cl;
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[i] = 0.0f;
+    if (c < nc) {                         // padded leaves stay +0.0
+      __syncthreads();
+      stash();
+      __syncthreads();
+      if (cl + 1 < CW && c + 1 < nc) fetch(c + 1);
+#pragma unroll 8
+      for (int h = 0; h < BLK; h++) {
+        const float4 a = *reinterpret_cast<const float4*>(&xs[h][ty * 4]);
+        const float4 b = *reinterpret_cast<const float4*>(&wsh[h][tx * 4]);
+        const float av[4] = {a.x, a.y, a.z, a.w};
+        const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) acc[i * 4 + j] = __builtin_fmaf(av[i], bv[j], acc[i * 4 + j]);
+      }
+    }
+    // binary-counter merge: leaf cl joins the pending subtrees of equal size
+    int lvl = 0;
+#pragma unroll
+    for (int b = 0; b < L; b++) {
+      if (((cl >> b) & 1) == 0) break;
+      lvl = b + 1;
+    }
+#pragma unroll
+    for (int b = 0; b < L; b++) {
+      if (b < lvl) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) acc[i] = st[b][i] + acc[i];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b <= L; b++)
+      if (b == lvl) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) st[b][i] = acc[i];
+      }
+  }
+  float* out = partials + (size_t)split * T * E;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) out[(size_t)t * E + e] = st[L][i * 4 + j];
+    }
+  }
+}
+
+hipError_t launch_router_partials(const void* x, int x_bf16, int T, int H, const float* w_router,
+                                  int E, const RouterSplit& sp, float* partials,
+                                  hipStream_t stream) {
+  dim3 grid((E + RE - 1) / RE, (T + RT - 1) / RT, sp.nsplit);
+#define MOEQ4_RP(BF, CWV)                                                                   \
+  hipLaunchKernelGGL((router_partials_kernel<BF, CWV>), grid, dim3(256), 0, stream, x, T, H, \
+                     w_router, E, sp.nc, partials)
+#define MOEQ4_RP_CW(BF)                      \
+  switch (sp.cw) {                           \
+    case 1: MOEQ4_RP(BF, 1); break;          \
+    case 2: MOEQ4_RP(BF, 2); break;          \
+    case 4: MOEQ4_RP(BF, 4); break;          \
+    default: MOEQ4_RP(BF, 8); break;         \
+  }
+  if (x_bf16) {
+    MOEQ4_RP_CW(true)
+  } else {
+    MOEQ4_RP_CW(false)
+  }
+#undef MOEQ4_RP_CW
+#undef MOEQ4_RP
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- top-k
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+
+// Finish one logit: pairwise tree over the nsplit (a power of two <= 64)
+// aligned subtree partials, by the same binary-counter merge as above.
+__device__ __forceinline__ float finish_logit(const float* __restrict__ partials, size_t stride,
+                                              int nsplit, size_t idx, const float* bias, int e) {
+  float st[7];
+#pragma unroll
+  for (int s = 0; s < 64; s++) {
+    if (s < nsplit) {
+      float a = partials[(size_t)s * stride + idx];
+      int lvl = 0;
+#pragma unroll
+      for (int b = 0; b < 6; b++) {
+        if (((s >> b) & 1) == 0) break;
+        lvl = b + 1;
+      }
+#pragma unroll
+      for (int b = 0; b < 6; b++)
+        if (b < lvl) a = st[b] + a;
+#pragma unroll
+      for (int b = 0; b < 7; b++)
+        if (b == lvl) st[b] = a;
+    }
+  }
+  const int top = 31 - __builtin_clz((unsigned)nsplit);   // log2(nsplit)
+  float l = st[0];
+#pragma unroll
+  for (int b = 1; b < 7; b++)
+    if (b == top) l = st[b];
+  if (bias) l = l + bias[e];
+  return l;
+}
+
+// Wave-wide (value desc, index asc) argmax.
+__device__ __forceinline__ void wave_argmax(float& v, int& e) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float ov = __shfl_xor(v, m, 64);
+    const int oe = __shfl_xor(e, m, 64);
+    if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
+  }
+}
+
+// Top-k of one token's logits held as lane + 64*j.  Returns, in lane s < k,
+// the s-th pick (my_v, my_e) and its weight my_w.
+template <int NJ>
+__device__ __forceinline__ void wave_topk(const float (&lv)[NJ], int E, int k, float& my_v,
+                                          int& my_e, float& my_w) {
+  const int lane = threadIdx.x % 64;
+  uint32_t taken = 0;
+  my_v = 0.0f;
+  my_e = -1;
+  for (int s = 0; s < k; s++) {
+    float bv = -__builtin_inff();
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      const int e = lane + 64 * j;
+      if (e < E && !((taken >> j) & 1u) && (be == 0x7fffffff || lv[j] > bv)) { bv = lv[j]; be = e; }
+    }
+    wave_argmax(bv, be);
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == s) { my_v = bv; my_e = be; }
+  }
+  // weights: m = l_0, e_s = exp(l_s - m), S = e_0 + e_1 + ... left to right
+  const float l0 = __shfl(my_v, 0, 64);
+  const float ex = (lane < k) ? exp_p(my_v - l0) : 0.0f;
+  float S = __shfl(ex, 0, 64);
+  for (int s = 1; s < k; s++) S = S + __shfl(ex, s, 64);
+  my_w = ex / S;
+}
+
+template <int NJ>
+__global__ void __launch_bounds__(256) topk_hist_kernel(
+    const float* __restrict__ partials, int nsplit, const float* __restrict__ bias, int T, int E,
+    int k, float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ w,
+    int32_t* __restrict__ counts_w, int32_t* __restrict__ rank) {
+  constexpr int TPB = kTopkTokensPerBlock;
+  __shared__ int32_t ids_l[TPB][kMaxK];
+  __shared__ uint32_t mask_l[TPB][kMaxE / 32 + 1];
+  __shared__ unsigned long long bal_l[kMaxE];
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int t0 = blockIdx.x * TPB;
+  const size_t stride = (size_t)T * E;
+
+  for (int q = 0; q < TPB / 4; q++) {
+    const int tl = wave * (TPB / 4) + q;
+    const int t = t0 + tl;
+    if (t >= T) break;                    // uniform per wave
+    float lv[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; j++) {
+      const int e = lane + 64 * j;
+      lv[j] = 0.0f;
+      if (e < E) {
+        lv[j] = finish_logit(partials, stride, nsplit, (size_t)t * E + e, bias, e);
+        if (logits_out) logits_out[(size_t)t * E + e] = lv[j];
+      }
+    }
+    float my_v, my_w;
+    int my_e;
+    wave_topk<NJ>(lv, E, k, my_v, my_e, my_w);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = my_e;
+      w[(size_t)t * k + lane] = my_w;
+      ids_l[tl][lane] = my_e;
+    }
+  }
+  // per-block expert histogram: bit e of mask_l[tl] says token tl picked e
+  const int nwords = (E + 31) / 32;
+  for (int i = threadIdx.x; i < TPB * (kMaxE / 32 + 1); i += blockDim.x)
+    (&mask_l[0][0])[i] = 0u;
+  __syncthreads();
+  if (threadIdx.x < TPB && t0 + (int)threadIdx.x < T) {
+    for (int s = 0; s < k; s++) {
+      const int e = ids_l[threadIdx.x][s];
+      mask_l[threadIdx.x][e >> 5] |= 1u << (e & 31);
+    }
+  }
+  __syncthreads();
+  // one ballot per expert over the 64 tokens of the block (lane = token)
+  for (int wd = wave; wd < nwords; wd += 4) {
+    const uint32_t word = mask_l[lane][wd];
+    for (int b = 0; b < 32; b++) {
+      const int e = wd * 32 + b;
+      if (e >= E) break;
+      const unsigned long long bal = __ballot((word >> b) & 1u);
+      if (lane == 0) {
+        bal_l[e] = bal;
+        counts_w[(size_t)blockIdx.x * E + e] = (int32_t)__popcll(bal);
+      }
+    }
+  }
+  __syncthreads();
+  // stable rank of each assignment inside the block: earlier tokens first
+  if (threadIdx.x < TPB && t0 + (int)threadIdx.x < T) {
+    const int tl = threadIdx.x;
+    const unsigned long long below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
+    for (int s = 0; s < k; s++) {
+      const int e = ids_l[tl][s];
+      rank[(size_t)(t0 + tl) * k + s] = (int32_t)__popcll(bal_l[e] & below);
+    }
+  }
+}
+
+hipError_t launch_topk_hist(const float* partials, const RouterSplit& sp, const float* bias,
+                            int T, int E, int k, float* logits_out, int32_t* ids, float* w,
+                            int32_t* counts_w, int32_t* rank, hipStream_t stream) {
+  dim3 grid((T + kTopkTokensPerBlock - 1) / kTopkTokensPerBlock);
+  const int nj = (E + 63) / 64;
+#define MOEQ4_TK(NJV)                                                                        \
+  hipLaunchKernelGGL((topk_hist_kernel<NJV>), grid, dim3(256), 0, stream, partials, sp.nsplit, \
+                     bias, T, E, k, logits_out, ids, w, counts_w, rank)
+  if (nj <= 1) MOEQ4_TK(1);
+  else if (nj <= 2) MOEQ4_TK(2);
+  else if (nj <= 4) MOEQ4_TK(4);
+  else if (nj <= 8) MOEQ4_TK(8);
+  else MOEQ4_TK(16);
+#undef MOEQ4_TK
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- scan
+// counts_w [nt][E] (per block, per expert) -> in place: base of block b's
+// first assignment to expert e inside perm.  offsets [E+1].
+__global__ void __launch_bounds__(1024) route_scan_kernel(int32_t* __restrict__ counts_w, int nt,
+                                                          int E, int total,
+                                                          int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t tot[kMaxE + 1];
+  const int tpe = blockDim.x / E;          // threads per expert (>= 1)
+  const int e = threadIdx.x % E, g = threadIdx.x / E;
+  const bool active = g < tpe;
+  const int per = (nt + tpe - 1) / tpe;
+  const int b0 = g * per, b1 = min(nt, b0 + per);
+  int run = 0;
+  if (active)
+    for (int b = b0; b < b1; b++) run += counts_w[(size_t)b * E + e];
+  part[threadIdx.x] = run;
+  __syncthreads();
+  // exclusive prefix of the groups of one expert; expert totals
+  int before = 0;
+  if (active) {
+    for (int q = 0; q < g; q++) before += part[q * E + e];
+    if (g == tpe - 1) tot[e] = before + run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {                  // E <= 1024: short serial scan
+    int acc = 0;
+    for (int i = 0; i < E; i++) { const int c = tot[i]; tot[i] = acc; acc += c; }
+    tot[E] = acc;
+  }
+  __syncthreads();
+  if (active) {
+    int acc = tot[e] + before;
+    for (int b = b0; b < b1; b++) {
+      const int c = counts_w[(size_t)b * E + e];
+      counts_w[(size_t)b * E + e] = acc;
+      acc += c;
+    }
+  }
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) offsets[i] = (i == E) ? total : tot[i];
+}
+
+hipError_t launch_route_scan(int32_t* counts_w, int n_tiles, int E, int total, int32_t* offsets,
+                             hipStream_t stream) {
+  const int threads = (1024 / E) * E;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(threads), 0, stream, counts_w, n_tiles, E,
+                     total, offsets);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- scatter
+__global__ void __launch_bounds__(256) route_scatter_kernel(const int32_t* __restrict__ ids,
+                                                            const int32_t* __restrict__ rank,
+                                                            const int32_t* __restrict__ base_w,
+                                                            int T, int k, int E,
+                                                            int32_t* __restrict__ perm,
+                                                            int32_t* __restrict__ inv_perm) {
+  const int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (f >= (int64_t)T * k) return;
+  const int t = (int)(f / k);
+  const int e = ids[f];
+  const int pos = base_w[(size_t)(t / kTopkTokensPerBlock) * E + e] + rank[f];
+  if (pos < 0 || (int64_t)pos >= (int64_t)T * k) return;   // unreachable for valid ranks
+  perm[pos] = (int32_t)f;
+  inv_perm[f] = pos;
+}
+
+hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* base_w,
+                                int T, int k, int E, int32_t* perm, int32_t* inv_perm,
+                                hipStream_t stream) {
+  const int64_t n = (int64_t)T * k;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream,
+                     ids, rank, base_w, T, k, E, perm, inv_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moeq4

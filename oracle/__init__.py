@@ -155,14 +155,28 @@ def q4_row_bytes(K: int) -> int:
     return (K // BLK) * Q4_BYTES
 
 
-def q4_pack(w, lib=None) -> np.ndarray:
-    """``orc_q4_pack``: fp32 [..., rows, K] -> uint8 [..., rows, K/32*18]."""
+def q4_pack(w, lib=None, threads: int = 1) -> np.ndarray:
+    """``orc_q4_pack``: fp32 [..., rows, K] -> uint8 [..., rows, K/32*18].
+
+    ``threads`` > 1 packs disjoint row ranges concurrently (each call is the
+    same single-threaded C function; rows are independent)."""
     w = _c(w, np.float32)
     K = w.shape[-1]
     assert K % BLK == 0
     rows = w.size // K
     out = np.empty(w.shape[:-1] + (q4_row_bytes(K),), dtype=np.uint8)
-    (lib or load()).orc_q4_pack(_p(w), rows, K, _p(out))
+    lib = lib or load()
+    w2, o2 = w.reshape(rows, K), out.reshape(rows, q4_row_bytes(K))
+    if threads <= 1 or rows < 2 * threads:
+        lib.orc_q4_pack(_p(w2), rows, K, _p(o2))
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    step = (rows + threads - 1) // threads
+    def job(r0):
+        r1 = min(rows, r0 + step)
+        lib.orc_q4_pack(_p(w2[r0:r1]), r1 - r0, K, _p(o2[r0:r1]))
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(job, range(0, rows, step)))
     return out
 
 
@@ -256,9 +270,9 @@ class PackedLayer:
 
     @classmethod
     def from_float(cls, w_router, bias, gate, up, down, s_gate=None, s_up=None,
-                   s_down=None, k=1, lib=None):
+                   s_down=None, k=1, lib=None, threads: int = 1):
         """Pack fp32 expert weights with the oracle's own ``orc_q4_pack``."""
-        pk = lambda a: None if a is None else q4_pack(a, lib=lib)  # noqa: E731
+        pk = lambda a: None if a is None else q4_pack(a, lib=lib, threads=threads)  # noqa: E731
         return cls(w_router, bias, pk(gate), pk(up), pk(down), pk(s_gate),
                    pk(s_up), pk(s_down), k=k)
 

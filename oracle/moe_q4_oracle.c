@@ -227,8 +227,8 @@ void orc_q8_quantize(const float *x, int64_t rows, int64_t K, int8_t *q, float *
 /* exp_p: the fp32 exponential both sides evaluate (it feeds int8 codes).    */
 /* Method: Cody & Waite additive range reduction (W. J. Cody, W. Waite,      */
 /* "Software Manual for the Elementary Functions", 1980):                    */
-/*   n = rint(x * log2(e)),  r = x - n*ln2  (ln2 split in a hi part with 16  */
-/*   significant bits, so n*hi is exact for |n| < 2^8, plus a lo part),      */
+/*   n = rint(x * log2(e)),  r = x - n*ln2  (ln2 split in a hi part with 15  */
+/*   significant bits, so n*hi is exact for |n| < 2^9, plus a lo part),      */
 /*   exp(x) = 2^n * exp(r),  |r| <= ln2/2,                                   */
 /* and exp(r) by its Taylor polynomial of degree 7 (coefficients 1/i!        */
 /* rounded to fp32) evaluated by Horner's rule with fused multiply-adds.     */
@@ -236,7 +236,7 @@ void orc_q8_quantize(const float *x, int64_t rows, int64_t K, int8_t *q, float *
 /* fp32 subnormal and exp(89) is above FLT_MAX, so ldexpf gives 0 and +inf.  */
 /* ------------------------------------------------------------------------ */
 #define EXPP_LOG2E 1.44269502162933349609375f        /* fp32(1/ln 2)          */
-#define EXPP_LN2_HI 0.693145751953125f               /* ln 2 to 16 bits      */
+#define EXPP_LN2_HI 0.693145751953125f               /* ln 2 to 15 bits      */
 #define EXPP_LN2_LO 1.428606765330187045e-06f        /* fp32(ln 2 - LN2_HI)  */
 
 float orc_exp_p(float x)

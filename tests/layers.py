@@ -1,0 +1,33 @@
+"""Test-side construction of one layer for both the oracle and the library.
+
+The same seeded fp32 weights feed the oracle's own packing (host) and the
+library's q4_pack (device); the packed bytes of the two are compared by the
+pack parity test, each side then runs on its own copy.
+"""
+import numpy as np
+import torch
+
+import moe_synth
+import oracle
+from bit_quantized_moe_q4_amd.synth_layer import device_layer
+
+
+def both_layers(cfg, layer=0, threads=16):
+    W = moe_synth.expert_weights(cfg, layer, threads=threads)
+    Wr = moe_synth.router(cfg, layer)
+    bias = moe_synth.router_bias(cfg, layer)
+    ol = oracle.PackedLayer.from_float(Wr, bias, W["gate"], W["up"], W["down"], W["s_gate"],
+                                       W["s_up"], W["s_down"], k=cfg.k, threads=threads)
+    gl = device_layer(cfg, layer, weights=W)
+    return ol, gl
+
+
+def tokens(cfg, step=0, T=None, layer=0):
+    """Host fp32 tokens, their bf16 bits, the bf16 values widened to fp32, and
+    the device tensors (fp32, bf16)."""
+    x = moe_synth.tokens(cfg, step=step, T=T, layer=layer)
+    bits = moe_synth.to_bf16_bits(x)
+    xw = moe_synth.bf16_bits_to_f32(bits)
+    xd = torch.from_numpy(x).cuda()
+    xbd = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    return x, bits, xw, xd, xbd

@@ -1,0 +1,150 @@
+"""The C-ABI library without a GPU: exported symbols and host-side checks.
+
+Nothing here launches a kernel: every call below fails (or returns) in the
+library's argument checks before anything is enqueued.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_q4.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from bit_quantized_moe_q4_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from bit_quantized_moe_q4_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_header_declares_the_api():
+    names = header_functions()
+    for n in ["q4_packed_bytes", "q4_pack", "q8_quantize", "moe_q4_route", "moe_q4_prefill",
+              "moe_q4_decode", "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
+              "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_rmsnorm",
+              "moe_q4_last_error"]:
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from bit_quantized_moe_q4_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in header_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def _layer(hidden=256, inter=128, E=8, k=2, shared=0, ptr=0x10000):
+    from bit_quantized_moe_q4_amd._lib import Layer
+    L = Layer()
+    L.hidden, L.inter, L.n_experts, L.top_k, L.has_shared = hidden, inter, E, k, shared
+    L.w_router = L.w_gate = L.w_up = L.w_down = ptr
+    if shared:
+        L.s_gate = L.s_up = L.s_down = ptr
+    return L
+
+
+def _err(lib):
+    return lib.moe_q4_last_error().decode()
+
+
+def test_packed_bytes(lib):
+    assert lib.q4_packed_bytes(512, 2048) == 512 * 64 * 18
+    assert lib.q4_packed_bytes(3, 33) == 0
+    assert lib.q4_packed_bytes(0, 32) == 0
+
+
+def test_pack_and_quantize_argument_checks(lib):
+    assert lib.q4_pack(C.c_void_p(0x1000), 4, 33, C.c_void_p(0x2000), None) == -1
+    assert "K" in _err(lib)
+    assert lib.q4_pack(None, 4, 32, C.c_void_p(0x2000), None) == -1
+    assert lib.q4_pack(C.c_void_p(0x1004), 4, 32, C.c_void_p(0x2000), None) == -1   # misaligned
+    assert lib.q4_pack(None, 0, 32, None, None) == 0                                 # nothing to do
+    assert lib.q8_quantize(C.c_void_p(0x1000), 2, 31, C.c_void_p(0x2000), C.c_void_p(0x3000), None) == -1
+    assert lib.q8_quantize(C.c_void_p(0x1000), -1, 32, C.c_void_p(0x2000), C.c_void_p(0x3000), None) == -1
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(hidden=33), "hidden"), (dict(inter=0), "inter"), (dict(E=0), "n_experts"),
+    (dict(E=2000), "n_experts"), (dict(k=0), "top_k"), (dict(k=9, E=8), "top_k"),
+    (dict(k=33, E=64), "top_k"), (dict(ptr=0x10008), "aligned"),
+])
+def test_layer_checks(lib, kw, frag):
+    L = _layer(**kw)
+    rc = lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, 16, None, None, None, 0, None)
+    assert rc == -1 and frag in _err(lib)
+    assert lib.moe_q4_route_workspace_bytes(C.byref(L), 16) == 0
+
+
+def test_shared_pointers_required(lib):
+    L = _layer(shared=1)
+    L.s_down = None
+    assert lib.moe_q4_decode(C.byref(L), C.c_void_p(0x1000), C.c_void_p(0x2000), None, None, 0, None) == -1
+    assert "shared" in _err(lib)
+
+
+def test_workspace_checks(lib):
+    from bit_quantized_moe_q4_amd._lib import Routing
+    L = _layer()
+    R = Routing()
+    R.topk_ids = R.topk_w = R.expert_offsets = R.perm = R.inv_perm = 0x4000
+    need = lib.moe_q4_route_workspace_bytes(C.byref(L), 100)
+    assert need > 0 and need % 256 == 0
+    rc = lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, 100, C.byref(R), None,
+                          C.c_void_p(0x100000), need - 1, None)
+    assert rc == -2 and "workspace" in _err(lib)
+    rc = lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, 100, C.byref(R), None,
+                          C.c_void_p(0x100010), need, None)
+    assert rc == -2 and "aligned" in _err(lib)
+    rc = lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 7, 100, C.byref(R), None,
+                          C.c_void_p(0x100000), need, None)
+    assert rc == -1 and "dtype" in _err(lib)
+    rc = lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, -1, C.byref(R), None, None, 0, None)
+    assert rc == -1
+    pneed = lib.moe_q4_prefill_workspace_bytes(C.byref(L), 100)
+    assert pneed >= 100 * 2 * 128 * 2 + 100 * 2 * 256 * 2
+    rc = lib.moe_q4_prefill(C.byref(L), C.c_void_p(0x1000), 100, C.byref(R), C.c_void_p(0x2000),
+                            C.c_void_p(0x100000), pneed - 256, None)
+    assert rc == -2
+    # no tokens: valid, nothing enqueued
+    assert lib.moe_q4_prefill(C.byref(L), None, 0, None, None, None, 0, None) == 0
+    dneed = lib.moe_q4_decode_workspace_bytes(C.byref(L))
+    assert dneed > 0
+    rc = lib.moe_q4_decode(C.byref(L), C.c_void_p(0x1000), C.c_void_p(0x2000), None,
+                           C.c_void_p(0x100000), dneed - 1, None)
+    assert rc == -2
+
+
+def test_gemv_and_rmsnorm_checks(lib):
+    assert lib.moe_q4_w4a8_gemv(C.c_void_p(0x1000), 4, 48, C.c_void_p(0x2000), C.c_void_p(0x3000),
+                                None, C.c_void_p(0x4000), None) == -1
+    assert lib.moe_q4_w4a8_gemv(None, 0, 64, None, None, None, None, None) == 0
+    assert lib.moe_q4_rmsnorm(C.c_void_p(0x1000), 4, 40, 1e-6, C.c_void_p(0x2000), None, None) == -1
+    assert lib.moe_q4_rmsnorm(C.c_void_p(0x1000), 4, 64, 1e-6, None, None, None) == -1
+    assert lib.moe_q4_rmsnorm(None, 0, 64, 1e-6, None, None, None) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    code = (
+        "import bit_quantized_moe_q4_amd._lib as L\n"
+        "L.LIB_PATH = %r\n"
+        "try:\n    L.lib()\nexcept RuntimeError as e:\n    print('RAISED', 'not built' in str(e))\n"
+    ) % str(tmp_path / "missing.so")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert "RAISED True" in r.stdout, r.stdout + r.stderr

@@ -1,0 +1,324 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars (the library's stated contract):
+  - bit-exact: Q4 packing bytes, int8 activation codes and scales, router
+    logits, top-k ids and weights, expert offsets / perm / inv_perm, every
+    per-block int32 W4A8 dot, decode q8(h) codes and scales;
+  - decode y: max|y - y_ref| / max|y_ref| <= 1e-5 (the fp32 program is the
+    same on both sides, so 0 is expected);
+  - prefill y (bf16 MFMA path): ||y - y_ref||_2 / ||y_ref||_2 <= 1e-2 against
+    the oracle's binary64 reference.
+Sizes: small shapes that span several tiles with ragged tails, plus the full
+workload shapes (decode 2048x128x512 top-8 + shared; prefill 2048 tokens;
+skewed 10240 tokens) on sampled tokens.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+import bit_quantized_moe_q4_amd as mq
+from layers import both_layers, tokens
+
+pytestmark = pytest.mark.gpu
+
+PREFILL_TOL = 1e-2
+DECODE_TOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    say("library:", mq.library_path())
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- packing
+@pytest.mark.parametrize("rows,K", [(1, 32), (7, 96), (300, 256), (513, 2048), (64, 16384)])
+def test_q4_pack_bytes(rows, K):
+    say("q4_pack", rows, K)
+    rng = np.random.default_rng(rows * 7 + K)
+    w = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    w[0, :32] = 0.0                                    # zero block
+    if rows > 2:
+        w[1, :32] *= 1e-6                             # fp16-subnormal scale
+        w[2, :32] = np.round(w[2, :32] * 64) / 64     # many exact halves
+    got = mq.q4_pack(torch.from_numpy(w).cuda()).cpu().numpy()
+    assert np.array_equal(got, oracle.q4_pack(w))
+
+
+def test_q4_pack_golden_blocks():
+    from conftest import read_golden
+    g = read_golden("q4_blocks.txt")
+    for tag in "ABCD":
+        unit = 2.0 ** int(g[tag + "_unit_log2"][0])
+        w = np.array([float(u) * unit for u in g[tag + "_w_units"]], dtype=np.float32)
+        exp = bytes(int(b, 16) for b in g[tag + "_bytes"])
+        got = mq.q4_pack(torch.from_numpy(w.reshape(1, 32)).cuda()).cpu().numpy().tobytes()
+        assert got == exp, tag
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (5, 2048), (33, 512)])
+def test_q8_quantize(rows, K):
+    say("q8", rows, K)
+    rng = np.random.default_rng(rows + K)
+    x = (rng.standard_normal((rows, K)) * 3).astype(np.float32)
+    x[0, :32] = 0.0
+    x[-1, 32:64] = np.round(x[-1, 32:64] * 2) / 2
+    q, d = mq.q8_quantize(torch.from_numpy(x).cuda())
+    qo, do = oracle.q8_quantize(x)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), do.view(np.uint32))
+
+
+# ---------------------------------------------------------------- W4A8 row
+@pytest.mark.parametrize("N,K", [(512, 2048), (2048, 512), (37, 256), (5, 128), (3, 96),
+                                 (64, 4096), (9, 16384)])
+def test_w4a8_gemv_dots_bit_exact(N, K):
+    say("w4a8_gemv", N, K)
+    rng = np.random.default_rng(N * 3 + K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W = oracle.q4_pack(w)
+    x = rng.standard_normal(K).astype(np.float32)
+    qa, da = oracle.q8_quantize(x[None])
+    dots_o, out_o = oracle.w4a8_gemv(W, K, qa[0], da[0])
+    dots, out = mq.moe_q4_w4a8_gemv(torch.from_numpy(W).cuda(), N, K, torch.from_numpy(qa[0]).cuda(),
+                                    torch.from_numpy(da[0]).cuda())
+    assert np.array_equal(dots.cpu().numpy(), dots_o)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), out_o.view(np.uint32))
+
+
+# ---------------------------------------------------------------- routing
+def _route_case(cfg, T, step=0, tie_cols=False):
+    ol, gl = both_layers(cfg)
+    if tie_cols:
+        # duplicate router columns: exactly equal logits, lower index must win
+        wr = ol.w_router.copy()
+        wr[:, 1] = wr[:, 0]
+        wr[:, cfg.E - 1] = wr[:, cfg.E // 2]
+        ol.w_router = np.ascontiguousarray(wr)
+        gl = mq.MoELayer(torch.from_numpy(wr).cuda(), gl.gate, gl.up, gl.down, cfg.k,
+                         gl.router_bias, gl.s_gate, gl.s_up, gl.s_down)
+    x, bits, xw, xd, xbd = tokens(cfg, step=step, T=T)
+    return ol, gl, xw, xbd
+
+
+def _check_route(ol, r, xw):
+    ref = oracle.route(ol, xw)
+    assert np.array_equal(r.logits.cpu().numpy().view(np.uint32), ref["logits"].view(np.uint32))
+    assert np.array_equal(r.topk_ids.cpu().numpy(), ref["ids"])
+    assert np.array_equal(r.topk_w.cpu().numpy().view(np.uint32), ref["w32"].view(np.uint32))
+    assert np.array_equal(r.expert_offsets.cpu().numpy(), ref["offsets"])
+    assert np.array_equal(r.perm.cpu().numpy(), ref["perm"])
+    assert np.array_equal(r.inv_perm.cpu().numpy(), ref["inv_perm"])
+    return ref
+
+
+@pytest.mark.parametrize("name,T,E,k,H,bias", [
+    ("tiny", 16, 8, 2, 256, None),
+    ("ragged", 1, 16, 4, 256, None),
+    ("ragged", 65, 16, 4, 256, None),
+    ("ragged", 200, 128, 8, 512, "zipf"),
+    ("odd_chunks", 70, 24, 3, 96, None),
+    ("wide", 130, 256, 8, 2048, None),
+    ("k_equals_e", 33, 4, 4, 128, None),
+    ("one_expert", 40, 1, 1, 64, None),
+])
+def test_route_bit_exact(name, T, E, k, H, bias):
+    say("route", name, T, E, k, H, bias)
+    cfg = moe_synth.CONFIGS["tiny"].with_(name=name, E=E, k=k, H=H, I=64, shared=False, bias=bias)
+    ol, gl, xw, xbd = _route_case(cfg, T)
+    r = mq.moe_q4_route(gl, xbd, logits=True)
+    _check_route(ol, r, xw)
+    # fp32 input path
+    r32 = mq.moe_q4_route(gl, torch.from_numpy(xw).cuda(), logits=True)
+    _check_route(ol, r32, xw)
+
+
+def test_route_ties_lower_index():
+    cfg = moe_synth.CONFIGS["tiny"].with_(name="ties", E=16, k=4, H=256, I=64, shared=False)
+    ol, gl, xw, xbd = _route_case(cfg, 96, tie_cols=True)
+    r = mq.moe_q4_route(gl, xbd, logits=True)
+    ref = _check_route(ol, r, xw)
+    ids = ref["ids"]
+    both = (ids == 0).any(1) & (ids == 1).any(1)
+    assert both.any()
+    for t in np.nonzero(both)[0]:
+        assert list(ids[t]).index(0) + 1 == list(ids[t]).index(1)
+
+
+def test_route_deterministic_and_empty():
+    cfg = moe_synth.CONFIGS["tiny"]
+    ol, gl = both_layers(cfg)
+    _, _, xw, _, xbd = tokens(cfg)
+    a = mq.moe_q4_route(gl, xbd)
+    b = mq.moe_q4_route(gl, xbd)
+    for f in ("topk_ids", "expert_offsets", "perm", "inv_perm"):
+        assert torch.equal(getattr(a, f), getattr(b, f))
+    e = mq.moe_q4_route(gl, xbd[:0])
+    assert torch.count_nonzero(e.expert_offsets).item() == 0
+    y = mq.moe_q4_prefill(gl, xbd[:0], e)
+    assert y.shape == (0, cfg.H)
+
+
+# ---------------------------------------------------------------- prefill
+def _prefill_err(ol, gl, cfg, T, sample=None, step=0):
+    x, bits, xw, xd, xbd = tokens(cfg, step=step, T=T)
+    r = mq.moe_q4_route(gl, xbd)
+    y = mq.moe_q4_prefill(gl, xbd, r).cpu().numpy().astype(np.float64)
+    ref_route = oracle.route(ol, xw)
+    assert np.array_equal(r.topk_ids.cpu().numpy(), ref_route["ids"])
+    toks = np.arange(T) if sample is None else np.asarray(sample)
+    yref = oracle.prefill_ref(ol, xw, ref_route["ids"], ref_route["w64"], tokens=toks)
+    ys = y[toks]
+    assert np.all(np.isfinite(ys))
+    rel = np.linalg.norm(ys - yref) / np.linalg.norm(yref)
+    per_tok = np.linalg.norm(ys - yref, axis=1) / np.linalg.norm(yref, axis=1)
+    say("prefill rel-L2 %.3e  worst token %.3e" % (rel, per_tok.max()))
+    return rel, per_tok, y, ref_route
+
+
+@pytest.mark.parametrize("name,T,H,E,I,k,shared", [
+    ("tiny", 16, 256, 8, 128, 2, False),
+    ("multi_tile", 300, 512, 16, 256, 4, True),
+    ("ragged_k_tail", 77, 96, 5, 96, 2, True),
+    ("one_expert_dense", 150, 256, 1, 128, 1, False),
+])
+def test_prefill_small(name, T, H, E, I, k, shared):
+    say("prefill", name, T, H, E, I, k, shared)
+    cfg = moe_synth.CONFIGS["tiny"].with_(name=name, H=H, E=E, I=I, k=k, shared=shared)
+    ol, gl = both_layers(cfg)
+    rel, per_tok, _, _ = _prefill_err(ol, gl, cfg, T)
+    assert rel <= PREFILL_TOL
+    assert per_tok.max() <= 3 * PREFILL_TOL
+
+
+@pytest.fixture(scope="module")
+def prefill_layer():
+    cfg = moe_synth.CONFIGS["prefill"]
+    say("building prefill-size layer")
+    return cfg, both_layers(cfg)
+
+
+def test_prefill_2k_sampled(prefill_layer):
+    cfg, (ol, gl) = prefill_layer
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([[0, 1, cfg.T - 1], rng.choice(cfg.T, 45, replace=False)]))
+    rel, per_tok, y, rr = _prefill_err(ol, gl, cfg, cfg.T, sample=sample)
+    assert rel <= PREFILL_TOL
+    # every expert segment is non-empty at this size; the y rows exist for all tokens
+    assert np.all(np.diff(rr["offsets"]) > 0)
+    assert np.all(np.isfinite(y))
+
+
+def test_prefill_2k_token_permutation_equivariance(prefill_layer):
+    cfg, (ol, gl) = prefill_layer
+    x, bits, xw, xd, xbd = tokens(cfg, T=512, step=5)
+    r = mq.moe_q4_route(gl, xbd)
+    y = mq.moe_q4_prefill(gl, xbd, r)
+    p = torch.randperm(512, generator=torch.Generator().manual_seed(0)).cuda()
+    xp = xbd[p].contiguous()
+    r2 = mq.moe_q4_route(gl, xp)
+    y2 = mq.moe_q4_prefill(gl, xp, r2)
+    # a token's rows are independent of its batch position (same tiles -> same sums
+    # is not guaranteed, the value is); compare within the bf16 path tolerance
+    rel = (torch.linalg.norm(y2 - y[p]) / torch.linalg.norm(y)).item()
+    assert rel <= 1e-3, rel
+
+
+def test_prefill_skewed_10k_sampled():
+    cfg = moe_synth.CONFIGS["skew"]
+    say("building skewed layer")
+    ol, gl = both_layers(cfg)
+    x, bits, xw, xd, xbd = tokens(cfg)
+    r = mq.moe_q4_route(gl, xbd)
+    ref = oracle.route(ol, xw)
+    assert np.array_equal(r.topk_ids.cpu().numpy(), ref["ids"])
+    assert np.array_equal(r.perm.cpu().numpy(), ref["perm"])
+    counts = np.diff(ref["offsets"])
+    say("skew: hottest expert %d rows, empty experts %d" % (counts.max(), (counts == 0).sum()))
+    y = mq.moe_q4_prefill(gl, xbd, r).cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(3)
+    sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 30, replace=False)]))
+    yref = oracle.prefill_ref(ol, xw, ref["ids"], ref["w64"], tokens=sample)
+    rel = np.linalg.norm(y[sample] - yref) / np.linalg.norm(yref)
+    say("skew prefill rel-L2 %.3e" % rel)
+    assert rel <= PREFILL_TOL
+    assert np.all(np.isfinite(y))
+
+
+# ---------------------------------------------------------------- decode
+def _decode_steps(ol, gl, cfg, steps):
+    ws = mq.decode_workspace(gl)
+    worst = 0.0
+    for step in steps:
+        x = moe_synth.tokens(cfg, step=step, T=1)[0]
+        y, tr = mq.moe_q4_decode(gl, torch.from_numpy(x).cuda(), ws=ws, trace=True)
+        yo, to = oracle.decode(ol, x, trace=True)
+        assert np.array_equal(tr["logits"].cpu().numpy().view(np.uint32), to["logits"].view(np.uint32))
+        assert np.array_equal(tr["ids"].cpu().numpy(), to["ids"])
+        assert np.array_equal(tr["w"].cpu().numpy().view(np.uint32), to["w"].view(np.uint32))
+        assert np.array_equal(tr["qx"].cpu().numpy(), to["qx"])
+        assert np.array_equal(tr["dx"].cpu().numpy().view(np.uint32), to["dx"].view(np.uint32))
+        assert np.array_equal(tr["qh"].cpu().numpy(), to["qh"])
+        assert np.array_equal(tr["dh"].cpu().numpy().view(np.uint32), to["dh"].view(np.uint32))
+        yg = y.cpu().numpy()
+        err = np.max(np.abs(yg.astype(np.float64) - yo)) / np.max(np.abs(yo))
+        worst = max(worst, err)
+        assert err <= DECODE_TOL, (step, err)
+    return worst
+
+
+@pytest.mark.parametrize("name,H,E,I,k,shared,bias", [
+    ("tiny", 256, 8, 128, 2, False, None),
+    ("tiny_shared", 256, 8, 128, 2, True, None),
+    ("odd_chunks", 96, 5, 96, 3, True, None),
+    ("zipf_bias", 512, 64, 256, 8, True, "zipf"),
+])
+def test_decode_small(name, H, E, I, k, shared, bias):
+    say("decode", name)
+    cfg = moe_synth.CONFIGS["tiny"].with_(name=name, H=H, E=E, I=I, k=k, shared=shared, bias=bias)
+    ol, gl = both_layers(cfg)
+    _decode_steps(ol, gl, cfg, range(6))
+
+
+def test_decode_full_layer():
+    cfg = moe_synth.CONFIGS["decode"]
+    say("building decode-size layer")
+    ol, gl = both_layers(cfg)
+    worst = _decode_steps(ol, gl, cfg, range(12))
+    say("decode worst max-rel %.3e" % worst)
+
+
+def test_w4a8_dots_of_decode_layer_rows():
+    # per-block int32 dots of real layer rows (gate rows of one expert) are exact
+    cfg = moe_synth.CONFIGS["tiny"].with_(name="dots", H=2048, E=2, I=512, k=1, shared=False)
+    ol, gl = both_layers(cfg)
+    x = moe_synth.tokens(cfg, step=0, T=1)[0]
+    qa, da = oracle.q8_quantize(x[None])
+    W = ol.gate[1]
+    dots_o, out_o = oracle.w4a8_gemv(W, cfg.H, qa[0], da[0])
+    dots, out = mq.moe_q4_w4a8_gemv(gl.gate[1].contiguous(), cfg.I, cfg.H, torch.from_numpy(qa[0]).cuda(),
+                                    torch.from_numpy(da[0]).cuda())
+    assert np.array_equal(dots.cpu().numpy(), dots_o)
+    assert np.array_equal(out.cpu().numpy(), out_o)
+
+
+# ---------------------------------------------------------------- glue
+@pytest.mark.parametrize("T,H", [(1, 2048), (9, 96), (64, 256)])
+def test_rmsnorm_bit_exact(T, H):
+    rng = np.random.default_rng(T + H)
+    y = (rng.standard_normal((T, H)) * 3).astype(np.float32)
+    o32, o16 = mq.moe_q4_rmsnorm(torch.from_numpy(y).cuda(), 1e-6, f32=True, bf16=True)
+    ref = oracle.rmsnorm(y, 1e-6)
+    assert np.array_equal(o32.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(o16.view(torch.int16).cpu().numpy().view(np.uint16), moe_synth.to_bf16_bits(ref))
