@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q4_0 MoE expert-FFN layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  Legs, all on seeded synthetic inputs already resident
+in HBM when timing starts:
+
+- prefill (the step, `value`): one pass of moe_q4_route + the three prefill
+  stages over a 2048-token bf16 batch of one layer (hidden 2048, 128 routed
+  experts + 1 shared, intermediate 512, top-8, Q4_0 weights).  `value` is
+  tokens/s = 2048 / (host wall time per step, bracketed by synchronisation).
+  Two packed copies of the layer alternate between steps so the 229 MB of
+  weights is not served from the 256 MB last-level cache.
+- decode: `decode_steps` single-token W4A8 steps (fresh x each) of the same
+  layer shape, captured once in a HIP graph and replayed; 16 packed copies
+  rotate so every step streams its experts from HBM.  Reported as weight
+  GB/s = 16,973,824 B per step / time per step.
+- roofline: the dominant prefill kernel (grouped gate/up GEMM) timed with HIP
+  events around its own launch on the stream it runs on.
+- cpu_baseline: the CPU oracle (single-threaded C) on a bounded token sample
+  of the same workload, scaled to tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E peak
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_quantized_moe_q4_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel, src_files, launches_per_unit=1):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/), only if
+    the kernel source is unchanged since the counters were taken."""
+    p = os.path.join(PROFILES, "traffic_%s.json" % kernel)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("src_hash") != _src_hash(*src_files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def clone_layer(L):
+    import bit_quantized_moe_q4_amd as mq
+    c = lambda t: None if t is None else t.clone()  # noqa: E731
+    return mq.MoELayer(c(L.w_router), c(L.gate), c(L.up), c(L.down), L.top_k, c(L.router_bias),
+                       c(L.s_gate), c(L.s_up), c(L.s_down))
+
+
+def bench_prefill(args, torch, mq, moe_synth, device_layer):
+    cfg = moe_synth.CONFIGS["prefill"]
+    W = moe_synth.expert_weights(cfg, threads=16)
+    layers = [device_layer(cfg, weights=W)]
+    layers.append(clone_layer(layers[0]))
+    x = moe_synth.tokens(cfg)
+    import numpy as np
+    xb = torch.from_numpy(moe_synth.to_bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+    T = cfg.T
+    routing = mq.Routing.empty(T, cfg.k, cfg.E, xb.device)
+    rws = torch.empty(mq.moe_q4_route_workspace_bytes(layers[0], T), dtype=torch.uint8, device="cuda")
+    pws = torch.empty(mq.moe_q4_prefill_workspace_bytes(layers[0], T), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+    S = mq._lib
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(i, evs=None):
+        L = layers[i % len(layers)]
+        if evs: evs[0].record()
+        mq.moe_q4_route(L, xb, out=routing, ws=rws)
+        if evs: evs[1].record()
+        mq.moe_q4_prefill_stage(L, xb, routing, y, pws, S.STAGE_GATEUP)
+        if evs: evs[2].record()
+        mq.moe_q4_prefill_stage(L, xb, routing, y, pws, S.STAGE_DOWN)
+        if evs: evs[3].record()
+        mq.moe_q4_prefill_stage(L, xb, routing, y, pws, S.STAGE_COMBINE)
+        if evs: evs[4].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    seg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in ev) / len(ev) * 1e-3  # noqa: E731
+    t_route, t_gu, t_dn, t_cb = seg(0, 1), seg(1, 2), seg(2, 3), seg(3, 4)
+    S_ = 1 if cfg.shared else 0
+    rows = T * cfg.k + T * S_
+    fl_gu = 2.0 * rows * (2 * cfg.I) * cfg.H
+    fl_dn = 2.0 * rows * cfg.I * cfg.H
+    fl_total = fl_gu + fl_dn
+    assert torch.isfinite(y).all().item()
+    return dict(cfg=cfg, W=W, step_s=step_s, t_route=t_route, t_gu=t_gu, t_dn=t_dn, t_cb=t_cb,
+                fl_gu=fl_gu, fl_dn=fl_dn, fl_total=fl_total, layers=layers)
+
+
+def bench_decode(args, torch, mq, moe_synth, device_layer):
+    cfg = moe_synth.CONFIGS["decode"]
+    base = device_layer(cfg)
+    copies = [base] + [clone_layer(base) for _ in range(args.decode_copies - 1)]
+    n = args.decode_steps
+    X = torch.from_numpy(moe_synth.tokens(cfg, step=0, T=n)).cuda()   # fresh seeded x per step
+    Y = torch.empty((n, cfg.H), dtype=torch.float32, device="cuda")
+    ws = mq.decode_workspace(base)
+    # eager warm-up of every copy (also checks the call path outside a graph)
+    for i in range(min(n, 2 * len(copies))):
+        mq.moe_q4_decode(copies[i % len(copies)], X[i], y=Y[i], ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                mq.moe_q4_decode(copies[i % len(copies)], X[i], y=Y[i], ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g.replay()                      # warm
+    torch.cuda.synchronize()
+    reps = args.decode_reps
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / (reps * n)
+    ns = cfg.k + (1 if cfg.shared else 0)
+    per_mat = cfg.I * (cfg.H // 32) * 18
+    bytes_step = ns * 3 * per_mat + cfg.H * cfg.E * 4
+    # eager (no graph) for reference: launch overhead included
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    m = min(n, 200)
+    for i in range(m):
+        mq.moe_q4_decode(copies[i % len(copies)], X[i], y=Y[i], ws=ws)
+    torch.cuda.synchronize()
+    eager_s = (time.perf_counter() - t2) / m
+    assert torch.isfinite(Y).all().item()
+    return dict(cfg=cfg, step_s=step_s, bytes_step=bytes_step, eager_s=eager_s, copies=len(copies))
+
+
+def cpu_baseline(args, pre):
+    """The oracle as it stands, single-threaded, on a bounded token sample."""
+    import numpy as np
+    import moe_synth
+    import oracle
+    cfg, W = pre["cfg"], pre["W"]
+    ol = oracle.PackedLayer.from_float(moe_synth.router(cfg), moe_synth.router_bias(cfg), W["gate"],
+                                       W["up"], W["down"], W["s_gate"], W["s_up"], W["s_down"],
+                                       k=cfg.k, threads=16)
+    x = moe_synth.tokens(cfg)
+    xw = moe_synth.bf16_bits_to_f32(moe_synth.to_bf16_bits(x))
+    n = args.cpu_sample_tokens
+    sample = np.arange(n)
+    t0 = time.perf_counter()
+    r = oracle.route(ol, xw[:n])
+    t1 = time.perf_counter()
+    oracle.prefill_ref(ol, xw[:n], r["ids"], r["w64"], tokens=sample)
+    t2 = time.perf_counter()
+    per_tok = (t2 - t0) / n
+    return {"value": round(1.0 / per_tok, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d tokens of the 2048-token batch: routing (fp32 program) + binary64 "
+                      "expert FFN reference; %.1f s of CPU time" % (n, t2 - t0)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--decode-copies", type=int, default=16)
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=768)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build measures the one-GPU share of the "
+              "layer (see the sharding notes in DESIGN.md); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_synth
+    import bit_quantized_moe_q4_amd as mq
+    from bit_quantized_moe_q4_amd.synth_layer import device_layer
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    pre = bench_prefill(args, torch, mq, moe_synth, device_layer)
+    dec = bench_decode(args, torch, mq, moe_synth, device_layer)
+    cfg = pre["cfg"]
+    tok_s = cfg.T / pre["step_s"]
+    ach_gu = pre["fl_gu"] / pre["t_gu"] / 1e12
+    dec_gbps = dec["bytes_step"] / dec["step_s"] / 1e9
+    out = {
+        "metric": "MoE-layer tok/s at 2k prefill; decode weight GB/s; % of HBM/MFMA roofline",
+        "value": round(tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["step_s"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights packed to Q4_0, N(0,1) bf16 tokens)",
+        "config": {
+            "workload": "one MoE FFN layer, prefill of 2048 tokens: hidden 2048, 128 routed experts "
+                        "+ 1 shared, intermediate 512, top-8, Q4_0 weights (route + grouped GEMM)",
+            "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E, "inter": cfg.I, "top_k": cfg.k,
+            "shared_expert": cfg.shared, "layer_copies_rotated": len(pre["layers"]),
+        },
+        "roofline": {
+            "kernel": "gateup_kernel (grouped gate/up GEMM + SwiGLU)",
+            "bound": "mfma",
+            "achieved": round(ach_gu, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ach_gu / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic("gateup", ["gemm.hip", "w4a8.hpp", "device_math.hpp"]),
+            "flop_per_launch": pre["fl_gu"],
+            "avg_launch_us": round(pre["t_gu"] * 1e6, 2),
+        },
+        "stages_us": {"route": round(pre["t_route"] * 1e6, 2), "gateup": round(pre["t_gu"] * 1e6, 2),
+                      "down": round(pre["t_dn"] * 1e6, 2), "combine": round(pre["t_cb"] * 1e6, 2)},
+        "step_mfma_frac": round(pre["fl_total"] / pre["step_s"] / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "decode": {
+            "metric": "decode weight GB/s",
+            "value": round(dec_gbps, 1),
+            "unit": "GB/s",
+            "us_per_step": round(dec["step_s"] * 1e6, 3),
+            "eager_us_per_step": round(dec["eager_s"] * 1e6, 3),
+            "steps": args.decode_steps,
+            "bytes_per_step": dec["bytes_step"],
+            "layer_copies_rotated": dec["copies"],
+            "workload": "one-token W4A8 decode, same layer shape, fresh x per step, HIP graph replay",
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+        },
+    }
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args, pre)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

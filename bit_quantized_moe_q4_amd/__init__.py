@@ -23,7 +23,7 @@ from . import _lib
 __all__ = [
     "q4_packed_bytes", "q4_pack", "q8_quantize", "MoELayer", "Routing",
     "moe_q4_route_workspace_bytes", "moe_q4_route",
-    "moe_q4_prefill_workspace_bytes", "moe_q4_prefill",
+    "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage",
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
     "moe_q4_w4a8_gemv", "moe_q4_rmsnorm", "library_path",
 ]
@@ -196,6 +196,19 @@ def moe_q4_prefill(layer: MoELayer, x_bf16: torch.Tensor, routing: Routing,
     rs = routing.cstruct()
     _lib.check(_lib.lib().moe_q4_prefill(layer.struct_ptr(), _p(x_bf16), T, C.byref(rs), _p(y),
                                          _p(w), w.numel(), _s(stream)), "moe_q4_prefill")
+    return y
+
+
+def moe_q4_prefill_stage(layer: MoELayer, x_bf16: torch.Tensor, routing: Routing,
+                         y: torch.Tensor, ws: torch.Tensor, stages: int, stream=None) -> torch.Tensor:
+    """Run some stages of moe_q4_prefill (mask of _lib.STAGE_GATEUP | _DOWN | _COMBINE)
+    with a caller-held workspace `ws` (its first bytes hold h after GATEUP)."""
+    _dev(x_bf16, "x_bf16")
+    T = int(x_bf16.shape[0])
+    rs = routing.cstruct()
+    _lib.check(_lib.lib().moe_q4_prefill_stage(layer.struct_ptr(), _p(x_bf16), T, C.byref(rs), _p(y),
+                                               _p(ws), ws.numel(), int(stages), _s(stream)),
+               "moe_q4_prefill_stage")
     return y
 
 

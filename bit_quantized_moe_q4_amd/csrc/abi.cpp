@@ -197,6 +197,14 @@ size_t moe_q4_prefill_workspace_bytes(const moe_q4_layer* L, int32_t T) {
 int moe_q4_prefill(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T,
                    const moe_q4_routing* routing, float* y, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
+  return moe_q4_prefill_stage(L, x_bf16, T, routing, y, ws, ws_bytes, MOE_Q4_STAGE_ALL, stream);
+}
+
+int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T,
+                         const moe_q4_routing* routing, float* y, void* ws, size_t ws_bytes,
+                         int32_t stages, hipStream_t stream) {
+  if (stages <= 0 || stages > MOE_Q4_STAGE_ALL)
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill_stage: stages=%d must be a non-empty mask of 1|2|4", stages);
   int rc = check_layer(L);
   if (rc) return rc;
   if (T < 0) return fail(MOE_Q4_EINVAL, "moe_q4_prefill: T=%d < 0", T);
@@ -230,7 +238,7 @@ int moe_q4_prefill(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T,
   a.h = at<uint16_t>(ws, W.h);
   a.o_perm = at<uint16_t>(ws, W.o);
   a.y = y;
-  hipError_t e = moeq4::launch_prefill(a, stream);
+  hipError_t e = moeq4::launch_prefill(a, stages, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_prefill");
 }
 

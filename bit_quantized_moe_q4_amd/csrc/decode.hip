@@ -48,10 +48,12 @@ __device__ __forceinline__ void dec_wave_argmax(float& v, int& e) {
 }
 
 // ---------------------------------------------------------------- router
-__global__ void __launch_bounds__(256) decode_router_kernel(DecodeArgs a, int nc, int cw,
-                                                            int nsplit) {
+template <int NS>
+__global__ void __launch_bounds__(256) decode_router_kernel(DecodeArgs a, int nc, int cw) {
+  constexpr int nsplit = NS;
   __shared__ float xs[256 * BLK];         // cw * 32 inputs (cw <= 256)
   __shared__ float part[1024];            // [cl][e] chain results (cw * E <= 1024)
+  __shared__ float logit_l[1024];
   __shared__ int s_last;
   const int tid = threadIdx.x, split = blockIdx.x;
   const int E = a.E, H = a.H;
@@ -127,26 +129,30 @@ __global__ void __launch_bounds__(256) decode_router_kernel(DecodeArgs a, int nc
   __syncthreads();
   if (!s_last) return;
   __threadfence();
+  // each thread finishes experts e = tid, tid+256, ...: NS loads in flight
+  for (int e = tid; e < E; e += blockDim.x) {
+    float v[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++) v[s] = __builtin_nontemporal_load(a.partials + (size_t)s * E + e);
+#pragma unroll
+    for (int w = NS; w > 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w / 2; i++) v[i] = v[2 * i] + v[2 * i + 1];
+    float l = v[0];
+    if (a.bias) l = l + a.bias[e];
+    logit_l[e] = l;
+    if (a.t_logits) a.t_logits[e] = l;
+  }
+  __syncthreads();
   if (tid < 64) {
     const int lane = tid;
     constexpr int NJ = 16;                // E <= 1024
     float lv[NJ];
     const int nj = (E + 63) / 64;
+#pragma unroll
     for (int j = 0; j < NJ; j++) {
-      lv[j] = -__builtin_inff();
       const int e = lane + 64 * j;
-      if (j < nj && e < E) {
-        // pairwise over the nsplit subtree partials (nsplit a power of two)
-        float v[64];
-        for (int s = 0; s < nsplit; s++)
-          v[s] = __builtin_nontemporal_load(a.partials + (size_t)s * E + e);
-        for (int n = nsplit; n > 1; n >>= 1)
-          for (int i = 0; i < n / 2; i++) v[i] = v[2 * i] + v[2 * i + 1];
-        float l = v[0];
-        if (a.bias) l = l + a.bias[e];
-        lv[j] = l;
-        if (a.t_logits) a.t_logits[e] = l;
-      }
+      lv[j] = (j < nj && e < E) ? logit_l[e] : -__builtin_inff();
     }
     uint32_t taken = 0;
     float my_v = 0.0f;
@@ -291,8 +297,18 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
 
 // ---------------------------------------------------------------- launch
 hipError_t launch_decode(const DecodeArgs& a, const RouterSplit& sp, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_router_kernel, dim3(sp.nsplit), dim3(256), 0, stream, a, sp.nc, sp.cw,
-                     sp.nsplit);
+#define MOEQ4_DR(NSV) \
+  hipLaunchKernelGGL((decode_router_kernel<NSV>), dim3(NSV), dim3(256), 0, stream, a, sp.nc, sp.cw)
+  switch (sp.nsplit) {
+    case 1: MOEQ4_DR(1); break;
+    case 2: MOEQ4_DR(2); break;
+    case 4: MOEQ4_DR(4); break;
+    case 8: MOEQ4_DR(8); break;
+    case 16: MOEQ4_DR(16); break;
+    case 32: MOEQ4_DR(32); break;
+    default: MOEQ4_DR(64); break;
+  }
+#undef MOEQ4_DR
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 

@@ -107,6 +107,11 @@ __device__ __forceinline__ Tile find_tile(const int32_t* __restrict__ offsets, i
   return t;
 }
 
+// Token of the tile's first row: padding rows of a tile read this valid row.
+__device__ __forceinline__ int tok_fill(const PrefillArgs& a, const Tile& t) {
+  return (t.expert >= 0) ? min(max(a.perm[t.pos0] / a.k, 0), a.T - 1) : t.m0;
+}
+
 // 8 bf16 weights of element group Q (0..3) of block J of a lane's 72-byte run.
 // Group 0: elements 0..7 (low nibbles of bytes 0..7), 1: 8..15 (low nibbles of
 // bytes 8..15), 2: 16..23 (high nibbles of bytes 0..7), 3: 24..31.
@@ -324,6 +329,257 @@ __global__ void __launch_bounds__(256, 2) down_kernel(PrefillArgs a, int vec_b) 
   }
 }
 
+// ---------------------------------------------------------------- fast path
+// Shapes with K a multiple of 128 (whole 4-block steps) and 4-byte aligned
+// weight rows.
+//
+// Tiles: expert e's c_e rows are cut into ceil(c_e / 160) near-equal tiles of
+// a multiple of 32 rows, so a thin expert (c_e ~ T*k/E) is ONE tile and each
+// of its weights is dequantised once per block of columns, not once per
+// fixed-size piece (the thin-M cost the pages identify).
+//
+// Block: 4 waves, each computing two 32-column MFMA operands per activation
+// fragment -- gate and up for the same 32 columns of I (gate/up kernel), or
+// two 32-column groups of H (down kernel) -- so one 1 KB LDS read of A feeds
+// two MFMAs.  gate/up blocks cover 128 columns of I, down blocks 256 of H.
+//
+// Software pipeline, one K-step ahead:
+//   - the next step's activation tile [rows][16 chunks of 16 B] goes straight
+//     from global memory into the other of two LDS buffers (direct
+//     global->LDS loads); chunk c of row m sits at slot c ^ (m & 15), so the
+//     32 rows a wave reads for one MFMA hit distinct banks;
+//   - each lane's next-step weight bytes (2 whole 18-byte blocks per row)
+//     go into registers;
+// while the current step's MFMAs run.  Raw barriers (no memory fence) keep
+// the prefetch in flight across them; each wave waits for its own loads of a
+// buffer before the barrier that publishes it.
+// K order inside a step: MFMA instruction i (0..7) takes, in lane half g,
+// elements 8*(i%4)..+8 of block 2g + i/4 -- lane (n, g) streams blocks
+// 2g, 2g+1 of weight row n and reads activations at step offset 64g + 8i.
+constexpr int FMAXS = 5;                 // max 32-row subtiles per tile
+constexpr int FMAXR = 32 * FMAXS;        // max rows per tile
+
+// Tile mt, found by every wave on its own (registers only, no LDS):
+// expert e owns ceil(c_e / FMAXR) consecutive tile indices, experts in
+// order, then the shared expert's tiles.
+__device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offsets, int E, int T,
+                                              int k, int has_shared, int mt) {
+  const int lane = threadIdx.x % 64;
+  Tile t;
+  t.valid = 0;
+  t.rows = 0;
+  t.pos0 = 0;
+  t.expert = -1;
+  t.m0 = 0;
+  int carry = 0, c = -1, q = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    int ce = 0;
+    if (e < E) ce = offsets[e + 1] - offsets[e];
+    const int nt = (ce + FMAXR - 1) / FMAXR;
+    int incl = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    const unsigned long long hit = __ballot(carry + incl > mt);
+    if (hit) {
+      const int f = __builtin_ctzll(hit);
+      t.expert = base + f;
+      c = __shfl(ce, f, 64);
+      q = mt - (carry + __shfl(incl, f, 64) - __shfl(nt, f, 64));
+      break;
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  if (c < 0) {
+    if (!has_shared) return t;
+    c = T;
+    q = mt - carry;
+  }
+  const int nt = (c + FMAXR - 1) / FMAXR;
+  if (q < 0 || q >= nt) return t;
+  const int tr = 32 * (((c + nt - 1) / nt + 31) / 32);   // rows per tile, <= FMAXR
+  t.m0 = q * tr;
+  t.rows = min(tr, c - t.m0);
+  if (t.rows <= 0) return t;
+  t.valid = 1;
+  t.pos0 = (t.expert >= 0) ? offsets[t.expert] + t.m0 : T * k + t.m0;
+  return t;
+}
+
+__device__ __forceinline__ void lds_load16(const void* g, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt vmcnt(N), expcnt/lgkmcnt untouched (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void load_run2(const uint8_t* __restrict__ p, uint32_t (&D)[9]) {
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+  for (int v = 0; v < 9; v++) D[v] = s[v];
+}
+
+// One K-step: 8 k-slices x MS subtiles x 2 operands.
+template <int MS>
+__device__ __forceinline__ void mma_step128(const uint16_t* As, int ln, int g, const uint32_t (&D0)[9],
+                                            const uint32_t (&D1)[9], f32x16_t (&acc0)[FMAXS],
+                                            f32x16_t (&acc1)[FMAXS]) {
+  const int x = ln & 15;
+  const uint16_t* base = As + ln * 128;
+#define MOEQ4_F(J, Q)                                                                      \
+  {                                                                                        \
+    const bf16x8_t b0 = dequant8<J, Q>(D0);                                                \
+    const bf16x8_t b1 = dequant8<J, Q>(D1);                                                \
+    const int ofs = 8 * ((8 * g + 4 * (J) + (Q)) ^ x);                                     \
+    _Pragma("unroll") for (int sub = 0; sub < MS; sub++) {                                 \
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(base + sub * 32 * 128 + ofs); \
+      acc0[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, acc0[sub], 0, 0, 0);     \
+      acc1[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, acc1[sub], 0, 0, 0);     \
+    }                                                                                      \
+  }
+  MOEQ4_F(0, 0) MOEQ4_F(0, 1) MOEQ4_F(0, 2) MOEQ4_F(0, 3)
+  MOEQ4_F(1, 0) MOEQ4_F(1, 1) MOEQ4_F(1, 2) MOEQ4_F(1, 3)
+#undef MOEQ4_F
+}
+
+// LDS of one block: two activation buffers of FMAXR rows x 256 B (80 KB:
+// two blocks fit a CU's 160 KB).
+struct FastSmem {
+  uint16_t a0[FMAXR * 128];
+  uint16_t a1[FMAXR * 128];
+};
+
+template <int MS, bool GATEUP>
+__device__ __forceinline__ void fast_tile(const PrefillArgs& a, const Tile& t, FastSmem& sm) {
+  constexpr int NA = 2 * MS;                   // direct 1 KB loads per wave per step (4 waves)
+  constexpr int NB = 18;                       // weight dword loads per lane per step
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, g = lane / 32;
+  const int H = a.H, I = a.I;
+  const int N = GATEUP ? I : H, K = GATEUP ? H : I;
+  const int nb = K / BLK;
+  // gate/up: 32 columns per wave; down: 64 columns per wave (two groups)
+  const int ncol0 = GATEUP ? blockIdx.x * 128 + wave * 32 : blockIdx.x * 256 + wave * 64;
+  const bool live0 = ncol0 < N;
+  const bool live1 = GATEUP ? live0 : (ncol0 + 32 < N);
+  const int n0 = min(ncol0, N - 32) + ln;      // dead groups load a valid row and store nothing
+  const int n1 = GATEUP ? n0 : min(ncol0 + 32, N - 32) + ln;
+  const size_t rb = (size_t)nb * Q4B;
+  const uint8_t *row0, *row1;
+  if (GATEUP) {
+    row0 = (t.expert >= 0) ? a.w_gate + ((size_t)t.expert * I + n0) * rb : a.s_gate + (size_t)n0 * rb;
+    row1 = (t.expert >= 0) ? a.w_up + ((size_t)t.expert * I + n0) * rb : a.s_up + (size_t)n0 * rb;
+  } else {
+    const uint8_t* wd = (t.expert >= 0) ? a.w_down + (size_t)t.expert * H * rb : a.s_down;
+    row0 = wd + (size_t)n0 * rb;
+    row1 = wd + (size_t)n1 * rb;
+  }
+  // element offsets (from abase) of this lane's direct-load rows, 4 rows per 1 KB instruction
+  const uint16_t* abase = GATEUP ? a.x : a.h + (size_t)t.pos0 * I;
+  uint32_t src[NA];
+#pragma unroll
+  for (int q = 0; q < NA; q++) {
+    const int jj = wave + 4 * q;
+    const int m = min(4 * jj + (lane >> 4), t.rows - 1);   // padding rows repeat the last row
+    const int c = ((lane & 15) ^ ((4 * jj + (lane >> 4)) & 15));
+    uint32_t rowel;
+    if (GATEUP) {
+      const int tk = (t.expert >= 0) ? a.perm[t.pos0 + m] / a.k : t.m0 + m;
+      rowel = (uint32_t)min(max(tk, 0), a.T - 1) * (uint32_t)H;
+    } else {
+      rowel = (uint32_t)m * (uint32_t)I;
+    }
+    src[q] = rowel + 8u * (uint32_t)c;
+  }
+  auto issue_a = [&](int s, uint16_t* buf) {
+#pragma unroll
+    for (int q = 0; q < NA; q++) lds_load16(abase + src[q] + 128 * s, buf + (wave + 4 * q) * 512);
+  };
+  auto load_b = [&](int s, uint32_t (&D0)[9], uint32_t (&D1)[9]) {
+    const size_t ofs = (size_t)(4 * s + 2 * g) * Q4B;
+    load_run2(row0 + ofs, D0);
+    load_run2(row1 + ofs, D1);
+  };
+
+  f32x16_t acc0[FMAXS], acc1[FMAXS];
+#pragma unroll
+  for (int q = 0; q < FMAXS; q++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) { acc0[q][r] = 0.0f; acc1[q][r] = 0.0f; }
+
+  const int nsteps = nb / 4;
+  uint32_t P0[9], P1[9], Q0[9], Q1[9];
+  issue_a(0, sm.a0);
+  load_b(0, P0, P1);
+  // pairs of steps (buffer 0 / registers P, then buffer 1 / registers Q),
+  // each prefetching the next; a single loop exit keeps the accumulators
+  // in place
+  const int npairs = nsteps / 2;
+  for (int pi = 0; pi < npairs; pi++) {
+    const int s = 2 * pi;
+    __builtin_amdgcn_s_barrier();               // buffer 1 free (step s-1 done everywhere)
+    issue_a(s + 1, sm.a1);
+    load_b(s + 1, Q0, Q1);
+    wait_vm<NA + NB>();                         // own loads of step s complete
+    __builtin_amdgcn_s_barrier();               // step s tile complete everywhere
+    mma_step128<MS>(sm.a0, ln, g, P0, P1, acc0, acc1);
+    __builtin_amdgcn_s_barrier();
+    if (s + 2 < nsteps) {
+      issue_a(s + 2, sm.a0);
+      load_b(s + 2, P0, P1);
+      wait_vm<NA + NB>();
+    } else {
+      wait_vm<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    mma_step128<MS>(sm.a1, ln, g, Q0, Q1, acc0, acc1);
+  }
+  if (nsteps & 1) {                             // last step in buffer 0 / registers P
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    mma_step128<MS>(sm.a0, ln, g, P0, P1, acc0, acc1);
+  }
+#pragma unroll
+  for (int sub = 0; sub < MS; sub++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int rr = 32 * sub + 8 * (r / 4) + 4 * g + (r % 4);
+      if (rr >= t.rows) continue;
+      if (GATEUP) {
+        if (!live0) continue;
+        const float gv = acc0[sub][r], uv = acc1[sub][r];
+        const float hv = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
+        a.h[(size_t)(t.pos0 + rr) * I + n0] = f32_to_bf16_bits(hv);
+      } else if (t.expert >= 0) {
+        if (live0) a.o_perm[(size_t)(t.pos0 + rr) * H + n0] = f32_to_bf16_bits(acc0[sub][r]);
+        if (live1) a.o_perm[(size_t)(t.pos0 + rr) * H + n1] = f32_to_bf16_bits(acc1[sub][r]);
+      } else {
+        if (live0) a.y[(size_t)(t.m0 + rr) * H + n0] = acc0[sub][r];
+        if (live1) a.y[(size_t)(t.m0 + rr) * H + n1] = acc1[sub][r];
+      }
+    }
+}
+
+template <bool GATEUP>
+__global__ void __launch_bounds__(256, 2) gemm_fast_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) FastSmem sm;
+  const Tile t = find_tile_bal(a.offsets, a.E, a.T, a.k, a.has_shared, blockIdx.y);
+  if (!t.valid) return;
+  const int ms = (t.rows + 31) / 32;
+  switch (ms) {
+    case 1: fast_tile<1, GATEUP>(a, t, sm); break;
+    case 2: fast_tile<2, GATEUP>(a, t, sm); break;
+    case 3: fast_tile<3, GATEUP>(a, t, sm); break;
+    case 4: fast_tile<4, GATEUP>(a, t, sm); break;
+    default: fast_tile<5, GATEUP>(a, t, sm); break;
+  }
+}
+
 // ---------------------------------------------------------------- combine
 __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
   const int H = a.H, k = a.k;
@@ -358,25 +614,47 @@ __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------- launch
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) {
   constexpr int MT = 4, BM = 32 * MT;
   const int64_t assignments = (int64_t)a.T * a.k;
   const int mtiles = (int)(assignments / BM) + a.E + (a.has_shared ? (a.T + BM - 1) / BM : 0);
+  const int ftiles = (int)(assignments / FMAXR) + a.E + (a.has_shared ? (a.T + FMAXR - 1) / FMAXR : 0);
   const int vec_g = ((a.H / BLK) % 4 == 0) && (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 8 == 0) &&
                     (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 8 == 0));
   const int vec_d = ((a.I / BLK) % 4 == 0) && ((uintptr_t)a.w_down % 8 == 0) &&
                     (!a.has_shared || ((uintptr_t)a.s_down % 8 == 0));
-  hipLaunchKernelGGL((gateup_kernel<MT>), dim3((a.I + GBN - 1) / GBN, mtiles), dim3(256), 0, stream,
-                     a, vec_g);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((down_kernel<MT>), dim3((a.H + GBN - 1) / GBN, mtiles), dim3(256), 0, stream,
-                     a, vec_d);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int64_t n = (int64_t)a.T * (a.H / 8);
-  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  const bool fast_g = (a.H / BLK) % 4 == 0 && ((uintptr_t)a.x % 16 == 0) &&
+                      (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 4 == 0) &&
+                      (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 4 == 0));
+  const bool fast_d = (a.I / BLK) % 4 == 0 && ((uintptr_t)a.h % 16 == 0) &&
+                      ((uintptr_t)a.w_down % 4 == 0) && (!a.has_shared || ((uintptr_t)a.s_down % 4 == 0));
+  hipError_t err = hipSuccess;
+  if (stages & 1) {
+    if (fast_g)
+      hipLaunchKernelGGL((gemm_fast_kernel<true>), dim3((a.I + 127) / 128, ftiles), dim3(256), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((gateup_kernel<MT>), dim3((a.I + GBN - 1) / GBN, mtiles), dim3(256), 0,
+                         stream, a, vec_g);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (stages & 2) {
+    if (fast_d)
+      hipLaunchKernelGGL((gemm_fast_kernel<false>), dim3((a.H + 255) / 256, ftiles), dim3(256), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((down_kernel<MT>), dim3((a.H + GBN - 1) / GBN, mtiles), dim3(256), 0,
+                         stream, a, vec_d);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (stages & 4) {
+    const int64_t n = (int64_t)a.T * (a.H / 8);
+    hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, a);
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 }  // namespace moeq4

@@ -31,7 +31,7 @@ hipError_t launch_route_scan(int32_t* counts_w, int n_tiles, int E, int total,
 hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* base_w,
                                 int T, int k, int E, int32_t* perm, int32_t* inv_perm,
                                 hipStream_t stream);
-constexpr int kTopkTokensPerBlock = 64;
+constexpr int kTopkTokensPerBlock = 16;   // tokens (= waves) per top-k block
 
 // Prefill expert FFN.
 struct PrefillArgs {
@@ -51,7 +51,7 @@ struct PrefillArgs {
   uint16_t* o_perm;         // [T*k][H] bf16
   float* y;                 // [T][H] fp32
 };
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream);
 
 // Decode.
 struct DecodeArgs {

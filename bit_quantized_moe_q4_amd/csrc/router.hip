@@ -190,34 +190,19 @@ hipError_t launch_router_partials(const void* x, int x_bf16, int T, int H, const
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 32;
 
-// Finish one logit: pairwise tree over the nsplit (a power of two <= 64)
-// aligned subtree partials, by the same binary-counter merge as above.
+// Logit of (row idx, expert e): pairwise tree over the NS (a power of two)
+// aligned subtree partials at idx + s*stride, loads all issued together.
+template <int NS>
 __device__ __forceinline__ float finish_logit(const float* __restrict__ partials, size_t stride,
-                                              int nsplit, size_t idx, const float* bias, int e) {
-  float st[7];
+                                              size_t idx, const float* bias, int e) {
+  float v[NS];
 #pragma unroll
-  for (int s = 0; s < 64; s++) {
-    if (s < nsplit) {
-      float a = partials[(size_t)s * stride + idx];
-      int lvl = 0;
+  for (int s = 0; s < NS; s++) v[s] = partials[(size_t)s * stride + idx];
 #pragma unroll
-      for (int b = 0; b < 6; b++) {
-        if (((s >> b) & 1) == 0) break;
-        lvl = b + 1;
-      }
+  for (int w = NS; w > 1; w >>= 1)
 #pragma unroll
-      for (int b = 0; b < 6; b++)
-        if (b < lvl) a = st[b] + a;
-#pragma unroll
-      for (int b = 0; b < 7; b++)
-        if (b == lvl) st[b] = a;
-    }
-  }
-  const int top = 31 - __builtin_clz((unsigned)nsplit);   // log2(nsplit)
-  float l = st[0];
-#pragma unroll
-  for (int b = 1; b < 7; b++)
-    if (b == top) l = st[b];
+    for (int i = 0; i < w / 2; i++) v[i] = v[2 * i] + v[2 * i + 1];
+  float l = v[0];
   if (bias) l = l + bias[e];
   return l;
 }
@@ -261,10 +246,13 @@ __device__ __forceinline__ void wave_topk(const float (&lv)[NJ], int E, int k, f
   my_w = ex / S;
 }
 
-template <int NJ>
-__global__ void __launch_bounds__(256) topk_hist_kernel(
-    const float* __restrict__ partials, int nsplit, const float* __restrict__ bias, int T, int E,
-    int k, float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ w,
+// Block = kTopkTokensPerBlock waves, one token per wave; then the block's
+// expert histogram by ballots over its tokens (lane = token) and each
+// assignment's stable rank inside the block.
+template <int NJ, int NS>
+__global__ void __launch_bounds__(1024) topk_hist_kernel(
+    const float* __restrict__ partials, const float* __restrict__ bias, int T, int E, int k,
+    float* __restrict__ logits_out, int32_t* __restrict__ ids, float* __restrict__ w,
     int32_t* __restrict__ counts_w, int32_t* __restrict__ rank) {
   constexpr int TPB = kTopkTokensPerBlock;
   __shared__ int32_t ids_l[TPB][kMaxK];
@@ -273,31 +261,33 @@ __global__ void __launch_bounds__(256) topk_hist_kernel(
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int t0 = blockIdx.x * TPB;
   const size_t stride = (size_t)T * E;
-
-  for (int q = 0; q < TPB / 4; q++) {
-    const int tl = wave * (TPB / 4) + q;
-    const int t = t0 + tl;
-    if (t >= T) break;                    // uniform per wave
-    float lv[NJ];
+  {
+    const int t = t0 + wave;
+    if (t < T) {                          // uniform per wave
+      float lv[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      const int e = lane + 64 * j;
-      lv[j] = 0.0f;
-      if (e < E) {
-        lv[j] = finish_logit(partials, stride, nsplit, (size_t)t * E + e, bias, e);
-        if (logits_out) logits_out[(size_t)t * E + e] = lv[j];
+      for (int j = 0; j < NJ; j++) {
+        const int e = lane + 64 * j;
+        lv[j] = 0.0f;
+        if (e < E) lv[j] = finish_logit<NS>(partials, stride, (size_t)t * E + e, bias, e);
+      }
+      if (logits_out) {
+#pragma unroll
+        for (int j = 0; j < NJ; j++) {
+          const int e = lane + 64 * j;
+          if (e < E) logits_out[(size_t)t * E + e] = lv[j];
+        }
+      }
+      float my_v, my_w;
+      int my_e;
+      wave_topk<NJ>(lv, E, k, my_v, my_e, my_w);
+      if (lane < k) {
+        ids[(size_t)t * k + lane] = my_e;
+        w[(size_t)t * k + lane] = my_w;
+        ids_l[wave][lane] = my_e;
       }
     }
-    float my_v, my_w;
-    int my_e;
-    wave_topk<NJ>(lv, E, k, my_v, my_e, my_w);
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = my_e;
-      w[(size_t)t * k + lane] = my_w;
-      ids_l[tl][lane] = my_e;
-    }
   }
-  // per-block expert histogram: bit e of mask_l[tl] says token tl picked e
   const int nwords = (E + 31) / 32;
   for (int i = threadIdx.x; i < TPB * (kMaxE / 32 + 1); i += blockDim.x)
     (&mask_l[0][0])[i] = 0u;
@@ -309,9 +299,9 @@ __global__ void __launch_bounds__(256) topk_hist_kernel(
     }
   }
   __syncthreads();
-  // one ballot per expert over the 64 tokens of the block (lane = token)
-  for (int wd = wave; wd < nwords; wd += 4) {
-    const uint32_t word = mask_l[lane][wd];
+  // one ballot per expert over the block's tokens (lane = token, lanes >= TPB read 0)
+  for (int wd = wave; wd < nwords; wd += blockDim.x / 64) {
+    const uint32_t word = (lane < TPB) ? mask_l[lane][wd] : 0u;
     for (int b = 0; b < 32; b++) {
       const int e = wd * 32 + b;
       if (e >= E) break;
@@ -323,7 +313,6 @@ __global__ void __launch_bounds__(256) topk_hist_kernel(
     }
   }
   __syncthreads();
-  // stable rank of each assignment inside the block: earlier tokens first
   if (threadIdx.x < TPB && t0 + (int)threadIdx.x < T) {
     const int tl = threadIdx.x;
     const unsigned long long below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
@@ -338,15 +327,27 @@ hipError_t launch_topk_hist(const float* partials, const RouterSplit& sp, const 
                             int T, int E, int k, float* logits_out, int32_t* ids, float* w,
                             int32_t* counts_w, int32_t* rank, hipStream_t stream) {
   dim3 grid((T + kTopkTokensPerBlock - 1) / kTopkTokensPerBlock);
+  dim3 block(64 * kTopkTokensPerBlock);
   const int nj = (E + 63) / 64;
-#define MOEQ4_TK(NJV)                                                                        \
-  hipLaunchKernelGGL((topk_hist_kernel<NJV>), grid, dim3(256), 0, stream, partials, sp.nsplit, \
-                     bias, T, E, k, logits_out, ids, w, counts_w, rank)
-  if (nj <= 1) MOEQ4_TK(1);
-  else if (nj <= 2) MOEQ4_TK(2);
-  else if (nj <= 4) MOEQ4_TK(4);
-  else if (nj <= 8) MOEQ4_TK(8);
-  else MOEQ4_TK(16);
+#define MOEQ4_TK(NJV, NSV)                                                                    \
+  hipLaunchKernelGGL((topk_hist_kernel<NJV, NSV>), grid, block, 0, stream, partials, bias, T, E, \
+                     k, logits_out, ids, w, counts_w, rank)
+#define MOEQ4_TK_NS(NJV)                          \
+  switch (sp.nsplit) {                            \
+    case 1: MOEQ4_TK(NJV, 1); break;              \
+    case 2: MOEQ4_TK(NJV, 2); break;              \
+    case 4: MOEQ4_TK(NJV, 4); break;              \
+    case 8: MOEQ4_TK(NJV, 8); break;              \
+    case 16: MOEQ4_TK(NJV, 16); break;            \
+    case 32: MOEQ4_TK(NJV, 32); break;            \
+    default: MOEQ4_TK(NJV, 64); break;            \
+  }
+  if (nj <= 1) { MOEQ4_TK_NS(1) }
+  else if (nj <= 2) { MOEQ4_TK_NS(2) }
+  else if (nj <= 4) { MOEQ4_TK_NS(4) }
+  else if (nj <= 8) { MOEQ4_TK_NS(8) }
+  else { MOEQ4_TK_NS(16) }
+#undef MOEQ4_TK_NS
 #undef MOEQ4_TK
   return hipGetLastError();
 }
@@ -359,36 +360,54 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t* __restrict__ 
                                                           int32_t* __restrict__ offsets) {
   __shared__ int32_t part[1024];
   __shared__ int32_t tot[kMaxE + 1];
+  constexpr int CH = 16;                   // loads issued together
   const int tpe = blockDim.x / E;          // threads per expert (>= 1)
   const int e = threadIdx.x % E, g = threadIdx.x / E;
-  const bool active = g < tpe;
   const int per = (nt + tpe - 1) / tpe;
   const int b0 = g * per, b1 = min(nt, b0 + per);
   int run = 0;
-  if (active)
-    for (int b = b0; b < b1; b++) run += counts_w[(size_t)b * E + e];
+  for (int b = b0; b < b1; b += CH) {
+    int c[CH];
+#pragma unroll
+    for (int i = 0; i < CH; i++) c[i] = (b + i < b1) ? counts_w[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < CH; i++) run += c[i];
+  }
   part[threadIdx.x] = run;
   __syncthreads();
   // exclusive prefix of the groups of one expert; expert totals
   int before = 0;
-  if (active) {
-    for (int q = 0; q < g; q++) before += part[q * E + e];
-    if (g == tpe - 1) tot[e] = before + run;
-  }
+  for (int q = 0; q < g; q++) before += part[q * E + e];
+  if (g == tpe - 1) tot[e] = before + run;
   __syncthreads();
-  if (threadIdx.x == 0) {                  // E <= 1024: short serial scan
-    int acc = 0;
-    for (int i = 0; i < E; i++) { const int c = tot[i]; tot[i] = acc; acc += c; }
-    tot[E] = acc;
-  }
-  __syncthreads();
-  if (active) {
-    int acc = tot[e] + before;
-    for (int b = b0; b < b1; b++) {
-      const int c = counts_w[(size_t)b * E + e];
-      counts_w[(size_t)b * E + e] = acc;
-      acc += c;
+  if (threadIdx.x < 64) {                  // exclusive scan of the E totals by one wave
+    int carry = 0;
+    for (int base = 0; base < E; base += 64) {
+      const int i = base + threadIdx.x;
+      const int v = (i < E) ? tot[i] : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if ((int)threadIdx.x >= d) incl += o;
+      }
+      if (i < E) tot[i] = carry + incl - v;
+      carry += __shfl(incl, 63, 64);
     }
+    if (threadIdx.x == 0) tot[E] = carry;
+  }
+  __syncthreads();
+  int acc = tot[e] + before;
+  for (int b = b0; b < b1; b += CH) {
+    int c[CH];
+#pragma unroll
+    for (int i = 0; i < CH; i++) c[i] = (b + i < b1) ? counts_w[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < CH; i++)
+      if (b + i < b1) {
+        counts_w[(size_t)(b + i) * E + e] = acc;
+        acc += c[i];
+      }
   }
   for (int i = threadIdx.x; i <= E; i += blockDim.x) offsets[i] = (i == E) ? total : tot[i];
 }
