@@ -112,28 +112,48 @@ __device__ __forceinline__ int tok_fill(const PrefillArgs& a, const Tile& t) {
   return (t.expert >= 0) ? min(max(a.perm[t.pos0] / a.k, 0), a.T - 1) : t.m0;
 }
 
-// 8 bf16 weights of element group Q (0..3) of block J of a lane's 72-byte run.
-// Group 0: elements 0..7 (low nibbles of bytes 0..7), 1: 8..15 (low nibbles of
-// bytes 8..15), 2: 16..23 (high nibbles of bytes 0..7), 3: 24..31.
-// Each value (q - 8) * d is exact in fp32 and rounded once to bf16.
+// 8 bf16 weights of element group Q (0..3) of block J of a lane's run of
+// whole blocks.  Group 0: elements 0..7 (low nibbles of bytes 0..7), 1: 8..15
+// (low nibbles of bytes 8..15), 2: 16..23 (high nibbles of bytes 0..7),
+// 3: 24..31.  Each value (q - 8) * d is exact in fp32 and rounded once to
+// bf16.  A high nibble is read in place as the byte 16q and scaled by d/16
+// (exact: a power-of-two step).  The nibble mask goes through an opaque
+// v_and_b32 so that each byte converts with one v_cvt_f32_ubyte{0..3}.
+__device__ __forceinline__ uint32_t opaque_and(uint32_t w, uint32_t m) {
+  uint32_t r;
+  asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(m));
+  return r;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  const bf16x2_t b = __builtin_convertvector(v, bf16x2_t);   // round to nearest even
+  return __builtin_bit_cast(uint32_t, b);
+}
+
 template <int J, int Q>
 __device__ __forceinline__ bf16x8_t dequant8(const uint32_t* D) {
   uint32_t sc, nib[4];
   span_block<J>(D, sc, nib);
   const float d = f16_bits_to_f32(sc);
   const float off = -8.0f * d;
-  const uint32_t w0 = nib[2 * (Q & 1)], w1 = nib[2 * (Q & 1) + 1];
-  const uint32_t v0 = (Q >> 1) ? ((w0 >> 4) & 0x0f0f0f0fu) : (w0 & 0x0f0f0f0fu);
-  const uint32_t v1 = (Q >> 1) ? ((w1 >> 4) & 0x0f0f0f0fu) : (w1 & 0x0f0f0f0fu);
-  bf16x8_t r;
+  const float mul = (Q >> 1) ? d * 0.0625f : d;
+  const uint32_t mask = (Q >> 1) ? 0xf0f0f0f0u : 0x0f0f0f0fu;
+  const uint32_t v0 = opaque_and(nib[2 * (Q & 1)], mask);
+  const uint32_t v1 = opaque_and(nib[2 * (Q & 1) + 1], mask);
+  float f[8];
 #pragma unroll
   for (int b = 0; b < 4; b++) {
-    const float f0 = __builtin_fmaf((float)((v0 >> (8 * b)) & 0xffu), d, off);
-    const float f1 = __builtin_fmaf((float)((v1 >> (8 * b)) & 0xffu), d, off);
-    r[b] = (short)f32_to_bf16_bits(f0);
-    r[4 + b] = (short)f32_to_bf16_bits(f1);
+    f[b] = __builtin_fmaf((float)((v0 >> (8 * b)) & 0xffu), mul, off);
+    f[4 + b] = __builtin_fmaf((float)((v1 >> (8 * b)) & 0xffu), mul, off);
   }
-  return r;
+  uint32_t w[4];
+#pragma unroll
+  for (int p = 0; p < 4; p++) w[p] = pack_bf16x2(f[2 * p], f[2 * p + 1]);
+  return __builtin_bit_cast(bf16x8_t, w);
 }
 
 // Load a lane's run of blocks 4g..4g+3 of one weight row for one K-step into
@@ -338,24 +358,28 @@ __global__ void __launch_bounds__(256, 2) down_kernel(PrefillArgs a, int vec_b) 
 // of its weights is dequantised once per block of columns, not once per
 // fixed-size piece (the thin-M cost the pages identify).
 //
-// Block: 4 waves, each computing two 32-column MFMA operands per activation
+// Block: 8 waves, each computing two 32-column MFMA operands per activation
 // fragment -- gate and up for the same 32 columns of I (gate/up kernel), or
 // two 32-column groups of H (down kernel) -- so one 1 KB LDS read of A feeds
-// two MFMAs.  gate/up blocks cover 128 columns of I, down blocks 256 of H.
+// two MFMAs.  gate/up blocks cover 256 columns of I, down blocks 512 of H;
+// the 8 waves share one activation tile.
 //
-// Software pipeline, one K-step ahead:
-//   - the next step's activation tile [rows][16 chunks of 16 B] goes straight
-//     from global memory into the other of two LDS buffers (direct
-//     global->LDS loads); chunk c of row m sits at slot c ^ (m & 15), so the
-//     32 rows a wave reads for one MFMA hit distinct banks;
-//   - each lane's next-step weight bytes (2 whole 18-byte blocks per row)
-//     go into registers;
+// Software pipeline, one K-step ahead, everything through LDS with direct
+// global->LDS loads (no register staging):
+//   - activations: the next step's tile [rows][16 chunks of 16 B] into the
+//     other of two buffers; chunk c of row m sits at slot c ^ (m & 15), so
+//     the 32 rows a wave reads for one MFMA hit distinct banks;
+//   - weights: each wave's next-step bytes of its 32 (or 2x32) weight rows,
+//     as 12-byte chunks of the rows' 72-byte step pieces (4 whole blocks), so
+//     each 64-lane load touches a few cache lines instead of one line per
+//     lane; the wave copies the current step's pieces into registers first,
+//     then reuses its LDS region for the next step's;
 // while the current step's MFMAs run.  Raw barriers (no memory fence) keep
 // the prefetch in flight across them; each wave waits for its own loads of a
 // buffer before the barrier that publishes it.
 // K order inside a step: MFMA instruction i (0..7) takes, in lane half g,
-// elements 8*(i%4)..+8 of block 2g + i/4 -- lane (n, g) streams blocks
-// 2g, 2g+1 of weight row n and reads activations at step offset 64g + 8i.
+// elements 8*(i%4)..+8 of block 2g + i/4 -- lane (n, g) reads blocks
+// 2g, 2g+1 of weight row n and activations at step offset 64g + 8i.
 constexpr int FMAXS = 5;                 // max 32-row subtiles per tile
 constexpr int FMAXR = 32 * FMAXS;        // max rows per tile
 
@@ -425,11 +449,15 @@ __device__ __forceinline__ void load_run2(const uint8_t* __restrict__ p, uint32_
   for (int v = 0; v < 9; v++) D[v] = s[v];
 }
 
-// One K-step: 8 k-slices x MS subtiles x 2 operands.
+__device__ __forceinline__ void lds_load12(const void* g, uint32_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 12, 0, 0);
+}
+
+// One K-step: 8 k-slices x MS subtiles x 2 operands (weights in D0, D1).
 template <int MS>
-__device__ __forceinline__ void mma_step128(const uint16_t* As, int ln, int g, const uint32_t (&D0)[9],
-                                            const uint32_t (&D1)[9], f32x16_t (&acc0)[FMAXS],
-                                            f32x16_t (&acc1)[FMAXS]) {
+__device__ __forceinline__ void mma_step128(const uint16_t* As, const uint32_t (&D0)[9],
+                                            const uint32_t (&D1)[9], int ln, int g,
+                                            f32x16_t (&acc0)[FMAXS], f32x16_t (&acc1)[FMAXS]) {
   const int x = ln & 15;
   const uint16_t* base = As + ln * 128;
 #define MOEQ4_F(J, Q)                                                                      \
@@ -448,43 +476,69 @@ __device__ __forceinline__ void mma_step128(const uint16_t* As, int ln, int g, c
 #undef MOEQ4_F
 }
 
-// LDS of one block: two activation buffers of FMAXR rows x 256 B (80 KB:
-// two blocks fit a CU's 160 KB).
+constexpr int FWAVES = 8;
+// 12-byte direct loads land at a 16-byte lane stride: one operand's 32 rows
+// x 6 chunks take 192 x 16 B of LDS
+constexpr int FBOP = 192 * 4;            // dwords per operand region
+constexpr int FBW = 2 * FBOP;            // dwords per wave
+
+// LDS of one block: two activation buffers of FMAXR rows x 256 B (80 KB) and
+// one weight region per wave (8 x 6 KB).
 struct FastSmem {
   uint16_t a0[FMAXR * 128];
   uint16_t a1[FMAXR * 128];
+  uint32_t b[FWAVES * FBW];
 };
+
+// Lane (n, g)'s 36 weight bytes of a step: row n's chunks 3g..3g+2.
+__device__ __forceinline__ void read_piece(const uint32_t* op, int n, int g, uint32_t (&D)[9]) {
+#pragma unroll
+  for (int j = 0; j < 3; j++) {
+    const uint32_t* c = op + 4 * (6 * n + 3 * g + j);
+    D[3 * j] = c[0];
+    D[3 * j + 1] = c[1];
+    D[3 * j + 2] = c[2];
+  }
+}
 
 template <int MS, bool GATEUP>
 __device__ __forceinline__ void fast_tile(const PrefillArgs& a, const Tile& t, FastSmem& sm) {
-  constexpr int NA = 2 * MS;                   // direct 1 KB loads per wave per step (4 waves)
-  constexpr int NB = 18;                       // weight dword loads per lane per step
+  constexpr int NA = MS;                       // activation 1 KB loads per wave per step
+  constexpr int NB = 6;                        // weight 12-byte-chunk loads per wave per step
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, g = lane / 32;
   const int H = a.H, I = a.I;
   const int N = GATEUP ? I : H, K = GATEUP ? H : I;
   const int nb = K / BLK;
   // gate/up: 32 columns per wave; down: 64 columns per wave (two groups)
-  const int ncol0 = GATEUP ? blockIdx.x * 128 + wave * 32 : blockIdx.x * 256 + wave * 64;
+  const int ncol0 = GATEUP ? blockIdx.x * 256 + wave * 32 : blockIdx.x * 512 + wave * 64;
   const bool live0 = ncol0 < N;
   const bool live1 = GATEUP ? live0 : (ncol0 + 32 < N);
-  const int n0 = min(ncol0, N - 32) + ln;      // dead groups load a valid row and store nothing
-  const int n1 = GATEUP ? n0 : min(ncol0 + 32, N - 32) + ln;
+  const int c0 = min(ncol0, N - 32);           // dead groups load valid rows and store nothing
+  const int c1 = GATEUP ? c0 : min(ncol0 + 32, N - 32);
   const size_t rb = (size_t)nb * Q4B;
-  const uint8_t *row0, *row1;
+  const uint8_t *rows0, *rows1;                // first weight row of each 32-row operand
   if (GATEUP) {
-    row0 = (t.expert >= 0) ? a.w_gate + ((size_t)t.expert * I + n0) * rb : a.s_gate + (size_t)n0 * rb;
-    row1 = (t.expert >= 0) ? a.w_up + ((size_t)t.expert * I + n0) * rb : a.s_up + (size_t)n0 * rb;
+    rows0 = (t.expert >= 0) ? a.w_gate + ((size_t)t.expert * I + c0) * rb : a.s_gate + (size_t)c0 * rb;
+    rows1 = (t.expert >= 0) ? a.w_up + ((size_t)t.expert * I + c0) * rb : a.s_up + (size_t)c0 * rb;
   } else {
     const uint8_t* wd = (t.expert >= 0) ? a.w_down + (size_t)t.expert * H * rb : a.s_down;
-    row0 = wd + (size_t)n0 * rb;
-    row1 = wd + (size_t)n1 * rb;
+    rows0 = wd + (size_t)c0 * rb;
+    rows1 = wd + (size_t)c1 * rb;
   }
-  // element offsets (from abase) of this lane's direct-load rows, 4 rows per 1 KB instruction
+  // weight loads: a row's 72 bytes of the step are six 12-byte chunks; wave-
+  // load v covers chunks 64v..64v+63 of the operand's 32 rows
+  uint32_t boff[3];
+#pragma unroll
+  for (int v = 0; v < 3; v++) {
+    const int d = 64 * v + lane;
+    boff[v] = (uint32_t)(d / 6) * (uint32_t)rb + 12u * (uint32_t)(d % 6);
+  }
+  // activation loads: 4 rows per 1 KB wave-load
   const uint16_t* abase = GATEUP ? a.x : a.h + (size_t)t.pos0 * I;
   uint32_t src[NA];
 #pragma unroll
   for (int q = 0; q < NA; q++) {
-    const int jj = wave + 4 * q;
+    const int jj = wave + FWAVES * q;
     const int m = min(4 * jj + (lane >> 4), t.rows - 1);   // padding rows repeat the last row
     const int c = ((lane & 15) ^ ((4 * jj + (lane >> 4)) & 15));
     uint32_t rowel;
@@ -496,14 +550,26 @@ __device__ __forceinline__ void fast_tile(const PrefillArgs& a, const Tile& t, F
     }
     src[q] = rowel + 8u * (uint32_t)c;
   }
-  auto issue_a = [&](int s, uint16_t* buf) {
+  uint32_t* bw = sm.b + wave * FBW;
+  auto issue_a = [&](int s, uint16_t* abuf) {
 #pragma unroll
-    for (int q = 0; q < NA; q++) lds_load16(abase + src[q] + 128 * s, buf + (wave + 4 * q) * 512);
+    for (int q = 0; q < NA; q++) lds_load16(abase + src[q] + 128 * s, abuf + (wave + FWAVES * q) * 512);
   };
-  auto load_b = [&](int s, uint32_t (&D0)[9], uint32_t (&D1)[9]) {
-    const size_t ofs = (size_t)(4 * s + 2 * g) * Q4B;
-    load_run2(row0 + ofs, D0);
-    load_run2(row1 + ofs, D1);
+  auto issue_b = [&](int s) {
+    const size_t ko = (size_t)s * 72;
+#pragma unroll
+    for (int v = 0; v < 3; v++) lds_load12(rows0 + ko + boff[v], bw + 256 * v);
+#pragma unroll
+    for (int v = 0; v < 3; v++) lds_load12(rows1 + ko + boff[v], bw + FBOP + 256 * v);
+  };
+  // step s: A(s) and B(s) landed; copy B(s) to registers, refill with B(s+1)
+  auto take_b = [&](int s, int nsteps, uint32_t (&D0)[9], uint32_t (&D1)[9]) {
+    read_piece(bw, ln, g, D0);
+    read_piece(bw + FBOP, ln, g, D1);
+    if (s + 1 < nsteps) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): the piece reads are done
+      issue_b(s + 1);
+    }
   };
 
   f32x16_t acc0[FMAXS], acc1[FMAXS];
@@ -513,37 +579,40 @@ __device__ __forceinline__ void fast_tile(const PrefillArgs& a, const Tile& t, F
     for (int r = 0; r < 16; r++) { acc0[q][r] = 0.0f; acc1[q][r] = 0.0f; }
 
   const int nsteps = nb / 4;
-  uint32_t P0[9], P1[9], Q0[9], Q1[9];
+  uint32_t D0[9], D1[9];
+  issue_b(0);
   issue_a(0, sm.a0);
-  load_b(0, P0, P1);
-  // pairs of steps (buffer 0 / registers P, then buffer 1 / registers Q),
-  // each prefetching the next; a single loop exit keeps the accumulators
-  // in place
+  // per step s: [barrier] issue A(s+1); wait (everything but A(s+1));
+  // [barrier]; take B(s) and issue B(s+1); MFMAs of step s.
+  // Pairs of steps use buffer 0 then buffer 1; a single loop exit keeps the
+  // accumulators in place.
   const int npairs = nsteps / 2;
   for (int pi = 0; pi < npairs; pi++) {
     const int s = 2 * pi;
     __builtin_amdgcn_s_barrier();               // buffer 1 free (step s-1 done everywhere)
     issue_a(s + 1, sm.a1);
-    load_b(s + 1, Q0, Q1);
-    wait_vm<NA + NB>();                         // own loads of step s complete
+    wait_vm<NA>();                              // own A(s), B(s) complete
     __builtin_amdgcn_s_barrier();               // step s tile complete everywhere
-    mma_step128<MS>(sm.a0, ln, g, P0, P1, acc0, acc1);
+    take_b(s, nsteps, D0, D1);
+    mma_step128<MS>(sm.a0, D0, D1, ln, g, acc0, acc1);
     __builtin_amdgcn_s_barrier();
     if (s + 2 < nsteps) {
       issue_a(s + 2, sm.a0);
-      load_b(s + 2, P0, P1);
-      wait_vm<NA + NB>();
+      wait_vm<NA>();
     } else {
       wait_vm<0>();
     }
     __builtin_amdgcn_s_barrier();
-    mma_step128<MS>(sm.a1, ln, g, Q0, Q1, acc0, acc1);
+    take_b(s + 1, nsteps, D0, D1);
+    mma_step128<MS>(sm.a1, D0, D1, ln, g, acc0, acc1);
   }
-  if (nsteps & 1) {                             // last step in buffer 0 / registers P
+  if (nsteps & 1) {                             // last step in buffer 0
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    mma_step128<MS>(sm.a0, ln, g, P0, P1, acc0, acc1);
+    take_b(nsteps - 1, nsteps, D0, D1);
+    mma_step128<MS>(sm.a0, D0, D1, ln, g, acc0, acc1);
   }
+  const int n0 = c0 + ln, n1 = c1 + ln;
 #pragma unroll
   for (int sub = 0; sub < MS; sub++)
 #pragma unroll
@@ -566,7 +635,7 @@ __device__ __forceinline__ void fast_tile(const PrefillArgs& a, const Tile& t, F
 }
 
 template <bool GATEUP>
-__global__ void __launch_bounds__(256, 2) gemm_fast_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(512, 2) gemm_fast_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) FastSmem sm;
   const Tile t = find_tile_bal(a.offsets, a.E, a.T, a.k, a.has_shared, blockIdx.y);
   if (!t.valid) return;
@@ -631,7 +700,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
   hipError_t err = hipSuccess;
   if (stages & 1) {
     if (fast_g)
-      hipLaunchKernelGGL((gemm_fast_kernel<true>), dim3((a.I + 127) / 128, ftiles), dim3(256), 0,
+      hipLaunchKernelGGL((gemm_fast_kernel<true>), dim3((a.I + 255) / 256, ftiles), dim3(512), 0,
                          stream, a);
     else
       hipLaunchKernelGGL((gateup_kernel<MT>), dim3((a.I + GBN - 1) / GBN, mtiles), dim3(256), 0,
@@ -641,7 +710,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
   }
   if (stages & 2) {
     if (fast_d)
-      hipLaunchKernelGGL((gemm_fast_kernel<false>), dim3((a.H + 255) / 256, ftiles), dim3(256), 0,
+      hipLaunchKernelGGL((gemm_fast_kernel<false>), dim3((a.H + 511) / 512, ftiles), dim3(512), 0,
                          stream, a);
     else
       hipLaunchKernelGGL((down_kernel<MT>), dim3((a.H + GBN - 1) / GBN, mtiles), dim3(256), 0,
