@@ -16,8 +16,8 @@ in HBM when timing starts:
   layer shape, captured once in a HIP graph and replayed; 16 packed copies
   rotate so every step streams its experts from HBM.  Reported as weight
   GB/s = 16,973,824 B per step / time per step.
-- roofline: the dominant prefill kernel (grouped gate/up GEMM) timed with HIP
-  events around its own launch on the stream it runs on.
+- roofline: the dominant prefill kernel (grouped gate/up GEMM, gemm_g2_kernel)
+  timed with HIP events around its own launch on the stream it runs on.
 - cpu_baseline: the CPU oracle (single-threaded C) on a bounded token sample
   of the same workload, scaled to tokens/s.
 """
@@ -236,7 +236,7 @@ def main():
             "shared_expert": cfg.shared, "layer_copies_rotated": len(pre["layers"]),
         },
         "roofline": {
-            "kernel": "gateup_kernel (grouped gate/up GEMM + SwiGLU)",
+            "kernel": "gemm_g2_kernel<true> (grouped gate/up GEMM + SwiGLU)",
             "bound": "mfma",
             "achieved": round(ach_gu, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -9,25 +9,28 @@
 // bf16 MFMA (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
 //
 // Kernels:
-//   gateup   per (expert tile of <=BM rows, 128 columns of I): G = X W_g^T and
-//            U = X W_u^T, epilogue h = silu(G) * U -> bf16, rows in segment order
-//   down     per (expert tile, 128 columns of H): O = h W_d^T -> bf16 rows in
-//            segment order (routed) or fp32 straight into y (shared expert)
+//   gateup/down (generic, any K a multiple of 32): per (expert tile of <= 128
+//            rows, 128 columns), 4 waves each owning 32 output columns and
+//            every row of the tile, activation rows staged in LDS per K-step
+//            of 256; one launch per projection.
+//   gemm_g2 (default for K a multiple of 64): 4-wave blocks, two per CU,
+//            balanced tiles of <= 160 rows, K-steps of 64, direct global->LDS
+//            activation loads double buffered, weights one step ahead in
+//            registers, column blocks of a tile on one XCD.
+//   gemm_g4 (alternative schedule, see its section).
 //   combine  y[t] += sum_s w[t,s] * O[inv_perm[t*k+s]]
+// Epilogues: gate/up writes h = silu(G) * U in bf16 (rows in segment order);
+// down writes each routed row's output in bf16 (segment order) and the shared
+// expert's output in fp32 straight into y.
 //
-// Work split inside a block: 4 waves, each owns 32 output columns and every
-// row of the tile (BM/32 MFMA subtiles), so each weight is dequantised once
-// per block.  Activation rows (gathered through perm) are staged in LDS per
-// K-step of 256 (8 Q4 blocks).  K inside a step is permuted, identically for
-// both operands (a dot product does not depend on the order of its terms):
-// MFMA instruction i (0..15) takes, in lane half g, elements 8*(i%4)..+8 of
-// block 4g + i/4 -- so lane (n, g) needs exactly blocks 4g..4g+3 of weight
-// row n, one contiguous 72-byte run of whole 18-byte blocks, and reads its
-// activations at step offset 128g + 8i.
+// Dequantisation: each weight value (q - 8) * d is exact in fp32 (a 4-bit
+// integer times an 11-bit significand) and is rounded once to bf16, in
+// registers, once per weight per block.  K inside a step is permuted
+// identically for both operands (a dot product does not depend on the order
+// of its terms), so the 8 bf16 values a lane feeds one MFMA are one element
+// group of one Q4 block.
 //
-// Tiles are found on the device from expert_offsets (no host round trip):
-// expert e has ceil(c_e / BM) tiles, in expert order, then the shared expert's
-// ceil(T / BM) tiles; blocks beyond the last tile exit.
+// Tiles are found on the device from expert_offsets (no host round trip).
 #include "launch.hpp"
 #include "device_math.hpp"
 #include "w4a8.hpp"
@@ -121,7 +124,7 @@ __device__ __forceinline__ int tok_fill(const PrefillArgs& a, const Tile& t) {
 // v_and_b32 so that each byte converts with one v_cvt_f32_ubyte{0..3}.
 __device__ __forceinline__ uint32_t opaque_and(uint32_t w, uint32_t m) {
   uint32_t r;
-  asm volatile("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(m));
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(w), "v"(m));
   return r;
 }
 
@@ -349,37 +352,11 @@ __global__ void __launch_bounds__(256, 2) down_kernel(PrefillArgs a, int vec_b) 
   }
 }
 
-// ---------------------------------------------------------------- fast path
-// Shapes with K a multiple of 128 (whole 4-block steps) and 4-byte aligned
-// weight rows.
-//
-// Tiles: expert e's c_e rows are cut into ceil(c_e / 160) near-equal tiles of
-// a multiple of 32 rows, so a thin expert (c_e ~ T*k/E) is ONE tile and each
-// of its weights is dequantised once per block of columns, not once per
-// fixed-size piece (the thin-M cost the pages identify).
-//
-// Block: 8 waves, each computing two 32-column MFMA operands per activation
-// fragment -- gate and up for the same 32 columns of I (gate/up kernel), or
-// two 32-column groups of H (down kernel) -- so one 1 KB LDS read of A feeds
-// two MFMAs.  gate/up blocks cover 256 columns of I, down blocks 512 of H;
-// the 8 waves share one activation tile.
-//
-// Software pipeline, one K-step ahead, everything through LDS with direct
-// global->LDS loads (no register staging):
-//   - activations: the next step's tile [rows][16 chunks of 16 B] into the
-//     other of two buffers; chunk c of row m sits at slot c ^ (m & 15), so
-//     the 32 rows a wave reads for one MFMA hit distinct banks;
-//   - weights: each wave's next-step bytes of its 32 (or 2x32) weight rows,
-//     as 12-byte chunks of the rows' 72-byte step pieces (4 whole blocks), so
-//     each 64-lane load touches a few cache lines instead of one line per
-//     lane; the wave copies the current step's pieces into registers first,
-//     then reuses its LDS region for the next step's;
-// while the current step's MFMAs run.  Raw barriers (no memory fence) keep
-// the prefetch in flight across them; each wave waits for its own loads of a
-// buffer before the barrier that publishes it.
-// K order inside a step: MFMA instruction i (0..7) takes, in lane half g,
-// elements 8*(i%4)..+8 of block 2g + i/4 -- lane (n, g) reads blocks
-// 2g, 2g+1 of weight row n and activations at step offset 64g + 8i.
+// ---------------------------------------------------------------- balanced tiles
+// Expert e's c_e rows are cut into ceil(c_e / 160) near-equal tiles of a
+// multiple of 32 rows, so a thin expert (c_e ~ T*k/E) is ONE tile and each of
+// its weights is dequantised once per column block, not once per fixed-size
+// piece (the thin-M cost the pages identify).
 constexpr int FMAXS = 5;                 // max 32-row subtiles per tile
 constexpr int FMAXR = 32 * FMAXS;        // max rows per tile
 
@@ -443,104 +420,109 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ void load_run2(const uint8_t* __restrict__ p, uint32_t (&D)[9]) {
-  const uint32_t* s = reinterpret_cast<const uint32_t*>(p);
-#pragma unroll
-  for (int v = 0; v < 9; v++) D[v] = s[v];
-}
+// ---------------------------------------------------------------- two blocks per CU
+// Shapes with K a multiple of 64 and 4-byte aligned weight rows.
+//
+// Block: 4 waves and 40 KB of LDS, so two blocks share a CU and one block's
+// barrier and load waits are covered by the other's MFMAs.  A block owns one
+// tile (<= 160 rows of one expert segment, found as in find_tile_bal) and a
+// column block: gate/up 128 columns of I (wave w: gate and up rows
+// 32w..32w+31, two MFMA operands per activation fragment), down 256 columns
+// of H (wave w: two groups of 32 columns).
+//
+// K-step 64 = two Q4 blocks.  Lane (n, g) owns block g of the step of weight
+// row n: MFMA slice i (0..3) takes, in lane half g, elements 8i..8i+7 of that
+// block (the same permutation of K on both operands).  The lane loads the
+// 20 bytes at offset 16g of the row's 36-byte step piece (the block sits at
+// byte 0 or 2 of them) one step ahead into registers and realigns them with
+// v_perm.
+//
+// Activations: the step's [rows][64] bf16 tile lands in LDS by direct
+// global->LDS loads, double buffered; 16-byte chunk cc of row m sits at slot
+// cc ^ (m & 7) ^ ((m >> 3) & 1), so the rows a fragment read touches in one
+// LDS cycle fall in distinct banks for 32 or 64 banks.  One barrier per step.
+//
+// Column blocks of a tile are placed on one XCD (blocks are dealt to the 8
+// XCDs round robin): block b serves tile 8 * ((b / 8) / NCB) + b % 8 and
+// column block (b / 8) % NCB, so a tile's activation rows are fetched into
+// that XCD's L2 once.
+constexpr int G2W = 4;                  // waves per block
+constexpr int G2S = FMAXS;              // max 32-row subtiles per tile
+constexpr int G2R = 32 * G2S;           // max rows per tile
+constexpr int G2K = 64;                 // K per step
 
-__device__ __forceinline__ void lds_load12(const void* g, uint32_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 12, 0, 0);
-}
-
-// One K-step: 8 k-slices x MS subtiles x 2 operands (weights in D0, D1).
-template <int MS>
-__device__ __forceinline__ void mma_step128(const uint16_t* As, const uint32_t (&D0)[9],
-                                            const uint32_t (&D1)[9], int ln, int g,
-                                            f32x16_t (&acc0)[FMAXS], f32x16_t (&acc1)[FMAXS]) {
-  const int x = ln & 15;
-  const uint16_t* base = As + ln * 128;
-#define MOEQ4_F(J, Q)                                                                      \
-  {                                                                                        \
-    const bf16x8_t b0 = dequant8<J, Q>(D0);                                                \
-    const bf16x8_t b1 = dequant8<J, Q>(D1);                                                \
-    const int ofs = 8 * ((8 * g + 4 * (J) + (Q)) ^ x);                                     \
-    _Pragma("unroll") for (int sub = 0; sub < MS; sub++) {                                 \
-      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(base + sub * 32 * 128 + ofs); \
-      acc0[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, acc0[sub], 0, 0, 0);     \
-      acc1[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, acc1[sub], 0, 0, 0);     \
-    }                                                                                      \
-  }
-  MOEQ4_F(0, 0) MOEQ4_F(0, 1) MOEQ4_F(0, 2) MOEQ4_F(0, 3)
-  MOEQ4_F(1, 0) MOEQ4_F(1, 1) MOEQ4_F(1, 2) MOEQ4_F(1, 3)
-#undef MOEQ4_F
-}
-
-constexpr int FWAVES = 8;
-// 12-byte direct loads land at a 16-byte lane stride: one operand's 32 rows
-// x 6 chunks take 192 x 16 B of LDS
-constexpr int FBOP = 192 * 4;            // dwords per operand region
-constexpr int FBW = 2 * FBOP;            // dwords per wave
-
-// LDS of one block: two activation buffers of FMAXR rows x 256 B (80 KB) and
-// one weight region per wave (8 x 6 KB).
-struct FastSmem {
-  uint16_t a0[FMAXR * 128];
-  uint16_t a1[FMAXR * 128];
-  uint32_t b[FWAVES * FBW];
+struct G2Smem {
+  uint16_t a[2][G2R * G2K];
 };
 
-// Lane (n, g)'s 36 weight bytes of a step: row n's chunks 3g..3g+2.
-__device__ __forceinline__ void read_piece(const uint32_t* op, int n, int g, uint32_t (&D)[9]) {
-#pragma unroll
-  for (int j = 0; j < 3; j++) {
-    const uint32_t* c = op + 4 * (6 * n + 3 * g + j);
-    D[3 * j] = c[0];
-    D[3 * j + 1] = c[1];
-    D[3 * j + 2] = c[2];
-  }
+__device__ __forceinline__ int g2_slot(int cc, int m) { return cc ^ (m & 7) ^ ((m >> 3) & 1); }
+
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ void g2_load_w(const uint8_t* p, uint32_t (&D)[5]) {
+  const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(p);
+  D[0] = v.x;
+  D[1] = v.y;
+  D[2] = v.z;
+  D[3] = v.w;
+  D[4] = *reinterpret_cast<const uint32_t*>(p + 16);
 }
 
+// 8 bf16 weights of element group Q of the lane's block: scale bits `sc`,
+// nibble dwords nib[0..3] (byte j of the 16 holds element j low, j+16 high).
+template <int Q>
+__device__ __forceinline__ bf16x8_t g2_deq(const uint32_t (&nib)[4], float d) {
+  const float off = -8.0f * d;
+  const float mul = (Q >> 1) ? d * 0.0625f : d;
+  const uint32_t mask = (Q >> 1) ? 0xf0f0f0f0u : 0x0f0f0f0fu;
+  const uint32_t v0 = opaque_and(nib[2 * (Q & 1)], mask);
+  const uint32_t v1 = opaque_and(nib[2 * (Q & 1) + 1], mask);
+  float f[8];
+#pragma unroll
+  for (int b = 0; b < 4; b++) {
+    f[b] = __builtin_fmaf((float)((v0 >> (8 * b)) & 0xffu), mul, off);
+    f[4 + b] = __builtin_fmaf((float)((v1 >> (8 * b)) & 0xffu), mul, off);
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int p = 0; p < 4; p++) w[p] = pack_bf16x2(f[2 * p], f[2 * p + 1]);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+__device__ __forceinline__ void g2_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int MS, bool GATEUP>
-__device__ __forceinline__ void fast_tile(const PrefillArgs& a, const Tile& t, FastSmem& sm) {
-  constexpr int NA = MS;                       // activation 1 KB loads per wave per step
-  constexpr int NB = 6;                        // weight 12-byte-chunk loads per wave per step
+__device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int cb, G2Smem& sm) {
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, g = lane / 32;
   const int H = a.H, I = a.I;
   const int N = GATEUP ? I : H, K = GATEUP ? H : I;
-  const int nb = K / BLK;
-  // gate/up: 32 columns per wave; down: 64 columns per wave (two groups)
-  const int ncol0 = GATEUP ? blockIdx.x * 256 + wave * 32 : blockIdx.x * 512 + wave * 64;
-  const bool live0 = ncol0 < N;
-  const bool live1 = GATEUP ? live0 : (ncol0 + 32 < N);
-  const int c0 = min(ncol0, N - 32);           // dead groups load valid rows and store nothing
-  const int c1 = GATEUP ? c0 : min(ncol0 + 32, N - 32);
-  const size_t rb = (size_t)nb * Q4B;
-  const uint8_t *rows0, *rows1;                // first weight row of each 32-row operand
+  const int nsteps = K / G2K;
+  const size_t rb = (size_t)(K / BLK) * Q4B;
+  const int col0 = GATEUP ? cb * 128 + wave * 32 : cb * 256 + wave * 64;
+  const int col1 = GATEUP ? col0 : col0 + 32;
+  const bool live0 = col0 < N, live1 = col1 < N;
+  const int c0 = min(col0, N - 32), c1 = min(col1, N - 32);   // dead groups load valid rows
+  const uint8_t *w0, *w1;
   if (GATEUP) {
-    rows0 = (t.expert >= 0) ? a.w_gate + ((size_t)t.expert * I + c0) * rb : a.s_gate + (size_t)c0 * rb;
-    rows1 = (t.expert >= 0) ? a.w_up + ((size_t)t.expert * I + c0) * rb : a.s_up + (size_t)c0 * rb;
+    w0 = (t.expert >= 0) ? a.w_gate + ((size_t)t.expert * I + c0) * rb : a.s_gate + (size_t)c0 * rb;
+    w1 = (t.expert >= 0) ? a.w_up + ((size_t)t.expert * I + c0) * rb : a.s_up + (size_t)c0 * rb;
   } else {
     const uint8_t* wd = (t.expert >= 0) ? a.w_down + (size_t)t.expert * H * rb : a.s_down;
-    rows0 = wd + (size_t)c0 * rb;
-    rows1 = wd + (size_t)c1 * rb;
+    w0 = wd + (size_t)c0 * rb;
+    w1 = wd + (size_t)c1 * rb;
   }
-  // weight loads: a row's 72 bytes of the step are six 12-byte chunks; wave-
-  // load v covers chunks 64v..64v+63 of the operand's 32 rows
-  uint32_t boff[3];
-#pragma unroll
-  for (int v = 0; v < 3; v++) {
-    const int d = 64 * v + lane;
-    boff[v] = (uint32_t)(d / 6) * (uint32_t)rb + 12u * (uint32_t)(d % 6);
-  }
-  // activation loads: 4 rows per 1 KB wave-load
+  const uint8_t* p0 = w0 + (size_t)ln * rb + 16 * g;
+  const uint8_t* p1 = w1 + (size_t)ln * rb + 16 * g;
+  const uint32_t sel_n = g ? 0x07060504u : 0x05040302u;      // nibble dword k of the block
+  const uint32_t sel_s = g ? 0x0c0c0302u : 0x0c0c0100u;      // its scale (upper half zero)
+
+  // activation rows: wave-load j = wave + 4q covers tile rows 8j..8j+7
   const uint16_t* abase = GATEUP ? a.x : a.h + (size_t)t.pos0 * I;
-  uint32_t src[NA];
+  uint32_t src[MS];
 #pragma unroll
-  for (int q = 0; q < NA; q++) {
-    const int jj = wave + FWAVES * q;
-    const int m = min(4 * jj + (lane >> 4), t.rows - 1);   // padding rows repeat the last row
-    const int c = ((lane & 15) ^ ((4 * jj + (lane >> 4)) & 15));
+  for (int q = 0; q < MS; q++) {
+    const int r = 8 * (wave + G2W * q) + lane / 8;            // LDS row
+    const int m = min(r, t.rows - 1);                         // padding rows repeat the last row
     uint32_t rowel;
     if (GATEUP) {
       const int tk = (t.expert >= 0) ? a.perm[t.pos0 + m] / a.k : t.m0 + m;
@@ -548,71 +530,63 @@ __device__ __forceinline__ void fast_tile(const PrefillArgs& a, const Tile& t, F
     } else {
       rowel = (uint32_t)m * (uint32_t)I;
     }
-    src[q] = rowel + 8u * (uint32_t)c;
+    src[q] = rowel + 8u * (uint32_t)g2_slot(lane & 7, r);
   }
-  uint32_t* bw = sm.b + wave * FBW;
-  auto issue_a = [&](int s, uint16_t* abuf) {
+  auto issue_a = [&](int s, uint16_t* buf) {
 #pragma unroll
-    for (int q = 0; q < NA; q++) lds_load16(abase + src[q] + 128 * s, abuf + (wave + FWAVES * q) * 512);
-  };
-  auto issue_b = [&](int s) {
-    const size_t ko = (size_t)s * 72;
-#pragma unroll
-    for (int v = 0; v < 3; v++) lds_load12(rows0 + ko + boff[v], bw + 256 * v);
-#pragma unroll
-    for (int v = 0; v < 3; v++) lds_load12(rows1 + ko + boff[v], bw + FBOP + 256 * v);
-  };
-  // step s: A(s) and B(s) landed; copy B(s) to registers, refill with B(s+1)
-  auto take_b = [&](int s, int nsteps, uint32_t (&D0)[9], uint32_t (&D1)[9]) {
-    read_piece(bw, ln, g, D0);
-    read_piece(bw + FBOP, ln, g, D1);
-    if (s + 1 < nsteps) {
-      __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): the piece reads are done
-      issue_b(s + 1);
-    }
+    for (int q = 0; q < MS; q++) lds_load16(abase + src[q] + G2K * s, buf + (wave + G2W * q) * 512);
   };
 
-  f32x16_t acc0[FMAXS], acc1[FMAXS];
+  f32x16_t acc0[MS], acc1[MS];
 #pragma unroll
-  for (int q = 0; q < FMAXS; q++)
+  for (int q = 0; q < MS; q++)
 #pragma unroll
     for (int r = 0; r < 16; r++) { acc0[q][r] = 0.0f; acc1[q][r] = 0.0f; }
 
-  const int nsteps = nb / 4;
-  uint32_t D0[9], D1[9];
-  issue_b(0);
-  issue_a(0, sm.a0);
-  // per step s: [barrier] issue A(s+1); wait (everything but A(s+1));
-  // [barrier]; take B(s) and issue B(s+1); MFMAs of step s.
-  // Pairs of steps use buffer 0 then buffer 1; a single loop exit keeps the
-  // accumulators in place.
-  const int npairs = nsteps / 2;
-  for (int pi = 0; pi < npairs; pi++) {
-    const int s = 2 * pi;
-    __builtin_amdgcn_s_barrier();               // buffer 1 free (step s-1 done everywhere)
-    issue_a(s + 1, sm.a1);
-    wait_vm<NA>();                              // own A(s), B(s) complete
-    __builtin_amdgcn_s_barrier();               // step s tile complete everywhere
-    take_b(s, nsteps, D0, D1);
-    mma_step128<MS>(sm.a0, D0, D1, ln, g, acc0, acc1);
-    __builtin_amdgcn_s_barrier();
-    if (s + 2 < nsteps) {
-      issue_a(s + 2, sm.a0);
-      wait_vm<NA>();
-    } else {
-      wait_vm<0>();
+  uint32_t Dn0[5], Dn1[5];
+  issue_a(0, sm.a[0]);
+  g2_load_w(p0, Dn0);
+  g2_load_w(p1, Dn1);
+  // fragment read offsets (elements) inside a buffer, per slice i: row 32*sub + ln
+  int aofs[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) aofs[i] = ln * G2K + 8 * g2_slot(4 * g + i, ln);
+
+  for (int s = 0; s < nsteps; s++) {
+    uint16_t* cur = sm.a[s & 1];
+    wait_vm<0>();                                // own A(s) and W(s) landed (issued a step ago)
+    g2_barrier();                                // everyone's A(s) landed; step s-1 done
+    uint32_t D0[5], D1[5];
+#pragma unroll
+    for (int v = 0; v < 5; v++) { D0[v] = Dn0[v]; D1[v] = Dn1[v]; }
+    if (s + 1 < nsteps) {
+      issue_a(s + 1, sm.a[(s + 1) & 1]);
+      g2_load_w(p0 + 36 * (s + 1), Dn0);
+      g2_load_w(p1 + 36 * (s + 1), Dn1);
     }
-    __builtin_amdgcn_s_barrier();
-    take_b(s + 1, nsteps, D0, D1);
-    mma_step128<MS>(sm.a1, D0, D1, ln, g, acc0, acc1);
+    uint32_t n0[4], n1[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      n0[v] = __builtin_amdgcn_perm(D0[v + 1], D0[v], sel_n);
+      n1[v] = __builtin_amdgcn_perm(D1[v + 1], D1[v], sel_n);
+    }
+    const float d0 = f16_bits_to_f32(__builtin_amdgcn_perm(D0[1], D0[0], sel_s));
+    const float d1 = f16_bits_to_f32(__builtin_amdgcn_perm(D1[1], D1[0], sel_s));
+#define MOEQ4_G2(Q)                                                                          \
+  {                                                                                          \
+    const bf16x8_t b0 = g2_deq<Q>(n0, d0);                                                   \
+    const bf16x8_t b1 = g2_deq<Q>(n1, d1);                                                   \
+    _Pragma("unroll") for (int sub = 0; sub < MS; sub++) {                                   \
+      const bf16x8_t av =                                                                    \
+          *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G2K + aofs[Q]);                \
+      acc0[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, acc0[sub], 0, 0, 0);       \
+      acc1[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, acc1[sub], 0, 0, 0);       \
+    }                                                                                        \
   }
-  if (nsteps & 1) {                             // last step in buffer 0
-    wait_vm<0>();
-    __builtin_amdgcn_s_barrier();
-    take_b(nsteps - 1, nsteps, D0, D1);
-    mma_step128<MS>(sm.a0, D0, D1, ln, g, acc0, acc1);
+    MOEQ4_G2(0) MOEQ4_G2(1) MOEQ4_G2(2) MOEQ4_G2(3)
+#undef MOEQ4_G2
   }
-  const int n0 = c0 + ln, n1 = c1 + ln;
+  const int n0c = c0 + ln, n1c = c1 + ln;
 #pragma unroll
   for (int sub = 0; sub < MS; sub++)
 #pragma unroll
@@ -623,29 +597,275 @@ __device__ __forceinline__ void fast_tile(const PrefillArgs& a, const Tile& t, F
         if (!live0) continue;
         const float gv = acc0[sub][r], uv = acc1[sub][r];
         const float hv = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
-        a.h[(size_t)(t.pos0 + rr) * I + n0] = f32_to_bf16_bits(hv);
+        a.h[(size_t)(t.pos0 + rr) * I + n0c] = f32_to_bf16_bits(hv);
       } else if (t.expert >= 0) {
-        if (live0) a.o_perm[(size_t)(t.pos0 + rr) * H + n0] = f32_to_bf16_bits(acc0[sub][r]);
-        if (live1) a.o_perm[(size_t)(t.pos0 + rr) * H + n1] = f32_to_bf16_bits(acc1[sub][r]);
+        if (live0) a.o_perm[(size_t)(t.pos0 + rr) * H + n0c] = f32_to_bf16_bits(acc0[sub][r]);
+        if (live1) a.o_perm[(size_t)(t.pos0 + rr) * H + n1c] = f32_to_bf16_bits(acc1[sub][r]);
       } else {
-        if (live0) a.y[(size_t)(t.m0 + rr) * H + n0] = acc0[sub][r];
-        if (live1) a.y[(size_t)(t.m0 + rr) * H + n1] = acc1[sub][r];
+        if (live0) a.y[(size_t)(t.m0 + rr) * H + n0c] = acc0[sub][r];
+        if (live1) a.y[(size_t)(t.m0 + rr) * H + n1c] = acc1[sub][r];
       }
     }
 }
 
 template <bool GATEUP>
-__global__ void __launch_bounds__(512, 2) gemm_fast_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) FastSmem sm;
-  const Tile t = find_tile_bal(a.offsets, a.E, a.T, a.k, a.has_shared, blockIdx.y);
+__global__ void __launch_bounds__(256, 2) gemm_g2_kernel(PrefillArgs a, int ncb) {
+  __shared__ __attribute__((aligned(16))) G2Smem sm;
+  const int b = blockIdx.x, q = b / 8;
+  const int tile = 8 * (q / ncb) + b % 8, cb = q % ncb;
+  const Tile t = find_tile_bal(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
   if (!t.valid) return;
-  const int ms = (t.rows + 31) / 32;
-  switch (ms) {
-    case 1: fast_tile<1, GATEUP>(a, t, sm); break;
-    case 2: fast_tile<2, GATEUP>(a, t, sm); break;
-    case 3: fast_tile<3, GATEUP>(a, t, sm); break;
-    case 4: fast_tile<4, GATEUP>(a, t, sm); break;
-    default: fast_tile<5, GATEUP>(a, t, sm); break;
+  switch ((t.rows + 31) / 32) {
+    case 1: g2_tile<1, GATEUP>(a, t, cb, sm); break;
+    case 2: g2_tile<2, GATEUP>(a, t, cb, sm); break;
+    case 3: g2_tile<3, GATEUP>(a, t, cb, sm); break;
+    case 4: g2_tile<4, GATEUP>(a, t, cb, sm); break;
+    default: g2_tile<5, GATEUP>(a, t, cb, sm); break;
+  }
+}
+
+// ---------------------------------------------------------------- persistent, weights through LDS
+// Alternative schedule (MOEQ4_GEMM_IMPL=4; shapes with K a multiple of 256
+// and 16-byte aligned weights).  Measured slower than the two-blocks-per-CU
+// kernel so far and kept for schedule work.
+//
+// One block of 4 waves per CU (one wave per SIMD, so a wave's dequantisation
+// VALU work runs beside its own MFMAs rather than contending with a second
+// wave's), persistent over a static list of units: the (tile, column block)
+// pairs of g2, tile t on XCD t % 8, block b (on XCD b % 8) serving units
+// b/8, b/8 + P, ... of its XCD's list (P blocks per XCD).
+//
+// K-steps of 64 as in g2.  Activation tiles go through a 4-slot LDS ring by
+// direct global->LDS loads issued 3 steps ahead.  A lane's 20 weight bytes
+// of a step sit in its own row, so loading them straight into registers makes
+// every 64-lane load touch 64 cache lines and saturates the texture
+// addresser; instead a wave fetches, per group of 4 steps (K = 256), its 64
+// weight rows' 144-byte pieces with 9 direct global->LDS loads in which
+// consecutive lanes read consecutive 16-byte chunks of a row (about 13 cache
+// lines per load), double buffered per group, and each lane reads its 5
+// dwords per step and operand from LDS.  Inside a step the B operand of
+// slice i+1 is dequantised and its activation fragments read while slice i's
+// MFMAs run.
+constexpr int G4S = 5;                  // max 32-row subtiles per tile (= FMAXS)
+constexpr int G4R = 32 * G4S;
+constexpr int G4K = 64;                 // K per step
+constexpr int G4NS = 4;                 // pipeline depth (steps in flight + 1)
+
+// A step of the software-pipelined slices: bc/ac hold slice Q's operands.
+template <int MS, int Q>
+__device__ __forceinline__ void g4_slice(const uint16_t* cur, const int (&aofs)[4], const uint32_t (&n0)[4],
+                                         const uint32_t (&n1)[4], float d0, float d1, bf16x8_t& bc0,
+                                         bf16x8_t& bc1, bf16x8_t (&ac)[MS], f32x16_t (&acc0)[MS],
+                                         f32x16_t (&acc1)[MS]) {
+  bf16x8_t bn0, bn1, an[MS];
+  if (Q < 3) {
+    bn0 = g2_deq<(Q + 1) & 3>(n0, d0);
+    bn1 = g2_deq<(Q + 1) & 3>(n1, d1);
+#pragma unroll
+    for (int sub = 0; sub < MS; sub++)
+      an[sub] = *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G4K + aofs[(Q + 1) & 3]);
+  }
+#pragma unroll
+  for (int sub = 0; sub < MS; sub++) {
+    acc0[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[sub], bc0, acc0[sub], 0, 0, 0);
+    acc1[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[sub], bc1, acc1[sub], 0, 0, 0);
+  }
+  if (Q < 3) {
+    bc0 = bn0;
+    bc1 = bn1;
+#pragma unroll
+    for (int sub = 0; sub < MS; sub++) ac[sub] = an[sub];
+  }
+}
+
+constexpr int G4WCH = 9;                // 16-byte chunks of a row's 144-byte group piece
+
+struct G4Smem {
+  uint16_t a[G4NS][G4R * G4K];          // 4 x 20 KB activation ring
+  uint32_t w[2][G2W][64 * G4WCH * 4];   // [buffer][wave]: 64 rows x 144 B
+};
+
+template <int MS, bool GATEUP>
+__device__ __forceinline__ void g4_unit(const PrefillArgs& a, const Tile& t, int cb, G4Smem& sm) {
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, g = lane / 32;
+  const int H = a.H, I = a.I;
+  const int N = GATEUP ? I : H, K = GATEUP ? H : I;
+  const int nsteps = K / G4K;                         // a multiple of 4, >= 4
+  const int ngroups = nsteps / 4;
+  const size_t rb = (size_t)(K / BLK) * Q4B;          // a multiple of 144
+  const int col0 = GATEUP ? cb * 128 + wave * 32 : cb * 256 + wave * 64;
+  const int col1 = GATEUP ? col0 : col0 + 32;
+  const bool live0 = col0 < N, live1 = col1 < N;
+  const int c0 = min(col0, N - 32), c1 = min(col1, N - 32);
+  const uint8_t *w0, *w1;
+  if (GATEUP) {
+    w0 = (t.expert >= 0) ? a.w_gate + ((size_t)t.expert * I + c0) * rb : a.s_gate + (size_t)c0 * rb;
+    w1 = (t.expert >= 0) ? a.w_up + ((size_t)t.expert * I + c0) * rb : a.s_up + (size_t)c0 * rb;
+  } else {
+    const uint8_t* wd = (t.expert >= 0) ? a.w_down + (size_t)t.expert * H * rb : a.s_down;
+    w0 = wd + (size_t)c0 * rb;
+    w1 = wd + (size_t)c1 * rb;
+  }
+  // weight chunk v of this lane: chunk c = 64v + lane of the wave's 64 rows
+  // (rows 0..31: operand 0, 32..63: operand 1), row c / 9, 16-byte part c % 9
+  const uint8_t* wsrc[G4WCH];
+#pragma unroll
+  for (int v = 0; v < G4WCH; v++) {
+    const int c = 64 * v + lane, r = c / G4WCH, part = c - G4WCH * r;
+    wsrc[v] = ((r >> 5) ? w1 : w0) + (size_t)(r & 31) * rb + 16 * part;
+  }
+  const uint32_t sel_n = g ? 0x07060504u : 0x05040302u;
+  const uint32_t sel_s = g ? 0x0c0c0302u : 0x0c0c0100u;
+
+  const uint16_t* abase = GATEUP ? a.x : a.h + (size_t)t.pos0 * I;
+  uint32_t src[MS];
+#pragma unroll
+  for (int q = 0; q < MS; q++) {
+    const int r = 8 * (wave + G2W * q) + lane / 8;
+    const int m = min(r, t.rows - 1);
+    uint32_t rowel;
+    if (GATEUP) {
+      const int tk = (t.expert >= 0) ? a.perm[t.pos0 + m] / a.k : t.m0 + m;
+      rowel = (uint32_t)min(max(tk, 0), a.T - 1) * (uint32_t)H;
+    } else {
+      rowel = (uint32_t)m * (uint32_t)I;
+    }
+    src[q] = rowel + 8u * (uint32_t)g2_slot(lane & 7, r);
+  }
+  int aofs[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) aofs[i] = ln * G4K + 8 * g2_slot(4 * g + i, ln);
+
+  f32x16_t acc0[MS], acc1[MS];
+#pragma unroll
+  for (int q = 0; q < MS; q++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) { acc0[q][r] = 0.0f; acc1[q][r] = 0.0f; }
+
+  auto issue_a = [&](int s, int slot) {
+#pragma unroll
+    for (int q = 0; q < MS; q++) lds_load16(abase + src[q] + G4K * s, sm.a[slot] + (wave + G2W * q) * 512);
+  };
+  auto issue_w = [&](int G, int buf) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(sm.w[buf][wave]);
+#pragma unroll
+    for (int v = 0; v < G4WCH; v++) lds_load16(wsrc[v] + 144 * (size_t)G, dst + 512 * v);
+  };
+  // step j (0..3) of the group in W buffer `buf`, activations in ring slot `slot`
+  auto compute = [&](int slot, int buf, int j) {
+    const uint16_t* cur = sm.a[slot];
+    const uint32_t* wl = sm.w[buf][wave];
+    uint32_t D0[5], D1[5];
+#pragma unroll
+    for (int v = 0; v < 5; v++) {
+      D0[v] = wl[36 * ln + 9 * j + 4 * g + v];
+      D1[v] = wl[36 * (32 + ln) + 9 * j + 4 * g + v];
+    }
+    uint32_t n0[4], n1[4];
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      n0[v] = __builtin_amdgcn_perm(D0[v + 1], D0[v], sel_n);
+      n1[v] = __builtin_amdgcn_perm(D1[v + 1], D1[v], sel_n);
+    }
+    const float d0 = f16_bits_to_f32(__builtin_amdgcn_perm(D0[1], D0[0], sel_s));
+    const float d1 = f16_bits_to_f32(__builtin_amdgcn_perm(D1[1], D1[0], sel_s));
+    bf16x8_t bc0 = g2_deq<0>(n0, d0), bc1 = g2_deq<0>(n1, d1);
+    bf16x8_t ac[MS];
+#pragma unroll
+    for (int sub = 0; sub < MS; sub++) ac[sub] = *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G4K + aofs[0]);
+    g4_slice<MS, 0>(cur, aofs, n0, n1, d0, d1, bc0, bc1, ac, acc0, acc1);
+    g4_slice<MS, 1>(cur, aofs, n0, n1, d0, d1, bc0, bc1, ac, acc0, acc1);
+    g4_slice<MS, 2>(cur, aofs, n0, n1, d0, d1, bc0, bc1, ac, acc0, acc1);
+    g4_slice<MS, 3>(cur, aofs, n0, n1, d0, d1, bc0, bc1, ac, acc0, acc1);
+  };
+
+  // Issue order: W(0), A(0), A(1), A(2); step s issues A(s+3) and, at the
+  // first step of group G, W(G+1).  At step s the wait leaves in flight only
+  // what was issued after A(s): A(s+1), A(s+2) (MS loads each, when they
+  // exist) and W(G+1) (9 loads) at steps 1..3 of a group that has a
+  // successor; W(G) was issued before A(4G), so the wait at step 4G covers it.
+  g2_barrier();                                       // ring and W buffers are free
+  issue_w(0, 0);
+  issue_a(0, 0);
+  issue_a(1, 1);
+  issue_a(2, 2);
+  int G = 0;
+  for (; G + 1 < ngroups; G++) {
+    const int s = 4 * G, buf = G & 1;
+    wait_vm<2 * MS>();
+    g2_barrier();
+    issue_a(s + 3, 3);
+    issue_w(G + 1, buf ^ 1);
+    compute(0, buf, 0);
+    wait_vm<2 * MS + G4WCH>();
+    g2_barrier();
+    issue_a(s + 4, 0);
+    compute(1, buf, 1);
+    wait_vm<2 * MS + G4WCH>();
+    g2_barrier();
+    issue_a(s + 5, 1);
+    compute(2, buf, 2);
+    wait_vm<2 * MS + G4WCH>();
+    g2_barrier();
+    issue_a(s + 6, 2);
+    compute(3, buf, 3);
+  }
+  {
+    const int s = 4 * G, buf = G & 1;
+    wait_vm<2 * MS>();
+    g2_barrier();
+    issue_a(s + 3, 3);
+    compute(0, buf, 0);
+    wait_vm<2 * MS>();
+    g2_barrier();
+    compute(1, buf, 1);
+    wait_vm<MS>();
+    g2_barrier();
+    compute(2, buf, 2);
+    wait_vm<0>();
+    g2_barrier();
+    compute(3, buf, 3);
+  }
+
+  const int n0c = c0 + ln, n1c = c1 + ln;
+#pragma unroll
+  for (int sub = 0; sub < MS; sub++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int rr = 32 * sub + 8 * (r / 4) + 4 * g + (r % 4);
+      if (rr >= t.rows) continue;
+      if (GATEUP) {
+        if (!live0) continue;
+        const float gv = acc0[sub][r], uv = acc1[sub][r];
+        const float hv = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
+        a.h[(size_t)(t.pos0 + rr) * I + n0c] = f32_to_bf16_bits(hv);
+      } else if (t.expert >= 0) {
+        if (live0) a.o_perm[(size_t)(t.pos0 + rr) * H + n0c] = f32_to_bf16_bits(acc0[sub][r]);
+        if (live1) a.o_perm[(size_t)(t.pos0 + rr) * H + n1c] = f32_to_bf16_bits(acc1[sub][r]);
+      } else {
+        if (live0) a.y[(size_t)(t.m0 + rr) * H + n0c] = acc0[sub][r];
+        if (live1) a.y[(size_t)(t.m0 + rr) * H + n1c] = acc1[sub][r];
+      }
+    }
+}
+
+template <bool GATEUP>
+__global__ void __launch_bounds__(256, 1) gemm_g4_kernel(PrefillArgs a, int ncb) {
+  __shared__ __attribute__((aligned(16))) G4Smem sm;
+  const int P = gridDim.x / 8;                        // blocks per XCD
+  const int x = blockIdx.x % 8, l = blockIdx.x / 8;
+  if (l >= P) return;
+  for (int j = l;; j += P) {
+    const int tile = 8 * (j / ncb) + x, cb = j % ncb;
+    const Tile t = find_tile_bal(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
+    if (!t.valid) break;                              // tiles are numbered densely
+    switch ((t.rows + 31) / 32) {
+      case 1: g4_unit<1, GATEUP>(a, t, cb, sm); break;
+      case 2: g4_unit<2, GATEUP>(a, t, cb, sm); break;
+      case 3: g4_unit<3, GATEUP>(a, t, cb, sm); break;
+      case 4: g4_unit<4, GATEUP>(a, t, cb, sm); break;
+      default: g4_unit<5, GATEUP>(a, t, cb, sm); break;
+    }
   }
 }
 
@@ -683,38 +903,77 @@ __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------- launch
+// Blocks of a persistent launch: the current device's CU count rounded down
+// to a multiple of 8 (blocks are dealt to the 8 XCDs round robin), cached per
+// device.
+static int persistent_blocks() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+      cus = 8;
+    cached[dev] = cus / 8 * 8;
+  }
+  return cached[dev];
+}
+
+// Kernel choice per stage: the two-blocks-per-CU grouped kernel (g2) when K
+// is a multiple of 64 and the pointers are aligned; the persistent
+// weights-through-LDS kernel (g4) only when built with MOEQ4_GEMM_IMPL=4
+// (kept for schedule work; slower than g2 so far); the generic kernels for
+// any other shape (K a multiple of 32).
+#ifndef MOEQ4_GEMM_IMPL
+#define MOEQ4_GEMM_IMPL 2
+#endif
 hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) {
   constexpr int MT = 4, BM = 32 * MT;
   const int64_t assignments = (int64_t)a.T * a.k;
   const int mtiles = (int)(assignments / BM) + a.E + (a.has_shared ? (a.T + BM - 1) / BM : 0);
-  const int ftiles = (int)(assignments / FMAXR) + a.E + (a.has_shared ? (a.T + FMAXR - 1) / FMAXR : 0);
+  // upper bound of the balanced tile count (find_tile_bal)
+  const int btiles = (int)(assignments / FMAXR) + a.E + (a.has_shared ? (a.T + FMAXR - 1) / FMAXR : 0);
   const int vec_g = ((a.H / BLK) % 4 == 0) && (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 8 == 0) &&
                     (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 8 == 0));
   const int vec_d = ((a.I / BLK) % 4 == 0) && ((uintptr_t)a.w_down % 8 == 0) &&
                     (!a.has_shared || ((uintptr_t)a.s_down % 8 == 0));
-  const bool fast_g = (a.H / BLK) % 4 == 0 && ((uintptr_t)a.x % 16 == 0) &&
-                      (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 4 == 0) &&
-                      (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 4 == 0));
-  const bool fast_d = (a.I / BLK) % 4 == 0 && ((uintptr_t)a.h % 16 == 0) &&
-                      ((uintptr_t)a.w_down % 4 == 0) && (!a.has_shared || ((uintptr_t)a.s_down % 4 == 0));
+  const bool g4_g = MOEQ4_GEMM_IMPL == 4 && a.H % 256 == 0 && ((uintptr_t)a.x % 16 == 0) &&
+                    (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 16 == 0) &&
+                    (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 16 == 0));
+  const bool g4_d = MOEQ4_GEMM_IMPL == 4 && a.I % 256 == 0 && ((uintptr_t)a.h % 16 == 0) &&
+                    ((uintptr_t)a.w_down % 16 == 0) && (!a.has_shared || ((uintptr_t)a.s_down % 16 == 0));
+  const bool g2_g = a.H % G2K == 0 && ((uintptr_t)a.x % 16 == 0) &&
+                    (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 4 == 0) &&
+                    (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 4 == 0));
+  const bool g2_d = a.I % G2K == 0 && ((uintptr_t)a.h % 16 == 0) &&
+                    ((uintptr_t)a.w_down % 4 == 0) && (!a.has_shared || ((uintptr_t)a.s_down % 4 == 0));
+  const int g2_groups = (btiles + 7) / 8;
   hipError_t err = hipSuccess;
   if (stages & 1) {
-    if (fast_g)
-      hipLaunchKernelGGL((gemm_fast_kernel<true>), dim3((a.I + 255) / 256, ftiles), dim3(512), 0,
-                         stream, a);
-    else
+    if (g4_g) {
+      hipLaunchKernelGGL((gemm_g4_kernel<true>), dim3(persistent_blocks()), dim3(256), 0, stream, a,
+                         (a.I + 127) / 128);
+    } else if (g2_g) {
+      const int ncb = (a.I + 127) / 128;
+      hipLaunchKernelGGL((gemm_g2_kernel<true>), dim3(g2_groups * 8 * ncb), dim3(256), 0, stream, a, ncb);
+    } else {
       hipLaunchKernelGGL((gateup_kernel<MT>), dim3((a.I + GBN - 1) / GBN, mtiles), dim3(256), 0,
                          stream, a, vec_g);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (stages & 2) {
-    if (fast_d)
-      hipLaunchKernelGGL((gemm_fast_kernel<false>), dim3((a.H + 511) / 512, ftiles), dim3(512), 0,
-                         stream, a);
-    else
+    if (g4_d) {
+      hipLaunchKernelGGL((gemm_g4_kernel<false>), dim3(persistent_blocks()), dim3(256), 0, stream, a,
+                         (a.H + 255) / 256);
+    } else if (g2_d) {
+      const int ncb = (a.H + 255) / 256;
+      hipLaunchKernelGGL((gemm_g2_kernel<false>), dim3(g2_groups * 8 * ncb), dim3(256), 0, stream, a, ncb);
+    } else {
       hipLaunchKernelGGL((down_kernel<MT>), dim3((a.H + GBN - 1) / GBN, mtiles), dim3(256), 0,
                          stream, a, vec_d);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
