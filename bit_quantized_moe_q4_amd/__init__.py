@@ -218,9 +218,9 @@ def moe_q4_decode_workspace_bytes(layer: MoELayer) -> int:
 
 
 def decode_workspace(layer: MoELayer, device=None) -> torch.Tensor:
-    """A zero-filled decode workspace (must be zero before its first use)."""
+    """A decode workspace (its contents need no initialisation)."""
     dev = device if device is not None else layer.w_router.device
-    return torch.zeros(max(moe_q4_decode_workspace_bytes(layer), 1), dtype=torch.uint8, device=dev)
+    return torch.empty(max(moe_q4_decode_workspace_bytes(layer), 1), dtype=torch.uint8, device=dev)
 
 
 def moe_q4_decode(layer: MoELayer, x: torch.Tensor, y: torch.Tensor | None = None,

@@ -83,15 +83,14 @@ PrefillWs prefill_ws(const moe_q4_layer* L, int32_t T) {
 }
 
 struct DecodeWs {
-  size_t ticket, partials, ids, w, qx, dx, sx, qh, dh, sh, total;
+  size_t partials, ids, w, qx, dx, sx, qh, dh, sh, total;
 };
-DecodeWs decode_ws(const moe_q4_layer* L, const moeq4::RouterSplit& sp) {
+DecodeWs decode_ws(const moe_q4_layer* L) {
   DecodeWs w;
   const size_t ns = (size_t)L->top_k + (L->has_shared ? 1 : 0);
   const size_t H = L->hidden, I = L->inter;
-  w.ticket = 0;
-  w.partials = 256;
-  w.ids = w.partials + up256((size_t)sp.nsplit * L->n_experts * 4);
+  w.partials = 0;
+  w.ids = w.partials + up256(H / 32 * (size_t)L->n_experts * 4);
   w.w = w.ids + up256((size_t)L->top_k * 4);
   w.qx = w.w + up256((size_t)L->top_k * 4);
   w.dx = w.qx + up256(H);
@@ -244,7 +243,7 @@ int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t 
 
 size_t moe_q4_decode_workspace_bytes(const moe_q4_layer* L) {
   if (check_layer(L) != MOE_Q4_OK) return 0;
-  return decode_ws(L, moeq4::decode_router_split(L->hidden, L->n_experts)).total;
+  return decode_ws(L).total;
 }
 
 int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_decode_trace* tr,
@@ -253,14 +252,11 @@ int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_
   if (rc) return rc;
   if (!x || !y) return fail(MOE_Q4_EINVAL, "moe_q4_decode: NULL pointer");
   if (!aligned(x, 16) || !aligned(y, 4)) return fail(MOE_Q4_EINVAL, "moe_q4_decode: x must be 16-byte aligned");
-  const moeq4::RouterSplit sp = moeq4::decode_router_split(L->hidden, L->n_experts);
-  if ((size_t)sp.cw * L->n_experts > 1024)
-    return fail(MOE_Q4_EINVAL, "moe_q4_decode: hidden=%d with n_experts=%d exceeds the router block", L->hidden, L->n_experts);
-  const DecodeWs W = decode_ws(L, sp);
+  const DecodeWs W = decode_ws(L);
   rc = check_ws(ws, ws_bytes, W.total);
   if (rc) return rc;
-  if (tr && ((tr->qx && !aligned(tr->qx, 16))))
-    return fail(MOE_Q4_EINVAL, "moe_q4_decode: trace qx must be 16-byte aligned");
+  if (tr && ((tr->qx && !aligned(tr->qx, 16)) || (tr->qh && !aligned(tr->qh, 16))))
+    return fail(MOE_Q4_EINVAL, "moe_q4_decode: trace qx and qh must be 16-byte aligned");
   moeq4::DecodeArgs a;
   memset(&a, 0, sizeof a);
   a.x = x;
@@ -278,7 +274,6 @@ int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_
   a.s_gate = static_cast<const uint8_t*>(L->s_gate);
   a.s_up = static_cast<const uint8_t*>(L->s_up);
   a.s_down = static_cast<const uint8_t*>(L->s_down);
-  a.ticket = at<uint32_t>(ws, W.ticket);
   a.partials = at<float>(ws, W.partials);
   a.ids = at<int32_t>(ws, W.ids);
   a.w = at<float>(ws, W.w);
@@ -297,7 +292,7 @@ int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_
     a.t_qh = tr->qh;
     a.t_dh = tr->dh;
   }
-  hipError_t e = moeq4::launch_decode(a, sp, stream);
+  hipError_t e = moeq4::launch_decode(a, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_decode");
 }
 

@@ -5,283 +5,386 @@
 // kernel over 4-bit weights read straight from memory) and Key Contribution 2.
 // On the pages the weights are read from host RAM by the CPU; here every
 // expert stays resident in HBM and the step is bound by streaming the k+S
-// selected experts' 18-byte blocks.
+// selected experts' 18-byte blocks, behind a short chain of dependent steps
+// (router -> expert choice -> gate/up -> down).  Each launch boundary is the
+// only cross-CU synchronisation: no atomics, flags or cache maintenance.
 //
 // Three launches on the caller's stream:
-//   decode_router   router GEMV split over aligned chunk subtrees; block 0
-//                   also quantises x; the last block to finish (atomic
-//                   ticket) completes the chunk tree, picks the top-k and
-//                   computes the weights, then re-arms the ticket
-//   decode_gateup   one block per (slot, 32 rows of I): gate and up rows by
-//                   the W4A8 row program, h = silu(g) * u, q8(h) of the block
-//   decode_down     one block per few output rows, all slots: down rows by
-//                   the row program, then the fixed-order weighted combine
+//   decode_router   one block per 32-element chunk c of x, one thread per
+//                   expert: the chunk's sequential FMA chain for every
+//                   expert (a leaf of the pinned pairwise tree), and the q8
+//                   codes of chunk c (a chunk is one q8 block).
+//   decode_gateup   one block per (slot, 32 values of i).  A routed slot's
+//                   block first finishes the router itself from the leaves
+//                   (tree, bias, top-k, weights: a few microseconds of
+//                   redundant work per block instead of a serial tail in
+//                   one block plus another launch); block (0, 0) publishes
+//                   ids and weights.  Then the 32 gate and 32 up rows by
+//                   the W4A8 row program with x's codes staged in LDS, and
+//                   h = silu(g) * u quantised to q8 -- the block holds
+//                   exactly one 32-group of h.
+//   decode_down     one block per few output rows: the down-row weights
+//                   into registers, every slot's q8(h) into LDS, then the
+//                   row program and the fixed-order weighted combine.
+//
+// Activation codes in LDS: block b of a row of activation blocks starts at
+// dword act_off(b) = 8b + 4*floor(b/8).  A lane owns 8 consecutive blocks,
+// so the lanes of one row start 68 dwords apart (4 banks apart) and their
+// 16-byte reads do not collide; without the pad they all hit one bank.
 #include "launch.hpp"
 #include "w4a8.hpp"
 
 namespace moeq4 {
 
-RouterSplit decode_router_split(int H, int E) {
-  RouterSplit s;
-  s.nc = H / BLK;
-  s.m = 1;
-  while (s.m < s.nc) s.m <<= 1;
-  int cw = 256 / E;
-  if (cw < 1) cw = 1;
-  int c = 1;
-  while (c * 2 <= cw) c *= 2;            // power of two <= 256/E
-  if (c > s.m) c = s.m;
-  while (s.m / c > 64) c *= 2;           // at most 64 subtrees
-  s.cw = c;
-  s.nsplit = s.m / c;
-  return s;
-}
+__device__ __forceinline__ int act_off(int b) { return 8 * b + 4 * (b >> 3); }
+__host__ __device__ inline int act_row_dwords(int nb) { return 8 * nb + 4 * ((nb + 7) / 8); }
 
-// Wave-wide (value desc, index asc) argmax.
-__device__ __forceinline__ void dec_wave_argmax(float& v, int& e) {
+// Pairwise tree over v[0 .. n-1] (n a power of two <= 64); returns the root.
+__device__ __forceinline__ float tree64(float (&v)[64], int n) {
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const float ov = __shfl_xor(v, m, 64);
-    const int oe = __shfl_xor(e, m, 64);
-    if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
-  }
+  for (int w = 64; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; i++)
+      if (w <= n) v[i] = v[2 * i] + v[2 * i + 1];
+  return v[0];
 }
 
 // ---------------------------------------------------------------- router
-template <int NS>
-__global__ void __launch_bounds__(256) decode_router_kernel(DecodeArgs a, int nc, int cw) {
-  constexpr int nsplit = NS;
-  __shared__ float xs[256 * BLK];         // cw * 32 inputs (cw <= 256)
-  __shared__ float part[1024];            // [cl][e] chain results (cw * E <= 1024)
-  __shared__ float logit_l[1024];
-  __shared__ int s_last;
-  const int tid = threadIdx.x, split = blockIdx.x;
-  const int E = a.E, H = a.H;
-  const int c0 = split * cw;
-
-  for (int i = tid; i < cw * BLK; i += blockDim.x) {
-    const int h = c0 * BLK + i;
-    xs[i] = (h < H) ? a.x[h] : 0.0f;
-  }
+__global__ void __launch_bounds__(1024) decode_router_kernel(DecodeArgs a) {
+  __shared__ float xs[BLK];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  const int E = a.E;
+  if (tid < BLK) xs[tid] = a.x[c * BLK + tid];
   __syncthreads();
-  // chunk chains: pair p = (cl, e)
-  for (int p = tid; p < cw * E; p += blockDim.x) {
-    const int cl = p / E, e = p % E;
-    const int c = c0 + cl;
+  for (int e = tid; e < E; e += blockDim.x) {
+    const float* w = a.w_router + (size_t)c * BLK * E + e;
+    float wv[BLK];
+#pragma unroll
+    for (int i = 0; i < BLK; i++) wv[i] = w[(size_t)i * E];
     float acc = 0.0f;
-    if (c < nc) {
-      const float* w = a.w_router + (size_t)c * BLK * E + e;
-#pragma unroll 8
-      for (int i = 0; i < BLK; i++) acc = __builtin_fmaf(xs[cl * BLK + i], w[(size_t)i * E], acc);
-    }
-    part[cl * E + e] = acc;
+#pragma unroll
+    for (int i = 0; i < BLK; i++) acc = __builtin_fmaf(xs[i], wv[i], acc);
+    a.partials[(size_t)c * E + e] = acc;
   }
-  __syncthreads();
-  // subtree of cw leaves per expert, level by level
-  for (int e = tid; e < E; e += blockDim.x) {
-    for (int w = cw; w > 1; w >>= 1)
-      for (int i = 0; i < w / 2; i++) part[i * E + e] = part[2 * i * E + e] + part[(2 * i + 1) * E + e];
-    a.partials[(size_t)split * E + e] = part[e];
-  }
-  // block 0 also quantises x: one thread per 32-block
-  if (split == 0) {
-    for (int b = tid; b < H / BLK; b += blockDim.x) {
-      const float* src = a.x + b * BLK;
-      float v[BLK];
-      float amax = 0.0f;
+  if (tid < BLK) {                        // q8 of chunk c: d = amax / 127, q = round(x / d)
+    const float v = xs[tid];
+    float amax = fabsf(v);
 #pragma unroll
-      for (int j = 0; j < BLK; j++) { v[j] = src[j]; amax = fmaxf(amax, fabsf(v[j])); }
-      const float d = amax / 127.0f;
-      int32_t sum = 0;
-      uint32_t words[8];
+    for (int m = 1; m < BLK; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, BLK));
+    const float d = amax / 127.0f;
+    const int q = (d == 0.0f) ? 0 : (int)roundf(v / d);
+    int sum = q;
 #pragma unroll
-      for (int c = 0; c < 8; c++) {
-        uint32_t wd = 0;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const int qi = (d == 0.0f) ? 0 : (int)roundf(v[4 * c + q] / d);
-          sum += qi;
-          wd |= ((uint32_t)qi & 0xffu) << (8 * q);
-        }
-        words[c] = wd;
-      }
-      uint4* dst = reinterpret_cast<uint4*>(a.qx + b * BLK);
-      dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-      dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
-      a.dx[b] = d;
-      a.sx[b] = sum;
-      if (a.t_qx) {
-        uint4* tq = reinterpret_cast<uint4*>(a.t_qx + b * BLK);
-        tq[0] = dst[0];
-        tq[1] = dst[1];
-      }
-      if (a.t_dx) a.t_dx[b] = d;
+    for (int m = 1; m < BLK; m <<= 1) sum += __shfl_xor(sum, m, BLK);
+    a.qx[c * BLK + tid] = (int8_t)q;
+    if (a.t_qx) a.t_qx[c * BLK + tid] = (int8_t)q;
+    if (tid == 0) {
+      a.dx[c] = d;
+      a.sx[c] = sum;
+      if (a.t_dx) a.t_dx[c] = d;
     }
-  }
-  // last block to finish completes the tree and routes
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == (uint32_t)(nsplit - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // each thread finishes experts e = tid, tid+256, ...: NS loads in flight
-  for (int e = tid; e < E; e += blockDim.x) {
-    float v[NS];
-#pragma unroll
-    for (int s = 0; s < NS; s++) v[s] = __builtin_nontemporal_load(a.partials + (size_t)s * E + e);
-#pragma unroll
-    for (int w = NS; w > 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w / 2; i++) v[i] = v[2 * i] + v[2 * i + 1];
-    float l = v[0];
-    if (a.bias) l = l + a.bias[e];
-    logit_l[e] = l;
-    if (a.t_logits) a.t_logits[e] = l;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const int lane = tid;
-    constexpr int NJ = 16;                // E <= 1024
-    float lv[NJ];
-    const int nj = (E + 63) / 64;
-#pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      const int e = lane + 64 * j;
-      lv[j] = (j < nj && e < E) ? logit_l[e] : -__builtin_inff();
-    }
-    uint32_t taken = 0;
-    float my_v = 0.0f;
-    int my_e = -1;
-    for (int s = 0; s < a.k; s++) {
-      float bv = -__builtin_inff();
-      int be = 0x7fffffff;
-      for (int j = 0; j < nj; j++) {
-        const int e = lane + 64 * j;
-        if (e < E && !((taken >> j) & 1u) && (be == 0x7fffffff || lv[j] > bv)) { bv = lv[j]; be = e; }
-      }
-      dec_wave_argmax(bv, be);
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (lane == s) { my_v = bv; my_e = be; }
-    }
-    const float l0 = __shfl(my_v, 0, 64);
-    const float ex = (lane < a.k) ? exp_p(my_v - l0) : 0.0f;
-    float S = __shfl(ex, 0, 64);
-    for (int s = 1; s < a.k; s++) S = S + __shfl(ex, s, 64);
-    const float wv = ex / S;
-    if (lane < a.k) {
-      a.ids[lane] = my_e;
-      a.w[lane] = wv;
-      if (a.t_ids) a.t_ids[lane] = my_e;
-      if (a.t_w) a.t_w[lane] = wv;
-    }
-    if (lane == 0)
-      __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ---------------------------------------------------------------- gate/up
-// Block: 64 rows (32 gate rows + the 32 matching up rows) x LPR lanes each.
-template <int BPL, bool FAST>
-__global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int lpr) {
-  extern __shared__ uint8_t dyn[];
-  const int H = a.H, I = a.I, nbh = H / BLK;
-  uint32_t* qx_l = reinterpret_cast<uint32_t*>(dyn);            // H bytes
-  float* dx_l = reinterpret_cast<float*>(dyn + H);              // nbh
-  int32_t* sx_l = reinterpret_cast<int32_t*>(dyn + H + 4 * nbh);
-  __shared__ float val[64];
-  const int tid = threadIdx.x;
-  const int slot = blockIdx.y, i0 = blockIdx.x * BLK;
+// Block: 32 values of i; rows 0..31 gate, 32..63 up, LPR lanes per row.
+constexpr int DGU_ROWS = 32;
 
-  for (int i = tid; i < H / 4; i += blockDim.x) qx_l[i] = reinterpret_cast<const uint32_t*>(a.qx)[i];
-  for (int i = tid; i < nbh; i += blockDim.x) { dx_l[i] = a.dx[i]; sx_l[i] = a.sx[i]; }
+// Router completion inside a gate/up block.  The nc leaves of expert e
+// (padded with +0 to m = next_pow2(nc)) are split into P aligned runs of
+// L = m / P <= 32 leaves, one run per lane of a group of P adjacent lanes;
+// each lane takes its run's pairwise tree, and log2(P) xor-shuffle levels
+// finish the same tree (the two operands of a level are the two subtree
+// sums, added in either order).  The top-k is taken by rank: expert e's
+// rank is the number of experts before it in (logit desc, index asc) order,
+// which for non-NaN logits picks the same experts in the same order as k
+// rounds of "first maximum among the rest".  The P lanes of a group split
+// the E comparisons.
+struct GuLds {
+  uint32_t* qa;    // act_row_dwords(nbh)   x's codes
+  float* da;       // nbh
+  int32_t* sa;     // nbh
+  float* logit;    // E
+  uint64_t* key;   // E
+};
+
+// (the key array is padded to an even count so that qa is 16-byte aligned)
+__host__ __device__ inline size_t gu_lds_bytes(int nbh, int E) {
+  return 8 * (size_t)((E + 1) & ~1) + 4 * ((size_t)act_row_dwords(nbh) + 2 * (size_t)nbh + (size_t)E);
+}
+
+__device__ __forceinline__ GuLds gu_lds(uint8_t* dyn, int nbh, int E) {
+  GuLds l;
+  l.key = reinterpret_cast<uint64_t*>(dyn);
+  l.qa = reinterpret_cast<uint32_t*>(l.key + ((E + 1) & ~1));
+  l.da = reinterpret_cast<float*>(l.qa + act_row_dwords(nbh));
+  l.sa = reinterpret_cast<int32_t*>(l.da + nbh);
+  l.logit = reinterpret_cast<float*>(l.sa + nbh);
+  return l;
+}
+
+// Order key: larger key = earlier in (logit desc, index asc); -0 and +0 tie
+// as they do under a float comparison.
+__device__ __forceinline__ uint64_t rank_key(float l, int e) {
+  uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+
+// Pairwise tree over the leaves c0 .. c0+L-1 of one expert (src = partials
+// + e, leaf stride E); leaves >= nc are +0.
+template <int L>
+__device__ __forceinline__ float leaf_run(const float* __restrict__ src, int E, int c0, int nc) {
+  float v[L];
+#pragma unroll
+  for (int j = 0; j < L; j++) {
+    const int cc = c0 + j;
+    const float t = src[(size_t)min(cc, nc - 1) * E];
+    v[j] = cc < nc ? t : 0.0f;
+  }
+#pragma unroll
+  for (int w = L; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; i++) v[i] = v[2 * i] + v[2 * i + 1];
+  return v[0];
+}
+
+__device__ __forceinline__ float leaf_tree(const float* src, int E, int c0, int L, int nc) {
+  switch (L) {
+    case 1: return leaf_run<1>(src, E, c0, nc);
+    case 2: return leaf_run<2>(src, E, c0, nc);
+    case 4: return leaf_run<4>(src, E, c0, nc);
+    case 8: return leaf_run<8>(src, E, c0, nc);
+    case 16: return leaf_run<16>(src, E, c0, nc);
+    default: return leaf_run<32>(src, E, c0, nc);
+  }
+}
+
+// Stages x's q8 blocks into LDS and, for a routed slot, finishes the router:
+// ids_l / vals_l receive the chosen experts and their logits.  Ends with a
+// barrier.
+__device__ void decode_gu_prologue(const DecodeArgs& a, const GuLds& l, int P, bool route,
+                                   int* ids_l, float* vals_l, bool publish) {
+  const int tid = threadIdx.x, nt = blockDim.x, E = a.E;
+  const int nbh = a.H / BLK, nc = nbh;
+  const int m = (int)next_pow2_u32((uint32_t)nc);
+  const int L = m / P;
+  // one memory round trip: x's codes, and each thread's first leaf run and bias
+  const bool stg = tid < nbh;             // nbh <= blockDim.x by the launch shape
+  uint4 q0 = {0, 0, 0, 0}, q1 = {0, 0, 0, 0};
+  float dv = 0.0f;
+  int32_t sv = 0;
+  if (stg) {
+    const uint4* src = reinterpret_cast<const uint4*>(a.qx) + 2 * tid;
+    q0 = src[0];
+    q1 = src[1];
+    dv = a.dx[tid];
+    sv = a.sx[tid];
+  }
+  const int items = E * P;                // item = e * P + p
+  float lv = 0.0f, bv = 0.0f;
+  if (route && tid < items) {
+    const int e = tid / P, p = tid % P;
+    lv = leaf_tree(a.partials + e, E, p * L, L, nc);
+    if (a.bias) bv = a.bias[e];
+  }
+  if (stg) {
+    uint4* dst = reinterpret_cast<uint4*>(l.qa + act_off(tid));
+    dst[0] = q0;
+    dst[1] = q1;
+    l.da[tid] = dv;
+    l.sa[tid] = sv;
+  }
+  if (!route) {
+    __syncthreads();
+    return;
+  }
+  // logits and order keys; the loop is uniform over the block (shuffles)
+  for (int b0 = 0; b0 < items; b0 += nt) {
+    const int it = b0 + tid;
+    const bool ok = it < items;
+    const int e = it / P, p = it % P;
+    if (b0 > 0 && ok) {
+      lv = leaf_tree(a.partials + e, E, p * L, L, nc);
+      if (a.bias) bv = a.bias[e];
+    }
+    for (int o = 1; o < P; o <<= 1) lv = lv + __shfl_xor(lv, o, 64);
+    if (ok && p == 0) {
+      const float lg = a.bias ? lv + bv : lv;
+      l.logit[e] = lg;
+      l.key[e] = rank_key(lg, e);
+      if (publish && a.t_logits) a.t_logits[e] = lg;
+    }
+  }
   __syncthreads();
+  for (int b0 = 0; b0 < items; b0 += nt) {
+    const int it = b0 + tid;
+    const bool ok = it < items;
+    const int e = ok ? it / P : 0, p = it % P;
+    const uint64_t ke = l.key[e];
+    int rank = 0;
+    // lane p compares against keys [j0, j1): pairs by 16-byte reads, unrolled
+    const int span = (E + P - 1) / P;
+    const int j0 = min(p * span, E), j1 = min(j0 + span, E);
+    int j = j0;
+    if (ok) {
+      if ((j & 1) && j < j1) { rank += (l.key[j] > ke) ? 1 : 0; j++; }
+      const ulonglong2* K2 = reinterpret_cast<const ulonglong2*>(l.key);
+#pragma unroll 4
+      for (; j + 2 <= j1; j += 2) {
+        const ulonglong2 q = K2[j >> 1];
+        rank += (q.x > ke) ? 1 : 0;
+        rank += (q.y > ke) ? 1 : 0;
+      }
+      if (j < j1) rank += (l.key[j] > ke) ? 1 : 0;
+    }
+    for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o, 64);
+    if (ok && p == 0 && rank < a.k) {
+      ids_l[rank] = e;
+      vals_l[rank] = l.logit[e];
+    }
+  }
+  __syncthreads();
+}
+
+template <int BPL, bool FAST>
+__global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int lpr, int P) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  const int H = a.H, I = a.I, nbh = H / BLK;
+  const GuLds l = gu_lds(dyn, nbh, a.E);
+  __shared__ float val[2 * DGU_ROWS];
+  __shared__ int ids_l[32];
+  __shared__ float vals_l[32], ex_l[32];
+  const int tid = threadIdx.x;
+  const int slot = blockIdx.y, i0 = blockIdx.x * DGU_ROWS;
+  const bool publish = blockIdx.x == 0 && slot == 0;
+  decode_gu_prologue(a, l, P, slot < a.k, ids_l, vals_l, publish);
 
   const int row = tid / lpr, lr = tid % lpr;
-  const bool is_up = row >= 32;
-  const int i = i0 + (row & 31);
+  const bool is_up = row >= DGU_ROWS;
+  const int i = i0 + (row % DGU_ROWS);
   const size_t rb = (size_t)nbh * Q4B;
   const uint8_t* base;
-  if (slot < a.k) {
-    const int e = min(max(a.ids[slot], 0), a.E - 1);
+  if (slot < a.k) {                      // (clamped: a NaN logit leaves ranks unfilled)
+    const int e = min(max(ids_l[slot], 0), a.E - 1);
     base = (is_up ? a.w_up : a.w_gate) + ((size_t)e * I + i) * rb;
   } else {
     base = (is_up ? a.s_up : a.s_gate) + (size_t)i * rb;
   }
   auto act = [&](int b) {
     ActBlock A;
-#pragma unroll
-    for (int q = 0; q < 8; q++) A.a[q] = qx_l[b * 8 + q];
-    A.d = dx_l[b];
-    A.s = sx_l[b];
+    const uint4* q = reinterpret_cast<const uint4*>(l.qa + act_off(b));
+    const uint4 u0 = q[0], u1 = q[1];
+    A.a[0] = u0.x; A.a[1] = u0.y; A.a[2] = u0.z; A.a[3] = u0.w;
+    A.a[4] = u1.x; A.a[5] = u1.y; A.a[6] = u1.z; A.a[7] = u1.w;
+    A.d = l.da[b];
+    A.s = l.sa[b];
     return A;
   };
   float v = w4a8_lane<BPL, FAST>(base, nbh, lr * BPL, act, nullptr);
   v = wave_tree_sum(v, lpr);
   if (lr == 0) val[row] = v;
   __syncthreads();
-  if (tid < 32) {
-    const float g = val[tid], u = val[32 + tid];
-    const float h = silu_p(g) * u;
+  if (tid < DGU_ROWS) {                   // h of one 32-group, then its q8
+    const float h = silu_p(val[tid]) * val[DGU_ROWS + tid];
     float amax = fabsf(h);
 #pragma unroll
-    for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+    for (int m = 1; m < BLK; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, BLK));
     const float d = amax / 127.0f;
     const int q = (d == 0.0f) ? 0 : (int)roundf(h / d);
     int sum = q;
 #pragma unroll
-    for (int m = 1; m < 32; m <<= 1) sum += __shfl_xor(sum, m, 32);
-    a.qh[(size_t)slot * I + i0 + tid] = (int8_t)q;
-    if (a.t_qh) a.t_qh[(size_t)slot * I + i0 + tid] = (int8_t)q;
+    for (int m = 1; m < BLK; m <<= 1) sum += __shfl_xor(sum, m, BLK);
+    const size_t hi = (size_t)slot * I + i0 + tid;
+    a.qh[hi] = (int8_t)q;
+    if (a.t_qh) a.t_qh[hi] = (int8_t)q;
     if (tid == 0) {
-      a.dh[(size_t)slot * (I / BLK) + blockIdx.x] = d;
-      a.sh[(size_t)slot * (I / BLK) + blockIdx.x] = sum;
-      if (a.t_dh) a.t_dh[(size_t)slot * (I / BLK) + blockIdx.x] = d;
+      const size_t g = hi / BLK;
+      a.dh[g] = d;
+      a.sh[g] = sum;
+      if (a.t_dh) a.t_dh[g] = d;
+    }
+  }
+  if (publish) {                          // w_s = e_s / ((e_0 + e_1) + ...), e_s = exp(l_s - l_0)
+    if (tid < a.k) ex_l[tid] = exp_p(vals_l[tid] - vals_l[0]);
+    __syncthreads();
+    if (tid < a.k) {
+      float S = ex_l[0];
+      for (int s = 1; s < a.k; s++) S = S + ex_l[s];
+      const float wv = ex_l[tid] / S;
+      a.ids[tid] = ids_l[tid];
+      a.w[tid] = wv;
+      if (a.t_ids) a.t_ids[tid] = ids_l[tid];
+      if (a.t_w) a.t_w[tid] = wv;
     }
   }
 }
 
 // ---------------------------------------------------------------- down + combine
-// Block: `rows` output rows x ns slots, LPR lanes per (row, slot).
-template <int BPL, bool FAST>
+// Block: `rows` output rows x ns slots, LPR lanes per (row, slot).  ALDS:
+// every slot's q8(h) staged in LDS; otherwise read from the workspace.
+template <int BPL, bool FAST, bool ALDS>
 __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr, int rows) {
-  extern __shared__ uint8_t dyn[];
+  extern __shared__ __align__(16) uint8_t dyn[];
   const int H = a.H, I = a.I, nbi = I / BLK;
   const int ns = a.k + (a.has_shared ? 1 : 0);
-  uint32_t* qh_l = reinterpret_cast<uint32_t*>(dyn);                     // ns * I bytes
-  float* dh_l = reinterpret_cast<float*>(dyn + (size_t)ns * I);           // ns * nbi
-  int32_t* sh_l = reinterpret_cast<int32_t*>(dyn + (size_t)ns * I + 4 * (size_t)ns * nbi);
-  float* o_l = reinterpret_cast<float*>(dyn + (size_t)ns * I + 8 * (size_t)ns * nbi);  // rows*ns
+  const int SS = act_row_dwords(nbi);
+  const size_t nact = ALDS ? (size_t)ns * SS + 2 * (size_t)ns * nbi : 0;
+  uint32_t* qh_l = reinterpret_cast<uint32_t*>(dyn);                     // ns * SS dwords
+  float* dh_l = reinterpret_cast<float*>(qh_l + (size_t)ns * SS);         // ns * nbi
+  int32_t* sh_l = reinterpret_cast<int32_t*>(dh_l + (size_t)ns * nbi);    // ns * nbi
+  float* o_l = reinterpret_cast<float*>(dyn) + nact;                      // rows * ns
   const int tid = threadIdx.x;
   const int r0 = blockIdx.x * rows;
-
-  for (int i = tid; i < ns * I / 4; i += blockDim.x) qh_l[i] = reinterpret_cast<const uint32_t*>(a.qh)[i];
-  for (int i = tid; i < ns * nbi; i += blockDim.x) { dh_l[i] = a.dh[i]; sh_l[i] = a.sh[i]; }
-  __syncthreads();
 
   const int item = tid / lpr, lr = tid % lpr;
   const int rl = item / ns, slot = item % ns;
   const int r = r0 + rl;
   const bool live = rl < rows && r < H;
+  const size_t rb = (size_t)nbi * Q4B;
+  const uint8_t* base = nullptr;
+  if (live)
+    base = (slot < a.k) ? a.w_down + ((size_t)min(max(a.ids[slot], 0), a.E - 1) * H + r) * rb
+                        : a.s_down + (size_t)r * rb;
+  // this lane's weight span into registers (fast shapes)
+  constexpr int NV = FAST ? 18 * BPL / 16 : 1;
+  uint32_t D[4 * NV + 1] = {};
+  if (FAST && live && lr * BPL < nbi) {
+    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * Q4B);
+#pragma unroll
+    for (int v = 0; v < NV; v++) {
+      const uint4 t = src[v];
+      D[4 * v] = t.x; D[4 * v + 1] = t.y; D[4 * v + 2] = t.z; D[4 * v + 3] = t.w;
+    }
+  }
+  D[4 * NV] = 0u;
+  // every slot's q8(h) into LDS
+  for (int g = tid; ALDS && g < ns * nbi; g += blockDim.x) {
+    const int s = g / nbi, b = g % nbi;
+    const uint4* src = reinterpret_cast<const uint4*>(a.qh) + 2 * (size_t)g;
+    uint4* dst = reinterpret_cast<uint4*>(qh_l + (size_t)s * SS + act_off(b));
+    dst[0] = src[0];
+    dst[1] = src[1];
+    dh_l[g] = a.dh[g];
+    sh_l[g] = a.sh[g];
+  }
+  __syncthreads();
   float v = 0.0f;
   if (live) {
-    const size_t rb = (size_t)nbi * Q4B;
-    const uint8_t* base = (slot < a.k)
-        ? a.w_down + ((size_t)min(max(a.ids[slot], 0), a.E - 1) * H + r) * rb
-        : a.s_down + (size_t)r * rb;
+    const uint32_t* qs = qh_l + (size_t)slot * SS;
+    const uint4* qg = reinterpret_cast<const uint4*>(a.qh) + 2 * (size_t)slot * nbi;
     auto act = [&](int b) {
       ActBlock A;
-#pragma unroll
-      for (int q = 0; q < 8; q++) A.a[q] = qh_l[(slot * I) / 4 + b * 8 + q];
-      A.d = dh_l[slot * nbi + b];
-      A.s = sh_l[slot * nbi + b];
+      const uint4* q = ALDS ? reinterpret_cast<const uint4*>(qs + act_off(b)) : qg + 2 * b;
+      const uint4 u0 = q[0], u1 = q[1];
+      A.a[0] = u0.x; A.a[1] = u0.y; A.a[2] = u0.z; A.a[3] = u0.w;
+      A.a[4] = u1.x; A.a[5] = u1.y; A.a[6] = u1.z; A.a[7] = u1.w;
+      A.d = ALDS ? dh_l[slot * nbi + b] : a.dh[slot * nbi + b];
+      A.s = ALDS ? sh_l[slot * nbi + b] : a.sh[slot * nbi + b];
       return A;
     };
-    v = w4a8_lane<BPL, FAST>(base, nbi, lr * BPL, act, nullptr);
+    if constexpr (FAST) v = w4a8_regs<BPL>(D, nbi, lr * BPL, act);
+    else v = w4a8_lane<BPL, false>(base, nbi, lr * BPL, act, nullptr);
   }
   v = wave_tree_sum(v, lpr);
   if (live && lr == 0) o_l[rl * ns + slot] = v;
@@ -296,71 +399,91 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
 }
 
 // ---------------------------------------------------------------- launch
-hipError_t launch_decode(const DecodeArgs& a, const RouterSplit& sp, hipStream_t stream) {
-#define MOEQ4_DR(NSV) \
-  hipLaunchKernelGGL((decode_router_kernel<NSV>), dim3(NSV), dim3(256), 0, stream, a, sp.nc, sp.cw)
-  switch (sp.nsplit) {
-    case 1: MOEQ4_DR(1); break;
-    case 2: MOEQ4_DR(2); break;
-    case 4: MOEQ4_DR(4); break;
-    case 8: MOEQ4_DR(8); break;
-    case 16: MOEQ4_DR(16); break;
-    case 32: MOEQ4_DR(32); break;
-    default: MOEQ4_DR(64); break;
-  }
-#undef MOEQ4_DR
+DecodeGeometry decode_geometry(int H, int I, int E, int k, int has_shared) {
+  DecodeGeometry g;
+  const int ns = k + (has_shared ? 1 : 0);
+  g.router_threads = (E + 63) / 64 * 64;
+  const RowSplit gu = row_split(H, 16);
+  g.gu_lpr = gu.lpr;
+  g.gu_bpl = gu.bpl;
+  g.gu_fast = (gu.bpl % 8 == 0) && (gu.nb % gu.bpl == 0);
+  g.gu_threads = 2 * DGU_ROWS * gu.lpr;
+  const int nc = H / BLK;
+  int m = 1;
+  while (m < nc) m <<= 1;
+  // lanes per expert: as many as the block allows (<= 64, <= m), at least
+  // enough for runs of <= 32 leaves
+  int P = 1;
+  while (P < 64 && P < m && E * P * 2 <= g.gu_threads) P <<= 1;
+  while (m / P > 32) P <<= 1;
+  g.gu_parts = P;
+  g.gu_lds = gu_lds_bytes(nc, E);
+  const RowSplit dn = row_split(I, 16);
+  g.dn_lpr = dn.lpr;
+  g.dn_bpl = dn.bpl;
+  g.dn_fast = (dn.bpl % 8 == 0) && (dn.nb % dn.bpl == 0);
+  const int per_row = ns * dn.lpr;
+  g.dn_rows = 256 / per_row < 1 ? 1 : 256 / per_row;
+  g.dn_threads = (g.dn_rows * per_row + 63) / 64 * 64;
+  const int nbi = I / BLK;
+  const size_t act = 4 * ((size_t)ns * act_row_dwords(nbi) + 2 * (size_t)ns * nbi);
+  const size_t out = 4 * (size_t)g.dn_rows * ns;
+  g.dn_act_lds = act + out <= kDecodeLdsMax;
+  g.dn_lds = (g.dn_act_lds ? act : 0) + out;
+  return g;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const DecodeGeometry g = decode_geometry(a.H, a.I, a.E, a.k, a.has_shared);
+  const int nc = a.H / BLK;
+  hipLaunchKernelGGL(decode_router_kernel, dim3(nc), dim3(g.router_threads), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
   const int ns = a.k + (a.has_shared ? 1 : 0);
-  // gate/up
   {
-    const RowSplit rs = row_split(a.H, 16);
-    const bool fast = (rs.bpl % 8 == 0) && (rs.nb % rs.bpl == 0);
-    const size_t lds = (size_t)a.H + 8 * (size_t)(a.H / BLK);
-    dim3 grid(a.I / BLK, ns);
-    dim3 block(64 * rs.lpr);
+    dim3 grid(a.I / DGU_ROWS, ns);
+    dim3 block(g.gu_threads);
 #define MOEQ4_GU(B, F) \
-  hipLaunchKernelGGL((decode_gateup_kernel<B, F>), grid, block, lds, stream, a, rs.lpr)
-    if (fast) {
-      if (rs.bpl == 8) MOEQ4_GU(8, true);
-      else if (rs.bpl == 16) MOEQ4_GU(16, true);
+  hipLaunchKernelGGL((decode_gateup_kernel<B, F>), grid, block, g.gu_lds, stream, a, g.gu_lpr, g.gu_parts)
+    if (g.gu_fast) {
+      if (g.gu_bpl == 8) MOEQ4_GU(8, true);
+      else if (g.gu_bpl == 16) MOEQ4_GU(16, true);
       else MOEQ4_GU(32, true);
     } else {
-      if (rs.bpl == 1) MOEQ4_GU(1, false);
-      else if (rs.bpl == 2) MOEQ4_GU(2, false);
-      else if (rs.bpl == 4) MOEQ4_GU(4, false);
-      else if (rs.bpl == 8) MOEQ4_GU(8, false);
-      else if (rs.bpl == 16) MOEQ4_GU(16, false);
+      if (g.gu_bpl == 1) MOEQ4_GU(1, false);
+      else if (g.gu_bpl == 2) MOEQ4_GU(2, false);
+      else if (g.gu_bpl == 4) MOEQ4_GU(4, false);
+      else if (g.gu_bpl == 8) MOEQ4_GU(8, false);
+      else if (g.gu_bpl == 16) MOEQ4_GU(16, false);
       else MOEQ4_GU(32, false);
     }
 #undef MOEQ4_GU
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // down + combine
   {
-    const RowSplit rs = row_split(a.I, 16);
-    const bool fast = (rs.bpl % 8 == 0) && (rs.nb % rs.bpl == 0);
-    int threads = 128;
-    while (threads / rs.lpr < ns) threads *= 2;
-    const int rows = (threads / rs.lpr) / ns;
-    const int nbi = a.I / BLK;
-    const size_t lds = (size_t)ns * a.I + 8 * (size_t)ns * nbi + 4 * (size_t)rows * ns;
-    dim3 grid((a.H + rows - 1) / rows);
-    dim3 block(threads);
-#define MOEQ4_DN(B, F) \
-  hipLaunchKernelGGL((decode_down_kernel<B, F>), grid, block, lds, stream, a, rs.lpr, rows)
-    if (fast) {
-      if (rs.bpl == 8) MOEQ4_DN(8, true);
-      else if (rs.bpl == 16) MOEQ4_DN(16, true);
+    dim3 grid((a.H + g.dn_rows - 1) / g.dn_rows);
+    dim3 block(g.dn_threads);
+#define MOEQ4_DN(B, F)                                                                     \
+  do {                                                                                     \
+    if (g.dn_act_lds)                                                                      \
+      hipLaunchKernelGGL((decode_down_kernel<B, F, true>), grid, block, g.dn_lds, stream, a, \
+                         g.dn_lpr, g.dn_rows);                                            \
+    else                                                                                   \
+      hipLaunchKernelGGL((decode_down_kernel<B, F, false>), grid, block, g.dn_lds, stream, a, \
+                         g.dn_lpr, g.dn_rows);                                            \
+  } while (0)
+    if (g.dn_fast) {
+      if (g.dn_bpl == 8) MOEQ4_DN(8, true);
+      else if (g.dn_bpl == 16) MOEQ4_DN(16, true);
       else MOEQ4_DN(32, true);
     } else {
-      if (rs.bpl == 1) MOEQ4_DN(1, false);
-      else if (rs.bpl == 2) MOEQ4_DN(2, false);
-      else if (rs.bpl == 4) MOEQ4_DN(4, false);
-      else if (rs.bpl == 8) MOEQ4_DN(8, false);
-      else if (rs.bpl == 16) MOEQ4_DN(16, false);
+      if (g.dn_bpl == 1) MOEQ4_DN(1, false);
+      else if (g.dn_bpl == 2) MOEQ4_DN(2, false);
+      else if (g.dn_bpl == 4) MOEQ4_DN(4, false);
+      else if (g.dn_bpl == 8) MOEQ4_DN(8, false);
+      else if (g.dn_bpl == 16) MOEQ4_DN(16, false);
       else MOEQ4_DN(32, false);
     }
 #undef MOEQ4_DN

@@ -17,7 +17,6 @@ struct RouterSplit {
   int nc, m, cw, nsplit;
 };
 RouterSplit prefill_router_split(int H);
-RouterSplit decode_router_split(int H, int E);
 
 // Prefill routing.
 hipError_t launch_router_partials(const void* x, int x_bf16, int T, int H, const float* w_router,
@@ -66,17 +65,17 @@ struct DecodeArgs {
   const uint8_t* s_gate;
   const uint8_t* s_up;
   const uint8_t* s_down;
-  // workspace pieces
-  float* partials;          // [nsplit][E]
-  uint32_t* ticket;         // one counter, zero between calls
+  // workspace pieces (no initialisation needed: every piece is written
+  // before it is read within one call)
+  float* partials;          // [H/32][E] router chunk chains
   int32_t* ids;             // [k]
   float* w;                 // [k]
-  int8_t* qx;               // [H]
+  int8_t* qx;               // [H]         (16-byte aligned)
   float* dx;                // [H/32]
   int32_t* sx;              // [H/32] sum of the int8 codes of each block
-  int8_t* qh;               // [k+S][I]
-  float* dh;                // [k+S][I/32]
-  int32_t* sh;              // [k+S][I/32]
+  int8_t* qh;               // [k+S][I]    (16-byte aligned)
+  float* dh;                // [(k+S) I/32]
+  int32_t* sh;              // [(k+S) I/32]
   // optional trace
   float* t_logits;
   int32_t* t_ids;
@@ -86,7 +85,19 @@ struct DecodeArgs {
   int8_t* t_qh;
   float* t_dh;
 };
-hipError_t launch_decode(const DecodeArgs& a, const RouterSplit& sp, hipStream_t stream);
+// Launch shapes of the three decode kernels.  The down kernel stages every
+// slot's q8(h) in LDS when that fits in kDecodeLdsMax bytes (dn_act_lds),
+// else it reads the activation blocks from the workspace in memory.
+constexpr size_t kDecodeLdsMax = 64 * 1024;
+struct DecodeGeometry {
+  int router_threads;
+  int gu_lpr, gu_bpl, gu_fast, gu_threads, gu_parts;
+  size_t gu_lds;
+  int dn_lpr, dn_bpl, dn_fast, dn_rows, dn_threads, dn_act_lds;
+  size_t dn_lds;
+};
+DecodeGeometry decode_geometry(int H, int I, int E, int k, int has_shared);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_w4a8_gemv(const uint8_t* W, int N, int K, const int8_t* qa, const float* da,
                             int32_t* dots, float* out, hipStream_t stream);

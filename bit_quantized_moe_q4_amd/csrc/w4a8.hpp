@@ -64,6 +64,41 @@ __device__ __forceinline__ float reg_tree(float (&v)[BPL]) {
   return v[0];
 }
 
+// The FAST row program on a lane's span already in registers: D holds the
+// 18*BPL bytes of blocks b0 .. b0+BPL-1 (BPL % 8 == 0; 8 blocks repeat every
+// 144 bytes = 36 dwords) plus one spare dword.  Blocks >= nb are +0 leaves.
+// dots (optional) receives dot_b at dots[b].
+template <int BPL, typename ActFn>
+__device__ __forceinline__ float w4a8_regs(const uint32_t* D, int nb, int b0, ActFn act,
+                                           int32_t* dots = nullptr) {
+  static_assert(BPL % 8 == 0, "register spans hold whole 144-byte groups");
+  if (b0 >= nb) return 0.0f;              // a lane of padding leaves only
+  float p[BPL];
+#pragma unroll
+  for (int g = 0; g < BPL / 8; g++) {
+    const uint32_t* Dg = D + 36 * g;
+    uint32_t sc[8], nib[8][4];
+    span_block<0>(Dg, sc[0], nib[0]);
+    span_block<1>(Dg, sc[1], nib[1]);
+    span_block<2>(Dg, sc[2], nib[2]);
+    span_block<3>(Dg, sc[3], nib[3]);
+    span_block<4>(Dg, sc[4], nib[4]);
+    span_block<5>(Dg, sc[5], nib[5]);
+    span_block<6>(Dg, sc[6], nib[6]);
+    span_block<7>(Dg, sc[7], nib[7]);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int b = b0 + 8 * g + j;
+      const ActBlock A = act(b);
+      const int32_t dot = q4_block_dot(nib[j], A.a, A.s);
+      if (dots) dots[b] = dot;
+      const float s = f16_bits_to_f32(sc[j]) * A.d;
+      p[8 * g + j] = s * (float)dot;
+    }
+  }
+  return reg_tree<BPL>(p);
+}
+
 // One lane's share of a W4A8 row: blocks b = b0 .. b0+BPL-1 (blocks >= nb are
 // +0 leaves).  `row` points at the row's first block.  `act(b)` returns the
 // activation block b.  FAST: the lane's span is 16-byte aligned and whole
@@ -72,10 +107,8 @@ __device__ __forceinline__ float reg_tree(float (&v)[BPL]) {
 template <int BPL, bool FAST, typename ActFn>
 __device__ __forceinline__ float w4a8_lane(const uint8_t* __restrict__ row, int nb, int b0,
                                            ActFn act, int32_t* dots) {
-  float p[BPL];
   if constexpr (FAST) {
-    static_assert(BPL % 8 == 0, "fast span needs whole 144-byte groups");
-    if (b0 >= nb) return 0.0f;            // a lane of padding leaves only
+    if (b0 >= nb) return 0.0f;
     constexpr int NV = 18 * BPL / 16;     // uint4 per span
     uint32_t D[4 * NV + 1];
     const uint4* src = reinterpret_cast<const uint4*>(row + (size_t)b0 * Q4B);
@@ -85,30 +118,9 @@ __device__ __forceinline__ float w4a8_lane(const uint8_t* __restrict__ row, int 
       D[4 * v] = t.x; D[4 * v + 1] = t.y; D[4 * v + 2] = t.z; D[4 * v + 3] = t.w;
     }
     D[4 * NV] = 0u;
-#pragma unroll
-    for (int g = 0; g < BPL / 8; g++) {
-      // blocks of 8 repeat every 144 bytes = 36 dwords
-      const uint32_t* Dg = D + 36 * g;
-      uint32_t sc[8], nib[8][4];
-      span_block<0>(Dg, sc[0], nib[0]);
-      span_block<1>(Dg, sc[1], nib[1]);
-      span_block<2>(Dg, sc[2], nib[2]);
-      span_block<3>(Dg, sc[3], nib[3]);
-      span_block<4>(Dg, sc[4], nib[4]);
-      span_block<5>(Dg, sc[5], nib[5]);
-      span_block<6>(Dg, sc[6], nib[6]);
-      span_block<7>(Dg, sc[7], nib[7]);
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int b = b0 + 8 * g + j;
-        const ActBlock A = act(b);
-        const int32_t dot = q4_block_dot(nib[j], A.a, A.s);
-        if (dots) dots[b] = dot;
-        const float s = f16_bits_to_f32(sc[j]) * A.d;
-        p[8 * g + j] = s * (float)dot;
-      }
-    }
+    return w4a8_regs<BPL>(D, nb, b0, act, dots);
   } else {
+    float p[BPL];
     const uint16_t* hw = reinterpret_cast<const uint16_t*>(row);
 #pragma unroll
     for (int j = 0; j < BPL; j++) {
@@ -127,8 +139,8 @@ __device__ __forceinline__ float w4a8_lane(const uint8_t* __restrict__ row, int 
         p[j] = s * (float)dot;
       }
     }
+    return reg_tree<BPL>(p);
   }
-  return reg_tree<BPL>(p);
 }
 
 // Geometry of the row program for a K-long row: m = next_pow2(K/32),

@@ -22,6 +22,7 @@ import moe_synth
 import oracle
 import bit_quantized_moe_q4_amd as mq
 from layers import both_layers, tokens
+from bit_quantized_moe_q4_amd.synth_layer import device_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -283,12 +284,46 @@ def _decode_steps(ol, gl, cfg, steps):
     ("tiny_shared", 256, 8, 128, 2, True, None),
     ("odd_chunks", 96, 5, 96, 3, True, None),
     ("zipf_bias", 512, 64, 256, 8, True, "zipf"),
+    # H = 16384: 32 blocks per lane, 16 lanes per row (1024-thread gate/up blocks)
+    ("wide_hidden", 16384, 8, 64, 2, True, None),
+    # 9 slots x I = 8192: q8(h) of every slot exceeds the down kernel's LDS
+    # budget, so its activation blocks are read from memory
+    ("wide_inter", 256, 16, 8192, 8, True, None),
+    # the largest expert count and top-k the library accepts
+    ("many_experts", 256, 1024, 64, 32, True, "zipf"),
 ])
 def test_decode_small(name, H, E, I, k, shared, bias):
     say("decode", name)
     cfg = moe_synth.CONFIGS["tiny"].with_(name=name, H=H, E=E, I=I, k=k, shared=shared, bias=bias)
     ol, gl = both_layers(cfg)
     _decode_steps(ol, gl, cfg, range(6))
+
+
+def test_decode_tied_logits():
+    # experts 2j and 2j+1 share a router column, so every logit ties with its
+    # pair: the choice takes the lower index first (k rounds of "first maximum
+    # among the rest").  An all-zero x ties every logit at zero.
+    cfg = moe_synth.CONFIGS["tiny"].with_(name="ties", H=256, E=16, I=64, k=5, shared=True, bias=None)
+    W = moe_synth.expert_weights(cfg, 0, threads=16)
+    Wr = moe_synth.router(cfg, 0).copy()
+    Wr[:, 1::2] = Wr[:, 0::2]
+    ol = oracle.PackedLayer.from_float(Wr, None, W["gate"], W["up"], W["down"], W["s_gate"], W["s_up"],
+                                       W["s_down"], k=cfg.k, threads=16)
+    g0 = device_layer(cfg, weights=W)
+    gl = mq.MoELayer(torch.from_numpy(Wr).cuda(), g0.gate, g0.up, g0.down, cfg.k, router_bias=None,
+                     s_gate=g0.s_gate, s_up=g0.s_up, s_down=g0.s_down)
+    _decode_steps(ol, gl, cfg, range(4))
+    for step in range(4):
+        x = moe_synth.tokens(cfg, step=step, T=1)[0]
+        _, tr = mq.moe_q4_decode(gl, torch.from_numpy(x).cuda(), trace=True)
+        ids = tr["ids"].cpu().numpy()
+        assert np.all(ids[0::2] % 2 == 0) and np.all(ids[1::2] == ids[0:4:2] + 1), ids
+    x0 = np.zeros(cfg.H, dtype=np.float32)
+    y, tr = mq.moe_q4_decode(gl, torch.from_numpy(x0).cuda(), trace=True)
+    yo, to = oracle.decode(ol, x0, trace=True)
+    assert np.array_equal(tr["ids"].cpu().numpy(), to["ids"])
+    assert np.array_equal(to["ids"], np.arange(cfg.k))
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), yo.astype(np.float32).view(np.uint32))
 
 
 def test_decode_full_layer():
