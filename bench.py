@@ -18,8 +18,15 @@ in HBM when timing starts:
   GB/s = 16,973,824 B per step / time per step.
 - roofline: the dominant prefill kernel (grouped gate/up GEMM, gemm_g2_kernel)
   timed with HIP events around its own launch on the stream it runs on.
+  `traffic` is the HBM bytes per launch from rocprofv3 FETCH_SIZE and
+  WRITE_SIZE counters, calibrated against a plain 1 GiB device copy, read
+  from profiles/traffic_*.json while the kernel sources are unchanged.
 - cpu_baseline: the CPU oracle (single-threaded C) on a bounded token sample
   of the same workload, scaled to tokens/s.
+
+Counter collection (two rocprofv3 --pmc runs of this script with
+--copy-probe, then `python bench.py --traffic-from FETCH.csv WRITE.csv`):
+see profiles/README.md.
 """
 from __future__ import annotations
 
@@ -47,17 +54,83 @@ def _src_hash(*names):
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel, src_files, launches_per_unit=1):
-    """HBM bytes per launch measured by rocprofv3 counters (profiles/), only if
-    the kernel source is unchanged since the counters were taken."""
-    p = os.path.join(PROFILES, "traffic_%s.json" % kernel)
+def _traffic(unit):
+    """HBM bytes per launch (per step for decode) measured by rocprofv3
+    counters (profiles/traffic_<unit>.json), only if the kernel sources are
+    unchanged since the counters were taken."""
+    p = os.path.join(PROFILES, "traffic_%s.json" % unit)
     if not os.path.exists(p):
         return None
     with open(p) as f:
         rec = json.load(f)
-    if rec.get("src_hash") != _src_hash(*src_files):
+    if rec.get("src_hash") != _src_hash(*TRAFFIC_KERNELS[unit][1]):
         return None
     return rec.get("bytes_per_launch")
+
+
+# kernels whose HBM traffic is recorded: name -> (kernel-name substrings
+# counted per unit, sources the record is valid for)
+TRAFFIC_KERNELS = {
+    "gateup": (["gemm_g2_kernel<true>"], ["gemm.hip", "launch.hpp", "device_math.hpp"]),
+    "decode": (["decode_router_kernel", "decode_gateup_kernel", "decode_down_kernel"],
+               ["decode.hip", "launch.hpp", "w4a8.hpp", "device_math.hpp"]),
+}
+COPY_PROBE_BYTES = 1 << 30
+
+
+def _counter_means(path):
+    """Per kernel name: the mean counter value (KiB) over its dispatches."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def write_traffic(fetch_csv, write_csv, command):
+    """profiles/traffic_<unit>.json from one FETCH_SIZE and one WRITE_SIZE run.
+    Each counter is scaled by the factor that maps its reading for the 1 GiB
+    copy probe (the largest __amd_rocclr_copyBuffer dispatch) to 1 GiB."""
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = _counter_means(path)
+        copies = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
+        probe_kib = max(copies)
+        factor = COPY_PROBE_BYTES / (probe_kib * 1024.0)
+        for unit, (names, _) in TRAFFIC_KERNELS.items():
+            tot = 0.0
+            for n in names:
+                hit = [vs for k, vs in vals.items() if n in k]
+                assert hit, "no dispatch of %s in %s" % (n, path)
+                vs = [v for h in hit for v in h]
+                tot += sum(vs) / len(vs) * 1024.0 * factor
+            out.setdefault(unit, {})[counter] = (tot, factor, probe_kib)
+    for unit, rec in out.items():
+        names, srcs = TRAFFIC_KERNELS[unit]
+        doc = {
+            "unit": unit, "kernels": names,
+            "fetch_bytes": round(rec["FETCH_SIZE"][0]), "write_bytes": round(rec["WRITE_SIZE"][0]),
+            "bytes_per_launch": round(rec["FETCH_SIZE"][0] + rec["WRITE_SIZE"][0]),
+            "copy_probe_bytes": COPY_PROBE_BYTES,
+            "copy_probe_kib": {"FETCH_SIZE": rec["FETCH_SIZE"][2], "WRITE_SIZE": rec["WRITE_SIZE"][2]},
+            "scale": {"FETCH_SIZE": round(rec["FETCH_SIZE"][1], 4), "WRITE_SIZE": round(rec["WRITE_SIZE"][1], 4)},
+            "src_files": srcs, "src_hash": _src_hash(*srcs), "command": command,
+        }
+        with open(os.path.join(PROFILES, "traffic_%s.json" % unit), "w") as f:
+            json.dump(doc, f, indent=1)
+            f.write("\n")
+        print(unit, doc["bytes_per_launch"], "bytes per launch")
+
+
+def copy_probe(torch):
+    """One plain device-to-device copy of COPY_PROBE_BYTES (counter calibration)."""
+    a = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def clone_layer(L):
@@ -158,7 +231,22 @@ def bench_decode(args, torch, mq, moe_synth, device_layer):
     torch.cuda.synchronize()
     eager_s = (time.perf_counter() - t2) / m
     assert torch.isfinite(Y).all().item()
-    return dict(cfg=cfg, step_s=step_s, bytes_step=bytes_step, eager_s=eager_s, copies=len(copies))
+    # single copy: the layer stays in the last-level cache (reported apart, labelled)
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g1, stream=s):
+            for i in range(n):
+                mq.moe_q4_decode(base, X[i], y=Y[i], ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    g1.replay()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for _ in range(reps):
+        g1.replay()
+    torch.cuda.synchronize()
+    hot_s = (time.perf_counter() - t3) / (reps * n)
+    return dict(cfg=cfg, step_s=step_s, bytes_step=bytes_step, eager_s=eager_s, hot_s=hot_s,
+                copies=len(copies))
 
 
 def cpu_baseline(args, pre):
@@ -195,7 +283,15 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--cpu-sample-tokens", type=int, default=768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="end with one 1 GiB device copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_*.json from two rocprofv3 counter CSVs and exit")
+    ap.add_argument("--traffic-command", default="", help="the command recorded with --traffic-from")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: this build measures the one-GPU share of the "
@@ -242,7 +338,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(ach_gu / PEAK_BF16_TFLOPS, 4),
-            "traffic": _traffic("gateup", ["gemm.hip", "w4a8.hpp", "device_math.hpp"]),
+            "traffic": _traffic("gateup"),
             "flop_per_launch": pre["fl_gu"],
             "avg_launch_us": round(pre["t_gu"] * 1e6, 2),
         },
@@ -255,15 +351,21 @@ def main():
             "unit": "GB/s",
             "us_per_step": round(dec["step_s"] * 1e6, 3),
             "eager_us_per_step": round(dec["eager_s"] * 1e6, 3),
+            "cache_resident_us_per_step": round(dec["hot_s"] * 1e6, 3),
+            "cache_resident_note": "one layer copy replayed, so its 17 MB per step stay in the 256 MB "
+                                   "last-level cache: not an HBM figure",
             "steps": args.decode_steps,
             "bytes_per_step": dec["bytes_step"],
             "layer_copies_rotated": dec["copies"],
             "workload": "one-token W4A8 decode, same layer shape, fresh x per step, HIP graph replay",
             "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
-                         "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                         "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                         "traffic": _traffic("decode")},
         },
     }
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args, pre)
+    if args.copy_probe:
+        copy_probe(torch)
     print(json.dumps(out), flush=True)
 
 

@@ -256,8 +256,9 @@ __global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int l
   __shared__ int ids_l[32];
   __shared__ float vals_l[32], ex_l[32];
   const int tid = threadIdx.x;
-  const int slot = blockIdx.y, i0 = blockIdx.x * DGU_ROWS;
-  const bool publish = blockIdx.x == 0 && slot == 0;
+  const int ngrp = I / DGU_ROWS, j = blockIdx.x;
+  const int slot = j / ngrp, gx = j % ngrp, i0 = gx * DGU_ROWS;
+  const bool publish = j == 0;
   decode_gu_prologue(a, l, P, slot < a.k, ids_l, vals_l, publish);
 
   const int row = tid / lpr, lr = tid % lpr;
@@ -334,8 +335,10 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
   float* dh_l = reinterpret_cast<float*>(qh_l + (size_t)ns * SS);         // ns * nbi
   int32_t* sh_l = reinterpret_cast<int32_t*>(dh_l + (size_t)ns * nbi);    // ns * nbi
   float* o_l = reinterpret_cast<float*>(dyn) + nact;                      // rows * ns
+  __shared__ float w_l[32];
   const int tid = threadIdx.x;
   const int r0 = blockIdx.x * rows;
+  if (tid < a.k) w_l[tid] = a.w[tid];     // early: the combine is the last step
 
   const int item = tid / lpr, lr = tid % lpr;
   const int rl = item / ns, slot = item % ns;
@@ -391,8 +394,8 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
   __syncthreads();
   if (tid < rows && r0 + tid < H) {
     const float* o = o_l + tid * ns;
-    float acc = a.w[0] * o[0];
-    for (int s = 1; s < a.k; s++) acc = acc + a.w[s] * o[s];
+    float acc = w_l[0] * o[0];
+    for (int s = 1; s < a.k; s++) acc = acc + w_l[s] * o[s];
     if (a.has_shared) acc = acc + o[a.k];
     a.y[r0 + tid] = acc;
   }
@@ -442,7 +445,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 
   const int ns = a.k + (a.has_shared ? 1 : 0);
   {
-    dim3 grid(a.I / DGU_ROWS, ns);
+    dim3 grid(a.I / DGU_ROWS * ns);
     dim3 block(g.gu_threads);
 #define MOEQ4_GU(B, F) \
   hipLaunchKernelGGL((decode_gateup_kernel<B, F>), grid, block, g.gu_lds, stream, a, g.gu_lpr, g.gu_parts)

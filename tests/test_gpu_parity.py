@@ -291,6 +291,9 @@ def _decode_steps(ol, gl, cfg, steps):
     ("wide_inter", 256, 16, 8192, 8, True, None),
     # the largest expert count and top-k the library accepts
     ("many_experts", 256, 1024, 64, 32, True, "zipf"),
+    # the largest top-k on the fast row programs (33 slots; 264 gate/up
+    # blocks and 33 rows per down block)
+    ("many_slots", 512, 128, 256, 32, True, "zipf"),
 ])
 def test_decode_small(name, H, E, I, k, shared, bias):
     say("decode", name)
