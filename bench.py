@@ -16,8 +16,9 @@ in HBM when timing starts:
   layer shape, captured once in a HIP graph and replayed; 16 packed copies
   rotate so every step streams its experts from HBM.  Reported as weight
   GB/s = 16,973,824 B per step / time per step.
-- roofline: the dominant prefill kernel (grouped gate/up GEMM, gemm_g2_kernel)
-  timed with HIP events around its own launch on the stream it runs on.
+- roofline: the dominant prefill kernel, gemm_ffn_kernel (the grouped gate/up
+  + SwiGLU and down GEMMs in one launch), timed with HIP events around its
+  launch (and the tiny counter fill before it) on the stream it runs on.
   `traffic` is the HBM bytes per launch from rocprofv3 FETCH_SIZE and
   WRITE_SIZE counters, calibrated against a plain 1 GiB device copy, read
   from profiles/traffic_*.json while the kernel sources are unchanged.
@@ -71,7 +72,7 @@ def _traffic(unit):
 # kernels whose HBM traffic is recorded: name -> (kernel-name substrings
 # counted per unit, sources the record is valid for)
 TRAFFIC_KERNELS = {
-    "gateup": (["gemm_g2_kernel<true>"], ["gemm.hip", "launch.hpp", "device_math.hpp"]),
+    "gemm": (["gemm_ffn_kernel"], ["gemm.hip", "launch.hpp", "device_math.hpp"]),
     "decode": (["decode_router_kernel", "decode_gateup_kernel", "decode_down_kernel"],
                ["decode.hip", "launch.hpp", "w4a8.hpp", "device_math.hpp"]),
 }
@@ -154,19 +155,19 @@ def bench_prefill(args, torch, mq, moe_synth, device_layer):
     pws = torch.empty(mq.moe_q4_prefill_workspace_bytes(layers[0], T), dtype=torch.uint8, device="cuda")
     y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
     S = mq._lib
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
     def step(i, evs=None):
+        # route, then the grouped GEMMs (one fused gate/up -> down launch after a
+        # counter fill), then the combine: the same kernels as moe_q4_prefill
         L = layers[i % len(layers)]
         if evs: evs[0].record()
         mq.moe_q4_route(L, xb, out=routing, ws=rws)
         if evs: evs[1].record()
-        mq.moe_q4_prefill_stage(L, xb, routing, y, pws, S.STAGE_GATEUP)
+        mq.moe_q4_prefill_stage(L, xb, routing, y, pws, S.STAGE_GATEUP | S.STAGE_DOWN)
         if evs: evs[2].record()
-        mq.moe_q4_prefill_stage(L, xb, routing, y, pws, S.STAGE_DOWN)
-        if evs: evs[3].record()
         mq.moe_q4_prefill_stage(L, xb, routing, y, pws, S.STAGE_COMBINE)
-        if evs: evs[4].record()
+        if evs: evs[3].record()
 
     for i in range(args.warmup):
         step(i)
@@ -178,14 +179,14 @@ def bench_prefill(args, torch, mq, moe_synth, device_layer):
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
     seg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in ev) / len(ev) * 1e-3  # noqa: E731
-    t_route, t_gu, t_dn, t_cb = seg(0, 1), seg(1, 2), seg(2, 3), seg(3, 4)
+    t_route, t_gemm, t_cb = seg(0, 1), seg(1, 2), seg(2, 3)
     S_ = 1 if cfg.shared else 0
     rows = T * cfg.k + T * S_
     fl_gu = 2.0 * rows * (2 * cfg.I) * cfg.H
     fl_dn = 2.0 * rows * cfg.I * cfg.H
     fl_total = fl_gu + fl_dn
     assert torch.isfinite(y).all().item()
-    return dict(cfg=cfg, W=W, step_s=step_s, t_route=t_route, t_gu=t_gu, t_dn=t_dn, t_cb=t_cb,
+    return dict(cfg=cfg, W=W, step_s=step_s, t_route=t_route, t_gemm=t_gemm, t_cb=t_cb,
                 fl_gu=fl_gu, fl_dn=fl_dn, fl_total=fl_total, layers=layers)
 
 
@@ -310,7 +311,8 @@ def main():
     dec = bench_decode(args, torch, mq, moe_synth, device_layer)
     cfg = pre["cfg"]
     tok_s = cfg.T / pre["step_s"]
-    ach_gu = pre["fl_gu"] / pre["t_gu"] / 1e12
+    fl_gemm = pre["fl_gu"] + pre["fl_dn"]
+    ach = fl_gemm / pre["t_gemm"] / 1e12
     dec_gbps = dec["bytes_step"] / dec["step_s"] / 1e9
     out = {
         "metric": "MoE-layer tok/s at 2k prefill; decode weight GB/s; % of HBM/MFMA roofline",
@@ -332,18 +334,18 @@ def main():
             "shared_expert": cfg.shared, "layer_copies_rotated": len(pre["layers"]),
         },
         "roofline": {
-            "kernel": "gemm_g2_kernel<true> (grouped gate/up GEMM + SwiGLU)",
+            "kernel": "gemm_ffn_kernel (grouped gate/up GEMM + SwiGLU, then grouped down GEMM, one launch)",
             "bound": "mfma",
-            "achieved": round(ach_gu, 2),
+            "achieved": round(ach, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(ach_gu / PEAK_BF16_TFLOPS, 4),
-            "traffic": _traffic("gateup"),
-            "flop_per_launch": pre["fl_gu"],
-            "avg_launch_us": round(pre["t_gu"] * 1e6, 2),
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic("gemm"),
+            "flop_per_launch": fl_gemm,
+            "avg_launch_us": round(pre["t_gemm"] * 1e6, 2),
         },
-        "stages_us": {"route": round(pre["t_route"] * 1e6, 2), "gateup": round(pre["t_gu"] * 1e6, 2),
-                      "down": round(pre["t_dn"] * 1e6, 2), "combine": round(pre["t_cb"] * 1e6, 2)},
+        "stages_us": {"route": round(pre["t_route"] * 1e6, 2), "gemm": round(pre["t_gemm"] * 1e6, 2),
+                      "combine": round(pre["t_cb"] * 1e6, 2)},
         "step_mfma_frac": round(pre["fl_total"] / pre["step_s"] / 1e12 / PEAK_BF16_TFLOPS, 4),
         "decode": {
             "metric": "decode weight GB/s",

@@ -71,14 +71,15 @@ RouteWs route_ws(const moe_q4_layer* L, int32_t T, const moeq4::RouterSplit& sp)
 }
 
 struct PrefillWs {
-  size_t h, o, total;
+  size_t h, o, tile_done, total;
 };
 PrefillWs prefill_ws(const moe_q4_layer* L, int32_t T) {
   PrefillWs w;
   const size_t rows = (size_t)T * L->top_k + (L->has_shared ? (size_t)T : 0);
   w.h = 0;
   w.o = w.h + up256(rows * L->inter * 2);
-  w.total = w.o + up256((size_t)T * L->top_k * L->hidden * 2);
+  w.tile_done = w.o + up256((size_t)T * L->top_k * L->hidden * 2);
+  w.total = w.tile_done + up256((size_t)moeq4::prefill_tile_bound(T, L->top_k, L->n_experts, L->has_shared) * 4);
   return w;
 }
 
@@ -236,6 +237,7 @@ int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t 
   a.s_down = static_cast<const uint8_t*>(L->s_down);
   a.h = at<uint16_t>(ws, W.h);
   a.o_perm = at<uint16_t>(ws, W.o);
+  a.tile_done = at<int32_t>(ws, W.tile_done);
   a.y = y;
   hipError_t e = moeq4::launch_prefill(a, stages, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_prefill");

@@ -359,10 +359,12 @@ __global__ void __launch_bounds__(256, 2) down_kernel(PrefillArgs a, int vec_b) 
 // piece (the thin-M cost the pages identify).
 constexpr int FMAXS = 5;                 // max 32-row subtiles per tile
 constexpr int FMAXR = 32 * FMAXS;        // max rows per tile
+static_assert(FMAXR == kPrefillTileRows, "tile rows shared with the workspace bound");
 
-// Tile mt, found by every wave on its own (registers only, no LDS):
-// expert e owns ceil(c_e / FMAXR) consecutive tile indices, experts in
-// order, then the shared expert's tiles.
+// Tile mt, found by every wave on its own (registers only, no LDS): the
+// shared expert's ceil(T / FMAXR) tiles come first (its dense M = T tiles
+// are the largest units and their down work the longest chain), then
+// expert e owns ceil(c_e / FMAXR) consecutive tile indices, experts in order.
 __device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offsets, int E, int T,
                                               int k, int has_shared, int mt) {
   const int lane = threadIdx.x % 64;
@@ -372,32 +374,36 @@ __device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offset
   t.pos0 = 0;
   t.expert = -1;
   t.m0 = 0;
-  int carry = 0, c = -1, q = 0;
-  for (int base = 0; base < E; base += 64) {
-    const int e = base + lane;
-    int ce = 0;
-    if (e < E) ce = offsets[e + 1] - offsets[e];
-    const int nt = (ce + FMAXR - 1) / FMAXR;
-    int incl = nt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    const unsigned long long hit = __ballot(carry + incl > mt);
-    if (hit) {
-      const int f = __builtin_ctzll(hit);
-      t.expert = base + f;
-      c = __shfl(ce, f, 64);
-      q = mt - (carry + __shfl(incl, f, 64) - __shfl(nt, f, 64));
-      break;
-    }
-    carry += __shfl(incl, 63, 64);
-  }
-  if (c < 0) {
-    if (!has_shared) return t;
+  int c = -1, q = 0;
+  const int n_sh = has_shared ? (T + FMAXR - 1) / FMAXR : 0;
+  if (mt < n_sh) {                        // (uniform per wave)
     c = T;
-    q = mt - carry;
+    q = mt;
+  } else {
+    const int mr = mt - n_sh;
+    int carry = 0;
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + lane;
+      int ce = 0;
+      if (e < E) ce = offsets[e + 1] - offsets[e];
+      const int nt = (ce + FMAXR - 1) / FMAXR;
+      int incl = nt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+      }
+      const unsigned long long hit = __ballot(carry + incl > mr);
+      if (hit) {
+        const int f = __builtin_ctzll(hit);
+        t.expert = base + f;
+        c = __shfl(ce, f, 64);
+        q = mr - (carry + __shfl(incl, f, 64) - __shfl(nt, f, 64));
+        break;
+      }
+      carry += __shfl(incl, 63, 64);
+    }
+    if (c < 0) return t;
   }
   const int nt = (c + FMAXR - 1) / FMAXR;
   if (q < 0 || q >= nt) return t;
@@ -621,6 +627,69 @@ __global__ void __launch_bounds__(256, 2) gemm_g2_kernel(PrefillArgs a, int ncb)
     case 3: g2_tile<3, GATEUP>(a, t, cb, sm); break;
     case 4: g2_tile<4, GATEUP>(a, t, cb, sm); break;
     default: g2_tile<5, GATEUP>(a, t, cb, sm); break;
+  }
+}
+
+// ---------------------------------------------------------------- fused gate/up -> down
+// One launch for both grouped GEMMs.  Blocks [0, n_gu) are the gate/up units
+// of g2 (tile, column block), the rest the down units, mapped the same way,
+// so a tile's gate/up and down units run on the same XCD.  A down unit starts
+// once all ncb_gu gate/up units of its tile have written their h rows: each
+// gate/up unit ends with an agent-scope release increment of tile_done[tile],
+// and the down unit's thread 0 polls it and takes an acquire fence.  Down
+// work thus fills the CUs that the last gate/up units leave idle, and the
+// other way round.  The wait always ends: every gate/up block has a lower
+// index than every down block, so it is dispatched first, and it waits on
+// nothing; the poll is bounded all the same.  tile_done is zeroed by a fill
+// launch just before.
+constexpr int kTileSpinMax = 1 << 22;
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ void __launch_bounds__(256, 2) gemm_ffn_kernel(PrefillArgs a, int ncb_gu, int ncb_dn, int n_gu) {
+  __shared__ __attribute__((aligned(16))) G2Smem sm;
+  const bool gu = (int)blockIdx.x < n_gu;
+  const int b = gu ? (int)blockIdx.x : (int)blockIdx.x - n_gu;   // n_gu % 8 == 0: same XCD mapping
+  const int ncb = gu ? ncb_gu : ncb_dn;
+  const int q = b / 8;
+  const int tile = 8 * (q / ncb) + b % 8, cb = q % ncb;
+  const Tile t = find_tile_bal(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
+  if (!t.valid) return;
+  const int S = (t.rows + 31) / 32;
+  if (gu) {
+    // gate/up waves issue ahead of a down unit sharing the CU: the last
+    // gate/up units gate the down units of their tiles
+    __builtin_amdgcn_s_setprio(2);
+    switch (S) {
+      case 1: g2_tile<1, true>(a, t, cb, sm); break;
+      case 2: g2_tile<2, true>(a, t, cb, sm); break;
+      case 3: g2_tile<3, true>(a, t, cb, sm); break;
+      case 4: g2_tile<4, true>(a, t, cb, sm); break;
+      default: g2_tile<5, true>(a, t, cb, sm); break;
+    }
+    __syncthreads();                      // every wave's h stores are complete
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(a.tile_done + tile, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    int n = __hip_atomic_load(a.tile_done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0; n < ncb_gu && it < kTileSpinMax; it++) {
+      __builtin_amdgcn_s_sleep(8);
+      n = __hip_atomic_load(a.tile_done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  switch (S) {
+    case 1: g2_tile<1, false>(a, t, cb, sm); break;
+    case 2: g2_tile<2, false>(a, t, cb, sm); break;
+    case 3: g2_tile<3, false>(a, t, cb, sm); break;
+    case 4: g2_tile<4, false>(a, t, cb, sm); break;
+    default: g2_tile<5, false>(a, t, cb, sm); break;
   }
 }
 
@@ -932,7 +1001,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
   const int64_t assignments = (int64_t)a.T * a.k;
   const int mtiles = (int)(assignments / BM) + a.E + (a.has_shared ? (a.T + BM - 1) / BM : 0);
   // upper bound of the balanced tile count (find_tile_bal)
-  const int btiles = (int)(assignments / FMAXR) + a.E + (a.has_shared ? (a.T + FMAXR - 1) / FMAXR : 0);
+  const int btiles = (int)prefill_tile_bound(a.T, a.k, a.E, a.has_shared);
   const int vec_g = ((a.H / BLK) % 4 == 0) && (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 8 == 0) &&
                     (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 8 == 0));
   const int vec_d = ((a.I / BLK) % 4 == 0) && ((uintptr_t)a.w_down % 8 == 0) &&
@@ -949,6 +1018,15 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
                     ((uintptr_t)a.w_down % 4 == 0) && (!a.has_shared || ((uintptr_t)a.s_down % 4 == 0));
   const int g2_groups = (btiles + 7) / 8;
   hipError_t err = hipSuccess;
+  if ((stages & 3) == 3 && MOEQ4_GEMM_IMPL == 2 && g2_g && g2_d && a.tile_done) {
+    const int ncb_gu = (a.I + 127) / 128, ncb_dn = (a.H + 255) / 256;
+    const int n_gu = g2_groups * 8 * ncb_gu, n_dn = g2_groups * 8 * ncb_dn;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((btiles + 255) / 256), dim3(256), 0, stream, a.tile_done, btiles);
+    hipLaunchKernelGGL(gemm_ffn_kernel, dim3(n_gu + n_dn), dim3(256), 0, stream, a, ncb_gu, ncb_dn, n_gu);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    stages &= ~3;
+  }
   if (stages & 1) {
     if (g4_g) {
       hipLaunchKernelGGL((gemm_g4_kernel<true>), dim3(persistent_blocks()), dim3(256), 0, stream, a,

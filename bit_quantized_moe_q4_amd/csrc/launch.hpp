@@ -49,8 +49,16 @@ struct PrefillArgs {
   uint16_t* h;              // [(T*k + T*S)][I] bf16
   uint16_t* o_perm;         // [T*k][H] bf16
   float* y;                 // [T][H] fp32
+  int32_t* tile_done;       // [prefill_tile_bound] gate/up units finished per tile (fused launch)
 };
 hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream);
+
+// Rows per tile of the grouped GEMMs (an expert segment of c rows is cut into
+// ceil(c / kPrefillTileRows) tiles) and an upper bound of the tile count.
+constexpr int kPrefillTileRows = 160;
+inline int64_t prefill_tile_bound(int64_t T, int k, int E, int has_shared) {
+  return T * k / kPrefillTileRows + E + (has_shared ? (T + kPrefillTileRows - 1) / kPrefillTileRows : 0);
+}
 
 // Decode.
 struct DecodeArgs {
