@@ -13,8 +13,9 @@
 // Kernels (one stream, no host round trip):
 //   router_partials  tiled fp32 VALU product, 64 tokens x 64 experts per
 //                    block, one aligned subtree of cw chunks per grid z
-//   topk_hist        finishes the chunk tree, top-k, weights, and a
-//                    wavefront-ballot histogram of the block's 64 tokens with
+//   topk_hist        finishes the chunk tree, top-k (k rounds of a DPP
+//                    wave maximum over 64-bit order keys), weights, and a
+//                    wavefront-ballot histogram of the block's tokens with
 //                    each assignment's stable rank inside the block
 //   route_scan       per-expert prefix over blocks -> segment bases, offsets
 //   route_scatter    perm / inv_perm
@@ -207,42 +208,76 @@ __device__ __forceinline__ float finish_logit(const float* __restrict__ partials
   return l;
 }
 
-// Wave-wide (value desc, index asc) argmax.
-__device__ __forceinline__ void wave_argmax(float& v, int& e) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const float ov = __shfl_xor(v, m, 64);
-    const int oe = __shfl_xor(e, m, 64);
-    if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
-  }
+// Order key: larger key = earlier in (logit desc, index asc); -0 and +0 tie
+// as under a float comparison.  Unique per expert.
+__device__ __forceinline__ uint64_t topk_key(float l, int e) {
+  uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
 }
 
-// Top-k of one token's logits held as lane + 64*j.  Returns, in lane s < k,
-// the s-th pick (my_v, my_e) and its weight my_w.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const int l2 = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xf, false);
+  const int h2 = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xf, false);
+  return ((uint64_t)(uint32_t)h2 << 32) | (uint32_t)l2;
+}
+
+// Maximum of v over the 64 lanes (all active), by DPP lane moves: xor 1 and
+// 2 inside quads, mirrors inside 8 and 16 lanes, then row broadcasts that
+// leave the maximum in lane 63; returned in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u64<0xb1, 0xf>(v));      // quad_perm [1,0,3,2]
+  v = mx(v, dpp_u64<0x4e, 0xf>(v));      // quad_perm [2,3,0,1]
+  v = mx(v, dpp_u64<0x141, 0xf>(v));     // row_half_mirror
+  v = mx(v, dpp_u64<0x140, 0xf>(v));     // row_mirror
+  v = mx(v, dpp_u64<0x142, 0xa>(v));     // row_bcast:15 into rows 1, 3
+  v = mx(v, dpp_u64<0x143, 0xc>(v));     // row_bcast:31 into rows 2, 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Top-k of one token's logits held as lane + 64*j (all 64 lanes active).
+// Round s takes the largest remaining key: the same pick as "first maximum
+// among the rest".  Returns, in lane s < k, the s-th pick (my_v, my_e) and
+// its weight my_w.
 template <int NJ>
 __device__ __forceinline__ void wave_topk(const float (&lv)[NJ], int E, int k, float& my_v,
                                           int& my_e, float& my_w) {
   const int lane = threadIdx.x % 64;
-  uint32_t taken = 0;
+  uint64_t key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; j++) {
+    const int e = lane + 64 * j;
+    key[j] = (e < E) ? topk_key(lv[j], e) : 0ull;
+  }
   my_v = 0.0f;
   my_e = -1;
+  float l0 = 0.0f;
   for (int s = 0; s < k; s++) {
-    float bv = -__builtin_inff();
-    int be = 0x7fffffff;
+    uint64_t best = 0;
 #pragma unroll
-    for (int j = 0; j < NJ; j++) {
-      const int e = lane + 64 * j;
-      if (e < E && !((taken >> j) & 1u) && (be == 0x7fffffff || lv[j] > bv)) { bv = lv[j]; be = e; }
-    }
-    wave_argmax(bv, be);
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == s) { my_v = bv; my_e = be; }
+    for (int j = 0; j < NJ; j++) best = key[j] > best ? key[j] : best;
+    const uint64_t win = wave_max_u64(best);
+    const int we = (int)(0xffffffffu - (uint32_t)win);
+    const int wj = we >> 6, wl = we & 63;
+    float sel = lv[0];
+#pragma unroll
+    for (int j = 1; j < NJ; j++) sel = (j == wj) ? lv[j] : sel;   // wj is uniform
+    const float wv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel), wl));
+#pragma unroll
+    for (int j = 0; j < NJ; j++)
+      if (j == wj && lane == wl) key[j] = 0ull;
+    if (s == 0) l0 = wv;
+    if (lane == s) { my_v = wv; my_e = we; }
   }
-  // weights: m = l_0, e_s = exp(l_s - m), S = e_0 + e_1 + ... left to right
-  const float l0 = __shfl(my_v, 0, 64);
+  // weights: e_s = exp(l_s - l_0), S = e_0 + e_1 + ... left to right
   const float ex = (lane < k) ? exp_p(my_v - l0) : 0.0f;
-  float S = __shfl(ex, 0, 64);
-  for (int s = 1; s < k; s++) S = S + __shfl(ex, s, 64);
+  float S = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), 0));
+  for (int s = 1; s < k; s++) S = S + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), s));
   my_w = ex / S;
 }
 

@@ -157,6 +157,21 @@ def test_route_ties_lower_index():
         assert list(ids[t]).index(0) + 1 == list(ids[t]).index(1)
 
 
+def test_route_all_tied_tokens():
+    # zero tokens tie every logit at +0 (no bias): the picks are experts 0..k-1
+    # in order, each weighted 1/k; mixed with ordinary tokens in one batch
+    cfg = moe_synth.CONFIGS["tiny"].with_(name="zero_tok", E=64, k=8, H=256, I=64, shared=False)
+    ol, gl = both_layers(cfg)
+    x, bits, xw, xd, xbd = tokens(cfg, T=48)
+    xw = xw.copy()
+    xw[::3] = 0.0
+    xbd = torch.from_numpy(moe_synth.to_bf16_bits(xw).view(np.int16)).cuda().view(torch.bfloat16)
+    r = mq.moe_q4_route(gl, xbd, logits=True)
+    ref = _check_route(ol, r, xw)
+    assert np.array_equal(ref["ids"][::3], np.tile(np.arange(cfg.k, dtype=np.int32), (16, 1)))
+    assert np.all(ref["w32"][::3] == np.float32(1.0 / cfg.k))
+
+
 def test_route_deterministic_and_empty():
     cfg = moe_synth.CONFIGS["tiny"]
     ol, gl = both_layers(cfg)
