@@ -13,11 +13,12 @@
 //            rows, 128 columns), 4 waves each owning 32 output columns and
 //            every row of the tile, activation rows staged in LDS per K-step
 //            of 256; one launch per projection.
-//   gemm_g2 (default for K a multiple of 64): 4-wave blocks, two per CU,
-//            balanced tiles of <= 160 rows, K-steps of 64, direct global->LDS
+//   g2 unit (K a multiple of 64): 4-wave blocks, two per CU, balanced
+//            tiles of <= 160 rows, K-steps of 64, direct global->LDS
 //            activation loads double buffered, weights one step ahead in
-//            registers, column blocks of a tile on one XCD.
-//   gemm_g4 (alternative schedule, see its section).
+//            registers, column blocks of a tile on one XCD.  Run as
+//            gemm_ffn (gate/up units, then down units that wait per tile,
+//            in one launch) or as gemm_g2 (one projection, for single stages).
 //   combine  y[t] += sum_s w[t,s] * O[inv_perm[t*k+s]]
 // Epilogues: gate/up writes h = silu(G) * U in bf16 (rows in segment order);
 // down writes each routed row's output in bf16 (segment order) and the shared
@@ -582,11 +583,12 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
   {                                                                                          \
     const bf16x8_t b0 = g2_deq<Q>(n0, d0);                                                   \
     const bf16x8_t b1 = g2_deq<Q>(n1, d1);                                                   \
+    bf16x8_t avs[MS];                                                                        \
+    _Pragma("unroll") for (int sub = 0; sub < MS; sub++)                                     \
+      avs[sub] = *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G2K + aofs[Q]);         \
     _Pragma("unroll") for (int sub = 0; sub < MS; sub++) {                                   \
-      const bf16x8_t av =                                                                    \
-          *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G2K + aofs[Q]);                \
-      acc0[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, acc0[sub], 0, 0, 0);       \
-      acc1[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, acc1[sub], 0, 0, 0);       \
+      acc0[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avs[sub], b0, acc0[sub], 0, 0, 0); \
+      acc1[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avs[sub], b1, acc1[sub], 0, 0, 0); \
     }                                                                                        \
   }
     MOEQ4_G2(0) MOEQ4_G2(1) MOEQ4_G2(2) MOEQ4_G2(3)
@@ -693,251 +695,6 @@ __global__ void __launch_bounds__(256, 2) gemm_ffn_kernel(PrefillArgs a, int ncb
   }
 }
 
-// ---------------------------------------------------------------- persistent, weights through LDS
-// Alternative schedule (MOEQ4_GEMM_IMPL=4; shapes with K a multiple of 256
-// and 16-byte aligned weights).  Measured slower than the two-blocks-per-CU
-// kernel so far and kept for schedule work.
-//
-// One block of 4 waves per CU (one wave per SIMD, so a wave's dequantisation
-// VALU work runs beside its own MFMAs rather than contending with a second
-// wave's), persistent over a static list of units: the (tile, column block)
-// pairs of g2, tile t on XCD t % 8, block b (on XCD b % 8) serving units
-// b/8, b/8 + P, ... of its XCD's list (P blocks per XCD).
-//
-// K-steps of 64 as in g2.  Activation tiles go through a 4-slot LDS ring by
-// direct global->LDS loads issued 3 steps ahead.  A lane's 20 weight bytes
-// of a step sit in its own row, so loading them straight into registers makes
-// every 64-lane load touch 64 cache lines and saturates the texture
-// addresser; instead a wave fetches, per group of 4 steps (K = 256), its 64
-// weight rows' 144-byte pieces with 9 direct global->LDS loads in which
-// consecutive lanes read consecutive 16-byte chunks of a row (about 13 cache
-// lines per load), double buffered per group, and each lane reads its 5
-// dwords per step and operand from LDS.  Inside a step the B operand of
-// slice i+1 is dequantised and its activation fragments read while slice i's
-// MFMAs run.
-constexpr int G4S = 5;                  // max 32-row subtiles per tile (= FMAXS)
-constexpr int G4R = 32 * G4S;
-constexpr int G4K = 64;                 // K per step
-constexpr int G4NS = 4;                 // pipeline depth (steps in flight + 1)
-
-// A step of the software-pipelined slices: bc/ac hold slice Q's operands.
-template <int MS, int Q>
-__device__ __forceinline__ void g4_slice(const uint16_t* cur, const int (&aofs)[4], const uint32_t (&n0)[4],
-                                         const uint32_t (&n1)[4], float d0, float d1, bf16x8_t& bc0,
-                                         bf16x8_t& bc1, bf16x8_t (&ac)[MS], f32x16_t (&acc0)[MS],
-                                         f32x16_t (&acc1)[MS]) {
-  bf16x8_t bn0, bn1, an[MS];
-  if (Q < 3) {
-    bn0 = g2_deq<(Q + 1) & 3>(n0, d0);
-    bn1 = g2_deq<(Q + 1) & 3>(n1, d1);
-#pragma unroll
-    for (int sub = 0; sub < MS; sub++)
-      an[sub] = *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G4K + aofs[(Q + 1) & 3]);
-  }
-#pragma unroll
-  for (int sub = 0; sub < MS; sub++) {
-    acc0[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[sub], bc0, acc0[sub], 0, 0, 0);
-    acc1[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[sub], bc1, acc1[sub], 0, 0, 0);
-  }
-  if (Q < 3) {
-    bc0 = bn0;
-    bc1 = bn1;
-#pragma unroll
-    for (int sub = 0; sub < MS; sub++) ac[sub] = an[sub];
-  }
-}
-
-constexpr int G4WCH = 9;                // 16-byte chunks of a row's 144-byte group piece
-
-struct G4Smem {
-  uint16_t a[G4NS][G4R * G4K];          // 4 x 20 KB activation ring
-  uint32_t w[2][G2W][64 * G4WCH * 4];   // [buffer][wave]: 64 rows x 144 B
-};
-
-template <int MS, bool GATEUP>
-__device__ __forceinline__ void g4_unit(const PrefillArgs& a, const Tile& t, int cb, G4Smem& sm) {
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, g = lane / 32;
-  const int H = a.H, I = a.I;
-  const int N = GATEUP ? I : H, K = GATEUP ? H : I;
-  const int nsteps = K / G4K;                         // a multiple of 4, >= 4
-  const int ngroups = nsteps / 4;
-  const size_t rb = (size_t)(K / BLK) * Q4B;          // a multiple of 144
-  const int col0 = GATEUP ? cb * 128 + wave * 32 : cb * 256 + wave * 64;
-  const int col1 = GATEUP ? col0 : col0 + 32;
-  const bool live0 = col0 < N, live1 = col1 < N;
-  const int c0 = min(col0, N - 32), c1 = min(col1, N - 32);
-  const uint8_t *w0, *w1;
-  if (GATEUP) {
-    w0 = (t.expert >= 0) ? a.w_gate + ((size_t)t.expert * I + c0) * rb : a.s_gate + (size_t)c0 * rb;
-    w1 = (t.expert >= 0) ? a.w_up + ((size_t)t.expert * I + c0) * rb : a.s_up + (size_t)c0 * rb;
-  } else {
-    const uint8_t* wd = (t.expert >= 0) ? a.w_down + (size_t)t.expert * H * rb : a.s_down;
-    w0 = wd + (size_t)c0 * rb;
-    w1 = wd + (size_t)c1 * rb;
-  }
-  // weight chunk v of this lane: chunk c = 64v + lane of the wave's 64 rows
-  // (rows 0..31: operand 0, 32..63: operand 1), row c / 9, 16-byte part c % 9
-  const uint8_t* wsrc[G4WCH];
-#pragma unroll
-  for (int v = 0; v < G4WCH; v++) {
-    const int c = 64 * v + lane, r = c / G4WCH, part = c - G4WCH * r;
-    wsrc[v] = ((r >> 5) ? w1 : w0) + (size_t)(r & 31) * rb + 16 * part;
-  }
-  const uint32_t sel_n = g ? 0x07060504u : 0x05040302u;
-  const uint32_t sel_s = g ? 0x0c0c0302u : 0x0c0c0100u;
-
-  const uint16_t* abase = GATEUP ? a.x : a.h + (size_t)t.pos0 * I;
-  uint32_t src[MS];
-#pragma unroll
-  for (int q = 0; q < MS; q++) {
-    const int r = 8 * (wave + G2W * q) + lane / 8;
-    const int m = min(r, t.rows - 1);
-    uint32_t rowel;
-    if (GATEUP) {
-      const int tk = (t.expert >= 0) ? a.perm[t.pos0 + m] / a.k : t.m0 + m;
-      rowel = (uint32_t)min(max(tk, 0), a.T - 1) * (uint32_t)H;
-    } else {
-      rowel = (uint32_t)m * (uint32_t)I;
-    }
-    src[q] = rowel + 8u * (uint32_t)g2_slot(lane & 7, r);
-  }
-  int aofs[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) aofs[i] = ln * G4K + 8 * g2_slot(4 * g + i, ln);
-
-  f32x16_t acc0[MS], acc1[MS];
-#pragma unroll
-  for (int q = 0; q < MS; q++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) { acc0[q][r] = 0.0f; acc1[q][r] = 0.0f; }
-
-  auto issue_a = [&](int s, int slot) {
-#pragma unroll
-    for (int q = 0; q < MS; q++) lds_load16(abase + src[q] + G4K * s, sm.a[slot] + (wave + G2W * q) * 512);
-  };
-  auto issue_w = [&](int G, int buf) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(sm.w[buf][wave]);
-#pragma unroll
-    for (int v = 0; v < G4WCH; v++) lds_load16(wsrc[v] + 144 * (size_t)G, dst + 512 * v);
-  };
-  // step j (0..3) of the group in W buffer `buf`, activations in ring slot `slot`
-  auto compute = [&](int slot, int buf, int j) {
-    const uint16_t* cur = sm.a[slot];
-    const uint32_t* wl = sm.w[buf][wave];
-    uint32_t D0[5], D1[5];
-#pragma unroll
-    for (int v = 0; v < 5; v++) {
-      D0[v] = wl[36 * ln + 9 * j + 4 * g + v];
-      D1[v] = wl[36 * (32 + ln) + 9 * j + 4 * g + v];
-    }
-    uint32_t n0[4], n1[4];
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      n0[v] = __builtin_amdgcn_perm(D0[v + 1], D0[v], sel_n);
-      n1[v] = __builtin_amdgcn_perm(D1[v + 1], D1[v], sel_n);
-    }
-    const float d0 = f16_bits_to_f32(__builtin_amdgcn_perm(D0[1], D0[0], sel_s));
-    const float d1 = f16_bits_to_f32(__builtin_amdgcn_perm(D1[1], D1[0], sel_s));
-    bf16x8_t bc0 = g2_deq<0>(n0, d0), bc1 = g2_deq<0>(n1, d1);
-    bf16x8_t ac[MS];
-#pragma unroll
-    for (int sub = 0; sub < MS; sub++) ac[sub] = *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G4K + aofs[0]);
-    g4_slice<MS, 0>(cur, aofs, n0, n1, d0, d1, bc0, bc1, ac, acc0, acc1);
-    g4_slice<MS, 1>(cur, aofs, n0, n1, d0, d1, bc0, bc1, ac, acc0, acc1);
-    g4_slice<MS, 2>(cur, aofs, n0, n1, d0, d1, bc0, bc1, ac, acc0, acc1);
-    g4_slice<MS, 3>(cur, aofs, n0, n1, d0, d1, bc0, bc1, ac, acc0, acc1);
-  };
-
-  // Issue order: W(0), A(0), A(1), A(2); step s issues A(s+3) and, at the
-  // first step of group G, W(G+1).  At step s the wait leaves in flight only
-  // what was issued after A(s): A(s+1), A(s+2) (MS loads each, when they
-  // exist) and W(G+1) (9 loads) at steps 1..3 of a group that has a
-  // successor; W(G) was issued before A(4G), so the wait at step 4G covers it.
-  g2_barrier();                                       // ring and W buffers are free
-  issue_w(0, 0);
-  issue_a(0, 0);
-  issue_a(1, 1);
-  issue_a(2, 2);
-  int G = 0;
-  for (; G + 1 < ngroups; G++) {
-    const int s = 4 * G, buf = G & 1;
-    wait_vm<2 * MS>();
-    g2_barrier();
-    issue_a(s + 3, 3);
-    issue_w(G + 1, buf ^ 1);
-    compute(0, buf, 0);
-    wait_vm<2 * MS + G4WCH>();
-    g2_barrier();
-    issue_a(s + 4, 0);
-    compute(1, buf, 1);
-    wait_vm<2 * MS + G4WCH>();
-    g2_barrier();
-    issue_a(s + 5, 1);
-    compute(2, buf, 2);
-    wait_vm<2 * MS + G4WCH>();
-    g2_barrier();
-    issue_a(s + 6, 2);
-    compute(3, buf, 3);
-  }
-  {
-    const int s = 4 * G, buf = G & 1;
-    wait_vm<2 * MS>();
-    g2_barrier();
-    issue_a(s + 3, 3);
-    compute(0, buf, 0);
-    wait_vm<2 * MS>();
-    g2_barrier();
-    compute(1, buf, 1);
-    wait_vm<MS>();
-    g2_barrier();
-    compute(2, buf, 2);
-    wait_vm<0>();
-    g2_barrier();
-    compute(3, buf, 3);
-  }
-
-  const int n0c = c0 + ln, n1c = c1 + ln;
-#pragma unroll
-  for (int sub = 0; sub < MS; sub++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int rr = 32 * sub + 8 * (r / 4) + 4 * g + (r % 4);
-      if (rr >= t.rows) continue;
-      if (GATEUP) {
-        if (!live0) continue;
-        const float gv = acc0[sub][r], uv = acc1[sub][r];
-        const float hv = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
-        a.h[(size_t)(t.pos0 + rr) * I + n0c] = f32_to_bf16_bits(hv);
-      } else if (t.expert >= 0) {
-        if (live0) a.o_perm[(size_t)(t.pos0 + rr) * H + n0c] = f32_to_bf16_bits(acc0[sub][r]);
-        if (live1) a.o_perm[(size_t)(t.pos0 + rr) * H + n1c] = f32_to_bf16_bits(acc1[sub][r]);
-      } else {
-        if (live0) a.y[(size_t)(t.m0 + rr) * H + n0c] = acc0[sub][r];
-        if (live1) a.y[(size_t)(t.m0 + rr) * H + n1c] = acc1[sub][r];
-      }
-    }
-}
-
-template <bool GATEUP>
-__global__ void __launch_bounds__(256, 1) gemm_g4_kernel(PrefillArgs a, int ncb) {
-  __shared__ __attribute__((aligned(16))) G4Smem sm;
-  const int P = gridDim.x / 8;                        // blocks per XCD
-  const int x = blockIdx.x % 8, l = blockIdx.x / 8;
-  if (l >= P) return;
-  for (int j = l;; j += P) {
-    const int tile = 8 * (j / ncb) + x, cb = j % ncb;
-    const Tile t = find_tile_bal(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
-    if (!t.valid) break;                              // tiles are numbered densely
-    switch ((t.rows + 31) / 32) {
-      case 1: g4_unit<1, GATEUP>(a, t, cb, sm); break;
-      case 2: g4_unit<2, GATEUP>(a, t, cb, sm); break;
-      case 3: g4_unit<3, GATEUP>(a, t, cb, sm); break;
-      case 4: g4_unit<4, GATEUP>(a, t, cb, sm); break;
-      default: g4_unit<5, GATEUP>(a, t, cb, sm); break;
-    }
-  }
-}
-
 // ---------------------------------------------------------------- combine
 __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
   const int H = a.H, k = a.k;
@@ -972,30 +729,10 @@ __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------- launch
-// Blocks of a persistent launch: the current device's CU count rounded down
-// to a multiple of 8 (blocks are dealt to the 8 XCDs round robin), cached per
-// device.
-static int persistent_blocks() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-      cus = 8;
-    cached[dev] = cus / 8 * 8;
-  }
-  return cached[dev];
-}
-
-// Kernel choice per stage: the two-blocks-per-CU grouped kernel (g2) when K
-// is a multiple of 64 and the pointers are aligned; the persistent
-// weights-through-LDS kernel (g4) only when built with MOEQ4_GEMM_IMPL=4
-// (kept for schedule work; slower than g2 so far); the generic kernels for
-// any other shape (K a multiple of 32).
-#ifndef MOEQ4_GEMM_IMPL
-#define MOEQ4_GEMM_IMPL 2
-#endif
+// Kernel choice: gate/up and down together take the fused launch when both
+// K are multiples of 64 and the pointers are aligned; a single projection
+// takes gemm_g2 under the same conditions; the generic kernels cover any
+// other shape (K a multiple of 32).
 hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) {
   constexpr int MT = 4, BM = 32 * MT;
   const int64_t assignments = (int64_t)a.T * a.k;
@@ -1006,11 +743,6 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
                     (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 8 == 0));
   const int vec_d = ((a.I / BLK) % 4 == 0) && ((uintptr_t)a.w_down % 8 == 0) &&
                     (!a.has_shared || ((uintptr_t)a.s_down % 8 == 0));
-  const bool g4_g = MOEQ4_GEMM_IMPL == 4 && a.H % 256 == 0 && ((uintptr_t)a.x % 16 == 0) &&
-                    (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 16 == 0) &&
-                    (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 16 == 0));
-  const bool g4_d = MOEQ4_GEMM_IMPL == 4 && a.I % 256 == 0 && ((uintptr_t)a.h % 16 == 0) &&
-                    ((uintptr_t)a.w_down % 16 == 0) && (!a.has_shared || ((uintptr_t)a.s_down % 16 == 0));
   const bool g2_g = a.H % G2K == 0 && ((uintptr_t)a.x % 16 == 0) &&
                     (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 4 == 0) &&
                     (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 4 == 0));
@@ -1018,7 +750,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
                     ((uintptr_t)a.w_down % 4 == 0) && (!a.has_shared || ((uintptr_t)a.s_down % 4 == 0));
   const int g2_groups = (btiles + 7) / 8;
   hipError_t err = hipSuccess;
-  if ((stages & 3) == 3 && MOEQ4_GEMM_IMPL == 2 && g2_g && g2_d && a.tile_done) {
+  if ((stages & 3) == 3 && g2_g && g2_d && a.tile_done) {
     const int ncb_gu = (a.I + 127) / 128, ncb_dn = (a.H + 255) / 256;
     const int n_gu = g2_groups * 8 * ncb_gu, n_dn = g2_groups * 8 * ncb_dn;
     hipLaunchKernelGGL(fill_zero_kernel, dim3((btiles + 255) / 256), dim3(256), 0, stream, a.tile_done, btiles);
@@ -1028,10 +760,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
     stages &= ~3;
   }
   if (stages & 1) {
-    if (g4_g) {
-      hipLaunchKernelGGL((gemm_g4_kernel<true>), dim3(persistent_blocks()), dim3(256), 0, stream, a,
-                         (a.I + 127) / 128);
-    } else if (g2_g) {
+    if (g2_g) {
       const int ncb = (a.I + 127) / 128;
       hipLaunchKernelGGL((gemm_g2_kernel<true>), dim3(g2_groups * 8 * ncb), dim3(256), 0, stream, a, ncb);
     } else {
@@ -1042,10 +771,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
     if (err != hipSuccess) return err;
   }
   if (stages & 2) {
-    if (g4_d) {
-      hipLaunchKernelGGL((gemm_g4_kernel<false>), dim3(persistent_blocks()), dim3(256), 0, stream, a,
-                         (a.H + 255) / 256);
-    } else if (g2_d) {
+    if (g2_d) {
       const int ncb = (a.H + 255) / 256;
       hipLaunchKernelGGL((gemm_g2_kernel<false>), dim3(g2_groups * 8 * ncb), dim3(256), 0, stream, a, ncb);
     } else {
