@@ -11,8 +11,9 @@
 // abstract) is the reason every tie and summation order is pinned.
 //
 // Kernels (one stream, no host round trip):
-//   router_partials  tiled fp32 VALU product, 64 tokens x 64 experts per
-//                    block, one aligned subtree of cw chunks per grid z
+//   router_partials  the per-chunk FMA chains as chained K=1 fp32 MFMAs (32
+//                    tokens x 64 experts per wave), one aligned subtree of
+//                    cw chunks per grid z
 //   topk_hist        finishes the chunk tree, top-k (k rounds of a DPP
 //                    wave maximum over 64-bit order keys), weights, and a
 //                    wavefront-ballot histogram of the block's tokens with
@@ -35,99 +36,79 @@ RouterSplit prefill_router_split(int H) {
 }
 
 // ---------------------------------------------------------------- partials
-constexpr int RT = 64;   // tokens per block
-constexpr int RE = 64;   // experts per block
-
 template <int CW>
 struct Log2 { static constexpr int v = 1 + Log2<CW / 2>::v; };
 template <>
 struct Log2<1> { static constexpr int v = 0; };
 
-template <bool BF16, int CW>
-__global__ void __launch_bounds__(256) router_partials_kernel(const void* __restrict__ xv, int T,
-                                                              int H, const float* __restrict__ Wr,
-                                                              int E, int nc,
-                                                              float* __restrict__ partials) {
-  constexpr int L = Log2<CW>::v;
-  __shared__ float xs[BLK][RT + 4];   // [h][token], rows 16-byte aligned
-  __shared__ float wsh[BLK][RE + 4];  // [h][expert]
-  const int tid = threadIdx.x;
-  const int tx = tid % 16, ty = tid / 16;
-  const int e0 = blockIdx.x * RE, t0 = blockIdx.y * RT, split = blockIdx.z;
-  const bool vecw = (E % 4) == 0;
+// Leaves on v_mfma_f32_32x32x1f32: one instruction is an outer
+// product of 32 values by 32 values for each of two blocks, and each output
+// gets exactly one fmaf per instruction (checked bit for bit against fmaf
+// chains on gfx950), so 32 instructions over k = 0..31 are the chunk's
+// sequential FMA chain, at twice the fp32 VALU rate.  A wave covers 32 tokens
+// x 64 experts: lane l supplies token t0 + l%32 (both lane halves) and
+// expert e0 + 32*(l/32) + l%32; block b's output (row i, column j) sits in
+// register 16b + 4*(i/8) + i%4 of lane 32*((i/4)%2) + j.  No LDS: a lane
+// reads its token's 32 chunk values and, per k, one dword of a W_r row that
+// the wave reads contiguously.  A chunk's operands are loaded two chunks
+// ahead, so the loads run under the previous chunks' MFMA chains.
+constexpr int RMW = 4;                    // waves (token tiles of 32) per block
 
-  // global -> register staging of one chunk: 8 x values and 8 W values per thread
-  const int xt = tid / 4, xh = (tid % 4) * 8;      // token row, h offset
-  const int wr = tid / 8, we = (tid % 8) * 8;      // W row, expert offset
-  float px[8], pw[8];
-  auto fetch = [&](int c) {
-    const int h0 = c * BLK;
-    const int t = t0 + xt;
-    if (t < T) {
-      if (BF16) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(
-            static_cast<const uint16_t*>(xv) + (size_t)t * H + h0 + xh);
+template <bool BF16, int CW>
+__global__ void __launch_bounds__(64 * RMW) router_partials_mfma_kernel(const void* __restrict__ xv, int T,
+                                                                         int H, const float* __restrict__ Wr,
+                                                                         int E, int nc,
+                                                                         float* __restrict__ partials) {
+  typedef float f32x32_t __attribute__((ext_vector_type(32)));
+  constexpr int L = Log2<CW>::v;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int t0 = (blockIdx.y * RMW + wave) * 32, e0 = blockIdx.x * 64, split = blockIdx.z;
+  const int t = t0 + lane % 32, e = e0 + 32 * (lane / 32) + lane % 32;
+  const bool tv = t < T, ev = e < E;
+  const int tc = tv ? t : T - 1, ec = ev ? e : E - 1;       // clamped: loads stay in bounds
+  f32x32_t st[L + 1];
+  const int cbase = split * CW;
+  float xa[BLK], wa[BLK];
+  auto load = [&](int c) {
+    if (BF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + (size_t)tc * H + c * BLK);
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint4 raw = src[q];
         const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          px[2 * i] = bf16_bits_to_f32(r[i] & 0xffffu);
-          px[2 * i + 1] = bf16_bits_to_f32(r[i] >> 16);
+          xa[8 * q + 2 * i] = bf16_bits_to_f32(r[i] & 0xffffu);
+          xa[8 * q + 2 * i + 1] = bf16_bits_to_f32(r[i] >> 16);
         }
-      } else {
-        const float* src = static_cast<const float*>(xv) + (size_t)t * H + h0 + xh;
-        const float4 a = *reinterpret_cast<const float4*>(src);
-        const float4 b = *reinterpret_cast<const float4*>(src + 4);
-        px[0] = a.x; px[1] = a.y; px[2] = a.z; px[3] = a.w;
-        px[4] = b.x; px[5] = b.y; px[6] = b.z; px[7] = b.w;
       }
     } else {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + (size_t)tc * H + c * BLK);
 #pragma unroll
-      for (int i = 0; i < 8; i++) px[i] = 0.0f;
+      for (int q = 0; q < 8; q++) {
+        const float4 v = src[q];
+        xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
+      }
     }
-    const float* wsrc = Wr + (size_t)(h0 + wr) * E;
-    const int e = e0 + we;
-    if (vecw && e + 8 <= E) {
-      const float4 a = *reinterpret_cast<const float4*>(wsrc + e);
-      const float4 b = *reinterpret_cast<const float4*>(wsrc + e + 4);
-      pw[0] = a.x; pw[1] = a.y; pw[2] = a.z; pw[3] = a.w;
-      pw[4] = b.x; pw[5] = b.y; pw[6] = b.z; pw[7] = b.w;
-    } else {
+    const float* wsrc = Wr + (size_t)c * BLK * E + ec;
 #pragma unroll
-      for (int i = 0; i < 8; i++) pw[i] = (e + i < E) ? wsrc[e + i] : 0.0f;
-    }
+    for (int k = 0; k < BLK; k++) wa[k] = wsrc[(size_t)k * E];
   };
-  auto stash = [&]() {
+  float xb[3][BLK], wb[3][BLK];
+  auto stage = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) xs[xh + i][xt] = px[i];
-    *reinterpret_cast<float4*>(&wsh[wr][we]) = make_float4(pw[0], pw[1], pw[2], pw[3]);
-    *reinterpret_cast<float4*>(&wsh[wr][we + 4]) = make_float4(pw[4], pw[5], pw[6], pw[7]);
+    for (int k = 0; k < BLK; k++) { xb[slot][k] = xa[k]; wb[slot][k] = wa[k]; }
   };
-
-  float st[L + 1][16];
-  const int cbase = split * CW;
-  if (cbase < nc) fetch(cbase);
+  if (cbase < nc) { load(cbase); stage(0); }
+  if (CW > 1 && cbase + 1 < nc) { load(cbase + 1); stage(1); }
 #pragma unroll
   for (int cl = 0; cl < CW; cl++) {
     const int c = cbase + cl;
-    float acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; i++) acc[i] = 0.0f;
+    f32x32_t acc = {};
     if (c < nc) {                         // padded leaves stay +0.0
-      __syncthreads();
-      stash();
-      __syncthreads();
-      if (cl + 1 < CW && c + 1 < nc) fetch(c + 1);
-#pragma unroll 8
-      for (int h = 0; h < BLK; h++) {
-        const float4 a = *reinterpret_cast<const float4*>(&xs[h][ty * 4]);
-        const float4 b = *reinterpret_cast<const float4*>(&wsh[h][tx * 4]);
-        const float av[4] = {a.x, a.y, a.z, a.w};
-        const float bv[4] = {b.x, b.y, b.z, b.w};
+      if (cl + 2 < CW && c + 2 < nc) { load(c + 2); stage((cl + 2) % 3); }   // two chunks ahead
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-          for (int j = 0; j < 4; j++) acc[i * 4 + j] = __builtin_fmaf(av[i], bv[j], acc[i * 4 + j]);
-      }
+      for (int k = 0; k < BLK; k++) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xb[cl % 3][k], wb[cl % 3][k], acc, 0, 0, 0);
     }
     // binary-counter merge: leaf cl joins the pending subtrees of equal size
     int lvl = 0;
@@ -137,38 +118,27 @@ __global__ void __launch_bounds__(256) router_partials_kernel(const void* __rest
       lvl = b + 1;
     }
 #pragma unroll
-    for (int b = 0; b < L; b++) {
-      if (b < lvl) {
-#pragma unroll
-        for (int i = 0; i < 16; i++) acc[i] = st[b][i] + acc[i];
-      }
-    }
+    for (int b = 0; b < L; b++)
+      if (b < lvl) acc = st[b] + acc;
 #pragma unroll
     for (int b = 0; b <= L; b++)
-      if (b == lvl) {
-#pragma unroll
-        for (int i = 0; i < 16; i++) st[b][i] = acc[i];
-      }
+      if (b == lvl) st[b] = acc;
   }
   float* out = partials + (size_t)split * T * E;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) out[(size_t)t * E + e] = st[L][i * 4 + j];
-    }
+  for (int r = 0; r < 32; r++) {
+    const int blk = r / 16, i = 8 * ((r % 16) / 4) + 4 * (lane / 32) + (r % 4), j = lane % 32;
+    const int to = t0 + i, eo = e0 + 32 * blk + j;
+    if (to < T && eo < E) out[(size_t)to * E + eo] = st[L][r];
   }
 }
 
 hipError_t launch_router_partials(const void* x, int x_bf16, int T, int H, const float* w_router,
                                   int E, const RouterSplit& sp, float* partials,
                                   hipStream_t stream) {
-  dim3 grid((E + RE - 1) / RE, (T + RT - 1) / RT, sp.nsplit);
-#define MOEQ4_RP(BF, CWV)                                                                   \
-  hipLaunchKernelGGL((router_partials_kernel<BF, CWV>), grid, dim3(256), 0, stream, x, T, H, \
+  dim3 grid((E + 63) / 64, (T + 32 * RMW - 1) / (32 * RMW), sp.nsplit);
+#define MOEQ4_RP(BF, CWV)                                                                         \
+  hipLaunchKernelGGL((router_partials_mfma_kernel<BF, CWV>), grid, dim3(64 * RMW), 0, stream, x, T, H, \
                      w_router, E, sp.nc, partials)
 #define MOEQ4_RP_CW(BF)                      \
   switch (sp.cw) {                           \
