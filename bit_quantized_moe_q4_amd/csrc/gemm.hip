@@ -696,12 +696,31 @@ __global__ void __launch_bounds__(256, 2) gemm_ffn_kernel(PrefillArgs a, int ncb
 }
 
 // ---------------------------------------------------------------- combine
+// Up to KU slots per token with every load issued before the first sum:
+// the k indices and weights, then the k expert-output rows.  Sum order:
+// y = (((shared + w_0 o_0) + w_1 o_1) + ...), slots in order.
+template <int KU>
 __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
   const int H = a.H, k = a.k;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int per_row = H / 8;
   if (idx >= (int64_t)a.T * per_row) return;
   const int t = (int)(idx / per_row), c = (int)(idx % per_row) * 8;
+  int p[KU];
+  float w[KU];
+#pragma unroll
+  for (int s = 0; s < KU; s++) {
+    p[s] = 0;
+    w[s] = 0.0f;
+    if (s < k) {
+      p[s] = min(max(a.inv_perm[(size_t)t * k + s], 0), a.T * k - 1);
+      w[s] = a.topk_w[(size_t)t * k + s];
+    }
+  }
+  uint4 v[KU];
+#pragma unroll
+  for (int s = 0; s < KU; s++)
+    if (s < k) v[s] = *reinterpret_cast<const uint4*>(a.o_perm + (size_t)p[s] * H + c);
   float acc[8];
   float* yr = a.y + (size_t)t * H + c;
   if (a.has_shared) {
@@ -713,15 +732,15 @@ __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; i++) acc[i] = 0.0f;
   }
-  for (int s = 0; s < k; s++) {
-    const int p = min(max(a.inv_perm[(size_t)t * k + s], 0), a.T * k - 1);
-    const float w = a.topk_w[(size_t)t * k + s];
-    const uint4 v = *reinterpret_cast<const uint4*>(a.o_perm + (size_t)p * H + c);
-    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      acc[2 * i] += w * bf16_bits_to_f32(q[i] & 0xffffu);
-      acc[2 * i + 1] += w * bf16_bits_to_f32(q[i] >> 16);
+  for (int s = 0; s < KU; s++) {
+    if (s < k) {
+      const uint32_t q[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        acc[2 * i] += w[s] * bf16_bits_to_f32(q[i] & 0xffffu);
+        acc[2 * i + 1] += w[s] * bf16_bits_to_f32(q[i] >> 16);
+      }
     }
   }
   *reinterpret_cast<float4*>(yr) = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -783,7 +802,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
   }
   if (stages & 4) {
     const int64_t n = (int64_t)a.T * (a.H / 8);
-    hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, a);
+    const dim3 grid((uint32_t)((n + 255) / 256));
+    if (a.k <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(combine_kernel<32>, grid, dim3(256), 0, stream, a);
     err = hipGetLastError();
   }
   return err;

@@ -208,6 +208,9 @@ def _prefill_err(ol, gl, cfg, T, sample=None, step=0):
     ("multi_tile", 300, 512, 16, 256, 4, True),
     ("ragged_k_tail", 77, 96, 5, 96, 2, True),
     ("one_expert_dense", 150, 256, 1, 128, 1, False),
+    # more than 8 slots per token (the combine's wide path), and k = E
+    ("wide_topk", 96, 256, 64, 128, 16, True),
+    ("every_expert", 64, 256, 32, 64, 32, True),
 ])
 def test_prefill_small(name, T, H, E, I, k, shared):
     say("prefill", name, T, H, E, I, k, shared)
