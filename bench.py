@@ -124,6 +124,27 @@ def write_traffic(fetch_csv, write_csv, command):
         print(unit, doc["bytes_per_launch"], "bytes per launch")
 
 
+def hbm_copy_gbps(torch, nbytes=1 << 30, reps=5):
+    """Achievable HBM bandwidth: a device-to-device copy of nbytes (read +
+    write counted), median over reps, timed with events."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    torch.cuda.empty_cache()
+    ts.sort()
+    return 2.0 * nbytes / ts[len(ts) // 2] / 1e9
+
+
 def copy_probe(torch):
     """One plain device-to-device copy of COPY_PROBE_BYTES (counter calibration)."""
     a = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -309,6 +330,7 @@ def main():
 
     pre = bench_prefill(args, torch, mq, moe_synth, device_layer)
     dec = bench_decode(args, torch, mq, moe_synth, device_layer)
+    copy_gbps = hbm_copy_gbps(torch)
     cfg = pre["cfg"]
     tok_s = cfg.T / pre["step_s"]
     fl_gemm = pre["fl_gu"] + pre["fl_dn"]
@@ -359,6 +381,9 @@ def main():
             "steps": args.decode_steps,
             "bytes_per_step": dec["bytes_step"],
             "layer_copies_rotated": dec["copies"],
+            "hbm_copy_gbps": round(copy_gbps, 1),
+            "hbm_copy_note": "achievable HBM bandwidth on this GPU: a 1 GiB device-to-device copy, "
+                             "read + write bytes over its time (median of 5)",
             "workload": "one-token W4A8 decode, same layer shape, fresh x per step, HIP graph replay",
             "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
