@@ -155,11 +155,11 @@ def copy_probe(torch):
     del a, b
 
 
-def clone_layer(L):
+def clone_layer(L, tiles=True):
     import bit_quantized_moe_q4_amd as mq
     c = lambda t: None if t is None else t.clone()  # noqa: E731
     return mq.MoELayer(c(L.w_router), c(L.gate), c(L.up), c(L.down), L.top_k, c(L.router_bias),
-                       c(L.s_gate), c(L.s_up), c(L.s_down))
+                       c(L.s_gate), c(L.s_up), c(L.s_down), tiles=tiles)
 
 
 def bench_prefill(args, torch, mq, moe_synth, device_layer):
@@ -213,8 +213,8 @@ def bench_prefill(args, torch, mq, moe_synth, device_layer):
 
 def bench_decode(args, torch, mq, moe_synth, device_layer):
     cfg = moe_synth.CONFIGS["decode"]
-    base = device_layer(cfg)
-    copies = [base] + [clone_layer(base) for _ in range(args.decode_copies - 1)]
+    base = device_layer(cfg, tiles=False)                 # decode reads the row-major matrices
+    copies = [base] + [clone_layer(base, tiles=False) for _ in range(args.decode_copies - 1)]
     n = args.decode_steps
     X = torch.from_numpy(moe_synth.tokens(cfg, step=0, T=n)).cuda()   # fresh seeded x per step
     Y = torch.empty((n, cfg.H), dtype=torch.float32, device="cuda")

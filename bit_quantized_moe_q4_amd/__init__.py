@@ -21,7 +21,7 @@ import torch
 from . import _lib
 
 __all__ = [
-    "q4_packed_bytes", "q4_pack", "q8_quantize", "MoELayer", "Routing",
+    "q4_packed_bytes", "q4_pack", "q4_tile", "q8_quantize", "MoELayer", "Routing",
     "moe_q4_route_workspace_bytes", "moe_q4_route",
     "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage",
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
@@ -67,6 +67,19 @@ def q4_pack(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> to
     return out
 
 
+def q4_tile(q4: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """uint8 [..., rows, K/32*18] Q4_0 blocks -> the same blocks in grouped-GEMM
+    tile order (q4_tile in moe_q4.h); rows % 32 == 0, K % 64 == 0."""
+    _dev(q4, "q4")
+    rb = q4.shape[-1]
+    K = rb // 18 * 32
+    rows = q4.numel() // rb
+    if out is None:
+        out = torch.empty_like(q4)
+    _lib.check(_lib.lib().q4_tile(_p(q4), rows, K, _p(out), _s(stream)), "q4_tile")
+    return out
+
+
 def q8_quantize(x: torch.Tensor, stream=None):
     """fp32 [..., K] -> (int8 [..., K], fp32 scales [..., K/32])."""
     _dev(x, "x")
@@ -85,10 +98,13 @@ class MoELayer:
     w_router fp32 [H, E]; gate/up uint8 [E, I, H/32*18]; down uint8
     [E, H, I/32*18]; optional router_bias fp32 [E] and shared expert
     s_gate/s_up uint8 [I, H/32*18], s_down uint8 [H, I/32*18].
+    With `tiles` (the default) and H, I multiples of 64 the layer also keeps
+    the matrices in grouped-GEMM tile order (q4_tile), which moe_q4_prefill's
+    fused GEMM reads; that doubles the resident weight bytes.
     """
 
     def __init__(self, w_router, gate, up, down, top_k, router_bias=None,
-                 s_gate=None, s_up=None, s_down=None):
+                 s_gate=None, s_up=None, s_down=None, tiles=True, stream=None):
         for n, t in (("w_router", w_router), ("gate", gate), ("up", up), ("down", down),
                      ("router_bias", router_bias), ("s_gate", s_gate), ("s_up", s_up),
                      ("s_down", s_down)):
@@ -106,15 +122,23 @@ class MoELayer:
         st.w_router, st.router_bias = _p(w_router), _p(router_bias)
         st.w_gate, st.w_up, st.w_down = _p(gate), _p(up), _p(down)
         st.s_gate, st.s_up, st.s_down = _p(s_gate), _p(s_up), _p(s_down)
+        self.tiles = None
+        if tiles and self.hidden % 64 == 0 and self.inter % 64 == 0:
+            tl = lambda t: None if t is None else q4_tile(t, stream=stream)  # noqa: E731
+            self.tiles = dict(gate=tl(gate), up=tl(up), down=tl(down),
+                              s_gate=tl(s_gate), s_up=tl(s_up), s_down=tl(s_down))
+            T_ = self.tiles
+            st.t_gate, st.t_up, st.t_down = _p(T_["gate"]), _p(T_["up"]), _p(T_["down"])
+            st.ts_gate, st.ts_up, st.ts_down = _p(T_["s_gate"]), _p(T_["s_up"]), _p(T_["s_down"])
         self._c = st
 
     @classmethod
     def from_float(cls, w_router, gate, up, down, top_k, router_bias=None,
-                   s_gate=None, s_up=None, s_down=None, stream=None):
+                   s_gate=None, s_up=None, s_down=None, tiles=True, stream=None):
         """Pack fp32 device weights with the library's q4_pack kernel."""
         pk = lambda t: None if t is None else q4_pack(t, stream=stream)  # noqa: E731
         return cls(w_router, pk(gate), pk(up), pk(down), top_k, router_bias,
-                   pk(s_gate), pk(s_up), pk(s_down))
+                   pk(s_gate), pk(s_up), pk(s_down), tiles=tiles, stream=stream)
 
     def struct_ptr(self):
         return C.byref(self._c)

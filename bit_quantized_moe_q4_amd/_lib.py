@@ -32,6 +32,8 @@ class Layer(C.Structure):
         ("w_router", C.c_void_p), ("router_bias", C.c_void_p),
         ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
         ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p),
+        ("t_gate", C.c_void_p), ("t_up", C.c_void_p), ("t_down", C.c_void_p),
+        ("ts_gate", C.c_void_p), ("ts_up", C.c_void_p), ("ts_down", C.c_void_p),
     ]
 
 
@@ -58,6 +60,7 @@ def _declare(lib):
     sig = {
         "q4_packed_bytes": (SZ, [I64, I64]),
         "q4_pack": (C.c_int, [P, I64, I64, P, P]),
+        "q4_tile": (C.c_int, [P, I64, I64, P, P]),
         "q8_quantize": (C.c_int, [P, I64, I64, P, P, P]),
         "moe_q4_route_workspace_bytes": (SZ, [P, I32]),
         "moe_q4_route": (C.c_int, [P, P, I32, I32, P, P, P, SZ, P]),

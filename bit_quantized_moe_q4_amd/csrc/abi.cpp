@@ -54,6 +54,21 @@ int check_layer(const moe_q4_layer* L) {
     return fail(MOE_Q4_EINVAL, "layer pointers must be 16-byte aligned (router_bias 4-byte)");
   if (L->has_shared && (!aligned(L->s_gate, 16) || !aligned(L->s_up, 16) || !aligned(L->s_down, 16)))
     return fail(MOE_Q4_EINVAL, "shared expert pointers must be 16-byte aligned");
+  const bool any_t = L->t_gate || L->t_up || L->t_down || L->ts_gate || L->ts_up || L->ts_down;
+  if (any_t) {
+    const bool routed = L->t_gate && L->t_up && L->t_down;
+    const bool shared = L->has_shared ? (L->ts_gate && L->ts_up && L->ts_down)
+                                      : !(L->ts_gate || L->ts_up || L->ts_down);
+    if (!routed || !shared)
+      return fail(MOE_Q4_EINVAL, "tile-order matrices: t_gate, t_up, t_down (and ts_* exactly when has_shared) "
+                                 "are given together or not at all");
+    if (L->hidden % 64 || L->inter % 64)
+      return fail(MOE_Q4_EINVAL, "tile-order matrices need hidden and inter multiples of 64 (H=%d I=%d)",
+                  L->hidden, L->inter);
+    if (!aligned(L->t_gate, 16) || !aligned(L->t_up, 16) || !aligned(L->t_down, 16) ||
+        (L->has_shared && (!aligned(L->ts_gate, 16) || !aligned(L->ts_up, 16) || !aligned(L->ts_down, 16))))
+      return fail(MOE_Q4_EINVAL, "tile-order matrices must be 16-byte aligned");
+  }
   return MOE_Q4_OK;
 }
 
@@ -133,6 +148,20 @@ int q4_pack(const float* w, int64_t rows, int64_t K, void* packed, hipStream_t s
   if (rows * (K / 32) > ((int64_t)1 << 40)) return fail(MOE_Q4_EINVAL, "q4_pack: too many blocks");
   hipError_t e = moeq4::launch_q4_pack(w, rows, K, packed, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "q4_pack");
+}
+
+int q4_tile(const void* q4, int64_t rows, int64_t K, void* tiled, hipStream_t stream) {
+  if (rows < 0 || rows % 32 || K <= 0 || K % 64)
+    return fail(MOE_Q4_EINVAL, "q4_tile: rows=%lld K=%lld (rows %% 32 == 0, K %% 64 == 0)", (long long)rows, (long long)K);
+  if (rows == 0) return MOE_Q4_OK;
+  if (!q4 || !tiled) return fail(MOE_Q4_EINVAL, "q4_tile: NULL pointer");
+  if (!aligned(q4, 2) || !aligned(tiled, 16)) return fail(MOE_Q4_EINVAL, "q4_tile: q4 must be 2-byte and tiled 16-byte aligned");
+  if (rows * (K / 32) > ((int64_t)1 << 40)) return fail(MOE_Q4_EINVAL, "q4_tile: too many blocks");
+  const size_t bytes = (size_t)rows * (size_t)(K / 32) * 18;
+  const uintptr_t a0 = (uintptr_t)q4, b0 = (uintptr_t)tiled;
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(MOE_Q4_EINVAL, "q4_tile: q4 and tiled overlap");
+  hipError_t e = moeq4::launch_q4_tile(q4, rows, K, tiled, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "q4_tile");
 }
 
 int q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d, hipStream_t stream) {
@@ -235,6 +264,12 @@ int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t 
   a.s_gate = static_cast<const uint8_t*>(L->s_gate);
   a.s_up = static_cast<const uint8_t*>(L->s_up);
   a.s_down = static_cast<const uint8_t*>(L->s_down);
+  a.t_gate = static_cast<const uint8_t*>(L->t_gate);
+  a.t_up = static_cast<const uint8_t*>(L->t_up);
+  a.t_down = static_cast<const uint8_t*>(L->t_down);
+  a.ts_gate = static_cast<const uint8_t*>(L->ts_gate);
+  a.ts_up = static_cast<const uint8_t*>(L->ts_up);
+  a.ts_down = static_cast<const uint8_t*>(L->ts_down);
   a.h = at<uint16_t>(ws, W.h);
   a.o_perm = at<uint16_t>(ws, W.o);
   a.tile_done = at<int32_t>(ws, W.tile_done);

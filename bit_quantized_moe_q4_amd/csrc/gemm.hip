@@ -428,7 +428,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // ---------------------------------------------------------------- two blocks per CU
-// Shapes with K a multiple of 64 and 4-byte aligned weight rows.
+// Shapes with K a multiple of 64, weights in the tile order of q4_tile.
 //
 // Block: 4 waves and 40 KB of LDS, so two blocks share a CU and one block's
 // barrier and load waits are covered by the other's MFMAs.  A block owns one
@@ -439,10 +439,11 @@ __device__ __forceinline__ void wait_vm() {
 //
 // K-step 64 = two Q4 blocks.  Lane (n, g) owns block g of the step of weight
 // row n: MFMA slice i (0..3) takes, in lane half g, elements 8i..8i+7 of that
-// block (the same permutation of K on both operands).  The lane loads the
-// 20 bytes at offset 16g of the row's 36-byte step piece (the block sits at
-// byte 0 or 2 of them) one step ahead into registers and realigns them with
-// v_perm.
+// block (the same permutation of K on both operands).  In tile order a step of
+// 32 rows is one 1152-byte piece: the lane reads its 16 nibble bytes at 16 *
+// lane and its scale at 1024 + 2 * lane, one step ahead into registers, so a
+// wave's weight loads cover 9 whole cache lines (row-major blocks would put
+// every lane on a line of its own).
 //
 // Activations: the step's [rows][64] bf16 tile lands in LDS by direct
 // global->LDS loads, double buffered; 16-byte chunk cc of row m sits at slot
@@ -464,15 +465,15 @@ struct G2Smem {
 
 __device__ __forceinline__ int g2_slot(int cc, int m) { return cc ^ (m & 7) ^ ((m >> 3) & 1); }
 
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-
-__device__ __forceinline__ void g2_load_w(const uint8_t* p, uint32_t (&D)[5]) {
-  const u32x4_a4 v = *reinterpret_cast<const u32x4_a4*>(p);
+// One step of the lane's weights: nibble dwords D[0..3] from `p`, the fp16
+// scale bits in D[4] from `p + sc`.
+__device__ __forceinline__ void g2_load_w(const uint8_t* p, int sc, uint32_t (&D)[5]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
   D[0] = v.x;
   D[1] = v.y;
   D[2] = v.z;
   D[3] = v.w;
-  D[4] = *reinterpret_cast<const uint32_t*>(p + 16);
+  D[4] = *reinterpret_cast<const uint16_t*>(p + sc);
 }
 
 // 8 bf16 weights of element group Q of the lane's block: scale bits `sc`,
@@ -496,6 +497,18 @@ __device__ __forceinline__ bf16x8_t g2_deq(const uint32_t (&nib)[4], float d) {
   return __builtin_bit_cast(bf16x8_t, w);
 }
 
+// Scheduling groups for one slice: each MFMA is followed by its share of the
+// next slice's dequantisation VALU, and every second one by a fragment read.
+template <int MS>
+__device__ __forceinline__ void g2_interleave() {
+#pragma unroll
+  for (int j = 0; j < 2 * MS; j++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, (44 + 2 * MS - 1) / (2 * MS), 0);  // VALU
+    if (j & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // DS read
+  }
+}
+
 __device__ __forceinline__ void g2_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int MS, bool GATEUP>
@@ -510,18 +523,18 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
   const bool live0 = col0 < N, live1 = col1 < N;
   const int c0 = min(col0, N - 32), c1 = min(col1, N - 32);   // dead groups load valid rows
   const uint8_t *w0, *w1;
+  // a 32-row group keeps its row-major byte range in tile order
   if (GATEUP) {
-    w0 = (t.expert >= 0) ? a.w_gate + ((size_t)t.expert * I + c0) * rb : a.s_gate + (size_t)c0 * rb;
-    w1 = (t.expert >= 0) ? a.w_up + ((size_t)t.expert * I + c0) * rb : a.s_up + (size_t)c0 * rb;
+    w0 = (t.expert >= 0) ? a.t_gate + ((size_t)t.expert * I + c0) * rb : a.ts_gate + (size_t)c0 * rb;
+    w1 = (t.expert >= 0) ? a.t_up + ((size_t)t.expert * I + c0) * rb : a.ts_up + (size_t)c0 * rb;
   } else {
-    const uint8_t* wd = (t.expert >= 0) ? a.w_down + (size_t)t.expert * H * rb : a.s_down;
+    const uint8_t* wd = (t.expert >= 0) ? a.t_down + (size_t)t.expert * H * rb : a.ts_down;
     w0 = wd + (size_t)c0 * rb;
     w1 = wd + (size_t)c1 * rb;
   }
-  const uint8_t* p0 = w0 + (size_t)ln * rb + 16 * g;
-  const uint8_t* p1 = w1 + (size_t)ln * rb + 16 * g;
-  const uint32_t sel_n = g ? 0x07060504u : 0x05040302u;      // nibble dword k of the block
-  const uint32_t sel_s = g ? 0x0c0c0302u : 0x0c0c0100u;      // its scale (upper half zero)
+  const uint8_t* p0 = w0 + 16 * lane;
+  const uint8_t* p1 = w1 + 16 * lane;
+  const int sc = 1024 - 14 * lane;                            // scale of the lane's block: piece + 1024 + 2 * lane
 
   // activation rows: wave-load j = wave + 4q covers tile rows 8j..8j+7
   const uint16_t* abase = GATEUP ? a.x : a.h + (size_t)t.pos0 * I;
@@ -552,8 +565,8 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
 
   uint32_t Dn0[5], Dn1[5];
   issue_a(0, sm.a[0]);
-  g2_load_w(p0, Dn0);
-  g2_load_w(p1, Dn1);
+  g2_load_w(p0, sc, Dn0);
+  g2_load_w(p1, sc, Dn1);
   // fragment read offsets (elements) inside a buffer, per slice i: row 32*sub + ln
   int aofs[4];
 #pragma unroll
@@ -563,37 +576,49 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
     uint16_t* cur = sm.a[s & 1];
     wait_vm<0>();                                // own A(s) and W(s) landed (issued a step ago)
     g2_barrier();                                // everyone's A(s) landed; step s-1 done
-    uint32_t D0[5], D1[5];
-#pragma unroll
-    for (int v = 0; v < 5; v++) { D0[v] = Dn0[v]; D1[v] = Dn1[v]; }
-    if (s + 1 < nsteps) {
-      issue_a(s + 1, sm.a[(s + 1) & 1]);
-      g2_load_w(p0 + 36 * (s + 1), Dn0);
-      g2_load_w(p1 + 36 * (s + 1), Dn1);
-    }
     uint32_t n0[4], n1[4];
 #pragma unroll
     for (int v = 0; v < 4; v++) {
-      n0[v] = __builtin_amdgcn_perm(D0[v + 1], D0[v], sel_n);
-      n1[v] = __builtin_amdgcn_perm(D1[v + 1], D1[v], sel_n);
+      n0[v] = Dn0[v];
+      n1[v] = Dn1[v];
     }
-    const float d0 = f16_bits_to_f32(__builtin_amdgcn_perm(D0[1], D0[0], sel_s));
-    const float d1 = f16_bits_to_f32(__builtin_amdgcn_perm(D1[1], D1[0], sel_s));
-#define MOEQ4_G2(Q)                                                                          \
-  {                                                                                          \
-    const bf16x8_t b0 = g2_deq<Q>(n0, d0);                                                   \
-    const bf16x8_t b1 = g2_deq<Q>(n1, d1);                                                   \
-    bf16x8_t avs[MS];                                                                        \
-    _Pragma("unroll") for (int sub = 0; sub < MS; sub++)                                     \
-      avs[sub] = *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G2K + aofs[Q]);         \
-    _Pragma("unroll") for (int sub = 0; sub < MS; sub++) {                                   \
-      acc0[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avs[sub], b0, acc0[sub], 0, 0, 0); \
-      acc1[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avs[sub], b1, acc1[sub], 0, 0, 0); \
-    }                                                                                        \
+    const float d0 = f16_bits_to_f32(Dn0[4]);
+    const float d1 = f16_bits_to_f32(Dn1[4]);
+    // next step's loads; the last step fetches its own data again (in bounds,
+    // unused) so the body stays one branch-free block
+    const int sn = min(s + 1, nsteps - 1);
+    issue_a(sn, sm.a[(s + 1) & 1]);
+    g2_load_w(p0 + 1152 * sn, sc, Dn0);
+    g2_load_w(p1 + 1152 * sn, sc, Dn1);
+    bf16x8_t b0 = g2_deq<0>(n0, d0), b1 = g2_deq<0>(n1, d1);
+    bf16x8_t avs[MS];
+#pragma unroll
+    for (int sub = 0; sub < MS; sub++) avs[sub] = *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G2K + aofs[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice Q's MFMAs with slice Q+1's dequantisation and fragment reads
+    // interleaved between them: a wave issues in order, so VALU work only
+    // runs under its own MFMAs when it sits between them in the stream
+#define MOEQ4_G2(Q)                                                                            \
+  {                                                                                            \
+    bf16x8_t c0, c1;                                                                           \
+    _Pragma("unroll") for (int sub = 0; sub < MS; sub++) {                                     \
+      acc0[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avs[sub], b0, acc0[sub], 0, 0, 0);   \
+      acc1[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avs[sub], b1, acc1[sub], 0, 0, 0);   \
+      if (Q < 3) avs[sub] = *reinterpret_cast<const bf16x8_t*>(cur + sub * 32 * G2K + aofs[(Q + 1) & 3]); \
+    }                                                                                          \
+    if (Q < 3) {                                                                               \
+      c0 = g2_deq<(Q + 1) & 3>(n0, d0);                                                        \
+      c1 = g2_deq<(Q + 1) & 3>(n1, d1);                                                        \
+      g2_interleave<MS>();                                                                     \
+      b0 = c0;                                                                                 \
+      b1 = c1;                                                                                 \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
   }
     MOEQ4_G2(0) MOEQ4_G2(1) MOEQ4_G2(2) MOEQ4_G2(3)
 #undef MOEQ4_G2
   }
+  wait_vm<0>();                                  // the repeated last fetch has landed in LDS
   const int n0c = c0 + ln, n1c = c1 + ln;
 #pragma unroll
   for (int sub = 0; sub < MS; sub++)
@@ -748,10 +773,10 @@ __global__ void __launch_bounds__(256) combine_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------- launch
-// Kernel choice: gate/up and down together take the fused launch when both
-// K are multiples of 64 and the pointers are aligned; a single projection
-// takes gemm_g2 under the same conditions; the generic kernels cover any
-// other shape (K a multiple of 32).
+// Kernel choice: with tile-order weights (H and I multiples of 64) gate/up and
+// down together take the fused launch and a single projection gemm_g2; the
+// generic kernels cover row-major weights and any shape with K a multiple of
+// 32.
 hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) {
   constexpr int MT = 4, BM = 32 * MT;
   const int64_t assignments = (int64_t)a.T * a.k;
@@ -762,11 +787,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
                     (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 8 == 0));
   const int vec_d = ((a.I / BLK) % 4 == 0) && ((uintptr_t)a.w_down % 8 == 0) &&
                     (!a.has_shared || ((uintptr_t)a.s_down % 8 == 0));
-  const bool g2_g = a.H % G2K == 0 && ((uintptr_t)a.x % 16 == 0) &&
-                    (((uintptr_t)a.w_gate | (uintptr_t)a.w_up) % 4 == 0) &&
-                    (!a.has_shared || (((uintptr_t)a.s_gate | (uintptr_t)a.s_up) % 4 == 0));
-  const bool g2_d = a.I % G2K == 0 && ((uintptr_t)a.h % 16 == 0) &&
-                    ((uintptr_t)a.w_down % 4 == 0) && (!a.has_shared || ((uintptr_t)a.s_down % 4 == 0));
+  const bool tiled = a.t_gate && a.t_up && a.t_down && (!a.has_shared || (a.ts_gate && a.ts_up && a.ts_down));
+  const bool g2_g = tiled && a.H % G2K == 0 && ((uintptr_t)a.x % 16 == 0);
+  const bool g2_d = tiled && a.I % G2K == 0 && ((uintptr_t)a.h % 16 == 0);
   const int g2_groups = (btiles + 7) / 8;
   hipError_t err = hipSuccess;
   if ((stages & 3) == 3 && g2_g && g2_d && a.tile_done) {

@@ -8,6 +8,7 @@ namespace moeq4 {
 
 hipError_t launch_q4_pack(const float* w, int64_t rows, int64_t K, void* packed,
                           hipStream_t stream);
+hipError_t launch_q4_tile(const void* q4, int64_t rows, int64_t K, void* tiled, hipStream_t stream);
 hipError_t launch_q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d,
                               hipStream_t stream);
 
@@ -46,6 +47,12 @@ struct PrefillArgs {
   const uint8_t* s_gate;
   const uint8_t* s_up;
   const uint8_t* s_down;
+  const uint8_t* t_gate;    // the same matrices in q4_tile order, or all NULL
+  const uint8_t* t_up;
+  const uint8_t* t_down;
+  const uint8_t* ts_gate;
+  const uint8_t* ts_up;
+  const uint8_t* ts_down;
   uint16_t* h;              // [(T*k + T*S)][I] bf16
   uint16_t* o_perm;         // [T*k][H] bf16
   float* y;                 // [T][H] fp32

@@ -90,6 +90,38 @@ hipError_t launch_q4_pack(const float* w, int64_t rows, int64_t K, void* packed,
   return hipGetLastError();
 }
 
+// Grouped-GEMM tile order (layout stated in moe_q4.h at q4_tile): one thread
+// per block; thread i = (G * nsteps + s) * 64 + l moves block 2s + l/32 of
+// row 32G + l%32.  Source blocks are 2-byte aligned, so the 16 nibble bytes
+// are read as halfwords and written as one 16-byte store.
+__global__ void __launch_bounds__(256) q4_tile_kernel(const uint16_t* __restrict__ q4, int64_t nblocks,
+                                                      int nsteps, uint8_t* __restrict__ tiled) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nblocks) return;
+  const int l = (int)(i & 63);
+  const int64_t gs = i >> 6;                       // G * nsteps + s
+  const int64_t G = gs / nsteps;
+  const int st = (int)(gs - G * nsteps);
+  const int64_t rbh = (int64_t)nsteps * 18;        // row bytes / 2 (halfwords per row)
+  const int64_t row = 32 * G + (l & 31);
+  const int blk = 2 * st + (l >> 5);
+  const uint16_t* src = q4 + row * rbh + (int64_t)blk * 9;
+  uint32_t w[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) w[c] = (uint32_t)src[1 + 2 * c] | ((uint32_t)src[2 + 2 * c] << 16);
+  uint8_t* piece = tiled + gs * 1152;
+  *reinterpret_cast<uint4*>(piece + 16 * l) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint16_t*>(piece + 1024 + 2 * l) = src[0];
+}
+
+hipError_t launch_q4_tile(const void* q4, int64_t rows, int64_t K, void* tiled, hipStream_t stream) {
+  const int64_t nblocks = rows * (K / BLK);
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(q4_tile_kernel, dim3((uint32_t)((nblocks + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q4), nblocks, (int)(K / 64), static_cast<uint8_t*>(tiled));
+  return hipGetLastError();
+}
+
 hipError_t launch_q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d,
                               hipStream_t stream) {
   int64_t nblocks = rows * (K / BLK);

@@ -22,18 +22,20 @@ def _pack_host(a: np.ndarray, device) -> torch.Tensor:
 
 
 def device_layer(cfg: moe_synth.Config, layer: int = 0, device="cuda", weights=None,
-                 threads: int = 16) -> MoELayer:
+                 threads: int = 16, tiles: bool = True) -> MoELayer:
     """Pack layer `layer` of workload `cfg` on `device`.  `weights` (the dict
-    from moe_synth.expert_weights) may be passed in to reuse a host copy."""
+    from moe_synth.expert_weights) may be passed in to reuse a host copy;
+    `tiles` as in MoELayer."""
     W = weights if weights is not None else moe_synth.expert_weights(cfg, layer, threads=threads)
     wr = torch.from_numpy(moe_synth.router(cfg, layer)).to(device)
     b = moe_synth.router_bias(cfg, layer)
     bias = None if b is None else torch.from_numpy(b).to(device)
     pk = {k: (None if W[k] is None else _pack_host(W[k], device))
           for k in ("gate", "up", "down", "s_gate", "s_up", "s_down")}
+    L = MoELayer(wr, pk["gate"], pk["up"], pk["down"], cfg.k, router_bias=bias,
+                 s_gate=pk["s_gate"], s_up=pk["s_up"], s_down=pk["s_down"], tiles=tiles)
     torch.cuda.synchronize(device)
-    return MoELayer(wr, pk["gate"], pk["up"], pk["down"], cfg.k, router_bias=bias,
-                    s_gate=pk["s_gate"], s_up=pk["s_up"], s_down=pk["s_down"])
+    return L
 
 
 def device_tokens(cfg: moe_synth.Config, step: int = 0, T: int | None = None, layer: int = 0,

@@ -99,6 +99,36 @@ def test_shared_pointers_required(lib):
     assert "shared" in _err(lib)
 
 
+@pytest.mark.parametrize("setup,frag", [
+    (lambda L: setattr(L, "t_gate", 0x20000), "together"),                 # t_up, t_down missing
+    (lambda L: [setattr(L, n, 0x20000) for n in ("t_gate", "t_up", "t_down", "ts_gate")], "together"),
+    (lambda L: [setattr(L, n, 0x20008) for n in ("t_gate", "t_up", "t_down")], "aligned"),
+])
+def test_tile_order_pointer_checks(lib, setup, frag):
+    L = _layer()
+    setup(L)
+    rc = lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, 16, None, None, None, 0, None)
+    assert rc == -1 and frag in _err(lib)
+
+
+def test_tile_order_needs_k_multiple_of_64(lib):
+    L = _layer(hidden=96, inter=128)
+    L.t_gate = L.t_up = L.t_down = 0x20000
+    assert lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, 16, None, None, None, 0, None) == -1
+    assert "64" in _err(lib)
+
+
+def test_q4_tile_argument_checks(lib):
+    assert lib.q4_tile(C.c_void_p(0x1000), 33, 64, C.c_void_p(0x100000), None) == -1      # rows % 32
+    assert lib.q4_tile(C.c_void_p(0x1000), 32, 96, C.c_void_p(0x100000), None) == -1      # K % 64
+    assert lib.q4_tile(C.c_void_p(0x1000), 32, 64, C.c_void_p(0x100008), None) == -1      # misaligned
+    assert "aligned" in _err(lib)
+    assert lib.q4_tile(C.c_void_p(0x1000), 32, 64, C.c_void_p(0x1100), None) == -1        # overlap
+    assert "overlap" in _err(lib)
+    assert lib.q4_tile(None, 32, 64, C.c_void_p(0x100000), None) == -1
+    assert lib.q4_tile(None, 0, 64, None, None) == 0                                        # nothing to do
+
+
 def test_workspace_checks(lib):
     from bit_quantized_moe_q4_amd._lib import Routing
     L = _layer()

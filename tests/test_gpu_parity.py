@@ -68,6 +68,46 @@ def test_q4_pack_golden_blocks():
         assert got == exp, tag
 
 
+def _tile_order_reference(packed: np.ndarray, K: int) -> np.ndarray:
+    """The tile order of moe_q4.h (q4_tile) as a byte permutation of row-major
+    Q4_0 blocks [rows][K/32][18]."""
+    rows = packed.shape[0]
+    nb, ns = K // 32, K // 64
+    blk = packed.reshape(rows // 32, 32, ns, 2, 18)          # group, row, step, block-of-step, byte
+    out = np.empty((rows // 32, ns, 1152), dtype=np.uint8)
+    lanes = blk.transpose(0, 2, 3, 1, 4).reshape(rows // 32, ns, 64, 18)   # lane = 32 * g + n
+    out[:, :, :1024] = lanes[:, :, :, 2:].reshape(rows // 32, ns, 1024)
+    out[:, :, 1024:] = lanes[:, :, :, :2].reshape(rows // 32, ns, 128)
+    return out.reshape(rows, nb * 18)
+
+
+@pytest.mark.parametrize("rows,K", [(32, 64), (96, 128), (512, 2048), (2048, 512)])
+def test_q4_tile_bytes(rows, K):
+    rng = np.random.default_rng(rows + K)
+    w = torch.from_numpy(rng.standard_normal((rows, K)).astype(np.float32)).cuda()
+    packed = mq.q4_pack(w)
+    tiled = mq.q4_tile(packed)
+    ref = _tile_order_reference(packed.cpu().numpy(), K)
+    assert np.array_equal(tiled.cpu().numpy(), ref)
+    # group G keeps its byte range: the multiset of bytes of each 32-row group is unchanged
+    a = np.sort(packed.cpu().numpy().reshape(rows // 32, -1), axis=1)
+    b = np.sort(tiled.cpu().numpy().reshape(rows // 32, -1), axis=1)
+    assert np.array_equal(a, b)
+
+
+def test_q4_tile_lane_map_spot_checks():
+    # row 37 (group 1, n = 5), block 3 (step 1, g = 1) -> lane 37 of piece (1, 1)
+    rows, K = 64, 256
+    w = torch.from_numpy(np.random.default_rng(3).standard_normal((rows, K)).astype(np.float32)).cuda()
+    packed = mq.q4_pack(w).cpu().numpy()
+    tiled = mq.q4_tile(torch.from_numpy(packed).cuda()).cpu().numpy().reshape(-1)
+    rb = K // 32 * 18
+    piece = 1 * 32 * rb + 1 * 1152
+    blk = packed[37, 3 * 18:4 * 18]
+    assert bytes(tiled[piece + 16 * 37: piece + 16 * 38]) == bytes(blk[2:])
+    assert bytes(tiled[piece + 1024 + 2 * 37: piece + 1024 + 2 * 38]) == bytes(blk[:2])
+
+
 @pytest.mark.parametrize("rows,K", [(1, 32), (5, 2048), (33, 512)])
 def test_q8_quantize(rows, K):
     say("q8", rows, K)
@@ -212,10 +252,12 @@ def _prefill_err(ol, gl, cfg, T, sample=None, step=0):
     ("wide_topk", 96, 256, 64, 128, 16, True),
     ("every_expert", 64, 256, 32, 64, 32, True),
 ])
-def test_prefill_small(name, T, H, E, I, k, shared):
-    say("prefill", name, T, H, E, I, k, shared)
+@pytest.mark.parametrize("tiles", [True, False], ids=["tiled", "rowmajor"])
+def test_prefill_small(name, T, H, E, I, k, shared, tiles):
+    say("prefill", name, T, H, E, I, k, shared, "tiles" if tiles else "row-major")
     cfg = moe_synth.CONFIGS["tiny"].with_(name=name, H=H, E=E, I=I, k=k, shared=shared)
-    ol, gl = both_layers(cfg)
+    ol, gl = both_layers(cfg, tiles=tiles)
+    assert (gl.tiles is not None) == (tiles and H % 64 == 0 and I % 64 == 0)
     rel, per_tok, _, _ = _prefill_err(ol, gl, cfg, T)
     assert rel <= PREFILL_TOL
     assert per_tok.max() <= 3 * PREFILL_TOL
@@ -237,6 +279,16 @@ def test_prefill_2k_sampled(prefill_layer):
     # every expert segment is non-empty at this size; the y rows exist for all tokens
     assert np.all(np.diff(rr["offsets"]) > 0)
     assert np.all(np.isfinite(y))
+
+
+def test_prefill_2k_sampled_generic_kernels(prefill_layer):
+    # the same packed layer without tile-order copies: the generic grouped GEMM
+    cfg, (ol, gl) = prefill_layer
+    g2 = mq.MoELayer(gl.w_router, gl.gate, gl.up, gl.down, gl.top_k, gl.router_bias,
+                     gl.s_gate, gl.s_up, gl.s_down, tiles=False)
+    sample = np.array([0, 7, 1000, cfg.T - 1])
+    rel, _, _, _ = _prefill_err(ol, g2, cfg, cfg.T, sample=sample)
+    assert rel <= PREFILL_TOL
 
 
 def test_prefill_2k_token_permutation_equivariance(prefill_layer):
