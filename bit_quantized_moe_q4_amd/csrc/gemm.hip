@@ -465,21 +465,36 @@ struct G2Smem {
 
 __device__ __forceinline__ int g2_slot(int cc, int m) { return cc ^ (m & 7) ^ ((m >> 3) & 1); }
 
-// One step of the lane's weights: nibble dwords D[0..3] from `p`, the fp16
-// scale bits in D[4] from `p + sc`.
-__device__ __forceinline__ void g2_load_w(const uint8_t* p, int sc, uint32_t (&D)[5]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer descriptors exist only in the device pass
+// Buffer resource of a wave-uniform range; readfirstlane makes its
+// uniformity explicit so the descriptor lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t g2_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+typedef uint32_t g2_u32x4 __attribute__((ext_vector_type(4)));
+
+// Step s of the lane's weights from a group's pieces: nibble dwords D[0..3]
+// at vn = 16 * lane, the fp16 scale bits in D[4] at 1024 + 2 * lane.
+__device__ __forceinline__ void g2_load_w(__amdgpu_buffer_rsrc_t r, uint32_t vn, int s, uint32_t (&D)[5]) {
+  const g2_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, vn, 1152 * s, 0);
   D[0] = v.x;
   D[1] = v.y;
   D[2] = v.z;
   D[3] = v.w;
-  D[4] = *reinterpret_cast<const uint16_t*>(p + sc);
+  D[4] = __builtin_amdgcn_raw_buffer_load_b16(r, 1024u + (vn >> 3), 1152 * s, 0);
 }
+
+#endif
 
 // 8 bf16 weights of element group Q of the lane's block: scale bits `sc`,
 // nibble dwords nib[0..3] (byte j of the 16 holds element j low, j+16 high).
 template <int Q>
-__device__ __forceinline__ bf16x8_t g2_deq(const uint32_t (&nib)[4], float d) {
+__device__ __forceinline__ bf16x8_t g2_deq(const uint32_t* nib, float d) {
   const float off = -8.0f * d;
   const float mul = (Q >> 1) ? d * 0.0625f : d;
   const uint32_t mask = (Q >> 1) ? 0xf0f0f0f0u : 0x0f0f0f0fu;
@@ -513,7 +528,9 @@ __device__ __forceinline__ void g2_barrier() { asm volatile("s_barrier" ::: "mem
 
 template <int MS, bool GATEUP>
 __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int cb, G2Smem& sm) {
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, ln = lane % 32, g = lane / 32;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int tid = threadIdx.x, lane = tid % 64, ln = lane % 32, g = lane / 32;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int H = a.H, I = a.I;
   const int N = GATEUP ? I : H, K = GATEUP ? H : I;
   const int nsteps = K / G2K;
@@ -532,13 +549,18 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
     w0 = wd + (size_t)c0 * rb;
     w1 = wd + (size_t)c1 * rb;
   }
-  const uint8_t* p0 = w0 + 16 * lane;
-  const uint8_t* p1 = w1 + 16 * lane;
-  const int sc = 1024 - 14 * lane;                            // scale of the lane's block: piece + 1024 + 2 * lane
+  // Raw buffer resources: the wave's two 32-row groups (their tile-order
+  // pieces) and the activation rows.  The per-step offset is a scalar, so the
+  // loop computes no addresses; an offset past num_records would read zeros.
+  const __amdgpu_buffer_rsrc_t rw0 = g2_rsrc(w0, (uint32_t)(32 * rb));
+  const __amdgpu_buffer_rsrc_t rw1 = g2_rsrc(w1, (uint32_t)(32 * rb));
+  const uint32_t vn = 16u * (uint32_t)lane;                   // the lane's nibbles in a piece (scale: 1024 + 2 * lane)
 
   // activation rows: wave-load j = wave + 4q covers tile rows 8j..8j+7
   const uint16_t* abase = GATEUP ? a.x : a.h + (size_t)t.pos0 * I;
-  uint32_t src[MS];
+  const __amdgpu_buffer_rsrc_t ra =
+      g2_rsrc(abase, GATEUP ? (uint32_t)a.T * (uint32_t)H * 2u : (uint32_t)t.rows * (uint32_t)I * 2u);
+  uint32_t voff[MS];                                          // byte offset of the lane's 16-byte chunk, step 0
 #pragma unroll
   for (int q = 0; q < MS; q++) {
     const int r = 8 * (wave + G2W * q) + lane / 8;            // LDS row
@@ -550,11 +572,13 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
     } else {
       rowel = (uint32_t)m * (uint32_t)I;
     }
-    src[q] = rowel + 8u * (uint32_t)g2_slot(lane & 7, r);
+    voff[q] = 2u * (rowel + 8u * (uint32_t)g2_slot(lane & 7, r));
   }
   auto issue_a = [&](int s, uint16_t* buf) {
 #pragma unroll
-    for (int q = 0; q < MS; q++) lds_load16(abase + src[q] + G2K * s, buf + (wave + G2W * q) * 512);
+    for (int q = 0; q < MS; q++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(buf + (wave + G2W * q) * 512),
+                                               16, voff[q], 2 * G2K * s, 0, 0);
   };
 
   f32x16_t acc0[MS], acc1[MS];
@@ -563,33 +587,35 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
 #pragma unroll
     for (int r = 0; r < 16; r++) { acc0[q][r] = 0.0f; acc1[q][r] = 0.0f; }
 
-  uint32_t Dn0[5], Dn1[5];
+  // weights of step s land in W[s & 1]: the loop is unrolled by two so that
+  // each register set has a fixed role and nothing is copied
+  uint32_t W[2][2][5];
   issue_a(0, sm.a[0]);
-  g2_load_w(p0, sc, Dn0);
-  g2_load_w(p1, sc, Dn1);
+  g2_load_w(rw0, vn, 0, W[0][0]);
+  g2_load_w(rw1, vn, 0, W[0][1]);
   // fragment read offsets (elements) inside a buffer, per slice i: row 32*sub + ln
   int aofs[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) aofs[i] = ln * G2K + 8 * g2_slot(4 * g + i, ln);
 
-  for (int s = 0; s < nsteps; s++) {
-    uint16_t* cur = sm.a[s & 1];
+  for (int s0 = 0; s0 < nsteps; s0 += 2) {
+#pragma unroll
+  for (int P = 0; P < 2; P++) {
+    const int s = s0 + P;
+    if (P == 1 && s >= nsteps) break;
+    uint16_t* cur = sm.a[P];
     wait_vm<0>();                                // own A(s) and W(s) landed (issued a step ago)
     g2_barrier();                                // everyone's A(s) landed; step s-1 done
-    uint32_t n0[4], n1[4];
-#pragma unroll
-    for (int v = 0; v < 4; v++) {
-      n0[v] = Dn0[v];
-      n1[v] = Dn1[v];
-    }
-    const float d0 = f16_bits_to_f32(Dn0[4]);
-    const float d1 = f16_bits_to_f32(Dn1[4]);
+    const uint32_t* n0 = W[P][0];
+    const uint32_t* n1 = W[P][1];
+    const float d0 = f16_bits_to_f32(n0[4]);
+    const float d1 = f16_bits_to_f32(n1[4]);
     // next step's loads; the last step fetches its own data again (in bounds,
     // unused) so the body stays one branch-free block
     const int sn = min(s + 1, nsteps - 1);
-    issue_a(sn, sm.a[(s + 1) & 1]);
-    g2_load_w(p0 + 1152 * sn, sc, Dn0);
-    g2_load_w(p1 + 1152 * sn, sc, Dn1);
+    issue_a(sn, sm.a[P ^ 1]);
+    g2_load_w(rw0, vn, sn, W[P ^ 1][0]);
+    g2_load_w(rw1, vn, sn, W[P ^ 1][1]);
     bf16x8_t b0 = g2_deq<0>(n0, d0), b1 = g2_deq<0>(n1, d1);
     bf16x8_t avs[MS];
 #pragma unroll
@@ -618,6 +644,7 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
     MOEQ4_G2(0) MOEQ4_G2(1) MOEQ4_G2(2) MOEQ4_G2(3)
 #undef MOEQ4_G2
   }
+  }
   wait_vm<0>();                                  // the repeated last fetch has landed in LDS
   const int n0c = c0 + ln, n1c = c1 + ln;
 #pragma unroll
@@ -639,6 +666,7 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
         if (live1) a.y[(size_t)(t.m0 + rr) * H + n1c] = acc1[sub][r];
       }
     }
+#endif
 }
 
 template <bool GATEUP>
