@@ -25,6 +25,7 @@ __all__ = [
     "moe_q4_route_workspace_bytes", "moe_q4_route",
     "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage",
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
+    "moe_q4_decode_batch_workspace_bytes", "moe_q4_decode_batch",
     "moe_q4_w4a8_gemv", "moe_q4_rmsnorm", "library_path",
 ]
 
@@ -274,6 +275,33 @@ def moe_q4_decode(layer: MoELayer, x: torch.Tensor, y: torch.Tensor | None = Non
                                         C.byref(tc) if tc is not None else None,
                                         _p(ws), ws.numel(), _s(stream)), "moe_q4_decode")
     return (y, tr) if trace else y
+
+
+def moe_q4_decode_batch_workspace_bytes(layer: MoELayer, M: int) -> int:
+    return int(_lib.lib().moe_q4_decode_batch_workspace_bytes(layer.struct_ptr(), int(M)))
+
+
+def moe_q4_decode_batch(layer: MoELayer, x: torch.Tensor, y: torch.Tensor | None = None,
+                        ws: torch.Tensor | None = None, routing: bool = False, stream=None):
+    """Decode of M <= 32 independent tokens: x [M, H] fp32 -> y [M, H] fp32, each
+    row bit-identical to moe_q4_decode of that token (with routing=True also
+    the ids [M, k] int32 and weights [M, k] fp32)."""
+    _dev(x, "x")
+    if x.dtype != torch.float32 or x.dim() != 2:
+        raise ValueError("x must be float32 [M, H]")
+    M = int(x.shape[0])
+    if y is None:
+        y = torch.empty((M, layer.hidden), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(1, moe_q4_decode_batch_workspace_bytes(layer, M)), dtype=torch.uint8,
+                         device=x.device)
+    ids = w = None
+    if routing:
+        ids = torch.empty((M, layer.top_k), dtype=torch.int32, device=x.device)
+        w = torch.empty((M, layer.top_k), dtype=torch.float32, device=x.device)
+    _lib.check(_lib.lib().moe_q4_decode_batch(layer.struct_ptr(), _p(x), M, _p(y), _p(ids), _p(w),
+                                              _p(ws), ws.numel(), _s(stream)), "moe_q4_decode_batch")
+    return (y, ids, w) if routing else y
 
 
 def moe_q4_w4a8_gemv(W: torch.Tensor, N: int, K: int, qa: torch.Tensor, da: torch.Tensor,

@@ -36,7 +36,7 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-SOURCES = ["abi.cpp", "pack.hip", "router.hip", "gemm.hip", "decode.hip", "rmsnorm.hip"]
+SOURCES = ["abi.cpp", "pack.hip", "router.hip", "gemm.hip", "decode.hip", "decode_batch.hip", "rmsnorm.hip"]
 
 
 def _compile(src: str) -> str:

@@ -118,6 +118,32 @@ DecodeWs decode_ws(const moe_q4_layer* L) {
   return w;
 }
 
+struct DecodeBatchWs {
+  size_t partials, qx, dx, sx, ids, w, elist_off, elist, hit, nhit, qh, dh, sh, total;
+};
+DecodeBatchWs decode_batch_ws(const moe_q4_layer* L, int32_t M) {
+  DecodeBatchWs w;
+  const size_t m = (size_t)M, k = (size_t)L->top_k, E = (size_t)L->n_experts;
+  const size_t H = L->hidden, I = L->inter, nc = H / 32;
+  const size_t np = m * k + (L->has_shared ? m : 0);
+  const size_t hb = E < m * k ? E : m * k;
+  w.partials = 0;
+  w.qx = w.partials + up256(m * nc * E * 4);
+  w.dx = w.qx + up256(m * H);
+  w.sx = w.dx + up256(m * nc * 4);
+  w.ids = w.sx + up256(m * nc * 4);
+  w.w = w.ids + up256(m * k * 4);
+  w.elist_off = w.w + up256(m * k * 4);
+  w.elist = w.elist_off + up256((E + 1) * 4);
+  w.hit = w.elist + up256(m * k * 4);
+  w.nhit = w.hit + up256(hb * 4);
+  w.qh = w.nhit + up256(4);
+  w.dh = w.qh + up256(np * I);
+  w.sh = w.dh + up256(np * I / 32 * 4);
+  w.total = w.sh + up256(np * I / 32 * 4);
+  return w;
+}
+
 int check_ws(void* ws, size_t have, size_t need) {
   if (need == 0) return MOE_Q4_OK;
   if (!ws) return fail(MOE_Q4_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -276,6 +302,62 @@ int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t 
   a.y = y;
   hipError_t e = moeq4::launch_prefill(a, stages, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_prefill");
+}
+
+size_t moe_q4_decode_batch_workspace_bytes(const moe_q4_layer* L, int32_t M) {
+  if (check_layer(L) != MOE_Q4_OK || M < 0 || M > moeq4::kDecodeBatchMax) return 0;
+  return decode_batch_ws(L, M).total;
+}
+
+int moe_q4_decode_batch(const moe_q4_layer* L, const float* x, int32_t M, float* y, int32_t* ids_out,
+                        float* w_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (M < 0 || M > moeq4::kDecodeBatchMax)
+    return fail(MOE_Q4_EINVAL, "moe_q4_decode_batch: M=%d must be in [0, %d]", M, moeq4::kDecodeBatchMax);
+  if (L->hidden > 32 * 512) return fail(MOE_Q4_EINVAL, "moe_q4_decode_batch: hidden=%d > 16384", L->hidden);
+  if (M == 0) return MOE_Q4_OK;
+  if (!x || !y) return fail(MOE_Q4_EINVAL, "moe_q4_decode_batch: NULL pointer");
+  if (!aligned(x, 16) || !aligned(y, 4)) return fail(MOE_Q4_EINVAL, "moe_q4_decode_batch: x must be 16-byte aligned");
+  const DecodeBatchWs W = decode_batch_ws(L, M);
+  rc = check_ws(ws, ws_bytes, W.total);
+  if (rc) return rc;
+  moeq4::DecodeBatchArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x;
+  a.y = y;
+  a.M = M;
+  a.H = L->hidden;
+  a.I = L->inter;
+  a.E = L->n_experts;
+  a.k = L->top_k;
+  a.has_shared = L->has_shared;
+  a.w_router = L->w_router;
+  a.bias = L->router_bias;
+  a.w_gate = static_cast<const uint8_t*>(L->w_gate);
+  a.w_up = static_cast<const uint8_t*>(L->w_up);
+  a.w_down = static_cast<const uint8_t*>(L->w_down);
+  a.s_gate = static_cast<const uint8_t*>(L->s_gate);
+  a.s_up = static_cast<const uint8_t*>(L->s_up);
+  a.s_down = static_cast<const uint8_t*>(L->s_down);
+  a.partials = at<float>(ws, W.partials);
+  a.qx = at<int8_t>(ws, W.qx);
+  a.dx = at<float>(ws, W.dx);
+  a.sx = at<int32_t>(ws, W.sx);
+  a.ids = at<int32_t>(ws, W.ids);
+  a.w = at<float>(ws, W.w);
+  a.elist_off = at<int32_t>(ws, W.elist_off);
+  a.elist = at<int32_t>(ws, W.elist);
+  a.hit = at<int32_t>(ws, W.hit);
+  a.nhit = at<int32_t>(ws, W.nhit);
+  a.hb = L->n_experts < M * L->top_k ? L->n_experts : M * L->top_k;
+  a.qh = at<int8_t>(ws, W.qh);
+  a.dh = at<float>(ws, W.dh);
+  a.sh = at<int32_t>(ws, W.sh);
+  a.t_ids = ids_out;
+  a.t_w = w_out;
+  hipError_t e = moeq4::launch_decode_batch(a, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_decode_batch");
 }
 
 size_t moe_q4_decode_workspace_bytes(const moe_q4_layer* L) {

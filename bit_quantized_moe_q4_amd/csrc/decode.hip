@@ -27,27 +27,12 @@
 //                   into registers, every slot's q8(h) into LDS, then the
 //                   row program and the fixed-order weighted combine.
 //
-// Activation codes in LDS: block b of a row of activation blocks starts at
-// dword act_off(b) = 8b + 4*floor(b/8).  A lane owns 8 consecutive blocks,
-// so the lanes of one row start 68 dwords apart (4 banks apart) and their
-// 16-byte reads do not collide; without the pad they all hit one bank.
+// Activation codes in LDS use the padded layout of decode_common.hpp.
 #include "launch.hpp"
 #include "w4a8.hpp"
+#include "decode_common.hpp"
 
 namespace moeq4 {
-
-__device__ __forceinline__ int act_off(int b) { return 8 * b + 4 * (b >> 3); }
-__host__ __device__ inline int act_row_dwords(int nb) { return 8 * nb + 4 * ((nb + 7) / 8); }
-
-// Pairwise tree over v[0 .. n-1] (n a power of two <= 64); returns the root.
-__device__ __forceinline__ float tree64(float (&v)[64], int n) {
-#pragma unroll
-  for (int w = 64; w > 1; w >>= 1)
-#pragma unroll
-    for (int i = 0; i < w / 2; i++)
-      if (w <= n) v[i] = v[2 * i] + v[2 * i + 1];
-  return v[0];
-}
 
 // ---------------------------------------------------------------- router
 __global__ void __launch_bounds__(1024) decode_router_kernel(DecodeArgs a) {
@@ -121,43 +106,6 @@ __device__ __forceinline__ GuLds gu_lds(uint8_t* dyn, int nbh, int E) {
   l.sa = reinterpret_cast<int32_t*>(l.da + nbh);
   l.logit = reinterpret_cast<float*>(l.sa + nbh);
   return l;
-}
-
-// Order key: larger key = earlier in (logit desc, index asc); -0 and +0 tie
-// as they do under a float comparison.
-__device__ __forceinline__ uint64_t rank_key(float l, int e) {
-  uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
-}
-
-// Pairwise tree over the leaves c0 .. c0+L-1 of one expert (src = partials
-// + e, leaf stride E); leaves >= nc are +0.
-template <int L>
-__device__ __forceinline__ float leaf_run(const float* __restrict__ src, int E, int c0, int nc) {
-  float v[L];
-#pragma unroll
-  for (int j = 0; j < L; j++) {
-    const int cc = c0 + j;
-    const float t = src[(size_t)min(cc, nc - 1) * E];
-    v[j] = cc < nc ? t : 0.0f;
-  }
-#pragma unroll
-  for (int w = L; w > 1; w >>= 1)
-#pragma unroll
-    for (int i = 0; i < w / 2; i++) v[i] = v[2 * i] + v[2 * i + 1];
-  return v[0];
-}
-
-__device__ __forceinline__ float leaf_tree(const float* src, int E, int c0, int L, int nc) {
-  switch (L) {
-    case 1: return leaf_run<1>(src, E, c0, nc);
-    case 2: return leaf_run<2>(src, E, c0, nc);
-    case 4: return leaf_run<4>(src, E, c0, nc);
-    case 8: return leaf_run<8>(src, E, c0, nc);
-    case 16: return leaf_run<16>(src, E, c0, nc);
-    default: return leaf_run<32>(src, E, c0, nc);
-  }
 }
 
 // Stages x's q8 blocks into LDS and, for a routed slot, finishes the router:

@@ -114,6 +114,49 @@ struct DecodeGeometry {
 DecodeGeometry decode_geometry(int H, int I, int E, int k, int has_shared);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Batched decode: M <= kDecodeBatchMax tokens, each through the single-token
+// program; the selected experts' weights are read once per call.
+constexpr int kDecodeBatchMax = 32;
+struct DecodeBatchArgs {
+  const float* x;           // [M][H]
+  float* y;                 // [M][H]
+  int M, H, I, E, k, has_shared;
+  const float* w_router;
+  const float* bias;
+  const uint8_t* w_gate;
+  const uint8_t* w_up;
+  const uint8_t* w_down;
+  const uint8_t* s_gate;
+  const uint8_t* s_up;
+  const uint8_t* s_down;
+  // workspace
+  float* partials;          // [M][H/32][E] router leaves
+  int8_t* qx;               // [M][H]
+  float* dx;                // [M][H/32]
+  int32_t* sx;              // [M][H/32]
+  int32_t* ids;             // [M][k]
+  float* w;                 // [M][k]
+  int32_t* elist_off;       // [E+1] pairs of expert e: elist[elist_off[e] .. elist_off[e+1])
+  int32_t* elist;           // [M*k] pair t*k+s, ascending within an expert
+  int32_t* hit;             // [hb] experts with at least one pair, ascending
+  int32_t* nhit;            // [1]
+  int hb;                   // min(E, M*k): bound of the hit list
+  int8_t* qh;               // [M*k + M*S][I] q8(h) per pair (shared expert: M*k + t)
+  float* dh;                // [M*k + M*S][I/32]
+  int32_t* sh;              // [M*k + M*S][I/32]
+  int32_t* t_ids;           // optional copies of ids / w, or NULL
+  float* t_w;
+};
+struct DecodeBatchGeometry {
+  int router_threads;
+  int gu_lpr, gu_bpl, gu_fast, gu_threads, gu_alds;
+  size_t gu_lds;
+  int dn_lpr, dn_bpl, dn_fast, dn_rows, dn_threads;
+  size_t dn_lds;
+};
+DecodeBatchGeometry decode_batch_geometry(int M, int H, int I, int E, int k, int has_shared);
+hipError_t launch_decode_batch(const DecodeBatchArgs& a, hipStream_t stream);
+
 hipError_t launch_w4a8_gemv(const uint8_t* W, int N, int K, const int8_t* qa, const float* da,
                             int32_t* dots, float* out, hipStream_t stream);
 

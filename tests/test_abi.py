@@ -33,8 +33,9 @@ def header_functions():
 
 def test_header_declares_the_api():
     names = header_functions()
-    for n in ["q4_packed_bytes", "q4_pack", "q8_quantize", "moe_q4_route", "moe_q4_prefill",
-              "moe_q4_decode", "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
+    for n in ["q4_packed_bytes", "q4_pack", "q4_tile", "q8_quantize", "moe_q4_route", "moe_q4_prefill",
+              "moe_q4_decode", "moe_q4_decode_batch", "moe_q4_decode_batch_workspace_bytes",
+              "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
               "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_rmsnorm",
               "moe_q4_last_error"]:
         assert n in names, n
@@ -127,6 +128,23 @@ def test_q4_tile_argument_checks(lib):
     assert "overlap" in _err(lib)
     assert lib.q4_tile(None, 32, 64, C.c_void_p(0x100000), None) == -1
     assert lib.q4_tile(None, 0, 64, None, None) == 0                                        # nothing to do
+
+
+def test_decode_batch_argument_checks(lib):
+    L = _layer()
+    ok = C.c_void_p(0x10000)
+    assert lib.moe_q4_decode_batch_workspace_bytes(C.byref(L), 33) == 0
+    assert lib.moe_q4_decode_batch_workspace_bytes(C.byref(L), -1) == 0
+    need = lib.moe_q4_decode_batch_workspace_bytes(C.byref(L), 32)
+    assert need > lib.moe_q4_decode_batch_workspace_bytes(C.byref(L), 1) > 0
+    assert lib.moe_q4_decode_batch(C.byref(L), ok, 33, ok, None, None, ok, need, None) == -1
+    assert "M=33" in _err(lib)
+    assert lib.moe_q4_decode_batch(C.byref(L), None, 2, ok, None, None, ok, need, None) == -1
+    assert lib.moe_q4_decode_batch(C.byref(L), C.c_void_p(0x10004), 2, ok, None, None, ok, need, None) == -1
+    assert lib.moe_q4_decode_batch(C.byref(L), ok, 2, ok, None, None, ok, 64, None) == -2
+    assert lib.moe_q4_decode_batch(C.byref(L), None, 0, None, None, None, None, 0, None) == 0   # nothing to do
+    wide = _layer(hidden=16384 + 32)
+    assert lib.moe_q4_decode_batch(C.byref(wide), ok, 1, ok, None, None, ok, need, None) == -1
 
 
 def test_workspace_checks(lib):
