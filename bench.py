@@ -283,7 +283,84 @@ def bench_decode(args, torch, mq, moe_synth, device_layer):
     torch.cuda.synchronize()
     hot_s = (time.perf_counter() - t3) / (reps * n)
     return dict(cfg=cfg, step_s=step_s, bytes_step=bytes_step, eager_s=eager_s, hot_s=hot_s,
-                copies=len(copies))
+                copies=len(copies), layers=copies)
+
+
+SMALL_M = (1, 2, 4, 8, 16, 32)
+
+
+def _graph_time(torch, calls, reps):
+    """Capture `calls` (a list of no-argument launches) in one HIP graph and
+    return the mean seconds per call over `reps` replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for c in calls:
+                c()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / (reps * len(calls))
+
+
+def bench_small_batch(args, torch, mq, moe_synth, dec, pre):
+    """Decode of M = 1..32 tokens: one batched W4A8 call (weights of an expert
+    read once per call) against M one-token steps and against the prefill
+    path (route + grouped bf16 GEMM) at T = M.  HIP graph replay throughout;
+    the decode layer copies rotate so weights stream from HBM."""
+    cfg = dec["cfg"]
+    copies, players = dec["layers"], pre["layers"]
+    ncall = 48
+    per_mat = cfg.I * (cfg.H // 32) * 18
+    out = {"M": [], "batched_us": [], "tok_s": [], "weight_gbps": [], "experts_read": [],
+           "one_token_steps_us": [], "prefill_path_us": []}
+    for M in SMALL_M:
+        X = torch.from_numpy(moe_synth.tokens(cfg, step=5000 + 100 * M, T=ncall * M)).cuda().view(ncall, M, cfg.H)
+        Y = torch.empty((ncall, M, cfg.H), dtype=torch.float32, device="cuda")
+        ws = torch.empty(mq.moe_q4_decode_batch_workspace_bytes(copies[0], M), dtype=torch.uint8, device="cuda")
+        uniq = 0
+        for i in range(ncall):              # eager pass: warm-up and the experts each call reads
+            _, ids, _ = mq.moe_q4_decode_batch(copies[i % len(copies)], X[i], y=Y[i], ws=ws, routing=True)
+            uniq += len(set(ids.cpu().numpy().ravel().tolist()))
+        uniq /= ncall
+        calls = [(lambda i=i: mq.moe_q4_decode_batch(copies[i % len(copies)], X[i], y=Y[i], ws=ws))
+                 for i in range(ncall)]
+        t_b = _graph_time(torch, calls, args.decode_reps)
+        nbytes = (uniq + (1 if cfg.shared else 0)) * 3 * per_mat + cfg.H * cfg.E * 4
+        # prefill path at T = M: route + grouped GEMM + combine
+        xb = X.to(torch.bfloat16)
+        R = mq.Routing.empty(M, cfg.k, cfg.E, xb.device)
+        rws = torch.empty(max(1, mq.moe_q4_route_workspace_bytes(players[0], M)), dtype=torch.uint8, device="cuda")
+        pws = torch.empty(max(1, mq.moe_q4_prefill_workspace_bytes(players[0], M)), dtype=torch.uint8, device="cuda")
+        yp = torch.empty((M, cfg.H), dtype=torch.float32, device="cuda")
+
+        def pcall(i):
+            L = players[i % len(players)]
+            mq.moe_q4_route(L, xb[i], out=R, ws=rws)
+            mq.moe_q4_prefill(L, xb[i], R, y=yp, ws=pws)
+        for i in range(4):
+            pcall(i)
+        torch.cuda.synchronize()
+        t_p = _graph_time(torch, [(lambda i=i: pcall(i)) for i in range(ncall)], args.decode_reps)
+        out["M"].append(M)
+        out["batched_us"].append(round(t_b * 1e6, 2))
+        out["tok_s"].append(round(M / t_b, 1))
+        out["weight_gbps"].append(round(nbytes / t_b / 1e9, 1))
+        out["experts_read"].append(round(uniq + (1 if cfg.shared else 0), 2))
+        out["one_token_steps_us"].append(round(M * dec["step_s"] * 1e6, 2))
+        out["prefill_path_us"].append(round(t_p * 1e6, 2))
+        del X, Y, ws, xb, R, rws, pws, yp
+    out["note"] = ("per call, graph replay, layer copies rotated: batched = moe_q4_decode_batch (each "
+                   "token bit-identical to one-token decode); one_token_steps = M x the one-token "
+                   "decode step; prefill_path = moe_q4_route + moe_q4_prefill at T = M (bf16 GEMM, "
+                   "2 layer copies); weight_gbps = bytes of the experts the call reads / time")
+    return out
 
 
 def cpu_baseline(args, pre):
@@ -320,6 +397,7 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--cpu-sample-tokens", type=int, default=768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-small-batch", action="store_true", help="skip the 1..32-token decode comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -345,6 +423,8 @@ def main():
 
     pre = bench_prefill(args, torch, mq, moe_synth, device_layer)
     dec = bench_decode(args, torch, mq, moe_synth, device_layer)
+    small = None if args.no_small_batch else bench_small_batch(args, torch, mq, moe_synth, dec, pre)
+    dec.pop("layers")
     copy_gbps = hbm_copy_gbps(torch)
     cfg = pre["cfg"]
     tok_s = cfg.T / pre["step_s"]
@@ -408,6 +488,7 @@ def main():
                          "traffic": _traffic("decode")},
         },
     }
+    out["small_batch_decode"] = small
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args, pre)
     if args.copy_probe:
         copy_probe(torch)

@@ -119,28 +119,24 @@ DecodeWs decode_ws(const moe_q4_layer* L) {
 }
 
 struct DecodeBatchWs {
-  size_t partials, qx, dx, sx, ids, w, elist_off, elist, hit, nhit, qh, dh, sh, total;
+  size_t partials, qx, dx, sx, ids, w, qh, dh, sh, o, total;
 };
 DecodeBatchWs decode_batch_ws(const moe_q4_layer* L, int32_t M) {
   DecodeBatchWs w;
   const size_t m = (size_t)M, k = (size_t)L->top_k, E = (size_t)L->n_experts;
   const size_t H = L->hidden, I = L->inter, nc = H / 32;
   const size_t np = m * k + (L->has_shared ? m : 0);
-  const size_t hb = E < m * k ? E : m * k;
   w.partials = 0;
   w.qx = w.partials + up256(m * nc * E * 4);
   w.dx = w.qx + up256(m * H);
   w.sx = w.dx + up256(m * nc * 4);
   w.ids = w.sx + up256(m * nc * 4);
   w.w = w.ids + up256(m * k * 4);
-  w.elist_off = w.w + up256(m * k * 4);
-  w.elist = w.elist_off + up256((E + 1) * 4);
-  w.hit = w.elist + up256(m * k * 4);
-  w.nhit = w.hit + up256(hb * 4);
-  w.qh = w.nhit + up256(4);
+  w.qh = w.w + up256(m * k * 4);
   w.dh = w.qh + up256(np * I);
   w.sh = w.dh + up256(np * I / 32 * 4);
-  w.total = w.sh + up256(np * I / 32 * 4);
+  w.o = w.sh + up256(np * I / 32 * 4);
+  w.total = w.o + up256(np * H * 4);
   return w;
 }
 
@@ -346,14 +342,10 @@ int moe_q4_decode_batch(const moe_q4_layer* L, const float* x, int32_t M, float*
   a.sx = at<int32_t>(ws, W.sx);
   a.ids = at<int32_t>(ws, W.ids);
   a.w = at<float>(ws, W.w);
-  a.elist_off = at<int32_t>(ws, W.elist_off);
-  a.elist = at<int32_t>(ws, W.elist);
-  a.hit = at<int32_t>(ws, W.hit);
-  a.nhit = at<int32_t>(ws, W.nhit);
-  a.hb = L->n_experts < M * L->top_k ? L->n_experts : M * L->top_k;
   a.qh = at<int8_t>(ws, W.qh);
   a.dh = at<float>(ws, W.dh);
   a.sh = at<int32_t>(ws, W.sh);
+  a.o = at<float>(ws, W.o);
   a.t_ids = ids_out;
   a.t_w = w_out;
   hipError_t e = moeq4::launch_decode_batch(a, stream);

@@ -10,22 +10,23 @@
 // changes is the memory traffic: an expert selected by several tokens is
 // read once per call, not once per token.
 //
-// Four launches on the caller's stream:
+// Five launches on the caller's stream:
 //   dbatch_router   one block per 32-element chunk c: W_r's chunk rows are
 //                   read once and every token's FMA chain (a leaf of the
 //                   pinned tree) is taken; q8 of chunk c of every token.
-//   dbatch_route    one block: per token (one wave) the tree over the leaves,
-//                   bias, the top-k in (logit desc, index asc) order and the
-//                   softmax weights; then per expert the ascending list of
-//                   its (token, slot) pairs and the ascending list of the
-//                   experts that have pairs.
-//   dbatch_gateup   one block per (listed expert, 32 values of i): the 32 gate
-//                   and 32 up rows stay in registers while the block runs the
-//                   row program for each of the expert's tokens (codes in
-//                   LDS), then h = silu(g) * u and its q8 per pair.
-//   dbatch_down     one block per few output rows: (row, listed expert) items
-//                   whose weights stay in registers over the expert's pairs,
-//                   then each token's combine in slot order.
+//   dbatch_route    one block per token: the tree over its leaves (P lanes
+//                   per expert, as in the one-token kernel), bias, the top-k
+//                   by rank in (logit desc, index asc) order and the softmax.
+//   dbatch_gateup   one block per (expert, 32 values of i): the block finds
+//                   the expert's tokens in ascending order (one ballot),
+//                   stages their x codes in LDS, keeps its 32 gate and 32 up
+//                   rows in registers over those tokens, then h = silu(g) * u
+//                   and its q8 per (token, slot) pair.  Experts no token
+//                   chose exit at once.
+//   dbatch_down     one block per (expert, 128 output rows): the pairs' q8(h)
+//                   in LDS, the rows in registers, fp32 outputs per pair.
+//   dbatch_combine  y[t] = ((w_0 o_0 + w_1 o_1) + ...) + o_shared per token,
+//                   in slot order.
 #include "launch.hpp"
 #include "w4a8.hpp"
 #include "decode_common.hpp"
@@ -73,163 +74,105 @@ __global__ void __launch_bounds__(1024) dbatch_router_kernel(DecodeBatchArgs a) 
 }
 
 // ---------------------------------------------------------------- routing
-// 64-bit wave maximum (keys are unique: the low word encodes the expert).
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    const uint64_t u = ((uint64_t)hi << 32) | lo;
-    v = u > v ? u : v;
+__global__ void __launch_bounds__(1024) dbatch_route_kernel(DecodeBatchArgs a, int P) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  uint64_t* key = reinterpret_cast<uint64_t*>(dyn);                 // [E]
+  float* logit = reinterpret_cast<float*>(key + a.E);                // [E]
+  __shared__ int ids_l[32];
+  __shared__ float vals_l[32], ex_l[32];
+  const int tid = threadIdx.x, nt = blockDim.x, t = blockIdx.x;
+  const int E = a.E, k = a.k, nc = a.H / BLK;
+  const int m = (int)next_pow2_u32((uint32_t)nc), L = m / P;
+  const float* src = a.partials + (size_t)t * nc * E;
+  const int items = E * P;                // item = e * P + p; the loop is uniform over the block
+  for (int b0 = 0; b0 < items; b0 += nt) {
+    const int it = b0 + tid;
+    const bool ok = it < items;
+    const int e = ok ? it / P : 0, p = it % P;
+    float lv = ok ? leaf_tree(src + e, E, p * L, L, nc) : 0.0f;
+    for (int o = 1; o < P; o <<= 1) lv = lv + __shfl_xor(lv, o, 64);
+    if (ok && p == 0) {
+      const float lg = a.bias ? lv + a.bias[e] : lv;
+      logit[e] = lg;
+      key[e] = rank_key(lg, e);
+    }
   }
-  return v;
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) {     // rank = experts before e in (logit desc, index asc)
+    const uint64_t ke = key[e];
+    int rank = 0;
+    for (int j = 0; j < E; j++) rank += key[j] > ke ? 1 : 0;
+    if (rank < k) {
+      ids_l[rank] = e;
+      vals_l[rank] = logit[e];
+    }
+  }
+  __syncthreads();
+  if (tid < k) ex_l[tid] = exp_p(vals_l[tid] - vals_l[0]);
+  __syncthreads();
+  if (tid < k) {                          // w_s = e_s / ((e_0 + e_1) + ...)
+    float S = ex_l[0];
+    for (int s = 1; s < k; s++) S = S + ex_l[s];
+    const float wv = ex_l[tid] / S;
+    a.ids[t * k + tid] = ids_l[tid];
+    a.w[t * k + tid] = wv;
+    if (a.t_ids) a.t_ids[t * k + tid] = ids_l[tid];
+    if (a.t_w) a.t_w[t * k + tid] = wv;
+  }
 }
 
-constexpr int kRouteKeysPerLane = 16;     // E <= 1024
-
-__global__ void __launch_bounds__(1024) dbatch_route_kernel(DecodeBatchArgs a) {
-  __shared__ int ids_l[kDecodeBatchMax * 32];
-  __shared__ float vals_l[kDecodeBatchMax * 32];
-  __shared__ int scan_l[1024];
-  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64, nw = blockDim.x / 64;
-  const int M = a.M, E = a.E, k = a.k, nc = a.H / BLK;
-  const int nj = (E + 63) / 64;
-  for (int t = wave; t < M; t += nw) {
-    const float* P = a.partials + (size_t)t * nc * E;
-    uint64_t kv[kRouteKeysPerLane];
-#pragma unroll
-    for (int j = 0; j < kRouteKeysPerLane; j++) {
-      kv[j] = 0;
-      const int e = lane + 64 * j;
-      if (j < nj && e < E) {
-        float l = root_tree(P + e, E, nc);
-        if (a.bias) l = l + a.bias[e];
-        kv[j] = rank_key(l, e);
+// ---------------------------------------------------------------- pairs of one expert
+// The (token, slot) pairs of expert e in token order (a token chooses an
+// expert at most once), found by wave 0 with one ballot over the tokens;
+// e == E is the shared expert (every token, pair M*k + t).  Returns n; the
+// pair indices land in pairs_l.  Ends with a barrier.
+__device__ __forceinline__ int expert_pairs(const DecodeBatchArgs& a, int e, int* pairs_l, int* n_l) {
+  const int tid = threadIdx.x, M = a.M, k = a.k;
+  if (tid < 64) {
+    int p = -1;
+    if (tid < M) {
+      if (e == a.E) {
+        p = M * k + tid;
+      } else {
+        for (int s = 0; s < k; s++)
+          if (a.ids[tid * k + s] == e) p = tid * k + s;
       }
     }
-    for (int r = 0; r < k; r++) {         // k rounds of the first maximum among the rest
-      uint64_t best = 0;
-#pragma unroll
-      for (int j = 0; j < kRouteKeysPerLane; j++) best = kv[j] > best ? kv[j] : best;
-      best = wave_max_u64(best);
-      const int e = (int)(0xffffffffu - (uint32_t)best);
-#pragma unroll
-      for (int j = 0; j < kRouteKeysPerLane; j++)
-        if (kv[j] == best) kv[j] = 0;
-      if (lane == 0) {
-        ids_l[t * k + r] = min(max(e, 0), E - 1);
-        vals_l[t * k + r] = key_logit(best);
-      }
-    }
+    const unsigned long long mask = __ballot(p >= 0);
+    if (p >= 0) pairs_l[__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u))] = p;
+    if (tid == 0) *n_l = __builtin_popcountll(mask);
   }
   __syncthreads();
-  // softmax weights: w_s = e_s / ((e_0 + e_1) + ...), e_s = exp(l_s - l_0)
-  for (int i = tid; i < M * k; i += blockDim.x) {
-    const int t = i / k;
-    const float l0 = vals_l[t * k];
-    float S = exp_p(vals_l[t * k] - l0);
-    for (int s = 1; s < k; s++) S = S + exp_p(vals_l[t * k + s] - l0);
-    const float wv = exp_p(vals_l[i] - l0) / S;
-    a.ids[i] = ids_l[i];
-    a.w[i] = wv;
-    if (a.t_ids) a.t_ids[i] = ids_l[i];
-    if (a.t_w) a.t_w[i] = wv;
-  }
-  // per-expert pair lists: expert e counts its pairs in pair order, an
-  // exclusive scan over (listed << 16 | count) places lists and hits
-  const int np = M * k;
-  int cnt = 0;
-  const int e = tid;
-  if (e < E)
-    for (int p = 0; p < np; p++) cnt += ids_l[p] == e ? 1 : 0;
-  int v = (e < E) ? (((cnt > 0) ? 1 : 0) << 16) | cnt : 0;
-  scan_l[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {    // inclusive Hillis-Steele scan over 1024 entries
-    const int add = (tid >= o && tid < (int)blockDim.x) ? scan_l[tid - o] : 0;
-    __syncthreads();
-    scan_l[tid] += add;
-    __syncthreads();
-  }
-  const int excl = scan_l[tid] - v;
-  if (e < E) {
-    const int off = excl & 0xffff, h = excl >> 16;
-    a.elist_off[e] = off;
-    if (cnt > 0) {
-      a.hit[h] = e;
-      int n = 0;
-      for (int p = 0; p < np && n < cnt; p++)
-        if (ids_l[p] == e) a.elist[off + n++] = p;
-    }
-  }
-  if (tid == 0) {
-    a.elist_off[E] = np;
-    a.nhit[0] = scan_l[E - 1] >> 16;
-  }
+  return *n_l;
 }
 
 // ---------------------------------------------------------------- gate/up
-// The n pairs of block row j: a listed expert's pairs, or (j == hb) every
-// token for the shared expert.  Pair u: index into qh, and its token.
-struct PairSet {
-  int n, p0, shared, e;
-};
-
-__device__ __forceinline__ PairSet pair_set(const DecodeBatchArgs& a, int j) {
-  PairSet ps;
-  ps.shared = a.has_shared && j == a.hb;
-  ps.n = 0;
-  ps.p0 = 0;
-  ps.e = 0;
-  if (ps.shared) {
-    ps.n = a.M;
-  } else if (j < a.nhit[0]) {
-    ps.e = a.hit[j];
-    ps.p0 = a.elist_off[ps.e];
-    ps.n = a.elist_off[ps.e + 1] - ps.p0;
-  }
-  return ps;
-}
-
-__device__ __forceinline__ int pair_index(const DecodeBatchArgs& a, const PairSet& ps, int u) {
-  return ps.shared ? a.M * a.k + u : a.elist[ps.p0 + u];
-}
-
-__device__ __forceinline__ int pair_token(const DecodeBatchArgs& a, const PairSet& ps, int u) {
-  return ps.shared ? u : a.elist[ps.p0 + u] / a.k;
-}
-
 constexpr int DBG_ROWS = 32;
 
-// ALDS: every token's x codes staged in LDS; otherwise read from the workspace.
-template <int BPL, bool FAST, bool ALDS>
-__global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, int lpr) {
+// tb: tokens whose codes fit the block's LDS at once; the expert's tokens are
+// taken tb at a time.
+template <int BPL, bool FAST>
+__global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, int lpr, int tb) {
   extern __shared__ __align__(16) uint8_t dyn[];
-  const int H = a.H, I = a.I, nbh = H / BLK, M = a.M;
+  __shared__ int pairs_l[kDecodeBatchMax];
+  __shared__ int n_l;
+  const int H = a.H, I = a.I, nbh = H / BLK, M = a.M, k = a.k;
   const int SS = act_row_dwords(nbh);
-  uint32_t* qa_l = reinterpret_cast<uint32_t*>(dyn);                       // [M][SS] (ALDS)
-  float* da_l = reinterpret_cast<float*>(qa_l + (ALDS ? (size_t)M * SS : 0));  // [M][nbh]
-  int32_t* sa_l = reinterpret_cast<int32_t*>(da_l + (ALDS ? (size_t)M * nbh : 0));
-  float* val = reinterpret_cast<float*>(sa_l + (ALDS ? (size_t)M * nbh : 0));  // [64][M]
+  float* val = reinterpret_cast<float*>(dyn);                              // [64][M]
+  uint32_t* qa_l = reinterpret_cast<uint32_t*>(val + 2 * DBG_ROWS * M);   // [tb][SS]
+  float* da_l = reinterpret_cast<float*>(qa_l + (size_t)tb * SS);          // [tb][nbh]
+  int32_t* sa_l = reinterpret_cast<int32_t*>(da_l + (size_t)tb * nbh);     // [tb][nbh]
   const int tid = threadIdx.x;
-  const int ngrp = I / DBG_ROWS, j = blockIdx.x / ngrp, gx = blockIdx.x % ngrp, i0 = gx * DBG_ROWS;
-  const PairSet ps = pair_set(a, j);
-  if (ps.n == 0) return;                  // uniform over the block
-  const int n = ps.n;
-  for (int g = tid; ALDS && g < n * nbh; g += blockDim.x) {
-    const int u = g / nbh, b = g % nbh, t = pair_token(a, ps, u);
-    const uint4* src = reinterpret_cast<const uint4*>(a.qx + (size_t)t * H) + 2 * b;
-    uint4* dst = reinterpret_cast<uint4*>(qa_l + (size_t)u * SS + act_off(b));
-    dst[0] = src[0];
-    dst[1] = src[1];
-    da_l[u * nbh + b] = a.dx[t * nbh + b];
-    sa_l[u * nbh + b] = a.sx[t * nbh + b];
-  }
+  const int ngrp = I / DBG_ROWS, e = blockIdx.x / ngrp, gx = blockIdx.x % ngrp, i0 = gx * DBG_ROWS;
+  const bool shared = e == a.E;
+  const int n = expert_pairs(a, e, pairs_l, &n_l);
+  if (n == 0) return;                     // uniform over the block
   const int row = tid / lpr, lr = tid % lpr;
   const bool is_up = row >= DBG_ROWS;
   const int i = i0 + (row % DBG_ROWS);
   const size_t rb = (size_t)nbh * Q4B;
-  const uint8_t* base = ps.shared ? (is_up ? a.s_up : a.s_gate) + (size_t)i * rb
-                                  : (is_up ? a.w_up : a.w_gate) + ((size_t)ps.e * I + i) * rb;
+  const uint8_t* base = shared ? (is_up ? a.s_up : a.s_gate) + (size_t)i * rb
+                               : (is_up ? a.w_up : a.w_gate) + ((size_t)e * I + i) * rb;
   constexpr int NV = FAST ? 18 * BPL / 16 : 1;
   uint32_t D[4 * NV + 1] = {};
   if (FAST && lr * BPL < nbh) {
@@ -240,27 +183,38 @@ __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, 
       D[4 * v] = q.x; D[4 * v + 1] = q.y; D[4 * v + 2] = q.z; D[4 * v + 3] = q.w;
     }
   }
-  __syncthreads();
-  for (int u = 0; u < n; u++) {
-    const int t = pair_token(a, ps, u);
-    auto act = [&](int b) {
-      ActBlock A;
-      const uint4* q = ALDS ? reinterpret_cast<const uint4*>(qa_l + (size_t)u * SS + act_off(b))
-                            : reinterpret_cast<const uint4*>(a.qx + (size_t)t * H) + 2 * b;
-      const uint4 u0 = q[0], u1 = q[1];
-      A.a[0] = u0.x; A.a[1] = u0.y; A.a[2] = u0.z; A.a[3] = u0.w;
-      A.a[4] = u1.x; A.a[5] = u1.y; A.a[6] = u1.z; A.a[7] = u1.w;
-      A.d = ALDS ? da_l[u * nbh + b] : a.dx[t * nbh + b];
-      A.s = ALDS ? sa_l[u * nbh + b] : a.sx[t * nbh + b];
-      return A;
-    };
-    float v;
-    if constexpr (FAST) v = w4a8_regs<BPL>(D, nbh, lr * BPL, act);
-    else v = w4a8_lane<BPL, false>(base, nbh, lr * BPL, act, nullptr);
-    v = wave_tree_sum(v, lpr);
-    if (lr == 0) val[row * M + u] = v;
+  for (int u0 = 0; u0 < n; u0 += tb) {
+    const int nu = min(tb, n - u0);
+    for (int g = tid; g < nu * nbh; g += blockDim.x) {
+      const int u = g / nbh, b = g % nbh;
+      const int p = pairs_l[u0 + u], t = shared ? p - M * k : p / k;
+      const uint4* src = reinterpret_cast<const uint4*>(a.qx + (size_t)t * H) + 2 * b;
+      uint4* dst = reinterpret_cast<uint4*>(qa_l + (size_t)u * SS + act_off(b));
+      dst[0] = src[0];
+      dst[1] = src[1];
+      da_l[u * nbh + b] = a.dx[t * nbh + b];
+      sa_l[u * nbh + b] = a.sx[t * nbh + b];
+    }
+    __syncthreads();
+    for (int u = 0; u < nu; u++) {
+      auto act = [&](int b) {
+        ActBlock A;
+        const uint4* q = reinterpret_cast<const uint4*>(qa_l + (size_t)u * SS + act_off(b));
+        const uint4 q0 = q[0], q1 = q[1];
+        A.a[0] = q0.x; A.a[1] = q0.y; A.a[2] = q0.z; A.a[3] = q0.w;
+        A.a[4] = q1.x; A.a[5] = q1.y; A.a[6] = q1.z; A.a[7] = q1.w;
+        A.d = da_l[u * nbh + b];
+        A.s = sa_l[u * nbh + b];
+        return A;
+      };
+      float v;
+      if constexpr (FAST) v = w4a8_regs<BPL>(D, nbh, lr * BPL, act);
+      else v = w4a8_lane<BPL, false>(base, nbh, lr * BPL, act, nullptr);
+      v = wave_tree_sum(v, lpr);
+      if (lr == 0) val[row * M + u0 + u] = v;
+    }
+    __syncthreads();                      // the chunk's codes are read; val is complete
   }
-  __syncthreads();
   // h of one 32-group per pair, then its q8 (a 32-lane group per pair)
   for (int idx = tid; idx < n * DBG_ROWS; idx += blockDim.x) {
     const int u = idx / DBG_ROWS, r = idx % DBG_ROWS;
@@ -273,7 +227,7 @@ __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, 
     int sum = q;
 #pragma unroll
     for (int m = 1; m < BLK; m <<= 1) sum += __shfl_xor(sum, m, BLK);
-    const int p = pair_index(a, ps, u);
+    const int p = pairs_l[u];
     a.qh[(size_t)p * I + i0 + r] = (int8_t)q;
     if (r == 0) {
       a.dh[(size_t)p * (I / BLK) + gx] = d;
@@ -282,141 +236,162 @@ __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, 
   }
 }
 
-// ---------------------------------------------------------------- down + combine
-// Block: `rows` output rows x (hb + S) listed experts, LPR lanes per (row,
-// expert) item; an item's weight span stays in registers over its pairs.
+// ---------------------------------------------------------------- down
+// Block: `rows` (<= 128) output rows of one expert, lpr lanes per row, the
+// rows' weights in registers over the expert's pairs; o[pair][r] fp32.
 template <int BPL, bool FAST>
-__global__ void __launch_bounds__(1024) dbatch_down_kernel(DecodeBatchArgs a, int lpr, int rows) {
-  extern __shared__ __align__(16) float o_l[];          // [rows][np + M*S]
-  const int H = a.H, I = a.I, nbi = I / BLK, M = a.M, k = a.k;
-  const int nlist = a.hb + (a.has_shared ? 1 : 0);
-  const int npair = M * k + (a.has_shared ? M : 0);
-  const int tid = threadIdx.x, r0 = blockIdx.x * rows;
-  const int lr = tid % lpr, stride = blockDim.x / lpr;
+__global__ void __launch_bounds__(1024) dbatch_down_kernel(DecodeBatchArgs a, int lpr, int tb, int rows) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  __shared__ int pairs_l[kDecodeBatchMax];
+  __shared__ int n_l;
+  const int H = a.H, I = a.I, nbi = I / BLK, M = a.M;
+  const int SS = act_row_dwords(nbi);
+  uint32_t* qh_l = reinterpret_cast<uint32_t*>(dyn);                       // [tb][SS]
+  float* dh_l = reinterpret_cast<float*>(qh_l + (size_t)tb * SS);          // [tb][nbi]
+  int32_t* sh_l = reinterpret_cast<int32_t*>(dh_l + (size_t)tb * nbi);     // [tb][nbi]
+  const int tid = threadIdx.x;
+  const int ngrp = (H + rows - 1) / rows, e = blockIdx.x / ngrp, r0 = (blockIdx.x % ngrp) * rows;
+  const bool shared = e == a.E;
+  const int n = expert_pairs(a, e, pairs_l, &n_l);
+  if (n == 0) return;                     // uniform over the block
+  const int rl = tid / lpr, lr = tid % lpr, r = r0 + rl;
+  const bool live = rl < rows && r < H;
   const size_t rb = (size_t)nbi * Q4B;
-  // items (row, listed expert), lpr lanes each; the lanes of an item run the
-  // same number of pairs, so the shuffles stay inside the item's lanes
-  for (int item = tid / lpr; item < rows * nlist; item += stride) {
-    const int rl = item / nlist, j = item % nlist, r = r0 + rl;
-    if (r >= H) continue;
-    const PairSet ps = pair_set(a, j);
-    if (ps.n == 0) continue;
-    const uint8_t* base = ps.shared ? a.s_down + (size_t)r * rb : a.w_down + ((size_t)ps.e * H + r) * rb;
-    constexpr int NV = FAST ? 18 * BPL / 16 : 1;
-    uint32_t D[4 * NV + 1] = {};
-    if (FAST && lr * BPL < nbi) {
-      const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * Q4B);
+  const uint8_t* base = shared ? a.s_down + (size_t)min(r, H - 1) * rb
+                               : a.w_down + ((size_t)e * H + min(r, H - 1)) * rb;
+  constexpr int NV = FAST ? 18 * BPL / 16 : 1;
+  uint32_t D[4 * NV + 1] = {};
+  if (FAST && live && lr * BPL < nbi) {
+    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * Q4B);
 #pragma unroll
-      for (int v = 0; v < NV; v++) {
-        const uint4 q = src[v];
-        D[4 * v] = q.x; D[4 * v + 1] = q.y; D[4 * v + 2] = q.z; D[4 * v + 3] = q.w;
-      }
+    for (int v = 0; v < NV; v++) {
+      const uint4 q = src[v];
+      D[4 * v] = q.x; D[4 * v + 1] = q.y; D[4 * v + 2] = q.z; D[4 * v + 3] = q.w;
     }
-    for (int u = 0; u < ps.n; u++) {
-      const int p = pair_index(a, ps, u);
+  }
+  for (int u0 = 0; u0 < n; u0 += tb) {
+    const int nu = min(tb, n - u0);
+    if (u0 > 0) __syncthreads();          // the previous chunk's activations are read
+    for (int g = tid; g < nu * nbi; g += blockDim.x) {
+      const int u = g / nbi, b = g % nbi, p = pairs_l[u0 + u];
+      const uint4* src = reinterpret_cast<const uint4*>(a.qh + (size_t)p * I) + 2 * b;
+      uint4* dst = reinterpret_cast<uint4*>(qh_l + (size_t)u * SS + act_off(b));
+      dst[0] = src[0];
+      dst[1] = src[1];
+      dh_l[u * nbi + b] = a.dh[(size_t)p * nbi + b];
+      sh_l[u * nbi + b] = a.sh[(size_t)p * nbi + b];
+    }
+    __syncthreads();
+    for (int u = 0; u < nu; u++) {
       auto act = [&](int b) {
         ActBlock A;
-        const uint4* q = reinterpret_cast<const uint4*>(a.qh + (size_t)p * I) + 2 * b;
-        const uint4 u0 = q[0], u1 = q[1];
-        A.a[0] = u0.x; A.a[1] = u0.y; A.a[2] = u0.z; A.a[3] = u0.w;
-        A.a[4] = u1.x; A.a[5] = u1.y; A.a[6] = u1.z; A.a[7] = u1.w;
-        A.d = a.dh[(size_t)p * nbi + b];
-        A.s = a.sh[(size_t)p * nbi + b];
+        const uint4* q = reinterpret_cast<const uint4*>(qh_l + (size_t)u * SS + act_off(b));
+        const uint4 q0 = q[0], q1 = q[1];
+        A.a[0] = q0.x; A.a[1] = q0.y; A.a[2] = q0.z; A.a[3] = q0.w;
+        A.a[4] = q1.x; A.a[5] = q1.y; A.a[6] = q1.z; A.a[7] = q1.w;
+        A.d = dh_l[u * nbi + b];
+        A.s = sh_l[u * nbi + b];
         return A;
       };
       float v;
       if constexpr (FAST) v = w4a8_regs<BPL>(D, nbi, lr * BPL, act);
       else v = w4a8_lane<BPL, false>(base, nbi, lr * BPL, act, nullptr);
       v = wave_tree_sum(v, lpr);
-      if (lr == 0) o_l[(size_t)rl * npair + p] = v;
+      if (live && lr == 0) a.o[(size_t)pairs_l[u0 + u] * H + r] = v;
     }
   }
-  __syncthreads();
-  for (int idx = tid; idx < rows * M; idx += blockDim.x) {
-    const int rr = idx / M, t = idx % M, ro = r0 + rr;
-    if (ro >= H) continue;
-    const float* o = o_l + (size_t)rr * npair;
-    const float* w = a.w + (size_t)t * k;
-    float acc = w[0] * o[t * k];
-    for (int s = 1; s < k; s++) acc = acc + w[s] * o[t * k + s];
-    if (a.has_shared) acc = acc + o[M * k + t];
-    a.y[(size_t)t * H + ro] = acc;
-  }
+}
+
+// ---------------------------------------------------------------- combine
+__global__ void __launch_bounds__(256) dbatch_combine_kernel(DecodeBatchArgs a) {
+  const int H = a.H, M = a.M, k = a.k;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)M * H) return;
+  const int t = (int)(i / H), r = (int)(i % H);
+  const float* w = a.w + (size_t)t * k;
+  const float* o = a.o + (size_t)t * k * H + r;
+  float acc = w[0] * o[0];
+  for (int s = 1; s < k; s++) acc = acc + w[s] * o[(size_t)s * H];
+  if (a.has_shared) acc = acc + a.o[((size_t)M * k + t) * H + r];
+  a.y[(size_t)t * H + r] = acc;
 }
 
 // ---------------------------------------------------------------- launch
 DecodeBatchGeometry decode_batch_geometry(int M, int H, int I, int E, int k, int has_shared) {
   DecodeBatchGeometry g;
-  const int hb = E < M * k ? E : M * k;
-  const int nlist = hb + (has_shared ? 1 : 0);
   int rt = (E + 63) / 64 * 64;
   if (rt < 32 * M) rt = 32 * M;
   g.router_threads = rt;
+  const int nc = H / BLK;
+  int m = 1;
+  while (m < nc) m <<= 1;
+  int P = 1;                              // lanes per expert: runs of <= 32 leaves
+  while (P < 64 && P < m && E * P * 2 <= 1024) P <<= 1;
+  while (m / P > 32) P <<= 1;
+  g.route_parts = P;
+  int rth = (E * P + 63) / 64 * 64;
+  g.route_threads = rth > 1024 ? 1024 : rth;
+  g.route_lds = 12 * (size_t)E;
   const RowSplit gu = row_split(H, 16);
   g.gu_lpr = gu.lpr;
   g.gu_bpl = gu.bpl;
   g.gu_fast = (gu.bpl % 8 == 0) && (gu.nb % gu.bpl == 0);
   g.gu_threads = 2 * DBG_ROWS * gu.lpr;
-  const int nbh = H / BLK;
-  const size_t act = 4 * ((size_t)M * act_row_dwords(nbh) + 2 * (size_t)M * nbh);
-  const size_t val = 4 * (size_t)2 * DBG_ROWS * M;
-  g.gu_alds = act + val <= kDecodeLdsMax;
-  g.gu_lds = (g.gu_alds ? act : 0) + val;
+  const size_t gu_tok = 4 * ((size_t)act_row_dwords(nc) + 2 * (size_t)nc);   // LDS bytes per staged token
+  const size_t gu_val = 4 * (size_t)2 * DBG_ROWS * M;
+  size_t tb = (kDecodeBatchLds - gu_val) / gu_tok;
+  g.gu_tb = (int)(tb < 1 ? 1 : (tb > (size_t)M ? (size_t)M : tb));
+  g.gu_lds = gu_val + gu_tok * g.gu_tb;
   const RowSplit dn = row_split(I, 16);
   g.dn_lpr = dn.lpr;
   g.dn_bpl = dn.bpl;
   g.dn_fast = (dn.bpl % 8 == 0) && (dn.nb % dn.bpl == 0);
-  const int per_row = nlist * dn.lpr;
-  int rows = 1024 / per_row;
-  if (rows < 1) rows = 1;
-  if (rows > 64) rows = 64;
-  g.dn_rows = rows;
-  g.dn_threads = (rows * per_row + 63) / 64 * 64;
-  if (g.dn_threads > 1024) g.dn_threads = 1024;   // the kernel loops over its items
-  const int npair = M * k + (has_shared ? M : 0);
-  g.dn_lds = 4 * (size_t)rows * npair;
+  g.dn_rows = 1024 / dn.lpr < 128 ? 1024 / dn.lpr : 128;
+  g.dn_threads = g.dn_rows * dn.lpr;
+  const int nbi = I / BLK;
+  const size_t dn_tok = 4 * ((size_t)act_row_dwords(nbi) + 2 * (size_t)nbi);
+  tb = kDecodeBatchLds / dn_tok;
+  g.dn_tb = (int)(tb < 1 ? 1 : (tb > (size_t)M ? (size_t)M : tb));
+  g.dn_lds = dn_tok * g.dn_tb;
+  (void)has_shared;
   return g;
 }
 
 hipError_t launch_decode_batch(const DecodeBatchArgs& a, hipStream_t stream) {
   const DecodeBatchGeometry g = decode_batch_geometry(a.M, a.H, a.I, a.E, a.k, a.has_shared);
-  const int nc = a.H / BLK;
+  const int nc = a.H / BLK, nexp = a.E + (a.has_shared ? 1 : 0);
   hipLaunchKernelGGL(dbatch_router_kernel, dim3(nc), dim3(g.router_threads), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dbatch_route_kernel, dim3(1), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(dbatch_route_kernel, dim3(a.M), dim3(g.route_threads), g.route_lds, stream, a, g.route_parts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int nlist = a.hb + (a.has_shared ? 1 : 0);
   {
-    dim3 grid(nlist * (a.I / DBG_ROWS));
+    dim3 grid(nexp * (a.I / DBG_ROWS));
     dim3 block(g.gu_threads);
-#define MOEQ4_GU(B, F, L) \
-  hipLaunchKernelGGL((dbatch_gateup_kernel<B, F, L>), grid, block, g.gu_lds, stream, a, g.gu_lpr)
-#define MOEQ4_GU_L(B, F) \
-  if (g.gu_alds) MOEQ4_GU(B, F, true); else MOEQ4_GU(B, F, false)
+#define MOEQ4_GU(B, F) \
+  hipLaunchKernelGGL((dbatch_gateup_kernel<B, F>), grid, block, g.gu_lds, stream, a, g.gu_lpr, g.gu_tb)
     if (g.gu_fast) {
-      if (g.gu_bpl == 8) { MOEQ4_GU_L(8, true); }
-      else if (g.gu_bpl == 16) { MOEQ4_GU_L(16, true); }
-      else { MOEQ4_GU_L(32, true); }
+      if (g.gu_bpl == 8) MOEQ4_GU(8, true);
+      else if (g.gu_bpl == 16) MOEQ4_GU(16, true);
+      else MOEQ4_GU(32, true);
     } else {
-      if (g.gu_bpl == 1) { MOEQ4_GU_L(1, false); }
-      else if (g.gu_bpl == 2) { MOEQ4_GU_L(2, false); }
-      else if (g.gu_bpl == 4) { MOEQ4_GU_L(4, false); }
-      else if (g.gu_bpl == 8) { MOEQ4_GU_L(8, false); }
-      else if (g.gu_bpl == 16) { MOEQ4_GU_L(16, false); }
-      else { MOEQ4_GU_L(32, false); }
+      if (g.gu_bpl == 1) MOEQ4_GU(1, false);
+      else if (g.gu_bpl == 2) MOEQ4_GU(2, false);
+      else if (g.gu_bpl == 4) MOEQ4_GU(4, false);
+      else if (g.gu_bpl == 8) MOEQ4_GU(8, false);
+      else if (g.gu_bpl == 16) MOEQ4_GU(16, false);
+      else MOEQ4_GU(32, false);
     }
-#undef MOEQ4_GU_L
 #undef MOEQ4_GU
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   {
-    dim3 grid((a.H + g.dn_rows - 1) / g.dn_rows);
+    dim3 grid(nexp * ((a.H + g.dn_rows - 1) / g.dn_rows));
     dim3 block(g.dn_threads);
 #define MOEQ4_DN(B, F) \
-  hipLaunchKernelGGL((dbatch_down_kernel<B, F>), grid, block, g.dn_lds, stream, a, g.dn_lpr, g.dn_rows)
+  hipLaunchKernelGGL((dbatch_down_kernel<B, F>), grid, block, g.dn_lds, stream, a, g.dn_lpr, g.dn_tb, g.dn_rows)
     if (g.dn_fast) {
       if (g.dn_bpl == 8) MOEQ4_DN(8, true);
       else if (g.dn_bpl == 16) MOEQ4_DN(16, true);
@@ -431,8 +406,11 @@ hipError_t launch_decode_batch(const DecodeBatchArgs& a, hipStream_t stream) {
     }
 #undef MOEQ4_DN
     err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  return err;
+  const int64_t n = (int64_t)a.M * a.H;
+  hipLaunchKernelGGL(dbatch_combine_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace moeq4

@@ -117,6 +117,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Batched decode: M <= kDecodeBatchMax tokens, each through the single-token
 // program; the selected experts' weights are read once per call.
 constexpr int kDecodeBatchMax = 32;
+constexpr size_t kDecodeBatchLds = 40 * 1024;   // LDS budget of the batched gate/up and down blocks
 struct DecodeBatchArgs {
   const float* x;           // [M][H]
   float* y;                 // [M][H]
@@ -136,22 +137,20 @@ struct DecodeBatchArgs {
   int32_t* sx;              // [M][H/32]
   int32_t* ids;             // [M][k]
   float* w;                 // [M][k]
-  int32_t* elist_off;       // [E+1] pairs of expert e: elist[elist_off[e] .. elist_off[e+1])
-  int32_t* elist;           // [M*k] pair t*k+s, ascending within an expert
-  int32_t* hit;             // [hb] experts with at least one pair, ascending
-  int32_t* nhit;            // [1]
-  int hb;                   // min(E, M*k): bound of the hit list
-  int8_t* qh;               // [M*k + M*S][I] q8(h) per pair (shared expert: M*k + t)
+  int8_t* qh;               // [M*k + M*S][I] q8(h) per pair t*k+s (shared expert: M*k + t)
   float* dh;                // [M*k + M*S][I/32]
   int32_t* sh;              // [M*k + M*S][I/32]
+  float* o;                 // [M*k + M*S][H] expert outputs per pair
   int32_t* t_ids;           // optional copies of ids / w, or NULL
   float* t_w;
 };
 struct DecodeBatchGeometry {
   int router_threads;
-  int gu_lpr, gu_bpl, gu_fast, gu_threads, gu_alds;
+  int route_parts, route_threads;
+  size_t route_lds;
+  int gu_lpr, gu_bpl, gu_fast, gu_threads, gu_tb;
   size_t gu_lds;
-  int dn_lpr, dn_bpl, dn_fast, dn_rows, dn_threads;
+  int dn_lpr, dn_bpl, dn_fast, dn_rows, dn_threads, dn_tb;
   size_t dn_lds;
 };
 DecodeBatchGeometry decode_batch_geometry(int M, int H, int I, int E, int k, int has_shared);

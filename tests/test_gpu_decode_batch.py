@@ -94,6 +94,10 @@ def test_decode_batch_repeated_token(decode_layers):
     ("many_experts", 256, 1024, 64, 32, True, "zipf", 32),
     # every expert chosen by every token (k = E)
     ("k_equals_E", 256, 16, 128, 16, True, None, 32),
+    # H = 16384: x codes staged a few tokens at a time; 16 lanes per row
+    ("wide_hidden", 16384, 8, 64, 2, True, None, 32),
+    # I = 8192: q8(h) staged a few pairs at a time; 16 lanes per down row
+    ("wide_inter", 256, 16, 8192, 8, True, None, 32),
 ])
 def test_decode_batch_small(name, H, E, I, k, shared, bias, M):
     say("decode batch", name, "M=%d" % M)
