@@ -29,6 +29,8 @@ _lib = None
 
 BLK = 32
 Q4_BYTES = 18
+Q8W_BYTES = 34
+Q4_0, Q8_0 = 0, 1          # weight formats of a layer (``orc_layer.wfmt``)
 
 
 def build(out: str = _LIB, src: str = _SRC, extra: tuple = ()) -> str:
@@ -49,6 +51,7 @@ class Layer(C.Structure):
         ("w_router", C.c_void_p), ("bias", C.c_void_p),
         ("gate", C.c_void_p), ("up", C.c_void_p), ("down", C.c_void_p),
         ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p),
+        ("wfmt", C.c_int32),
     ]
 
 
@@ -73,6 +76,10 @@ def _declare(lib):
         "orc_q4_pack": (None, [P, I64, I64, P]),
         "orc_q4_dequant": (None, [P, I64, I64, P]),
         "orc_q8_quantize": (None, [P, I64, I64, P, P]),
+        "orc_q8w_row_bytes": (C.c_size_t, [I64]),
+        "orc_q8w_pack": (None, [P, I64, I64, P]),
+        "orc_q8w_dequant": (None, [P, I64, I64, P]),
+        "orc_w8a8_gemv": (None, [P, I64, I64, P, P, P, P]),
         "orc_exp_p": (F, [F]),
         "orc_silu_p": (F, [F]),
         "orc_router_logits": (None, [P, I64, I64, P, I64, P, P]),
@@ -190,6 +197,42 @@ def q4_dequant(packed, K: int, lib=None) -> np.ndarray:
     return out
 
 
+def q8w_row_bytes(K: int) -> int:
+    return (K // BLK) * Q8W_BYTES
+
+
+def q8w_pack(w, lib=None, threads: int = 1) -> np.ndarray:
+    """``orc_q8w_pack``: fp32 [..., rows, K] -> uint8 [..., rows, K/32*34] (Q8_0)."""
+    w = _c(w, np.float32)
+    K = w.shape[-1]
+    assert K % BLK == 0
+    rows = w.size // K
+    out = np.empty(w.shape[:-1] + (q8w_row_bytes(K),), dtype=np.uint8)
+    lib = lib or load()
+    w2, o2 = w.reshape(rows, K), out.reshape(rows, q8w_row_bytes(K))
+    if threads <= 1 or rows < 2 * threads:
+        lib.orc_q8w_pack(_p(w2), rows, K, _p(o2))
+        return out
+    from concurrent.futures import ThreadPoolExecutor
+    step = (rows + threads - 1) // threads
+    def job(r0):
+        r1 = min(rows, r0 + step)
+        lib.orc_q8w_pack(_p(w2[r0:r1]), r1 - r0, K, _p(o2[r0:r1]))
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(job, range(0, rows, step)))
+    return out
+
+
+def q8w_dequant(packed, K: int, lib=None) -> np.ndarray:
+    """``orc_q8w_dequant``: uint8 [..., rows, K/32*34] -> fp32 [..., rows, K]."""
+    packed = _c(packed, np.uint8)
+    rb = q8w_row_bytes(K)
+    rows = packed.size // rb
+    out = np.empty(packed.shape[:-1] + (K,), dtype=np.float32)
+    (lib or load()).orc_q8w_dequant(_p(packed), rows, K, _p(out))
+    return out
+
+
 def q8_quantize(x, lib=None):
     """``orc_q8_quantize``: fp32 [..., K] -> (int8 [..., K], fp32 [..., K/32])."""
     x = _c(x, np.float32)
@@ -247,12 +290,13 @@ def route_permutation(ids, E: int, lib=None):
 class PackedLayer:
     """Host copy of one packed layer, laid out as the oracle's ``orc_layer``.
 
-    gate/up: uint8 [E, I, H/32*18]; down: uint8 [E, H, I/32*18];
-    s_gate/s_up/s_down: the shared expert (single matrices) or None.
+    gate/up: uint8 [E, I, H/32*B]; down: uint8 [E, H, I/32*B] with B = 18
+    (Q4_0) or 34 (Q8_0, wfmt = Q8_0: decode only); s_gate/s_up/s_down: the
+    shared expert (single matrices) or None.
     """
 
     def __init__(self, w_router, bias, gate, up, down, s_gate=None, s_up=None,
-                 s_down=None, k=1):
+                 s_down=None, k=1, wfmt=Q4_0):
         self.w_router = _c(w_router, np.float32)
         self.bias = None if bias is None else _c(bias, np.float32)
         self.gate = _c(gate, np.uint8)
@@ -265,16 +309,20 @@ class PackedLayer:
         self.H, self.E = self.w_router.shape
         self.I = self.gate.shape[1]
         self.k = int(k)
-        assert self.gate.shape == (self.E, self.I, q4_row_bytes(self.H))
-        assert self.down.shape == (self.E, self.H, q4_row_bytes(self.I))
+        self.wfmt = int(wfmt)
+        rb = q8w_row_bytes if self.wfmt == Q8_0 else q4_row_bytes
+        assert self.gate.shape == (self.E, self.I, rb(self.H))
+        assert self.down.shape == (self.E, self.H, rb(self.I))
 
     @classmethod
     def from_float(cls, w_router, bias, gate, up, down, s_gate=None, s_up=None,
-                   s_down=None, k=1, lib=None, threads: int = 1):
-        """Pack fp32 expert weights with the oracle's own ``orc_q4_pack``."""
-        pk = lambda a: None if a is None else q4_pack(a, lib=lib, threads=threads)  # noqa: E731
+                   s_down=None, k=1, lib=None, threads: int = 1, wfmt=Q4_0):
+        """Pack fp32 expert weights with the oracle's own ``orc_q4_pack`` (or
+        ``orc_q8w_pack`` for wfmt = Q8_0)."""
+        pack = q8w_pack if wfmt == Q8_0 else q4_pack
+        pk = lambda a: None if a is None else pack(a, lib=lib, threads=threads)  # noqa: E731
         return cls(w_router, bias, pk(gate), pk(up), pk(down), pk(s_gate),
-                   pk(s_up), pk(s_down), k=k)
+                   pk(s_up), pk(s_down), k=k, wfmt=wfmt)
 
     def cstruct(self) -> Layer:
         L = Layer()
@@ -283,6 +331,7 @@ class PackedLayer:
         L.w_router, L.bias = _p(self.w_router), _p(self.bias)
         L.gate, L.up, L.down = _p(self.gate), _p(self.up), _p(self.down)
         L.s_gate, L.s_up, L.s_down = _p(self.s_gate), _p(self.s_up), _p(self.s_down)
+        L.wfmt = self.wfmt
         return L
 
 
@@ -298,6 +347,7 @@ def route(layer: PackedLayer, x, lib=None) -> dict:
 
 def prefill_ref(layer: PackedLayer, x, ids, w64, tokens=None, lib=None) -> np.ndarray:
     """``orc_prefill_ref``: binary64 y for the listed tokens -> [n, H] fp64."""
+    assert layer.wfmt == Q4_0, "the prefill reference is defined for Q4_0 layers"
     lib = lib or load()
     x = _c(x, np.float32)
     ids = _c(ids, np.int32)
@@ -323,6 +373,18 @@ def w4a8_gemv(W, K: int, qa, da, lib=None):
     dots = np.empty((N, K // BLK), dtype=np.int32)
     out = np.empty(N, dtype=np.float32)
     (lib or load()).orc_w4a8_gemv(_p(W), N, K, _p(qa), _p(da), _p(dots), _p(out))
+    return dots, out
+
+
+def w8a8_gemv(W, K: int, qa, da, lib=None):
+    """``orc_w8a8_gemv``: Q8_0 rows -> (dots int32 [N, K/32], out fp32 [N])."""
+    W = _c(W, np.uint8)
+    N = W.size // q8w_row_bytes(K)
+    qa = _c(qa, np.int8)
+    da = _c(da, np.float32)
+    dots = np.empty((N, K // BLK), dtype=np.int32)
+    out = np.empty(N, dtype=np.float32)
+    (lib or load()).orc_w8a8_gemv(_p(W), N, K, _p(qa), _p(da), _p(dots), _p(out))
     return dots, out
 
 

@@ -31,6 +31,9 @@
  *     q = clamp(roundf(w/d), -8, 7) + 8; 18 bytes = d (little endian) then 16
  *     bytes whose byte j holds q_j (low nibble) and q_{j+16} (high nibble).
  *   - 8-bit activations: per 32-block d = amax/127 (fp32), q = roundf(x/d).
+ *   - Q8_0 weight block (the 8-bit weights of [COMP], decode only): 32
+ *     consecutive K-elements; d = fp16(amax/127); q = clamp(roundf(w/d),
+ *     -127, 127); 34 bytes = d (little endian) then the 32 int8 codes.
  *   - Experts: SwiGLU FFN  down( silu(gate x) * (up x) ).
  *   - Router: logits = x . W_r (+ bias), top-k by (logit desc, index asc),
  *     weights = softmax over the k selected logits.  Optional always-on
@@ -51,6 +54,7 @@
 
 #define ORC_BLK 32          /* elements per quantisation block */
 #define ORC_Q4_BYTES 18     /* bytes per Q4_0 block            */
+#define ORC_Q8W_BYTES 34    /* bytes per Q8_0 weight block     */
 
 /* ------------------------------------------------------------------------ */
 /* IEEE-754 binary16 <-> binary32, written from the format definition.       */
@@ -196,6 +200,66 @@ void orc_q4_dequant(const uint8_t *packed, int64_t rows, int64_t K, float *out)
             float d = q4_scale(blk);
             for (int j = 0; j < ORC_BLK; j++)
                 out[r * K + b * ORC_BLK + j] = (float)(q4_code(blk, j) - 8) * d;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q8_0 weights [COMP abstract: 8-bit weights, against which 4-bit decode    */
+/* was measured slower on Fermi].  The page names 8-bit weights but no       */
+/* format; the plain reading, by analogy with Q4_0: per 32 elements          */
+/* d = fp16(amax/127), q = clamp(roundf(w/d), -127, 127), weight = q*d.      */
+/* The clamp only acts when d is an fp16 subnormal (relative rounding of d   */
+/* up to 1/2 ulp of 2^-24); for normal d, |w/d| <= 127*(1 + 2^-11) < 127.5.  */
+/* ------------------------------------------------------------------------ */
+
+size_t orc_q8w_row_bytes(int64_t K) { return (size_t)(K / ORC_BLK) * ORC_Q8W_BYTES; }
+
+/* w: [rows][K] fp32 row-major, K % 32 == 0.  out: rows * (K/32) * 34 bytes. */
+void orc_q8w_pack(const float *w, int64_t rows, int64_t K, uint8_t *out)
+{
+    int64_t nb = K / ORC_BLK;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *v = w + r * K + b * ORC_BLK;
+            float amax = 0.0f;
+            for (int j = 0; j < ORC_BLK; j++) {
+                float a = fabsf(v[j]);
+                if (a > amax) amax = a;
+            }
+            float d32 = amax / 127.0f;
+            uint16_t dh = orc_f32_to_f16(d32);
+            float df = orc_f16_to_f32(dh);
+            uint8_t *blk = out + (r * nb + b) * ORC_Q8W_BYTES;
+            blk[0] = (uint8_t)(dh & 0xffu);
+            blk[1] = (uint8_t)(dh >> 8);
+            for (int j = 0; j < ORC_BLK; j++) {
+                float t = (df == 0.0f) ? 0.0f : roundf(v[j] / df);   /* half away from zero */
+                if (t < -127.0f) t = -127.0f;
+                if (t > 127.0f) t = 127.0f;
+                blk[2 + j] = (uint8_t)(int8_t)(int)t;
+            }
+        }
+    }
+}
+
+static int q8w_code(const uint8_t *blk, int j) { return (int)(int8_t)blk[2 + j]; }
+
+static float q8w_scale(const uint8_t *blk)
+{
+    return orc_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+}
+
+/* Dequantised value q*d: an 8-bit integer times an 11-bit significand, exact
+ * in binary32 and binary64. */
+void orc_q8w_dequant(const uint8_t *packed, int64_t rows, int64_t K, float *out)
+{
+    int64_t nb = K / ORC_BLK;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *blk = packed + (r * nb + b) * ORC_Q8W_BYTES;
+            float d = q8w_scale(blk);
+            for (int j = 0; j < ORC_BLK; j++)
+                out[r * K + b * ORC_BLK + j] = (float)q8w_code(blk, j) * d;
         }
 }
 
@@ -373,11 +437,23 @@ typedef struct {
     const float *bias;              /* [E] or NULL */
     const uint8_t *gate, *up, *down;
     const uint8_t *s_gate, *s_up, *s_down;
+    int32_t wfmt;                   /* 0: Q4_0 (every path); 1: Q8_0 (decode only) */
 } orc_layer;
+
+static size_t layer_row_bytes(const orc_layer *L, int64_t K)
+{
+    return L->wfmt ? orc_q8w_row_bytes(K) : orc_q4_row_bytes(K);
+}
 
 static const uint8_t *expert_mat(const uint8_t *base, int64_t e, int64_t rows, int64_t K)
 {
     return base + (size_t)e * (size_t)rows * orc_q4_row_bytes(K);
+}
+
+static const uint8_t *layer_expert_mat(const orc_layer *L, const uint8_t *base, int64_t e,
+                                       int64_t rows, int64_t K)
+{
+    return base + (size_t)e * (size_t)rows * layer_row_bytes(L, K);
 }
 
 /* binary64 dot of one dequantised Q4 row with a binary64 vector. */
@@ -462,6 +538,46 @@ static float w4a8_row(const uint8_t *row, int64_t K, const int8_t *qa,
     return tree_sum(buf, (size_t)nb);
 }
 
+/* One Q8_0 row against int8 activations (W8A8): the W4A8 program with the
+ * signed codes in place of q - 8.  Block b:
+ *   dot_b = sum_j q_w[j] * q_a[j]               exact integer, |dot_b| <= 516128
+ *   p_b   = (d_w[b] * d_a[b]) * (float)dot_b    two fp32 multiplies
+ * row value = tree_sum(p_0 .. p_{nb-1}). */
+static float w8a8_row(const uint8_t *row, int64_t K, const int8_t *qa,
+                      const float *da, int32_t *dots, float *buf)
+{
+    int64_t nb = K / ORC_BLK;
+    for (int64_t b = 0; b < nb; b++) {
+        const uint8_t *blk = row + b * ORC_Q8W_BYTES;
+        int32_t dot = 0;
+        for (int j = 0; j < ORC_BLK; j++)
+            dot += (int32_t)q8w_code(blk, j) * (int32_t)qa[b * ORC_BLK + j];
+        if (dots) dots[b] = dot;
+        float s = q8w_scale(blk) * da[b];
+        buf[b] = s * (float)dot;
+    }
+    return tree_sum(buf, (size_t)nb);
+}
+
+/* W: [N] Q8_0 rows of K/32 blocks; as orc_w4a8_gemv. */
+void orc_w8a8_gemv(const uint8_t *W, int64_t N, int64_t K, const int8_t *qa,
+                   const float *da, int32_t *dots, float *out)
+{
+    int64_t nb = K / ORC_BLK;
+    float *buf = (float *)malloc(next_pow2((size_t)nb) * sizeof(float));
+    for (int64_t r = 0; r < N; r++)
+        out[r] = w8a8_row(W + r * orc_q8w_row_bytes(K), K, qa, da,
+                          dots ? dots + r * nb : NULL, buf);
+    free(buf);
+}
+
+/* The decode row program of the layer's weight format. */
+static float layer_row(const orc_layer *L, const uint8_t *row, int64_t K, const int8_t *qa,
+                       const float *da, float *buf)
+{
+    return L->wfmt ? w8a8_row(row, K, qa, da, NULL, buf) : w4a8_row(row, K, qa, da, NULL, buf);
+}
+
 /* W: [N] rows of K/32 blocks; qa [K], da [K/32]; dots [N][K/32] or NULL;
  * out [N]. */
 void orc_w4a8_gemv(const uint8_t *W, int64_t N, int64_t K, const int8_t *qa,
@@ -489,7 +605,8 @@ typedef struct {
     float *o;             /* [k+S][H]              */
 } orc_decode_trace;
 
-/* One decode step (fp32 program, the target of bit-exact comparison):
+/* One decode step (fp32 program, the target of bit-exact comparison); with
+ * Q8_0 weights (wfmt = 1) every row program below is w8a8_row:
  *   logits, ids, w      router_logit + orc_topk (fp32 weights)
  *   qx, dx = q8(x)
  *   per slot expert (and the shared one):
@@ -522,20 +639,20 @@ void orc_decode(const orc_layer *L, const float *x, float *y, orc_decode_trace *
     for (int32_t s = 0; s < k + S; s++) {
         const uint8_t *G, *U, *D;
         if (s < k) {
-            G = expert_mat(L->gate, ids[s], I, H);
-            U = expert_mat(L->up, ids[s], I, H);
-            D = expert_mat(L->down, ids[s], H, I);
+            G = layer_expert_mat(L, L->gate, ids[s], I, H);
+            U = layer_expert_mat(L, L->up, ids[s], I, H);
+            D = layer_expert_mat(L, L->down, ids[s], H, I);
         } else {
             G = L->s_gate; U = L->s_up; D = L->s_down;
         }
         for (int64_t i = 0; i < I; i++) {
-            g[i] = w4a8_row(G + i * orc_q4_row_bytes(H), H, qx, dx, NULL, buf);
-            u[i] = w4a8_row(U + i * orc_q4_row_bytes(H), H, qx, dx, NULL, buf);
+            g[i] = layer_row(L, G + i * layer_row_bytes(L, H), H, qx, dx, buf);
+            u[i] = layer_row(L, U + i * layer_row_bytes(L, H), H, qx, dx, buf);
             h[i] = orc_silu_p(g[i]) * u[i];
         }
         orc_q8_quantize(h, 1, I, qh, dh);
         for (int64_t r = 0; r < H; r++)
-            o[s * H + r] = w4a8_row(D + r * orc_q4_row_bytes(I), I, qh, dh, NULL, buf);
+            o[s * H + r] = layer_row(L, D + r * layer_row_bytes(L, I), I, qh, dh, buf);
         if (tr) {
             if (tr->gate) memcpy(tr->gate + s * I, g, (size_t)I * sizeof(float));
             if (tr->up) memcpy(tr->up + s * I, u, (size_t)I * sizeof(float));

@@ -178,3 +178,57 @@ def test_q8_round_half_away():
     q, d = oracle.q8_quantize(x.reshape(1, 32))
     assert d[0, 0] == 1.0
     assert list(q[0, 1:9]) == [1, 2, 3, 4, -1, -2, -3, -4]
+
+
+# ---------------------------------------------------------------- Q8_0 weights
+def _golden_q8w_block(g, tag):
+    if tag + "_w_dec" in g:
+        w = np.array([float(u) for u in g[tag + "_w_dec"]], dtype=np.float32)
+    else:
+        unit = 2.0 ** int(g[tag + "_unit_log2"][0])
+        w = np.array([float(u) * unit for u in g[tag + "_w_units"]], dtype=np.float32)
+    assert w.size == 32
+    exp = bytes(int(b, 16) for b in g[tag + "_bytes"])
+    assert len(exp) == 34
+    return w, exp
+
+
+@pytest.mark.parametrize("tag", ["A", "B", "C", "D", "E"])
+def test_q8w_golden_blocks(tag):
+    w, exp = _golden_q8w_block(read_golden("q8w_blocks.txt"), tag)
+    got = oracle.q8w_pack(w.reshape(1, 32)).tobytes()
+    assert got == exp, (got.hex(), exp.hex())
+
+
+def test_q8w_grid_roundtrip_lossless():
+    # w = q*d with d a power of two (exact in fp16) and |q| = 127 in every
+    # block: packing returns q and d, dequantising returns w exactly
+    rng = np.random.default_rng(11)
+    rows, K = 48, 256
+    nb = K // 32
+    q = rng.integers(-127, 128, size=(rows, nb, 32))
+    q[:, :, 5] = rng.choice([-127, 127], size=(rows, nb))
+    d = 2.0 ** rng.integers(-14, -2, size=(rows, nb, 1))
+    w = (q * d).reshape(rows, K).astype(np.float32)
+    packed = oracle.q8w_pack(w).reshape(rows, nb, 34)
+    codes = packed[:, :, 2:].view(np.int8)
+    scale = packed[:, :, :2].copy().view(np.float16).astype(np.float64)[:, :, 0]
+    assert np.array_equal(codes, q)
+    assert np.array_equal(scale, d[:, :, 0])
+    assert np.array_equal(oracle.q8w_dequant(packed.reshape(rows, -1), K), w)
+
+
+def test_q8w_rounding_error_bound():
+    # normal-range d: |w - q d| <= d / 2, and the block's largest |w| maps to
+    # +-127 (|w/d| <= 127 (1 + 2^-11) < 127.5, so the clamp never acts)
+    rng = np.random.default_rng(12)
+    rows, K = 64, 512
+    w = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    packed = oracle.q8w_pack(w).reshape(rows, K // 32, 34)
+    d = packed[:, :, :2].copy().view(np.float16).astype(np.float64)[:, :, :1]
+    q = packed[:, :, 2:].view(np.int8).astype(np.float64)
+    wb = w.astype(np.float64).reshape(rows, K // 32, 32)
+    assert np.all(np.abs(wb - q * d) <= d / 2 * (1 + 1e-6))
+    top = np.argmax(np.abs(wb), axis=2)
+    qt = np.take_along_axis(q, top[:, :, None], axis=2)[:, :, 0]
+    assert np.all(np.abs(qt) == 127)

@@ -229,3 +229,78 @@ def test_rmsnorm_vs_binary64():
     assert np.allclose(out, ref, rtol=2e-6, atol=0)
     c = np.full((1, 64), 3.0, np.float32)
     assert np.allclose(oracle.rmsnorm(c, 0.0), 1.0, rtol=1e-7)
+
+
+# ---------------------------------------------------------------- Q8_0 weights (W8A8 decode)
+@pytest.mark.parametrize("N,K", [(7, 64), (33, 512)])
+def test_w8a8_block_dots_are_integer_dots(N, K):
+    rng = np.random.default_rng(N * K)
+    nb = K // 32
+    q = rng.integers(-127, 128, size=(N, nb, 32))
+    q[:, :, 0] = 127
+    d = 2.0 ** rng.integers(-10, -4, size=(N, nb, 1))
+    W = oracle.q8w_pack((q * d).reshape(N, K).astype(np.float32))
+    x, qa = _int_activation(rng, K)
+    qx, dx = oracle.q8_quantize(x.reshape(1, K))
+    dots, out = oracle.w8a8_gemv(W, K, qx[0], dx[0])
+    assert np.array_equal(dots, (q * qa.reshape(nb, 32)).sum(axis=2))
+    ideal = (d[:, :, 0] * 2.0 ** -5 * dots).sum(axis=1)
+    mag = np.abs(d[:, :, 0] * 2.0 ** -5 * dots).sum(axis=1)
+    assert np.all(np.abs(out.astype(np.float64) - ideal) <= 1e-6 * mag + 1e-30)
+
+
+def _tiny_q8_layer(shared=True, E=8, k=2, H=256, I=128):
+    cfg = moe_synth.CONFIGS["tiny"].with_(E=E, k=k, H=H, I=I, shared=shared)
+    W = moe_synth.expert_weights(cfg)
+    Wr = moe_synth.router(cfg)
+    return cfg, oracle.PackedLayer.from_float(Wr, None, W["gate"], W["up"], W["down"],
+                                              W["s_gate"], W["s_up"], W["s_down"], k=k,
+                                              wfmt=oracle.Q8_0), W
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_decode_q8w_trace_vs_binary64(shared):
+    cfg, L, _ = _tiny_q8_layer(shared)
+    H, I = cfg.H, cfg.I
+    x = moe_synth.tokens(cfg, step=4, T=1)[0]
+    y, tr = oracle.decode(L, x, trace=True)
+    experts = list(tr["ids"]) + (["s"] if shared else [])
+    xq = (tr["qx"].astype(np.float64).reshape(-1, 32) * tr["dx"][:, None]).ravel()
+    y64 = np.zeros(H)
+    ybound = np.zeros(H)
+    w = list(tr["w"]) + ([1.0] if shared else [])
+    for s, e in enumerate(experts):
+        G = L.s_gate if e == "s" else L.gate[e]
+        Um = L.s_up if e == "s" else L.up[e]
+        D = L.s_down if e == "s" else L.down[e]
+        Gd, Ud, Dd = (oracle.q8w_dequant(M, K).astype(np.float64) for M, K in ((G, H), (Um, H), (D, I)))
+        assert np.all(np.abs(tr["gate"][s] - Gd @ xq) <= 1e-6 * (np.abs(Gd) @ np.abs(xq)) + 1e-30)
+        assert np.all(np.abs(tr["up"][s] - Ud @ xq) <= 1e-6 * (np.abs(Ud) @ np.abs(xq)) + 1e-30)
+        hq = (tr["qh"][s].astype(np.float64).reshape(-1, 32) * tr["dh"][s][:, None]).ravel()
+        o64 = Dd @ hq
+        assert np.all(np.abs(tr["o"][s] - o64) <= 1e-6 * (np.abs(Dd) @ np.abs(hq)) + 1e-30)
+        y64 += w[s] * o64
+        ybound += abs(w[s]) * (np.abs(Dd) @ np.abs(hq))
+    assert np.all(np.abs(y - y64) <= 1e-5 * ybound + 1e-30)
+
+
+def test_decode_q8w_closer_to_float_than_q4():
+    # 8-bit weights: the decode output sits closer to the unquantised layer's
+    # binary64 FFN than the 4-bit decode does (same int8 activations)
+    cfg, L8, W = _tiny_q8_layer(True)
+    L4 = oracle.PackedLayer.from_float(L8.w_router, None, W["gate"], W["up"], W["down"],
+                                       W["s_gate"], W["s_up"], W["s_down"], k=cfg.k)
+    e4, e8 = [], []
+    for step in range(4):
+        x = moe_synth.tokens(cfg, step=20 + step, T=1)[0]
+        r = oracle.route(L8, x[None])
+        ref = np.zeros(cfg.H)
+        xd = x.astype(np.float64)
+        experts = [(W["gate"][e], W["up"][e], W["down"][e], float(wv)) for e, wv in zip(r["ids"][0], r["w64"][0])]
+        experts.append((W["s_gate"], W["s_up"], W["s_down"], 1.0))
+        for G, U, D, wv in experts:
+            g, u = G.astype(np.float64) @ xd, U.astype(np.float64) @ xd
+            ref += wv * (D.astype(np.float64) @ (g / (1 + np.exp(-g)) * u))
+        e4.append(np.linalg.norm(oracle.decode(L4, x) - ref) / np.linalg.norm(ref))
+        e8.append(np.linalg.norm(oracle.decode(L8, x) - ref) / np.linalg.norm(ref))
+    assert max(e8) < min(e4), (e8, e4)

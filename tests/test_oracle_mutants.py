@@ -52,8 +52,17 @@ MUTANTS = [
     ("prefill_weight_dropped", "for (int64_t h = 0; h < H; h++) yt[h] += w64[t * L->k + s] * o[h];",
      "for (int64_t h = 0; h < H; h++) yt[h] += o[h];"),
     ("decode_shared_dropped", "if (S) acc = acc + o[k * H + r];", ";"),
-    ("decode_up_for_gate", "g[i] = w4a8_row(G + i * orc_q4_row_bytes(H), H, qx, dx, NULL, buf);",
-     "g[i] = w4a8_row(U + i * orc_q4_row_bytes(H), H, qx, dx, NULL, buf);"),
+    ("decode_up_for_gate", "g[i] = layer_row(L, G + i * layer_row_bytes(L, H), H, qx, dx, buf);",
+     "g[i] = layer_row(L, U + i * layer_row_bytes(L, H), H, qx, dx, buf);"),
+    ("q8w_scale_128", "float d32 = amax / 127.0f;", "float d32 = amax / 128.0f;"),
+    ("q8w_round_even", "float t = (df == 0.0f) ? 0.0f : roundf(v[j] / df);",
+     "float t = (df == 0.0f) ? 0.0f : rintf(v[j] / df);"),
+    ("q8w_no_clamp_high", "if (t > 127.0f) t = 127.0f;", ";"),
+    ("w8a8_offset_8", "dot += (int32_t)q8w_code(blk, j) * (int32_t)qa[b * ORC_BLK + j];",
+     "dot += (int32_t)(q8w_code(blk, j) - 8) * (int32_t)qa[b * ORC_BLK + j];"),
+    ("w8a8_act_scale_dropped", "float s = q8w_scale(blk) * da[b];", "float s = q8w_scale(blk);"),
+    ("decode_q8_read_as_q4", "return L->wfmt ? w8a8_row(row, K, qa, da, NULL, buf) : w4a8_row(row, K, qa, da, NULL, buf);",
+     "return w4a8_row(row, K, qa, da, NULL, buf);"),
     ("rmsnorm_mean_h_minus_1", "float r = sqrtf(ss / (float)H + eps);",
      "float r = sqrtf(ss / (float)(H - 1) + eps);"),
 ]
