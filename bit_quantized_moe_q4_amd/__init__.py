@@ -21,7 +21,7 @@ import torch
 from . import _lib
 
 __all__ = [
-    "q4_packed_bytes", "q4_pack", "q4_tile", "q8_quantize", "MoELayer", "Routing",
+    "q4_packed_bytes", "q4_pack", "q4_tile", "q8w_pack", "q8_quantize", "MoELayer", "Routing",
     "moe_q4_route_workspace_bytes", "moe_q4_route",
     "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage",
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
@@ -68,6 +68,17 @@ def q4_pack(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> to
     return out
 
 
+def q8w_pack(w: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fp32 [..., rows, K] device tensor -> uint8 [..., rows, K/32*34] Q8_0 blocks."""
+    _dev(w, "w")
+    K = w.shape[-1]
+    rows = w.numel() // K
+    if out is None:
+        out = torch.empty(w.shape[:-1] + (K // 32 * 34,), dtype=torch.uint8, device=w.device)
+    _lib.check(_lib.lib().q8w_pack(_p(w), rows, K, _p(out), _s(stream)), "q8w_pack")
+    return out
+
+
 def q4_tile(q4: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """uint8 [..., rows, K/32*18] Q4_0 blocks -> the same blocks in grouped-GEMM
     tile order (q4_tile in moe_q4.h); rows % 32 == 0, K % 64 == 0."""
@@ -101,11 +112,13 @@ class MoELayer:
     s_gate/s_up uint8 [I, H/32*18], s_down uint8 [H, I/32*18].
     With `tiles` (the default) and H, I multiples of 64 the layer also keeps
     the matrices in grouped-GEMM tile order (q4_tile), which moe_q4_prefill's
-    fused GEMM reads; that doubles the resident weight bytes.
+    fused GEMM reads; that doubles the resident weight bytes.  wfmt="q8":
+    the matrices are Q8_0 blocks (34 bytes per 32 weights; routing and decode
+    only, no tiles).
     """
 
     def __init__(self, w_router, gate, up, down, top_k, router_bias=None,
-                 s_gate=None, s_up=None, s_down=None, tiles=True, stream=None):
+                 s_gate=None, s_up=None, s_down=None, tiles=True, stream=None, wfmt="q4"):
         for n, t in (("w_router", w_router), ("gate", gate), ("up", up), ("down", down),
                      ("router_bias", router_bias), ("s_gate", s_gate), ("s_up", s_up),
                      ("s_down", s_down)):
@@ -123,8 +136,12 @@ class MoELayer:
         st.w_router, st.router_bias = _p(w_router), _p(router_bias)
         st.w_gate, st.w_up, st.w_down = _p(gate), _p(up), _p(down)
         st.s_gate, st.s_up, st.s_down = _p(s_gate), _p(s_up), _p(s_down)
+        if wfmt not in ("q4", "q8"):
+            raise ValueError("wfmt must be 'q4' or 'q8'")
+        self.wfmt = wfmt
+        st.weight_format = _lib.WEIGHTS_Q8_0 if wfmt == "q8" else _lib.WEIGHTS_Q4_0
         self.tiles = None
-        if tiles and self.hidden % 64 == 0 and self.inter % 64 == 0:
+        if tiles and wfmt == "q4" and self.hidden % 64 == 0 and self.inter % 64 == 0:
             tl = lambda t: None if t is None else q4_tile(t, stream=stream)  # noqa: E731
             self.tiles = dict(gate=tl(gate), up=tl(up), down=tl(down),
                               s_gate=tl(s_gate), s_up=tl(s_up), s_down=tl(s_down))
@@ -135,11 +152,12 @@ class MoELayer:
 
     @classmethod
     def from_float(cls, w_router, gate, up, down, top_k, router_bias=None,
-                   s_gate=None, s_up=None, s_down=None, tiles=True, stream=None):
-        """Pack fp32 device weights with the library's q4_pack kernel."""
-        pk = lambda t: None if t is None else q4_pack(t, stream=stream)  # noqa: E731
+                   s_gate=None, s_up=None, s_down=None, tiles=True, stream=None, wfmt="q4"):
+        """Pack fp32 device weights with the library's q4_pack (or q8w_pack) kernel."""
+        pack = q8w_pack if wfmt == "q8" else q4_pack
+        pk = lambda t: None if t is None else pack(t, stream=stream)  # noqa: E731
         return cls(w_router, pk(gate), pk(up), pk(down), top_k, router_bias,
-                   pk(s_gate), pk(s_up), pk(s_down), tiles=tiles, stream=stream)
+                   pk(s_gate), pk(s_up), pk(s_down), tiles=tiles, stream=stream, wfmt=wfmt)
 
     def struct_ptr(self):
         return C.byref(self._c)

@@ -25,6 +25,9 @@ EXPORTS = [
 ]
 
 
+WEIGHTS_Q4_0, WEIGHTS_Q8_0 = 0, 1
+
+
 class Layer(C.Structure):
     _fields_ = [
         ("hidden", C.c_int32), ("inter", C.c_int32), ("n_experts", C.c_int32),
@@ -34,6 +37,7 @@ class Layer(C.Structure):
         ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p),
         ("t_gate", C.c_void_p), ("t_up", C.c_void_p), ("t_down", C.c_void_p),
         ("ts_gate", C.c_void_p), ("ts_up", C.c_void_p), ("ts_down", C.c_void_p),
+        ("weight_format", C.c_int32),
     ]
 
 
@@ -61,6 +65,8 @@ def _declare(lib):
         "q4_packed_bytes": (SZ, [I64, I64]),
         "q4_pack": (C.c_int, [P, I64, I64, P, P]),
         "q4_tile": (C.c_int, [P, I64, I64, P, P]),
+        "q8w_packed_bytes": (SZ, [I64, I64]),
+        "q8w_pack": (C.c_int, [P, I64, I64, P, P]),
         "q8_quantize": (C.c_int, [P, I64, I64, P, P, P]),
         "moe_q4_route_workspace_bytes": (SZ, [P, I32]),
         "moe_q4_route": (C.c_int, [P, P, I32, I32, P, P, P, SZ, P]),

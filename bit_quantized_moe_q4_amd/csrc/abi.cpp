@@ -54,7 +54,11 @@ int check_layer(const moe_q4_layer* L) {
     return fail(MOE_Q4_EINVAL, "layer pointers must be 16-byte aligned (router_bias 4-byte)");
   if (L->has_shared && (!aligned(L->s_gate, 16) || !aligned(L->s_up, 16) || !aligned(L->s_down, 16)))
     return fail(MOE_Q4_EINVAL, "shared expert pointers must be 16-byte aligned");
+  if (L->weight_format != MOE_Q4_WEIGHTS_Q4_0 && L->weight_format != MOE_Q4_WEIGHTS_Q8_0)
+    return fail(MOE_Q4_EINVAL, "weight_format=%d must be MOE_Q4_WEIGHTS_Q4_0 or _Q8_0", L->weight_format);
   const bool any_t = L->t_gate || L->t_up || L->t_down || L->ts_gate || L->ts_up || L->ts_down;
+  if (any_t && L->weight_format != MOE_Q4_WEIGHTS_Q4_0)
+    return fail(MOE_Q4_EINVAL, "tile-order matrices exist only for Q4_0 weights");
   if (any_t) {
     const bool routed = L->t_gate && L->t_up && L->t_down;
     const bool shared = L->has_shared ? (L->ts_gate && L->ts_up && L->ts_down)
@@ -172,6 +176,21 @@ int q4_pack(const float* w, int64_t rows, int64_t K, void* packed, hipStream_t s
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "q4_pack");
 }
 
+size_t q8w_packed_bytes(int64_t rows, int64_t K) {
+  if (rows < 0 || K <= 0 || K % 32) return 0;
+  return (size_t)rows * (size_t)(K / 32) * 34;
+}
+
+int q8w_pack(const float* w, int64_t rows, int64_t K, void* packed, hipStream_t stream) {
+  if (rows < 0 || K <= 0 || K % 32) return fail(MOE_Q4_EINVAL, "q8w_pack: rows=%lld K=%lld (K %% 32 == 0)", (long long)rows, (long long)K);
+  if (rows == 0) return MOE_Q4_OK;
+  if (!w || !packed) return fail(MOE_Q4_EINVAL, "q8w_pack: NULL pointer");
+  if (!aligned(w, 16) || !aligned(packed, 2)) return fail(MOE_Q4_EINVAL, "q8w_pack: w must be 16-byte and packed 2-byte aligned");
+  if (rows * (K / 32) > ((int64_t)1 << 40)) return fail(MOE_Q4_EINVAL, "q8w_pack: too many blocks");
+  hipError_t e = moeq4::launch_q8w_pack(w, rows, K, packed, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "q8w_pack");
+}
+
 int q4_tile(const void* q4, int64_t rows, int64_t K, void* tiled, hipStream_t stream) {
   if (rows < 0 || rows % 32 || K <= 0 || K % 64)
     return fail(MOE_Q4_EINVAL, "q4_tile: rows=%lld K=%lld (rows %% 32 == 0, K %% 64 == 0)", (long long)rows, (long long)K);
@@ -260,6 +279,8 @@ int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t 
   if (rc) return rc;
   if (T < 0) return fail(MOE_Q4_EINVAL, "moe_q4_prefill: T=%d < 0", T);
   if ((int64_t)T * L->top_k > 0x7fffffff) return fail(MOE_Q4_EINVAL, "moe_q4_prefill: T*k exceeds int32");
+  if (L->weight_format != MOE_Q4_WEIGHTS_Q4_0)
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill: the grouped GEMM takes Q4_0 weights (weight_format=%d)", L->weight_format);
   if (T == 0) return MOE_Q4_OK;
   if (!x_bf16 || !routing || !y || !routing->topk_w || !routing->expert_offsets || !routing->perm ||
       !routing->inv_perm)
@@ -328,6 +349,7 @@ int moe_q4_decode_batch(const moe_q4_layer* L, const float* x, int32_t M, float*
   a.E = L->n_experts;
   a.k = L->top_k;
   a.has_shared = L->has_shared;
+  a.wfmt = L->weight_format;
   a.w_router = L->w_router;
   a.bias = L->router_bias;
   a.w_gate = static_cast<const uint8_t*>(L->w_gate);
@@ -377,6 +399,7 @@ int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_
   a.E = L->n_experts;
   a.k = L->top_k;
   a.has_shared = L->has_shared;
+  a.wfmt = L->weight_format;
   a.w_router = L->w_router;
   a.bias = L->router_bias;
   a.w_gate = static_cast<const uint8_t*>(L->w_gate);

@@ -195,7 +195,7 @@ __device__ void decode_gu_prologue(const DecodeArgs& a, const GuLds& l, int P, b
   __syncthreads();
 }
 
-template <int BPL, bool FAST>
+template <int BPL, bool FAST, int FMT>
 __global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int lpr, int P) {
   extern __shared__ __align__(16) uint8_t dyn[];
   const int H = a.H, I = a.I, nbh = H / BLK;
@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int l
   const int row = tid / lpr, lr = tid % lpr;
   const bool is_up = row >= DGU_ROWS;
   const int i = i0 + (row % DGU_ROWS);
-  const size_t rb = (size_t)nbh * Q4B;
+  const size_t rb = (size_t)nbh * WFmt<FMT>::bytes;
   const uint8_t* base;
   if (slot < a.k) {                      // (clamped: a NaN logit leaves ranks unfilled)
     const int e = min(max(ids_l[slot], 0), a.E - 1);
@@ -230,7 +230,7 @@ __global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int l
     A.s = l.sa[b];
     return A;
   };
-  float v = w4a8_lane<BPL, FAST>(base, nbh, lr * BPL, act, nullptr);
+  float v = wxa8_lane<BPL, FAST, FMT>(base, nbh, lr * BPL, act, nullptr);
   v = wave_tree_sum(v, lpr);
   if (lr == 0) val[row] = v;
   __syncthreads();
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int l
 // ---------------------------------------------------------------- down + combine
 // Block: `rows` output rows x ns slots, LPR lanes per (row, slot).  ALDS:
 // every slot's q8(h) staged in LDS; otherwise read from the workspace.
-template <int BPL, bool FAST, bool ALDS>
+template <int BPL, bool FAST, bool ALDS, int FMT>
 __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr, int rows) {
   extern __shared__ __align__(16) uint8_t dyn[];
   const int H = a.H, I = a.I, nbi = I / BLK;
@@ -292,16 +292,17 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
   const int rl = item / ns, slot = item % ns;
   const int r = r0 + rl;
   const bool live = rl < rows && r < H;
-  const size_t rb = (size_t)nbi * Q4B;
+  constexpr int QB = WFmt<FMT>::bytes;
+  const size_t rb = (size_t)nbi * QB;
   const uint8_t* base = nullptr;
   if (live)
     base = (slot < a.k) ? a.w_down + ((size_t)min(max(a.ids[slot], 0), a.E - 1) * H + r) * rb
                         : a.s_down + (size_t)r * rb;
   // this lane's weight span into registers (fast shapes)
-  constexpr int NV = FAST ? 18 * BPL / 16 : 1;
+  constexpr int NV = FAST ? QB * BPL / 16 : 1;
   uint32_t D[4 * NV + 1] = {};
   if (FAST && live && lr * BPL < nbi) {
-    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * Q4B);
+    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * QB);
 #pragma unroll
     for (int v = 0; v < NV; v++) {
       const uint4 t = src[v];
@@ -334,8 +335,8 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
       A.s = ALDS ? sh_l[slot * nbi + b] : a.sh[slot * nbi + b];
       return A;
     };
-    if constexpr (FAST) v = w4a8_regs<BPL>(D, nbi, lr * BPL, act);
-    else v = w4a8_lane<BPL, false>(base, nbi, lr * BPL, act, nullptr);
+    if constexpr (FAST) v = wxa8_regs<BPL, FMT>(D, nbi, lr * BPL, act);
+    else v = wxa8_lane<BPL, false, FMT>(base, nbi, lr * BPL, act, nullptr);
   }
   v = wave_tree_sum(v, lpr);
   if (live && lr == 0) o_l[rl * ns + slot] = v;
@@ -384,19 +385,16 @@ DecodeGeometry decode_geometry(int H, int I, int E, int k, int has_shared) {
   return g;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  const DecodeGeometry g = decode_geometry(a.H, a.I, a.E, a.k, a.has_shared);
-  const int nc = a.H / BLK;
-  hipLaunchKernelGGL(decode_router_kernel, dim3(nc), dim3(g.router_threads), 0, stream, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
+// gate/up and down launches for one weight format
+template <int FMT>
+hipError_t launch_decode_experts(const DecodeArgs& a, const DecodeGeometry& g, hipStream_t stream) {
+  hipError_t err = hipSuccess;
   const int ns = a.k + (a.has_shared ? 1 : 0);
   {
     dim3 grid(a.I / DGU_ROWS * ns);
     dim3 block(g.gu_threads);
 #define MOEQ4_GU(B, F) \
-  hipLaunchKernelGGL((decode_gateup_kernel<B, F>), grid, block, g.gu_lds, stream, a, g.gu_lpr, g.gu_parts)
+  hipLaunchKernelGGL((decode_gateup_kernel<B, F, FMT>), grid, block, g.gu_lds, stream, a, g.gu_lpr, g.gu_parts)
     if (g.gu_fast) {
       if (g.gu_bpl == 8) MOEQ4_GU(8, true);
       else if (g.gu_bpl == 16) MOEQ4_GU(16, true);
@@ -419,10 +417,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 #define MOEQ4_DN(B, F)                                                                     \
   do {                                                                                     \
     if (g.dn_act_lds)                                                                      \
-      hipLaunchKernelGGL((decode_down_kernel<B, F, true>), grid, block, g.dn_lds, stream, a, \
+      hipLaunchKernelGGL((decode_down_kernel<B, F, true, FMT>), grid, block, g.dn_lds, stream, a, \
                          g.dn_lpr, g.dn_rows);                                            \
     else                                                                                   \
-      hipLaunchKernelGGL((decode_down_kernel<B, F, false>), grid, block, g.dn_lds, stream, a, \
+      hipLaunchKernelGGL((decode_down_kernel<B, F, false, FMT>), grid, block, g.dn_lds, stream, a, \
                          g.dn_lpr, g.dn_rows);                                            \
   } while (0)
     if (g.dn_fast) {
@@ -441,6 +439,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     err = hipGetLastError();
   }
   return err;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  const DecodeGeometry g = decode_geometry(a.H, a.I, a.E, a.k, a.has_shared);
+  const int nc = a.H / BLK;
+  hipLaunchKernelGGL(decode_router_kernel, dim3(nc), dim3(g.router_threads), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return a.wfmt == kQ8 ? launch_decode_experts<kQ8>(a, g, stream) : launch_decode_experts<kQ4>(a, g, stream);
 }
 
 // ---------------------------------------------------------------- test GEMV

@@ -151,7 +151,7 @@ constexpr int DBG_ROWS = 32;
 
 // tb: tokens whose codes fit the block's LDS at once; the expert's tokens are
 // taken tb at a time.
-template <int BPL, bool FAST>
+template <int BPL, bool FAST, int FMT>
 __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, int lpr, int tb) {
   extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ int pairs_l[kDecodeBatchMax];
@@ -170,13 +170,14 @@ __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, 
   const int row = tid / lpr, lr = tid % lpr;
   const bool is_up = row >= DBG_ROWS;
   const int i = i0 + (row % DBG_ROWS);
-  const size_t rb = (size_t)nbh * Q4B;
+  constexpr int QB = WFmt<FMT>::bytes;
+  const size_t rb = (size_t)nbh * QB;
   const uint8_t* base = shared ? (is_up ? a.s_up : a.s_gate) + (size_t)i * rb
                                : (is_up ? a.w_up : a.w_gate) + ((size_t)e * I + i) * rb;
-  constexpr int NV = FAST ? 18 * BPL / 16 : 1;
+  constexpr int NV = FAST ? QB * BPL / 16 : 1;
   uint32_t D[4 * NV + 1] = {};
   if (FAST && lr * BPL < nbh) {
-    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * Q4B);
+    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * QB);
 #pragma unroll
     for (int v = 0; v < NV; v++) {
       const uint4 q = src[v];
@@ -208,8 +209,8 @@ __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, 
         return A;
       };
       float v;
-      if constexpr (FAST) v = w4a8_regs<BPL>(D, nbh, lr * BPL, act);
-      else v = w4a8_lane<BPL, false>(base, nbh, lr * BPL, act, nullptr);
+      if constexpr (FAST) v = wxa8_regs<BPL, FMT>(D, nbh, lr * BPL, act);
+      else v = wxa8_lane<BPL, false, FMT>(base, nbh, lr * BPL, act, nullptr);
       v = wave_tree_sum(v, lpr);
       if (lr == 0) val[row * M + u0 + u] = v;
     }
@@ -239,7 +240,7 @@ __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, 
 // ---------------------------------------------------------------- down
 // Block: `rows` (<= 128) output rows of one expert, lpr lanes per row, the
 // rows' weights in registers over the expert's pairs; o[pair][r] fp32.
-template <int BPL, bool FAST>
+template <int BPL, bool FAST, int FMT>
 __global__ void __launch_bounds__(1024) dbatch_down_kernel(DecodeBatchArgs a, int lpr, int tb, int rows) {
   extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ int pairs_l[kDecodeBatchMax];
@@ -256,13 +257,14 @@ __global__ void __launch_bounds__(1024) dbatch_down_kernel(DecodeBatchArgs a, in
   if (n == 0) return;                     // uniform over the block
   const int rl = tid / lpr, lr = tid % lpr, r = r0 + rl;
   const bool live = rl < rows && r < H;
-  const size_t rb = (size_t)nbi * Q4B;
+  constexpr int QB = WFmt<FMT>::bytes;
+  const size_t rb = (size_t)nbi * QB;
   const uint8_t* base = shared ? a.s_down + (size_t)min(r, H - 1) * rb
                                : a.w_down + ((size_t)e * H + min(r, H - 1)) * rb;
-  constexpr int NV = FAST ? 18 * BPL / 16 : 1;
+  constexpr int NV = FAST ? QB * BPL / 16 : 1;
   uint32_t D[4 * NV + 1] = {};
   if (FAST && live && lr * BPL < nbi) {
-    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * Q4B);
+    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * QB);
 #pragma unroll
     for (int v = 0; v < NV; v++) {
       const uint4 q = src[v];
@@ -294,8 +296,8 @@ __global__ void __launch_bounds__(1024) dbatch_down_kernel(DecodeBatchArgs a, in
         return A;
       };
       float v;
-      if constexpr (FAST) v = w4a8_regs<BPL>(D, nbi, lr * BPL, act);
-      else v = w4a8_lane<BPL, false>(base, nbi, lr * BPL, act, nullptr);
+      if constexpr (FAST) v = wxa8_regs<BPL, FMT>(D, nbi, lr * BPL, act);
+      else v = wxa8_lane<BPL, false, FMT>(base, nbi, lr * BPL, act, nullptr);
       v = wave_tree_sum(v, lpr);
       if (live && lr == 0) a.o[(size_t)pairs_l[u0 + u] * H + r] = v;
     }
@@ -357,20 +359,16 @@ DecodeBatchGeometry decode_batch_geometry(int M, int H, int I, int E, int k, int
   return g;
 }
 
-hipError_t launch_decode_batch(const DecodeBatchArgs& a, hipStream_t stream) {
-  const DecodeBatchGeometry g = decode_batch_geometry(a.M, a.H, a.I, a.E, a.k, a.has_shared);
-  const int nc = a.H / BLK, nexp = a.E + (a.has_shared ? 1 : 0);
-  hipLaunchKernelGGL(dbatch_router_kernel, dim3(nc), dim3(g.router_threads), 0, stream, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dbatch_route_kernel, dim3(a.M), dim3(g.route_threads), g.route_lds, stream, a, g.route_parts);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+// gate/up and down launches for one weight format
+template <int FMT>
+hipError_t launch_dbatch_experts(const DecodeBatchArgs& a, const DecodeBatchGeometry& g, int nexp,
+                                 hipStream_t stream) {
+  hipError_t err = hipSuccess;
   {
     dim3 grid(nexp * (a.I / DBG_ROWS));
     dim3 block(g.gu_threads);
 #define MOEQ4_GU(B, F) \
-  hipLaunchKernelGGL((dbatch_gateup_kernel<B, F>), grid, block, g.gu_lds, stream, a, g.gu_lpr, g.gu_tb)
+  hipLaunchKernelGGL((dbatch_gateup_kernel<B, F, FMT>), grid, block, g.gu_lds, stream, a, g.gu_lpr, g.gu_tb)
     if (g.gu_fast) {
       if (g.gu_bpl == 8) MOEQ4_GU(8, true);
       else if (g.gu_bpl == 16) MOEQ4_GU(16, true);
@@ -391,7 +389,7 @@ hipError_t launch_decode_batch(const DecodeBatchArgs& a, hipStream_t stream) {
     dim3 grid(nexp * ((a.H + g.dn_rows - 1) / g.dn_rows));
     dim3 block(g.dn_threads);
 #define MOEQ4_DN(B, F) \
-  hipLaunchKernelGGL((dbatch_down_kernel<B, F>), grid, block, g.dn_lds, stream, a, g.dn_lpr, g.dn_tb, g.dn_rows)
+  hipLaunchKernelGGL((dbatch_down_kernel<B, F, FMT>), grid, block, g.dn_lds, stream, a, g.dn_lpr, g.dn_tb, g.dn_rows)
     if (g.dn_fast) {
       if (g.dn_bpl == 8) MOEQ4_DN(8, true);
       else if (g.dn_bpl == 16) MOEQ4_DN(16, true);
@@ -408,6 +406,21 @@ hipError_t launch_decode_batch(const DecodeBatchArgs& a, hipStream_t stream) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  return err;
+}
+
+hipError_t launch_decode_batch(const DecodeBatchArgs& a, hipStream_t stream) {
+  const DecodeBatchGeometry g = decode_batch_geometry(a.M, a.H, a.I, a.E, a.k, a.has_shared);
+  const int nc = a.H / BLK, nexp = a.E + (a.has_shared ? 1 : 0);
+  hipLaunchKernelGGL(dbatch_router_kernel, dim3(nc), dim3(g.router_threads), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dbatch_route_kernel, dim3(a.M), dim3(g.route_threads), g.route_lds, stream, a, g.route_parts);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = a.wfmt == kQ8 ? launch_dbatch_experts<kQ8>(a, g, nexp, stream)
+                      : launch_dbatch_experts<kQ4>(a, g, nexp, stream);
+  if (err != hipSuccess) return err;
   const int64_t n = (int64_t)a.M * a.H;
   hipLaunchKernelGGL(dbatch_combine_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();

@@ -8,6 +8,7 @@ namespace moeq4 {
 
 hipError_t launch_q4_pack(const float* w, int64_t rows, int64_t K, void* packed,
                           hipStream_t stream);
+hipError_t launch_q8w_pack(const float* w, int64_t rows, int64_t K, void* packed, hipStream_t stream);
 hipError_t launch_q4_tile(const void* q4, int64_t rows, int64_t K, void* tiled, hipStream_t stream);
 hipError_t launch_q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d,
                               hipStream_t stream);
@@ -69,6 +70,7 @@ inline int64_t prefill_tile_bound(int64_t T, int k, int E, int has_shared) {
 
 // Decode.
 struct DecodeArgs {
+  int wfmt;                 // weight format: 0 Q4_0, 1 Q8_0
   const float* x;           // [H]
   float* y;                 // [H]
   int H, I, E, k, has_shared;
@@ -119,6 +121,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 constexpr int kDecodeBatchMax = 32;
 constexpr size_t kDecodeBatchLds = 40 * 1024;   // LDS budget of the batched gate/up and down blocks
 struct DecodeBatchArgs {
+  int wfmt;                 // weight format: 0 Q4_0, 1 Q8_0
   const float* x;           // [M][H]
   float* y;                 // [M][H]
   int M, H, I, E, k, has_shared;

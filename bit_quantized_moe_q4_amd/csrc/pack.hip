@@ -47,6 +47,47 @@ __global__ void __launch_bounds__(256) q4_pack_kernel(const float* __restrict__ 
   }
 }
 
+// Q8_0 weights ("A Modern Multimodal Assistant on a 6 GB 2011 GPU", abstract:
+// 8-bit weights): d = fp16(amax/127), q = clamp(roundf(w/d), -127, 127);
+// 34 bytes = d then the 32 int8 codes in element order.
+__global__ void __launch_bounds__(256) q8w_pack_kernel(const float* __restrict__ w, int64_t nblocks,
+                                                       uint16_t* __restrict__ out) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nblocks) return;
+  const float4* src = reinterpret_cast<const float4*>(w + i * BLK);
+  float v[BLK];
+#pragma unroll
+  for (int c = 0; c < BLK / 4; c++) {
+    float4 t = src[c];
+    v[4 * c] = t.x; v[4 * c + 1] = t.y; v[4 * c + 2] = t.z; v[4 * c + 3] = t.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < BLK; j++) amax = fmaxf(amax, fabsf(v[j]));
+  uint16_t dh = f32_to_f16_bits(amax / 127.0f);
+  float df = f16_bits_to_f32(dh);
+  uint32_t q[BLK];
+#pragma unroll
+  for (int j = 0; j < BLK; j++) {
+    float t = (df == 0.0f) ? 0.0f : roundf(v[j] / df);
+    t = fminf(fmaxf(t, -127.0f), 127.0f);
+    q[j] = (uint32_t)(int)t & 0xffu;
+  }
+  // 34 bytes = 17 little-endian halfwords: d, then code pairs (q_2p | q_2p+1 << 8)
+  uint16_t* dst = out + i * 17;
+  dst[0] = dh;
+#pragma unroll
+  for (int p = 0; p < 16; p++) dst[1 + p] = (uint16_t)(q[2 * p] | (q[2 * p + 1] << 8));
+}
+
+hipError_t launch_q8w_pack(const float* w, int64_t rows, int64_t K, void* packed, hipStream_t stream) {
+  int64_t nblocks = rows * (K / BLK);
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(q8w_pack_kernel, dim3((uint32_t)((nblocks + 255) / 256)), dim3(256), 0, stream, w,
+                     nblocks, static_cast<uint16_t*>(packed));
+  return hipGetLastError();
+}
+
 __global__ void __launch_bounds__(256) q8_quantize_kernel(const float* __restrict__ x,
                                                           int64_t nblocks, int8_t* __restrict__ q,
                                                           float* __restrict__ d) {

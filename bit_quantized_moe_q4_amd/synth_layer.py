@@ -11,29 +11,29 @@ import torch
 
 import moe_synth
 
-from . import MoELayer, q4_pack
+from . import MoELayer, q4_pack, q8w_pack
 
 
-def _pack_host(a: np.ndarray, device) -> torch.Tensor:
+def _pack_host(a: np.ndarray, device, wfmt="q4") -> torch.Tensor:
     t = torch.from_numpy(a).to(device)
-    p = q4_pack(t)
+    p = q8w_pack(t) if wfmt == "q8" else q4_pack(t)
     del t
     return p
 
 
 def device_layer(cfg: moe_synth.Config, layer: int = 0, device="cuda", weights=None,
-                 threads: int = 16, tiles: bool = True) -> MoELayer:
+                 threads: int = 16, tiles: bool = True, wfmt: str = "q4") -> MoELayer:
     """Pack layer `layer` of workload `cfg` on `device`.  `weights` (the dict
     from moe_synth.expert_weights) may be passed in to reuse a host copy;
-    `tiles` as in MoELayer."""
+    `tiles` and `wfmt` as in MoELayer."""
     W = weights if weights is not None else moe_synth.expert_weights(cfg, layer, threads=threads)
     wr = torch.from_numpy(moe_synth.router(cfg, layer)).to(device)
     b = moe_synth.router_bias(cfg, layer)
     bias = None if b is None else torch.from_numpy(b).to(device)
-    pk = {k: (None if W[k] is None else _pack_host(W[k], device))
+    pk = {k: (None if W[k] is None else _pack_host(W[k], device, wfmt))
           for k in ("gate", "up", "down", "s_gate", "s_up", "s_down")}
     L = MoELayer(wr, pk["gate"], pk["up"], pk["down"], cfg.k, router_bias=bias,
-                 s_gate=pk["s_gate"], s_up=pk["s_up"], s_down=pk["s_down"], tiles=tiles)
+                 s_gate=pk["s_gate"], s_up=pk["s_up"], s_down=pk["s_down"], tiles=tiles, wfmt=wfmt)
     torch.cuda.synchronize(device)
     return L
 

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_header_declares_the_api():
     names = header_functions()
-    for n in ["q4_packed_bytes", "q4_pack", "q4_tile", "q8_quantize", "moe_q4_route", "moe_q4_prefill",
+    for n in ["q4_packed_bytes", "q4_pack", "q4_tile", "q8w_packed_bytes", "q8w_pack", "q8_quantize", "moe_q4_route", "moe_q4_prefill",
               "moe_q4_decode", "moe_q4_decode_batch", "moe_q4_decode_batch_workspace_bytes",
               "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
               "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_rmsnorm",
@@ -145,6 +145,31 @@ def test_decode_batch_argument_checks(lib):
     assert lib.moe_q4_decode_batch(C.byref(L), None, 0, None, None, None, None, 0, None) == 0   # nothing to do
     wide = _layer(hidden=16384 + 32)
     assert lib.moe_q4_decode_batch(C.byref(wide), ok, 1, ok, None, None, ok, need, None) == -1
+
+
+def test_q8_weight_checks(lib):
+    assert lib.q8w_packed_bytes(512, 2048) == 512 * 64 * 34
+    assert lib.q8w_packed_bytes(3, 33) == 0
+    assert lib.q8w_pack(C.c_void_p(0x1000), 4, 33, C.c_void_p(0x2000), None) == -1
+    assert lib.q8w_pack(None, 4, 32, C.c_void_p(0x2000), None) == -1
+    assert lib.q8w_pack(C.c_void_p(0x1004), 4, 32, C.c_void_p(0x2000), None) == -1   # misaligned
+    assert lib.q8w_pack(None, 0, 32, None, None) == 0
+    L = _layer()
+    L.weight_format = 2
+    assert lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, 16, None, None, None, 0, None) == -1
+    assert "weight_format" in _err(lib)
+    L.weight_format = 1                     # Q8_0 with tile-order copies
+    L.t_gate = L.t_up = L.t_down = 0x20000
+    assert lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, 16, None, None, None, 0, None) == -1
+    assert "Q4_0" in _err(lib)
+    L = _layer()
+    L.weight_format = 1                     # prefill refuses Q8_0 before anything else
+    from bit_quantized_moe_q4_amd._lib import Routing
+    R = Routing()
+    R.topk_ids = R.topk_w = R.expert_offsets = R.perm = R.inv_perm = 0x30000
+    assert lib.moe_q4_prefill(C.byref(L), C.c_void_p(0x1000), 4, C.byref(R), C.c_void_p(0x2000),
+                              C.c_void_p(0x40000), 1 << 30, None) == -1
+    assert "Q4_0" in _err(lib)
 
 
 def test_workspace_checks(lib):
