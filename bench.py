@@ -159,7 +159,7 @@ def clone_layer(L, tiles=True):
     import bit_quantized_moe_q4_amd as mq
     c = lambda t: None if t is None else t.clone()  # noqa: E731
     return mq.MoELayer(c(L.w_router), c(L.gate), c(L.up), c(L.down), L.top_k, c(L.router_bias),
-                       c(L.s_gate), c(L.s_up), c(L.s_down), tiles=tiles)
+                       c(L.s_gate), c(L.s_up), c(L.s_down), tiles=tiles, wfmt=L.wfmt)
 
 
 def bench_prefill(args, torch, mq, moe_synth, device_layer):
@@ -226,9 +226,9 @@ def bench_prefill(args, torch, mq, moe_synth, device_layer):
                 fl_gu=fl_gu, fl_dn=fl_dn, fl_total=fl_total, layers=layers)
 
 
-def bench_decode(args, torch, mq, moe_synth, device_layer):
+def bench_decode(args, torch, mq, moe_synth, device_layer, wfmt="q4"):
     cfg = moe_synth.CONFIGS["decode"]
-    base = device_layer(cfg, tiles=False)                 # decode reads the row-major matrices
+    base = device_layer(cfg, tiles=False, wfmt=wfmt)      # decode reads the row-major matrices
     copies = [base] + [clone_layer(base, tiles=False) for _ in range(args.decode_copies - 1)]
     n = args.decode_steps
     X = torch.from_numpy(moe_synth.tokens(cfg, step=0, T=n)).cuda()   # fresh seeded x per step
@@ -257,7 +257,7 @@ def bench_decode(args, torch, mq, moe_synth, device_layer):
     t1 = time.perf_counter()
     step_s = (t1 - t0) / (reps * n)
     ns = cfg.k + (1 if cfg.shared else 0)
-    per_mat = cfg.I * (cfg.H // 32) * 18
+    per_mat = cfg.I * (cfg.H // 32) * (34 if wfmt == "q8" else 18)
     bytes_step = ns * 3 * per_mat + cfg.H * cfg.E * 4
     # eager (no graph) for reference: launch overhead included
     torch.cuda.synchronize()
@@ -398,6 +398,7 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true", help="skip the 1..32-token decode comparison")
+    ap.add_argument("--no-q8", action="store_true", help="skip the Q8_0-weight decode comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -425,6 +426,10 @@ def main():
     dec = bench_decode(args, torch, mq, moe_synth, device_layer)
     small = None if args.no_small_batch else bench_small_batch(args, torch, mq, moe_synth, dec, pre)
     dec.pop("layers")
+    dec8 = None
+    if not args.no_q8:
+        dec8 = bench_decode(args, torch, mq, moe_synth, device_layer, wfmt="q8")
+        dec8.pop("layers")
     copy_gbps = hbm_copy_gbps(torch)
     cfg = pre["cfg"]
     tok_s = cfg.T / pre["step_s"]
@@ -489,6 +494,18 @@ def main():
         },
     }
     out["small_batch_decode"] = small
+    if dec8 is not None:
+        g8 = dec8["bytes_step"] / dec8["step_s"] / 1e9
+        out["decode_q8_0"] = {
+            "note": "the same one-token decode with Q8_0 weights (34-byte blocks, W8A8 dots); "
+                    "4-bit vs 8-bit weights on the decode path",
+            "us_per_step": round(dec8["step_s"] * 1e6, 3),
+            "eager_us_per_step": round(dec8["eager_s"] * 1e6, 3),
+            "cache_resident_us_per_step": round(dec8["hot_s"] * 1e6, 3),
+            "bytes_per_step": dec8["bytes_step"],
+            "weight_gbps": round(g8, 1),
+            "q4_over_q8_step_time": round(dec["step_s"] / dec8["step_s"], 4),
+        }
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(args, pre)
     if args.copy_probe:
         copy_probe(torch)
