@@ -287,6 +287,49 @@ def bench_decode(args, torch, mq, moe_synth, device_layer, wfmt="q4"):
 
 
 SMALL_M = (1, 2, 4, 8, 16, 32)
+STACK_LAYERS = 40
+
+
+def bench_stack(args, torch, mq, moe_synth, dec):
+    """One decode token through a 40-layer stack (the decode layer's shape,
+    cycling through the rotated layer copies so every layer streams from HBM):
+    moe_q4_decode_stack (RMSNorm inside each next layer's first kernel, three
+    launches per layer) against the chain of moe_q4_decode + moe_q4_rmsnorm
+    (four), both as graph replays of `ntok` tokens."""
+    cfg, copies = dec["cfg"], dec["layers"]
+    seq = [copies[i % len(copies)] for i in range(STACK_LAYERS)]
+    stack = mq.LayerStack(seq)
+    ntok = 10
+    X = torch.from_numpy(moe_synth.tokens(cfg, step=9000, T=ntok)).cuda()
+    Y = torch.empty((ntok, cfg.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(mq.moe_q4_decode_stack_workspace_bytes(stack), dtype=torch.uint8, device="cuda")
+    dws = mq.decode_workspace(seq[0])
+    yb = torch.empty(cfg.H, dtype=torch.float32, device="cuda")
+    xb = torch.empty((1, cfg.H), dtype=torch.float32, device="cuda")
+
+    def fused(i):
+        mq.moe_q4_decode_stack(stack, X[i], 1e-6, y=Y[i], ws=ws)
+
+    def chain(i):
+        x = X[i]
+        for l, L in enumerate(seq):
+            out = Y[i] if l == len(seq) - 1 else yb
+            mq.moe_q4_decode(L, x, y=out, ws=dws)
+            if l < len(seq) - 1:
+                mq.moe_q4_rmsnorm(yb[None], 1e-6, f32=True, out_f32=xb)
+                x = xb[0]
+    for i in range(2):
+        fused(i)
+        chain(i)
+    torch.cuda.synchronize()
+    t_f = _graph_time(torch, [(lambda i=i: fused(i)) for i in range(ntok)], args.decode_reps)
+    t_c = _graph_time(torch, [(lambda i=i: chain(i)) for i in range(ntok)], args.decode_reps)
+    return {"layers": STACK_LAYERS, "layer_copies": len(copies),
+            "us_per_token_fused_norm": round(t_f * 1e6, 2), "us_per_token_chain": round(t_c * 1e6, 2),
+            "us_per_layer_fused_norm": round(t_f * 1e6 / STACK_LAYERS, 3),
+            "note": "one decode token through 40 layers of the decode layer's shape, graph replay: "
+                    "moe_q4_decode_stack (RMSNorm fused into each next layer, 3 launches per layer) vs "
+                    "moe_q4_decode + moe_q4_rmsnorm per layer (4 launches)"}
 
 
 def _graph_time(torch, calls, reps):
@@ -399,6 +442,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true", help="skip the 1..32-token decode comparison")
     ap.add_argument("--no-q8", action="store_true", help="skip the Q8_0-weight decode comparison")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer stack decode")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -425,6 +469,7 @@ def main():
     pre = bench_prefill(args, torch, mq, moe_synth, device_layer)
     dec = bench_decode(args, torch, mq, moe_synth, device_layer)
     small = None if args.no_small_batch else bench_small_batch(args, torch, mq, moe_synth, dec, pre)
+    stackr = None if args.no_stack else bench_stack(args, torch, mq, moe_synth, dec)
     dec.pop("layers")
     dec8 = None
     if not args.no_q8:
@@ -494,6 +539,7 @@ def main():
         },
     }
     out["small_batch_decode"] = small
+    out["stack_decode"] = stackr
     if dec8 is not None:
         g8 = dec8["bytes_step"] / dec8["step_s"] / 1e9
         out["decode_q8_0"] = {

@@ -26,6 +26,7 @@ __all__ = [
     "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage",
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
     "moe_q4_decode_batch_workspace_bytes", "moe_q4_decode_batch",
+    "LayerStack", "moe_q4_decode_stack_workspace_bytes", "moe_q4_decode_stack",
     "moe_q4_w4a8_gemv", "moe_q4_rmsnorm", "library_path",
 ]
 
@@ -295,6 +296,44 @@ def moe_q4_decode(layer: MoELayer, x: torch.Tensor, y: torch.Tensor | None = Non
     return (y, tr) if trace else y
 
 
+class LayerStack:
+    """A host array of moe_q4_layer descriptors for moe_q4_decode_stack (the
+    MoELayer objects must stay alive while it is used)."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        arr = (_lib.Layer * len(self.layers))()
+        for i, L in enumerate(self.layers):
+            arr[i] = L._c
+        self._arr = arr
+        self.hidden = self.layers[0].hidden if self.layers else 0
+
+    def __len__(self):
+        return len(self.layers)
+
+    def ptr(self):
+        return C.cast(self._arr, C.c_void_p)
+
+
+def moe_q4_decode_stack_workspace_bytes(stack: LayerStack) -> int:
+    return int(_lib.lib().moe_q4_decode_stack_workspace_bytes(stack.ptr(), len(stack)))
+
+
+def moe_q4_decode_stack(stack: LayerStack, x: torch.Tensor, eps: float = 1e-6,
+                        y: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    """One decode step through the stack: x [H] fp32 -> y [H] fp32, the last
+    layer's output (RMSNorm between layers, fused into each next layer)."""
+    _dev(x, "x")
+    if y is None:
+        y = torch.empty(stack.hidden, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(1, moe_q4_decode_stack_workspace_bytes(stack)), dtype=torch.uint8,
+                         device=x.device)
+    _lib.check(_lib.lib().moe_q4_decode_stack(stack.ptr(), len(stack), _p(x), _p(y), float(eps), _p(ws),
+                                              ws.numel(), _s(stream)), "moe_q4_decode_stack")
+    return y
+
+
 def moe_q4_decode_batch_workspace_bytes(layer: MoELayer, M: int) -> int:
     return int(_lib.lib().moe_q4_decode_batch_workspace_bytes(layer.struct_ptr(), int(M)))
 
@@ -335,12 +374,14 @@ def moe_q4_w4a8_gemv(W: torch.Tensor, N: int, K: int, qa: torch.Tensor, da: torc
 
 
 def moe_q4_rmsnorm(y: torch.Tensor, eps: float = 1e-6, f32: bool = True, bf16: bool = False,
-                   stream=None):
-    """Unit-gain RMSNorm of y [T, H] fp32 -> (fp32 | None, bf16 | None)."""
+                   stream=None, out_f32: torch.Tensor | None = None, out_bf16: torch.Tensor | None = None):
+    """Unit-gain RMSNorm of y [T, H] fp32 -> (fp32 | None, bf16 | None); out_f32 /
+    out_bf16 may be given (then nothing is allocated)."""
     _dev(y, "y")
     T, H = int(y.shape[0]), int(y.shape[1])
-    o32 = torch.empty_like(y) if f32 else None
-    o16 = torch.empty((T, H), dtype=torch.bfloat16, device=y.device) if bf16 else None
+    o32 = out_f32 if out_f32 is not None else (torch.empty_like(y) if f32 else None)
+    o16 = out_bf16 if out_bf16 is not None else (
+        torch.empty((T, H), dtype=torch.bfloat16, device=y.device) if bf16 else None)
     _lib.check(_lib.lib().moe_q4_rmsnorm(_p(y), T, H, float(eps), _p(o32), _p(o16), _s(stream)),
                "moe_q4_rmsnorm")
     return o32, o16

@@ -75,6 +75,8 @@ def _declare(lib):
         "moe_q4_prefill_stage": (C.c_int, [P, P, I32, P, P, P, SZ, I32, P]),
         "moe_q4_decode_workspace_bytes": (SZ, [P]),
         "moe_q4_decode_batch_workspace_bytes": (SZ, [P, I32]),
+        "moe_q4_decode_stack_workspace_bytes": (SZ, [P, I32]),
+        "moe_q4_decode_stack": (C.c_int, [P, I32, P, P, C.c_float, P, SZ, P]),
         "moe_q4_decode_batch": (C.c_int, [P, P, I32, P, P, P, P, SZ, P]),
         "moe_q4_decode": (C.c_int, [P, P, P, P, P, SZ, P]),
         "moe_q4_w4a8_gemv": (C.c_int, [P, I32, I32, P, P, P, P, P]),

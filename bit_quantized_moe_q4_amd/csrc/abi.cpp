@@ -430,6 +430,77 @@ int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_decode");
 }
 
+size_t moe_q4_decode_stack_workspace_bytes(const moe_q4_layer* layers, int32_t n_layers) {
+  if (!layers || n_layers < 0) return 0;
+  size_t need = 0;
+  for (int32_t l = 0; l < n_layers; l++) {
+    if (check_layer(&layers[l]) != MOE_Q4_OK) return 0;
+    const size_t w = decode_ws(&layers[l]).total;
+    need = w > need ? w : need;
+  }
+  return need + (n_layers > 0 ? 2 * up256((size_t)layers[0].hidden * 4) : 0);
+}
+
+int moe_q4_decode_stack(const moe_q4_layer* layers, int32_t n_layers, const float* x, float* y,
+                        float eps, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n_layers < 0) return fail(MOE_Q4_EINVAL, "moe_q4_decode_stack: n_layers=%d < 0", n_layers);
+  if (n_layers == 0) return MOE_Q4_OK;
+  if (!layers || !x || !y) return fail(MOE_Q4_EINVAL, "moe_q4_decode_stack: NULL pointer");
+  if (!(eps >= 0.0f)) return fail(MOE_Q4_EINVAL, "moe_q4_decode_stack: eps must be >= 0");
+  size_t dws = 0;
+  for (int32_t l = 0; l < n_layers; l++) {
+    int rc = check_layer(&layers[l]);
+    if (rc) return rc;
+    if (layers[l].hidden != layers[0].hidden)
+      return fail(MOE_Q4_EINVAL, "moe_q4_decode_stack: layer %d has hidden=%d, layer 0 %d", l,
+                  layers[l].hidden, layers[0].hidden);
+    const size_t w = decode_ws(&layers[l]).total;
+    dws = w > dws ? w : dws;
+  }
+  if (!aligned(x, 16) || !aligned(y, 4)) return fail(MOE_Q4_EINVAL, "moe_q4_decode_stack: x must be 16-byte aligned");
+  const size_t H = (size_t)layers[0].hidden;
+  const size_t need = dws + 2 * up256(H * 4);
+  int rc = check_ws(ws, ws_bytes, need);
+  if (rc) return rc;
+  float* ybuf[2] = {at<float>(ws, dws), at<float>(ws, dws + up256(H * 4))};
+  for (int32_t l = 0; l < n_layers; l++) {
+    const moe_q4_layer* L = &layers[l];
+    const DecodeWs W = decode_ws(L);
+    moeq4::DecodeArgs a;
+    memset(&a, 0, sizeof a);
+    a.norm_in = l > 0;
+    a.norm_eps = eps;
+    a.x = l == 0 ? x : ybuf[(l - 1) & 1];
+    a.y = l == n_layers - 1 ? y : ybuf[l & 1];
+    a.H = L->hidden;
+    a.I = L->inter;
+    a.E = L->n_experts;
+    a.k = L->top_k;
+    a.has_shared = L->has_shared;
+    a.wfmt = L->weight_format;
+    a.w_router = L->w_router;
+    a.bias = L->router_bias;
+    a.w_gate = static_cast<const uint8_t*>(L->w_gate);
+    a.w_up = static_cast<const uint8_t*>(L->w_up);
+    a.w_down = static_cast<const uint8_t*>(L->w_down);
+    a.s_gate = static_cast<const uint8_t*>(L->s_gate);
+    a.s_up = static_cast<const uint8_t*>(L->s_up);
+    a.s_down = static_cast<const uint8_t*>(L->s_down);
+    a.partials = at<float>(ws, W.partials);
+    a.ids = at<int32_t>(ws, W.ids);
+    a.w = at<float>(ws, W.w);
+    a.qx = at<int8_t>(ws, W.qx);
+    a.dx = at<float>(ws, W.dx);
+    a.sx = at<int32_t>(ws, W.sx);
+    a.qh = at<int8_t>(ws, W.qh);
+    a.dh = at<float>(ws, W.dh);
+    a.sh = at<int32_t>(ws, W.sh);
+    hipError_t e = moeq4::launch_decode(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_q4_decode_stack");
+  }
+  return MOE_Q4_OK;
+}
+
 int moe_q4_w4a8_gemv(const void* W, int32_t N, int32_t K, const int8_t* qa, const float* da,
                      int32_t* dots, float* out, hipStream_t stream) {
   if (N < 0 || K <= 0 || K % 32 || K > kMaxDim)

@@ -35,11 +35,20 @@
 namespace moeq4 {
 
 // ---------------------------------------------------------------- router
+// With a.norm_in the input is the previous layer's y and the block first
+// takes x = y / r, r the RMSNorm scale of y (every block computes r itself:
+// the stack's glue without a launch of its own).
 __global__ void __launch_bounds__(1024) decode_router_kernel(DecodeArgs a) {
   __shared__ float xs[BLK];
+  __shared__ float part[512], tmp[512];
   const int tid = threadIdx.x, c = blockIdx.x;
   const int E = a.E;
-  if (tid < BLK) xs[tid] = a.x[c * BLK + tid];
+  if (a.norm_in) {
+    const float r = rms_scale(a.x, a.H, a.norm_eps, part, tmp);
+    if (tid < BLK) xs[tid] = a.x[c * BLK + tid] / r;
+  } else if (tid < BLK) {
+    xs[tid] = a.x[c * BLK + tid];
+  }
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
     const float* w = a.w_router + (size_t)c * BLK * E + e;

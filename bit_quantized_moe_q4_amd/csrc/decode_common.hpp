@@ -79,6 +79,37 @@ __device__ __forceinline__ float root_tree(const float* __restrict__ src, int E,
   return r[0];
 }
 
+// The RMSNorm scale r = sqrtf(ss / H + eps) of one row y [H] (H/32 <= 512):
+// ss is the per-32-chunk fused chain y*y from +0, the chunk partials summed
+// pairwise level by level (padded with +0 to a power of two), the program of
+// the library's RMSNorm.  Every thread of the block returns r; part and tmp
+// are 512-float LDS buffers.  Contains barriers: call from the whole block.
+__device__ __forceinline__ float rms_scale(const float* __restrict__ row, int H, float eps,
+                                           float* part, float* tmp) {
+  const int nc = H / BLK;
+  const int m = (int)next_pow2_u32((uint32_t)nc);
+  for (int c = threadIdx.x; c < m; c += blockDim.x) {
+    float acc = 0.0f;
+    if (c < nc)
+      for (int i = 0; i < BLK; i++) {
+        const float v = row[c * BLK + i];
+        acc = __builtin_fmaf(v, v, acc);
+      }
+    part[c] = acc;
+  }
+  __syncthreads();
+  float* src = part;
+  float* dst = tmp;
+  for (int w = m; w > 1; w >>= 1) {      // one level: dst[i] = src[2i] + src[2i+1]
+    for (int i = threadIdx.x; i < w / 2; i += blockDim.x) dst[i] = src[2 * i] + src[2 * i + 1];
+    __syncthreads();
+    float* t = src;
+    src = dst;
+    dst = t;
+  }
+  return sqrtf(src[0] / (float)H + eps);
+}
+
 // Inverse of rank_key's logit part (-0 comes back as +0).
 __device__ __forceinline__ float key_logit(uint64_t key) {
   const uint32_t u = (uint32_t)(key >> 32);

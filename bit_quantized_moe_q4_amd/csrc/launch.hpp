@@ -71,6 +71,8 @@ inline int64_t prefill_tile_bound(int64_t T, int k, int E, int has_shared) {
 // Decode.
 struct DecodeArgs {
   int wfmt;                 // weight format: 0 Q4_0, 1 Q8_0
+  int norm_in;              // 1: x is the previous layer's y, RMSNorm-ed on the fly
+  float norm_eps;
   const float* x;           // [H]
   float* y;                 // [H]
   int H, I, E, k, has_shared;

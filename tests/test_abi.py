@@ -35,6 +35,7 @@ def test_header_declares_the_api():
     names = header_functions()
     for n in ["q4_packed_bytes", "q4_pack", "q4_tile", "q8w_packed_bytes", "q8w_pack", "q8_quantize", "moe_q4_route", "moe_q4_prefill",
               "moe_q4_decode", "moe_q4_decode_batch", "moe_q4_decode_batch_workspace_bytes",
+              "moe_q4_decode_stack", "moe_q4_decode_stack_workspace_bytes",
               "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
               "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_rmsnorm",
               "moe_q4_last_error"]:
@@ -170,6 +171,23 @@ def test_q8_weight_checks(lib):
     assert lib.moe_q4_prefill(C.byref(L), C.c_void_p(0x1000), 4, C.byref(R), C.c_void_p(0x2000),
                               C.c_void_p(0x40000), 1 << 30, None) == -1
     assert "Q4_0" in _err(lib)
+
+
+def test_decode_stack_checks(lib):
+    from bit_quantized_moe_q4_amd._lib import Layer
+    arr = (Layer * 2)(_layer(), _layer())
+    ok = C.c_void_p(0x10000)
+    need = lib.moe_q4_decode_stack_workspace_bytes(arr, 2)
+    assert need > 0
+    assert lib.moe_q4_decode_stack(arr, 0, None, None, 1e-6, None, 0, None) == 0       # nothing to do
+    assert lib.moe_q4_decode_stack(arr, -1, ok, ok, 1e-6, ok, need, None) == -1
+    assert lib.moe_q4_decode_stack(None, 2, ok, ok, 1e-6, ok, need, None) == -1
+    assert lib.moe_q4_decode_stack(arr, 2, ok, ok, -1.0, ok, need, None) == -1
+    assert "eps" in _err(lib)
+    assert lib.moe_q4_decode_stack(arr, 2, ok, ok, 1e-6, ok, 64, None) == -2
+    arr[1].hidden = 512
+    assert lib.moe_q4_decode_stack(arr, 2, ok, ok, 1e-6, ok, need, None) == -1
+    assert "hidden" in _err(lib)
 
 
 def test_workspace_checks(lib):
