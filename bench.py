@@ -228,8 +228,11 @@ def bench_prefill(args, torch, mq, moe_synth, device_layer):
 
 def bench_decode(args, torch, mq, moe_synth, device_layer, wfmt="q4"):
     cfg = moe_synth.CONFIGS["decode"]
-    base = device_layer(cfg, tiles=False, wfmt=wfmt)      # decode reads the row-major matrices
-    copies = [base] + [clone_layer(base, tiles=False) for _ in range(args.decode_copies - 1)]
+    # Q4_0: with the tile-order copies, as moe_q4_prefill needs them (the
+    # gate/up launch reads those, the down launch the row-major matrices)
+    tiles = wfmt == "q4"
+    base = device_layer(cfg, tiles=tiles, wfmt=wfmt)
+    copies = [base] + [clone_layer(base, tiles=tiles) for _ in range(args.decode_copies - 1)]
     n = args.decode_steps
     X = torch.from_numpy(moe_synth.tokens(cfg, step=0, T=n)).cuda()   # fresh seeded x per step
     Y = torch.empty((n, cfg.H), dtype=torch.float32, device="cuda")

@@ -408,6 +408,10 @@ int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_
   a.s_gate = static_cast<const uint8_t*>(L->s_gate);
   a.s_up = static_cast<const uint8_t*>(L->s_up);
   a.s_down = static_cast<const uint8_t*>(L->s_down);
+  a.t_gate = static_cast<const uint8_t*>(L->t_gate);
+  a.t_up = static_cast<const uint8_t*>(L->t_up);
+  a.ts_gate = static_cast<const uint8_t*>(L->ts_gate);
+  a.ts_up = static_cast<const uint8_t*>(L->ts_up);
   a.partials = at<float>(ws, W.partials);
   a.ids = at<int32_t>(ws, W.ids);
   a.w = at<float>(ws, W.w);
@@ -486,6 +490,10 @@ int moe_q4_decode_stack(const moe_q4_layer* layers, int32_t n_layers, const floa
     a.s_gate = static_cast<const uint8_t*>(L->s_gate);
     a.s_up = static_cast<const uint8_t*>(L->s_up);
     a.s_down = static_cast<const uint8_t*>(L->s_down);
+    a.t_gate = static_cast<const uint8_t*>(L->t_gate);
+    a.t_up = static_cast<const uint8_t*>(L->t_up);
+    a.ts_gate = static_cast<const uint8_t*>(L->ts_gate);
+    a.ts_up = static_cast<const uint8_t*>(L->ts_up);
     a.partials = at<float>(ws, W.partials);
     a.ids = at<int32_t>(ws, W.ids);
     a.w = at<float>(ws, W.w);

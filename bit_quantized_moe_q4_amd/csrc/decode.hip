@@ -174,34 +174,83 @@ __device__ void decode_gu_prologue(const DecodeArgs& a, const GuLds& l, int P, b
     }
   }
   __syncthreads();
-  for (int b0 = 0; b0 < items; b0 += nt) {
-    const int it = b0 + tid;
-    const bool ok = it < items;
-    const int e = ok ? it / P : 0, p = it % P;
-    const uint64_t ke = l.key[e];
+  // Rank pass.  A wave task is (64 experts, one range of Q equal key ranges):
+  // every lane compares its expert's key against the range's keys, all lanes
+  // reading the same key at once (an LDS broadcast, no bank conflicts).  The
+  // Q partial counts of an expert are then summed by one thread.
+  __shared__ int32_t rpart[1024];         // [Q][E]; Q * E <= max(E, 64 * waves) <= 1024
+  const int nw = nt / 64, lane = tid % 64;
+  const int nchunk = (E + 63) / 64;
+  const int Q = nw / nchunk > 1 ? nw / nchunk : 1;
+  const int span = ((E + Q - 1) / Q + 1) & ~1;          // even: 16-byte key pairs
+  const ulonglong2* K2 = reinterpret_cast<const ulonglong2*>(l.key);
+  for (int task = tid / 64; task < nchunk * Q; task += nw) {
+    const int e = (task % nchunk) * 64 + lane, q = task / nchunk;
+    const uint64_t ke = l.key[e < E ? e : 0];
+    const int j0 = min(q * span, E), j1 = min(j0 + span, E);
     int rank = 0;
-    // lane p compares against keys [j0, j1): pairs by 16-byte reads, unrolled
-    const int span = (E + P - 1) / P;
-    const int j0 = min(p * span, E), j1 = min(j0 + span, E);
-    int j = j0;
-    if (ok) {
-      if ((j & 1) && j < j1) { rank += (l.key[j] > ke) ? 1 : 0; j++; }
-      const ulonglong2* K2 = reinterpret_cast<const ulonglong2*>(l.key);
-#pragma unroll 4
-      for (; j + 2 <= j1; j += 2) {
-        const ulonglong2 q = K2[j >> 1];
-        rank += (q.x > ke) ? 1 : 0;
-        rank += (q.y > ke) ? 1 : 0;
-      }
-      if (j < j1) rank += (l.key[j] > ke) ? 1 : 0;
+    int j = j0;                           // j0 is even
+#pragma unroll 8
+    for (; j + 2 <= j1; j += 2) {
+      const ulonglong2 kk = K2[j >> 1];
+      rank += (kk.x > ke) ? 1 : 0;
+      rank += (kk.y > ke) ? 1 : 0;
     }
-    for (int o = 1; o < P; o <<= 1) rank += __shfl_xor(rank, o, 64);
-    if (ok && p == 0 && rank < a.k) {
+    if (j < j1) rank += (l.key[j] > ke) ? 1 : 0;
+    if (e < E) rpart[q * E + e] = rank;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) {
+    int rank = 0;
+    for (int q = 0; q < Q; q++) rank += rpart[q * E + e];
+    if (rank < a.k) {
       ids_l[rank] = e;
       vals_l[rank] = l.logit[e];
     }
   }
   __syncthreads();
+}
+
+// h = silu(g) * u of the block's 32-group from val[0..31] (gate) and
+// val[32..63] (up), then its q8; block 0 also publishes ids and weights.
+// Called by every thread after the barrier that completes val.
+__device__ __forceinline__ void gu_epilogue(const DecodeArgs& a, const float* val, int slot, int i0,
+                                            bool publish, const int* ids_l, const float* vals_l,
+                                            float* ex_l) {
+  const int tid = threadIdx.x, I = a.I;
+  if (tid < DGU_ROWS) {                   // h of one 32-group, then its q8
+    const float h = silu_p(val[tid]) * val[DGU_ROWS + tid];
+    float amax = fabsf(h);
+#pragma unroll
+    for (int m = 1; m < BLK; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, BLK));
+    const float d = amax / 127.0f;
+    const int q = (d == 0.0f) ? 0 : (int)roundf(h / d);
+    int sum = q;
+#pragma unroll
+    for (int m = 1; m < BLK; m <<= 1) sum += __shfl_xor(sum, m, BLK);
+    const size_t hi = (size_t)slot * I + i0 + tid;
+    a.qh[hi] = (int8_t)q;
+    if (a.t_qh) a.t_qh[hi] = (int8_t)q;
+    if (tid == 0) {
+      const size_t g = hi / BLK;
+      a.dh[g] = d;
+      a.sh[g] = sum;
+      if (a.t_dh) a.t_dh[g] = d;
+    }
+  }
+  if (publish) {                          // w_s = e_s / ((e_0 + e_1) + ...), e_s = exp(l_s - l_0)
+    if (tid < a.k) ex_l[tid] = exp_p(vals_l[tid] - vals_l[0]);
+    __syncthreads();
+    if (tid < a.k) {
+      float S = ex_l[0];
+      for (int s = 1; s < a.k; s++) S = S + ex_l[s];
+      const float wv = ex_l[tid] / S;
+      a.ids[tid] = ids_l[tid];
+      a.w[tid] = wv;
+      if (a.t_ids) a.t_ids[tid] = ids_l[tid];
+      if (a.t_w) a.t_w[tid] = wv;
+    }
+  }
 }
 
 template <int BPL, bool FAST, int FMT>
@@ -243,39 +292,121 @@ __global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int l
   v = wave_tree_sum(v, lpr);
   if (lr == 0) val[row] = v;
   __syncthreads();
-  if (tid < DGU_ROWS) {                   // h of one 32-group, then its q8
-    const float h = silu_p(val[tid]) * val[DGU_ROWS + tid];
-    float amax = fabsf(h);
-#pragma unroll
-    for (int m = 1; m < BLK; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, BLK));
-    const float d = amax / 127.0f;
-    const int q = (d == 0.0f) ? 0 : (int)roundf(h / d);
-    int sum = q;
-#pragma unroll
-    for (int m = 1; m < BLK; m <<= 1) sum += __shfl_xor(sum, m, BLK);
-    const size_t hi = (size_t)slot * I + i0 + tid;
-    a.qh[hi] = (int8_t)q;
-    if (a.t_qh) a.t_qh[hi] = (int8_t)q;
-    if (tid == 0) {
-      const size_t g = hi / BLK;
-      a.dh[g] = d;
-      a.sh[g] = sum;
-      if (a.t_dh) a.t_dh[g] = d;
-    }
+  gu_epilogue(a, val, slot, i0, publish, ids_l, vals_l, ex_l);
+}
+
+// Gate/up over the tile-order copies (Q4_0, H % 64 == 0; layout at q4_tile
+// in moe_q4.h).  Same blocks, prologue and epilogue as decode_gateup_kernel.
+// The block's W waves split the row's m = next_pow2(H/32) blocks (+0 leaves
+// past H/32) into W aligned runs of 2*SP blocks, SP tile pieces per wave: in
+// piece s, lane l holds block 2s + l/32 of row l%32 of the gate group and of
+// the up group -- one 16-byte and one 2-byte load per lane and matrix, with
+// consecutive lanes on consecutive addresses (a row-major span load touches
+// 64 cache lines per instruction).  The sums follow the row's pairwise tree:
+// blocks 2s and 2s+1 (lanes l and l^32) first, then the lane's pieces
+// pairwise (CH pieces loaded together, then the chunk sums), then the W wave
+// sums pairwise.
+constexpr int kGtWaves = 16, kGtRouteThreads = 512;
+
+template <int SP>
+__global__ void __launch_bounds__(1024) decode_gateup_tiled_kernel(DecodeArgs a, int P) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  constexpr int CH = SP < 4 ? SP : 4;     // pieces whose loads are issued together
+  constexpr int NCH = SP / CH;
+  const int H = a.H, I = a.I, nbh = H / BLK, nsteps = H / 64;
+  const GuLds l = gu_lds(dyn, nbh, a.E);
+  __shared__ float val[2 * DGU_ROWS];
+  __shared__ float wsum[16][2 * DGU_ROWS];
+  __shared__ int ids_l[32];
+  __shared__ float vals_l[32], ex_l[32];
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), W = blockDim.x / 64;
+  const int ngrp = I / DGU_ROWS, j = blockIdx.x;
+  const int slot = j / ngrp, gx = j % ngrp, i0 = gx * DGU_ROWS;
+  const bool publish = j == 0;
+  decode_gu_prologue(a, l, P, slot < a.k, ids_l, vals_l, publish);
+
+  const size_t gbytes = (size_t)DGU_ROWS * nbh * 18;   // one 32-row group
+  const uint8_t* gb;
+  const uint8_t* ub;
+  if (slot < a.k) {                      // (clamped: a NaN logit leaves ranks unfilled)
+    const size_t G = (size_t)min(max(ids_l[slot], 0), a.E - 1) * ngrp + gx;
+    gb = a.t_gate + G * gbytes;
+    ub = a.t_up + G * gbytes;
+  } else {
+    gb = a.ts_gate + (size_t)gx * gbytes;
+    ub = a.ts_up + (size_t)gx * gbytes;
   }
-  if (publish) {                          // w_s = e_s / ((e_0 + e_1) + ...), e_s = exp(l_s - l_0)
-    if (tid < a.k) ex_l[tid] = exp_p(vals_l[tid] - vals_l[0]);
-    __syncthreads();
-    if (tid < a.k) {
-      float S = ex_l[0];
-      for (int s = 1; s < a.k; s++) S = S + ex_l[s];
-      const float wv = ex_l[tid] / S;
-      a.ids[tid] = ids_l[tid];
-      a.w[tid] = wv;
-      if (a.t_ids) a.t_ids[tid] = ids_l[tid];
-      if (a.t_w) a.t_w[tid] = wv;
+  const int half = lane >> 5;
+  float cg[NCH], cu[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    uint4 gn[CH], un[CH];
+    uint32_t gs[CH], us[CH];
+#pragma unroll
+    for (int q = 0; q < CH; q++) {
+      const int st = wave * SP + c * CH + q;
+      gn[q] = make_uint4(0, 0, 0, 0);
+      un[q] = make_uint4(0, 0, 0, 0);
+      gs[q] = 0;
+      us[q] = 0;
+      if (st < nsteps) {
+        const size_t o = (size_t)st * 1152;
+        gn[q] = *reinterpret_cast<const uint4*>(gb + o + 16 * lane);
+        un[q] = *reinterpret_cast<const uint4*>(ub + o + 16 * lane);
+        gs[q] = *reinterpret_cast<const uint16_t*>(gb + o + 1024 + 2 * lane);
+        us[q] = *reinterpret_cast<const uint16_t*>(ub + o + 1024 + 2 * lane);
+      }
     }
+    float gv[CH], uv[CH];
+#pragma unroll
+    for (int q = 0; q < CH; q++) {
+      const int st = wave * SP + c * CH + q;
+      gv[q] = 0.0f;
+      uv[q] = 0.0f;
+      if (st < nsteps) {
+        const int b = 2 * st + half;
+        const uint4* qa = reinterpret_cast<const uint4*>(l.qa + act_off(b));
+        const uint4 a0 = qa[0], a1 = qa[1];
+        const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float da = l.da[b];
+        const int32_t sa = l.sa[b];
+        const uint32_t gw[4] = {gn[q].x, gn[q].y, gn[q].z, gn[q].w};
+        const uint32_t uw[4] = {un[q].x, un[q].y, un[q].z, un[q].w};
+        const int32_t dg = q4_block_dot(gw, av, sa);
+        const int32_t du = q4_block_dot(uw, av, sa);
+        gv[q] = (f16_bits_to_f32(gs[q]) * da) * (float)dg;
+        uv[q] = (f16_bits_to_f32(us[q]) * da) * (float)du;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < CH; q++) {        // blocks 2s and 2s+1
+      gv[q] = gv[q] + __shfl_xor(gv[q], 32, 64);
+      uv[q] = uv[q] + __shfl_xor(uv[q], 32, 64);
+    }
+    cg[c] = reg_tree<CH>(gv);
+    cu[c] = reg_tree<CH>(uv);
   }
+  const float tg = reg_tree<NCH>(cg), tu = reg_tree<NCH>(cu);
+  if (lane < DGU_ROWS) {
+    wsum[wave][lane] = tg;
+    wsum[wave][DGU_ROWS + lane] = tu;
+  }
+  __syncthreads();
+  if (tid < 2 * DGU_ROWS) {               // the W wave sums, pairwise
+    float t[16];
+#pragma unroll
+    for (int w = 0; w < 16; w++) t[w] = w < W ? wsum[w][tid] : 0.0f;
+#pragma unroll
+    for (int n = 16; n > 1; n >>= 1)
+      if (n <= W) {
+#pragma unroll
+        for (int i = 0; i < n / 2; i++) t[i] = t[2 * i] + t[2 * i + 1];
+      }
+    val[tid] = t[0];
+  }
+  __syncthreads();
+  gu_epilogue(a, val, slot, i0, publish, ids_l, vals_l, ex_l);
 }
 
 // ---------------------------------------------------------------- down + combine
@@ -379,6 +510,22 @@ DecodeGeometry decode_geometry(int H, int I, int E, int k, int has_shared) {
   while (m / P > 32) P <<= 1;
   g.gu_parts = P;
   g.gu_lds = gu_lds_bytes(nc, E);
+  // tile-order gate/up: W = min(kGtWaves, m/2) waves of SP = m / (2W)
+  // pieces.  The router finish keeps the lane split of a kGtRouteThreads
+  // block: more lanes per expert make its leaf loads less coalesced.
+  g.gt_sp = 0;
+  g.gt_threads = 0;
+  g.gt_parts = 0;
+  if (H % 64 == 0) {
+    const int W = m / 2 < kGtWaves ? m / 2 : kGtWaves;
+    g.gt_threads = 64 * W;
+    const int rt = g.gt_threads < kGtRouteThreads ? g.gt_threads : kGtRouteThreads;
+    int Pt = 1;
+    while (Pt < 64 && Pt < m && E * Pt * 2 <= rt) Pt <<= 1;
+    while (m / Pt > 32) Pt <<= 1;
+    g.gt_parts = Pt;
+    g.gt_sp = m / (2 * W) <= 16 ? m / (2 * W) : 0;
+  }
   const RowSplit dn = row_split(I, 16);
   g.dn_lpr = dn.lpr;
   g.dn_bpl = dn.bpl;
@@ -399,7 +546,22 @@ template <int FMT>
 hipError_t launch_decode_experts(const DecodeArgs& a, const DecodeGeometry& g, hipStream_t stream) {
   hipError_t err = hipSuccess;
   const int ns = a.k + (a.has_shared ? 1 : 0);
-  {
+  if (FMT == kQ4 && g.gt_sp > 0 && a.t_gate && a.t_up && (!a.has_shared || (a.ts_gate && a.ts_up))) {
+    dim3 grid(a.I / DGU_ROWS * ns);
+    dim3 block(g.gt_threads);
+#define MOEQ4_GT(SPV) \
+  hipLaunchKernelGGL((decode_gateup_tiled_kernel<SPV>), grid, block, g.gu_lds, stream, a, g.gt_parts)
+    switch (g.gt_sp) {
+      case 1: MOEQ4_GT(1); break;
+      case 2: MOEQ4_GT(2); break;
+      case 4: MOEQ4_GT(4); break;
+      case 8: MOEQ4_GT(8); break;
+      default: MOEQ4_GT(16); break;
+    }
+#undef MOEQ4_GT
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  } else {
     dim3 grid(a.I / DGU_ROWS * ns);
     dim3 block(g.gu_threads);
 #define MOEQ4_GU(B, F) \

@@ -84,6 +84,12 @@ struct DecodeArgs {
   const uint8_t* s_gate;
   const uint8_t* s_up;
   const uint8_t* s_down;
+  // tile-order copies of the gate and up matrices (Q4_0), or NULL: the
+  // gate/up launch then reads these instead of the row-major blocks
+  const uint8_t* t_gate;
+  const uint8_t* t_up;
+  const uint8_t* ts_gate;
+  const uint8_t* ts_up;
   // workspace pieces (no initialisation needed: every piece is written
   // before it is read within one call)
   float* partials;          // [H/32][E] router chunk chains
@@ -112,6 +118,7 @@ struct DecodeGeometry {
   int router_threads;
   int gu_lpr, gu_bpl, gu_fast, gu_threads, gu_parts;
   size_t gu_lds;
+  int gt_sp, gt_threads, gt_parts;   // tile-order gate/up (gt_sp 0: not available)
   int dn_lpr, dn_bpl, dn_fast, dn_rows, dn_threads, dn_act_lds;
   size_t dn_lds;
 };

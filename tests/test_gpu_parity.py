@@ -372,6 +372,34 @@ def test_decode_small(name, H, E, I, k, shared, bias):
     _decode_steps(ol, gl, cfg, range(6))
 
 
+@pytest.mark.parametrize("name,H,E,I,k,shared", [
+    ("tiny_shared", 256, 8, 128, 2, True),
+    # H = 192 and 320: 3 and 5 tile pieces per row, padded to 4 and 8 waves
+    # of one piece, the last waves holding only +0 leaves
+    ("ragged_pieces", 192, 16, 128, 4, True),
+    ("ragged_pieces5", 320, 8, 64, 3, False),
+    # H = 16384: 16 pieces per wave in 4 chunks
+    ("wide_hidden", 16384, 8, 64, 2, True),
+    ("many_experts", 256, 1024, 64, 32, True),
+])
+def test_decode_tiled_matches_rowmajor(name, H, E, I, k, shared):
+    # the gate/up launch over the tile-order copies realises the same pinned
+    # trees as the row-major one: every traced value and y are bit-identical
+    say("decode tiled vs row-major", name)
+    cfg = moe_synth.CONFIGS["tiny"].with_(name=name, H=H, E=E, I=I, k=k, shared=shared, bias="zipf")
+    W = moe_synth.expert_weights(cfg, 0, threads=16)
+    gt = device_layer(cfg, weights=W, tiles=True)
+    gr = device_layer(cfg, weights=W, tiles=False)
+    assert gt.tiles is not None and gr.tiles is None
+    for step in range(4):
+        x = torch.from_numpy(moe_synth.tokens(cfg, step=step, T=1)[0]).cuda()
+        yt, tt = mq.moe_q4_decode(gt, x, trace=True)
+        yr, trr = mq.moe_q4_decode(gr, x, trace=True)
+        assert np.array_equal(yt.cpu().numpy().view(np.uint32), yr.cpu().numpy().view(np.uint32)), step
+        for key in ("ids", "w", "qh", "dh", "logits"):
+            assert np.array_equal(tt[key].cpu().numpy(), trr[key].cpu().numpy()), (step, key)
+
+
 def test_decode_tied_logits():
     # experts 2j and 2j+1 share a router column, so every logit ties with its
     # pair: the choice takes the lower index first (k rounds of "first maximum
