@@ -412,6 +412,8 @@ int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_
   a.t_up = static_cast<const uint8_t*>(L->t_up);
   a.ts_gate = static_cast<const uint8_t*>(L->ts_gate);
   a.ts_up = static_cast<const uint8_t*>(L->ts_up);
+  a.t_down = static_cast<const uint8_t*>(L->t_down);
+  a.ts_down = static_cast<const uint8_t*>(L->ts_down);
   a.partials = at<float>(ws, W.partials);
   a.ids = at<int32_t>(ws, W.ids);
   a.w = at<float>(ws, W.w);
@@ -494,6 +496,8 @@ int moe_q4_decode_stack(const moe_q4_layer* layers, int32_t n_layers, const floa
     a.t_up = static_cast<const uint8_t*>(L->t_up);
     a.ts_gate = static_cast<const uint8_t*>(L->ts_gate);
     a.ts_up = static_cast<const uint8_t*>(L->ts_up);
+    a.t_down = static_cast<const uint8_t*>(L->t_down);
+    a.ts_down = static_cast<const uint8_t*>(L->ts_down);
     a.partials = at<float>(ws, W.partials);
     a.ids = at<int32_t>(ws, W.ids);
     a.w = at<float>(ws, W.w);

@@ -343,41 +343,38 @@ __global__ void __launch_bounds__(1024) decode_gateup_tiled_kernel(DecodeArgs a,
   for (int c = 0; c < NCH; c++) {
     uint4 gn[CH], un[CH];
     uint32_t gs[CH], us[CH];
+    // every load unconditional (pieces past the row re-read its last piece
+    // and are zeroed below): branches around loads make each piece wait
+    // for the one before
 #pragma unroll
     for (int q = 0; q < CH; q++) {
-      const int st = wave * SP + c * CH + q;
-      gn[q] = make_uint4(0, 0, 0, 0);
-      un[q] = make_uint4(0, 0, 0, 0);
-      gs[q] = 0;
-      us[q] = 0;
-      if (st < nsteps) {
-        const size_t o = (size_t)st * 1152;
-        gn[q] = *reinterpret_cast<const uint4*>(gb + o + 16 * lane);
-        un[q] = *reinterpret_cast<const uint4*>(ub + o + 16 * lane);
-        gs[q] = *reinterpret_cast<const uint16_t*>(gb + o + 1024 + 2 * lane);
-        us[q] = *reinterpret_cast<const uint16_t*>(ub + o + 1024 + 2 * lane);
-      }
+      const size_t o = (size_t)min(wave * SP + c * CH + q, nsteps - 1) * 1152;
+      gn[q] = *reinterpret_cast<const uint4*>(gb + o + 16 * lane);
+      un[q] = *reinterpret_cast<const uint4*>(ub + o + 16 * lane);
+    }
+#pragma unroll
+    for (int q = 0; q < CH; q++) {
+      const size_t o = (size_t)min(wave * SP + c * CH + q, nsteps - 1) * 1152;
+      gs[q] = *reinterpret_cast<const uint16_t*>(gb + o + 1024 + 2 * lane);
+      us[q] = *reinterpret_cast<const uint16_t*>(ub + o + 1024 + 2 * lane);
     }
     float gv[CH], uv[CH];
 #pragma unroll
     for (int q = 0; q < CH; q++) {
       const int st = wave * SP + c * CH + q;
-      gv[q] = 0.0f;
-      uv[q] = 0.0f;
-      if (st < nsteps) {
-        const int b = 2 * st + half;
-        const uint4* qa = reinterpret_cast<const uint4*>(l.qa + act_off(b));
-        const uint4 a0 = qa[0], a1 = qa[1];
-        const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float da = l.da[b];
-        const int32_t sa = l.sa[b];
-        const uint32_t gw[4] = {gn[q].x, gn[q].y, gn[q].z, gn[q].w};
-        const uint32_t uw[4] = {un[q].x, un[q].y, un[q].z, un[q].w};
-        const int32_t dg = q4_block_dot(gw, av, sa);
-        const int32_t du = q4_block_dot(uw, av, sa);
-        gv[q] = (f16_bits_to_f32(gs[q]) * da) * (float)dg;
-        uv[q] = (f16_bits_to_f32(us[q]) * da) * (float)du;
-      }
+      const int b = 2 * min(st, nsteps - 1) + half;
+      const uint4* qa = reinterpret_cast<const uint4*>(l.qa + act_off(b));
+      const uint4 a0 = qa[0], a1 = qa[1];
+      const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float da = l.da[b];
+      const int32_t sa = l.sa[b];
+      const uint32_t gw[4] = {gn[q].x, gn[q].y, gn[q].z, gn[q].w};
+      const uint32_t uw[4] = {un[q].x, un[q].y, un[q].z, un[q].w};
+      const int32_t dg = q4_block_dot(gw, av, sa);
+      const int32_t du = q4_block_dot(uw, av, sa);
+      const bool ok = st < nsteps;
+      gv[q] = ok ? (f16_bits_to_f32(gs[q]) * da) * (float)dg : 0.0f;
+      uv[q] = ok ? (f16_bits_to_f32(us[q]) * da) * (float)du : 0.0f;
     }
 #pragma unroll
     for (int q = 0; q < CH; q++) {        // blocks 2s and 2s+1
@@ -490,6 +487,116 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
   }
 }
 
+// Down + combine over the tile-order copies (Q4_0, I % 64 == 0; layout at
+// q4_tile in moe_q4.h).  Block: 8 output rows r0..r0+7 (inside one 32-row
+// group) x every slot; wave w serves slots 4w..4w+3.  In piece s of a
+// slot's row group, lane L = 32*half + 8*g + rr loads the piece lane
+// 32*half + (r0 % 32) + rr of slot 4w+g: block 2s + half of row r0 + rr,
+// so one load instruction reads 8 runs of 128 contiguous bytes.  Every lane
+// covers the whole row (the padded m = next_pow2(I/32) blocks: SP = m/2
+// pieces, +0 leaves past I/32); the sums follow the row's pairwise tree:
+// blocks 2s and 2s+1 (lanes L and L^32) first, then the pieces pairwise
+// (CH loaded together, then the chunk sums).  Then the fixed-order combine.
+constexpr int kDtRows = 8;
+template <int SP>
+__global__ void __launch_bounds__(1024) decode_down_tiled_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  constexpr int CH = SP < 8 ? SP : 8;     // pieces whose loads are issued together
+  constexpr int NCH = SP / CH;
+  const int H = a.H, I = a.I, nbi = I / BLK, nsteps = I / 64;
+  const int ns = a.k + (a.has_shared ? 1 : 0);
+  const int SS = act_row_dwords(nbi);
+  uint32_t* qh_l = reinterpret_cast<uint32_t*>(dyn);                     // ns * SS dwords
+  float* dh_l = reinterpret_cast<float*>(qh_l + (size_t)ns * SS);         // ns * nbi
+  int32_t* sh_l = reinterpret_cast<int32_t*>(dh_l + (size_t)ns * nbi);    // ns * nbi
+  __shared__ float o_l[kDtRows * 33];
+  __shared__ float w_l[32];
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int r0 = blockIdx.x * kDtRows;
+  const int half = lane >> 5, g = (lane >> 3) & 3, rr = lane & 7;
+  const int slot = 4 * wave + g;
+  const bool live = slot < ns;
+  const int sl = live ? slot : ns - 1;    // lanes past the last slot mirror it (results unused)
+  // Straight-line loads, none behind a branch or in a loop (either makes
+  // the compiler wait for loads issued earlier): the expert id first, then
+  // the routing weights and this thread's first q8(h) group; once the id
+  // is in, the first chunk of weights; then the LDS stores.
+  const int eid = a.ids[min(sl, a.k - 1)];
+  const float wr = a.w[min(tid, a.k - 1)];
+  const int nact = ns * nbi;
+  const int i0 = min(tid, nact - 1);
+  const uint4 h0 = reinterpret_cast<const uint4*>(a.qh)[2 * (size_t)i0];
+  const uint4 h1 = reinterpret_cast<const uint4*>(a.qh)[2 * (size_t)i0 + 1];
+  const float hd = a.dh[i0];
+  const int32_t hs = a.sh[i0];
+  const size_t gbytes = (size_t)nsteps * 1152;                           // one 32-row group
+  const int pl = 32 * half + (r0 % 32) + rr;                             // lane inside a piece
+  const size_t G = (size_t)(r0 / 32);
+  const uint8_t* base = (sl < a.k) ? a.t_down + ((size_t)min(max(eid, 0), a.E - 1) * (H / 32) + G) * gbytes
+                                   : a.ts_down + G * gbytes;
+  // pieces past the row re-read its last piece and are zeroed below
+  uint4 wn[CH];
+  uint32_t ws[CH];
+  auto load_chunk = [&](int c) {
+#pragma unroll
+    for (int q = 0; q < CH; q++)
+      wn[q] = *reinterpret_cast<const uint4*>(base + (size_t)min(c * CH + q, nsteps - 1) * 1152 + 16 * pl);
+#pragma unroll
+    for (int q = 0; q < CH; q++)
+      ws[q] = *reinterpret_cast<const uint16_t*>(base + (size_t)min(c * CH + q, nsteps - 1) * 1152 + 1024 + 2 * pl);
+  };
+  load_chunk(0);
+  if (tid < nact) {                       // every slot's q8(h) into LDS
+    uint4* dst = reinterpret_cast<uint4*>(qh_l + (size_t)(tid / nbi) * SS + act_off(tid % nbi));
+    dst[0] = h0;
+    dst[1] = h1;
+    dh_l[tid] = hd;
+    sh_l[tid] = hs;
+  }
+  for (int i = tid + (int)blockDim.x; i < nact; i += blockDim.x) {      // wide rows only
+    const uint4* src = reinterpret_cast<const uint4*>(a.qh) + 2 * (size_t)i;
+    uint4* dst = reinterpret_cast<uint4*>(qh_l + (size_t)(i / nbi) * SS + act_off(i % nbi));
+    dst[0] = src[0];
+    dst[1] = src[1];
+    dh_l[i] = a.dh[i];
+    sh_l[i] = a.sh[i];
+  }
+  if (tid < a.k) w_l[tid] = wr;
+  __syncthreads();
+  const uint32_t* qs = qh_l + (size_t)sl * SS;
+  float cs[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    if (c > 0) load_chunk(c);
+    float v[CH];
+#pragma unroll
+    for (int q = 0; q < CH; q++) {
+      const int st = c * CH + q;
+      const int b = 2 * min(st, nsteps - 1) + half;
+      const uint4* qa = reinterpret_cast<const uint4*>(qs + act_off(b));
+      const uint4 a0 = qa[0], a1 = qa[1];
+      const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const uint32_t wv[4] = {wn[q].x, wn[q].y, wn[q].z, wn[q].w};
+      const int32_t dot = q4_block_dot(wv, av, sh_l[sl * nbi + b]);
+      v[q] = st < nsteps ? (f16_bits_to_f32(ws[q]) * dh_l[sl * nbi + b]) * (float)dot : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < CH; q++) v[q] = v[q] + __shfl_xor(v[q], 32, 64);   // blocks 2s and 2s+1
+    cs[c] = reg_tree<CH>(v);
+  }
+  const float o = reg_tree<NCH>(cs);
+  if (live && half == 0) o_l[rr * 33 + slot] = o;
+  __syncthreads();
+  if (tid < kDtRows && r0 + tid < H) {
+    const float* ov = o_l + tid * 33;
+    float acc = w_l[0] * ov[0];
+    for (int s = 1; s < a.k; s++) acc = acc + w_l[s] * ov[s];
+    if (a.has_shared) acc = acc + ov[a.k];
+    a.y[r0 + tid] = acc;
+  }
+}
+
 // ---------------------------------------------------------------- launch
 DecodeGeometry decode_geometry(int H, int I, int E, int k, int has_shared) {
   DecodeGeometry g;
@@ -538,6 +645,15 @@ DecodeGeometry decode_geometry(int H, int I, int E, int k, int has_shared) {
   const size_t out = 4 * (size_t)g.dn_rows * ns;
   g.dn_act_lds = act + out <= kDecodeLdsMax;
   g.dn_lds = (g.dn_act_lds ? act : 0) + out;
+  // tile-order down: SP = m/2 pieces per lane, every slot's q8(h) in LDS
+  g.dt_sp = 0;
+  g.dt_threads = 64 * ((ns + 3) / 4);
+  g.dt_lds = act;
+  {
+    int md = 1;
+    while (md < nbi) md <<= 1;
+    if (I % 64 == 0 && H % 64 == 0 && md / 2 <= 32 && act <= kDecodeLdsMax) g.dt_sp = md / 2;
+  }
   return g;
 }
 
@@ -582,7 +698,22 @@ hipError_t launch_decode_experts(const DecodeArgs& a, const DecodeGeometry& g, h
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  {
+  if (FMT == kQ4 && g.dt_sp > 0 && a.t_down && (!a.has_shared || a.ts_down)) {
+    dim3 grid(a.H / kDtRows);
+    dim3 block(g.dt_threads);
+#define MOEQ4_DT(SPV) \
+  hipLaunchKernelGGL((decode_down_tiled_kernel<SPV>), grid, block, g.dt_lds, stream, a)
+    switch (g.dt_sp) {
+      case 1: MOEQ4_DT(1); break;
+      case 2: MOEQ4_DT(2); break;
+      case 4: MOEQ4_DT(4); break;
+      case 8: MOEQ4_DT(8); break;
+      case 16: MOEQ4_DT(16); break;
+      default: MOEQ4_DT(32); break;
+    }
+#undef MOEQ4_DT
+    err = hipGetLastError();
+  } else {
     dim3 grid((a.H + g.dn_rows - 1) / g.dn_rows);
     dim3 block(g.dn_threads);
 #define MOEQ4_DN(B, F)                                                                     \

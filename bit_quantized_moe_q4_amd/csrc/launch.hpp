@@ -84,12 +84,14 @@ struct DecodeArgs {
   const uint8_t* s_gate;
   const uint8_t* s_up;
   const uint8_t* s_down;
-  // tile-order copies of the gate and up matrices (Q4_0), or NULL: the
-  // gate/up launch then reads these instead of the row-major blocks
+  // tile-order copies (Q4_0), or NULL: the gate/up and down launches then
+  // read these instead of the row-major blocks
   const uint8_t* t_gate;
   const uint8_t* t_up;
   const uint8_t* ts_gate;
   const uint8_t* ts_up;
+  const uint8_t* t_down;
+  const uint8_t* ts_down;
   // workspace pieces (no initialisation needed: every piece is written
   // before it is read within one call)
   float* partials;          // [H/32][E] router chunk chains
@@ -121,6 +123,8 @@ struct DecodeGeometry {
   int gt_sp, gt_threads, gt_parts;   // tile-order gate/up (gt_sp 0: not available)
   int dn_lpr, dn_bpl, dn_fast, dn_rows, dn_threads, dn_act_lds;
   size_t dn_lds;
+  int dt_sp, dt_threads;             // tile-order down (dt_sp 0: not available)
+  size_t dt_lds;
 };
 DecodeGeometry decode_geometry(int H, int I, int E, int k, int has_shared);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -381,10 +381,16 @@ def test_decode_small(name, H, E, I, k, shared, bias):
     # H = 16384: 16 pieces per wave in 4 chunks
     ("wide_hidden", 16384, 8, 64, 2, True),
     ("many_experts", 256, 1024, 64, 32, True),
+    # down rows of I = 192 (3 pieces, one +0 piece), 2048 (32 pieces in 4
+    # chunks) and 4096 (past the tiled down kernel's 32 pieces: row-major)
+    ("ragged_inter", 256, 8, 192, 3, True),
+    ("wide_inter", 128, 8, 2048, 4, True),
+    ("wider_inter", 128, 8, 4096, 2, True),
 ])
 def test_decode_tiled_matches_rowmajor(name, H, E, I, k, shared):
-    # the gate/up launch over the tile-order copies realises the same pinned
-    # trees as the row-major one: every traced value and y are bit-identical
+    # the gate/up and down launches over the tile-order copies realise the
+    # same pinned trees as the row-major ones: every traced value and y are
+    # bit-identical
     say("decode tiled vs row-major", name)
     cfg = moe_synth.CONFIGS["tiny"].with_(name=name, H=H, E=E, I=I, k=k, shared=shared, bias="zipf")
     W = moe_synth.expert_weights(cfg, 0, threads=16)
