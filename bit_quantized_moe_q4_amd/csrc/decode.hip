@@ -423,23 +423,41 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
   __shared__ float w_l[32];
   const int tid = threadIdx.x;
   const int r0 = blockIdx.x * rows;
-  if (tid < a.k) w_l[tid] = a.w[tid];     // early: the combine is the last step
-
   const int item = tid / lpr, lr = tid % lpr;
   const int rl = item / ns, slot = item % ns;
   const int r = r0 + rl;
   const bool live = rl < rows && r < H;
   constexpr int QB = WFmt<FMT>::bytes;
   const size_t rb = (size_t)nbi * QB;
-  const uint8_t* base = nullptr;
-  if (live)
-    base = (slot < a.k) ? a.w_down + ((size_t)min(max(a.ids[slot], 0), a.E - 1) * H + r) * rb
-                        : a.s_down + (size_t)r * rb;
-  // this lane's weight span into registers (fast shapes)
+  // Straight-line loads, none behind a branch or in a loop (either makes
+  // the compiler wait for loads issued earlier): the expert id first (lanes
+  // past the block's rows mirror a valid row; their results are unused),
+  // the routing weights and this thread's first q8(h) group, then the
+  // weight span, then the LDS stores.
+  const int rc = min(r, H - 1);
+  const int eid = a.ids[min(slot, a.k - 1)];
+  const float wr = a.w[min(tid, a.k - 1)];
+  const int nq = ALDS ? ns * nbi : 0;
+  const int g0 = min(tid, max(nq - 1, 0));
+  uint4 h0 = make_uint4(0, 0, 0, 0), h1 = make_uint4(0, 0, 0, 0);
+  float hd = 0.0f;
+  int32_t hs = 0;
+  if constexpr (ALDS) {
+    h0 = reinterpret_cast<const uint4*>(a.qh)[2 * (size_t)g0];
+    h1 = reinterpret_cast<const uint4*>(a.qh)[2 * (size_t)g0 + 1];
+    hd = a.dh[g0];
+    hs = a.sh[g0];
+  }
+  const uint8_t* base = (slot < a.k) ? a.w_down + ((size_t)min(max(eid, 0), a.E - 1) * H + rc) * rb
+                                     : a.s_down + (size_t)rc * rb;
+  // this lane's weight span into registers (fast shapes; a lane of padding
+  // leaves, lr * BPL >= nbi, re-reads the row's last span and is zeroed in
+  // the row program)
   constexpr int NV = FAST ? QB * BPL / 16 : 1;
   uint32_t D[4 * NV + 1] = {};
-  if (FAST && live && lr * BPL < nbi) {
-    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * QB);
+  if constexpr (FAST) {
+    const int lrc = min(lr, nbi / BPL - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lrc * BPL * QB);
 #pragma unroll
     for (int v = 0; v < NV; v++) {
       const uint4 t = src[v];
@@ -448,7 +466,14 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
   }
   D[4 * NV] = 0u;
   // every slot's q8(h) into LDS
-  for (int g = tid; ALDS && g < ns * nbi; g += blockDim.x) {
+  if (ALDS && tid < nq) {
+    uint4* dst = reinterpret_cast<uint4*>(qh_l + (size_t)(tid / nbi) * SS + act_off(tid % nbi));
+    dst[0] = h0;
+    dst[1] = h1;
+    dh_l[tid] = hd;
+    sh_l[tid] = hs;
+  }
+  for (int g = tid + (int)blockDim.x; ALDS && g < nq; g += blockDim.x) {    // wide rows only
     const int s = g / nbi, b = g % nbi;
     const uint4* src = reinterpret_cast<const uint4*>(a.qh) + 2 * (size_t)g;
     uint4* dst = reinterpret_cast<uint4*>(qh_l + (size_t)s * SS + act_off(b));
@@ -457,6 +482,7 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
     dh_l[g] = a.dh[g];
     sh_l[g] = a.sh[g];
   }
+  if (tid < a.k) w_l[tid] = wr;
   __syncthreads();
   float v = 0.0f;
   if (live) {
