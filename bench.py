@@ -73,7 +73,7 @@ def _traffic(unit):
 # counted per unit, sources the record is valid for)
 TRAFFIC_KERNELS = {
     "gemm": (["gemm_ffn_kernel"], ["gemm.hip", "launch.hpp", "device_math.hpp"]),
-    "decode": (["decode_router_kernel", "decode_gateup_kernel", "decode_down_kernel"],
+    "decode": (["decode_router_kernel", "decode_gateup_tiled_kernel", "decode_down_tiled_kernel"],
                ["decode.hip", "launch.hpp", "w4a8.hpp", "device_math.hpp"]),
 }
 COPY_PROBE_BYTES = 1 << 30

@@ -539,7 +539,12 @@ __global__ void __launch_bounds__(1024) decode_down_tiled_kernel(DecodeArgs a) {
   __shared__ float w_l[32];
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int r0 = blockIdx.x * kDtRows;
+  // The four blocks of a 32-row group share each piece's scale line: keep
+  // them on one XCD (blocks are dealt to the 8 XCDs round robin) so that
+  // line comes from HBM once.  b = 32*(G/8) + 8*quarter + G%8 when H/32 is
+  // a multiple of 8; otherwise blocks in order.
+  const int bx = blockIdx.x;
+  const int r0 = (H % 256 == 0) ? 32 * (8 * (bx / 32) + bx % 8) + kDtRows * ((bx / 8) % 4) : bx * kDtRows;
   const int half = lane >> 5, g = (lane >> 3) & 3, rr = lane & 7;
   const int slot = 4 * wave + g;
   const bool live = slot < ns;
