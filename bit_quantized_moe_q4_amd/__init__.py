@@ -113,7 +113,8 @@ class MoELayer:
     s_gate/s_up uint8 [I, H/32*18], s_down uint8 [H, I/32*18].
     With `tiles` (the default) and H, I multiples of 64 the layer also keeps
     the matrices in grouped-GEMM tile order (q4_tile), which moe_q4_prefill's
-    fused GEMM reads; that doubles the resident weight bytes.  wfmt="q8":
+    fused GEMM and the one-token decode kernels read; that doubles the
+    resident weight bytes.  wfmt="q8":
     the matrices are Q8_0 blocks (34 bytes per 32 weights; routing and decode
     only, no tiles).
     """
