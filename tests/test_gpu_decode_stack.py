@@ -4,7 +4,8 @@ The stack runs each layer's decode with the RMSNorm between layers taken
 inside the next layer's first kernel.  Bars: y bit-identical to the chain of
 moe_q4_decode and moe_q4_rmsnorm calls, and to the oracle's chain of decode
 and rmsnorm (both are the same fp32 programs), on a 6-layer stack of small
-layers (Q4_0 and Q8_0) and a 4-layer stack at the decode layer's shape.
+layers (Q4_0 row-major and tile order, Q8_0) and a 4-layer stack at the
+decode layer's shape (both Q4_0 layouts).
 """
 import sys
 
@@ -44,10 +45,11 @@ def _oracle_chain(ols, x):
     return y
 
 
-@pytest.mark.parametrize("wfmt", ["q4", "q8"])
-def test_stack_small_layers(wfmt):
+@pytest.mark.parametrize("wfmt,tiles", [("q4", False), ("q4", True), ("q8", False)],
+                         ids=["q4-rowmajor", "q4-tiled", "q8"])
+def test_stack_small_layers(wfmt, tiles):
     cfg = moe_synth.CONFIGS["tiny"].with_(name="stack_small", H=256, E=8, I=128, k=2, shared=True)
-    pairs = [both_layers(cfg, layer=l, tiles=False, wfmt=wfmt) for l in range(6)]
+    pairs = [both_layers(cfg, layer=l, tiles=tiles, wfmt=wfmt) for l in range(6)]
     ols, gls = [p[0] for p in pairs], [p[1] for p in pairs]
     stack = mq.LayerStack(gls)
     for step in range(3):
@@ -61,11 +63,12 @@ def test_stack_small_layers(wfmt):
         assert err <= 1e-5, (step, err)
 
 
-def test_stack_decode_layers():
+@pytest.mark.parametrize("tiles", [False, True], ids=["rowmajor", "tiled"])
+def test_stack_decode_layers(tiles):
     cfg = moe_synth.CONFIGS["decode"]
     say("building 4 decode-size layers")
     from bit_quantized_moe_q4_amd.synth_layer import device_layer
-    gls = [device_layer(cfg, layer=l, tiles=False) for l in range(4)]
+    gls = [device_layer(cfg, layer=l, tiles=tiles) for l in range(4)]
     stack = mq.LayerStack(gls)
     ws = torch.empty(mq.moe_q4_decode_stack_workspace_bytes(stack), dtype=torch.uint8, device="cuda")
     for step in range(3):

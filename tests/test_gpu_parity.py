@@ -374,6 +374,8 @@ def test_decode_small(name, H, E, I, k, shared, bias):
 
 @pytest.mark.parametrize("name,H,E,I,k,shared", [
     ("tiny_shared", 256, 8, 128, 2, True),
+    # the smallest tiled shape: H = I = 64, one piece per row, one wave
+    ("minimal", 64, 4, 64, 2, True),
     # H = 192 and 320: 3 and 5 tile pieces per row, padded to 4 and 8 waves
     # of one piece, the last waves holding only +0 leaves
     ("ragged_pieces", 192, 16, 128, 4, True),
