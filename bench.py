@@ -228,9 +228,9 @@ def bench_prefill(args, torch, mq, moe_synth, device_layer):
 
 def bench_decode(args, torch, mq, moe_synth, device_layer, wfmt="q4"):
     cfg = moe_synth.CONFIGS["decode"]
-    # Q4_0: with the tile-order copies, as moe_q4_prefill needs them (the
-    # gate/up launch reads those, the down launch the row-major matrices)
-    tiles = wfmt == "q4"
+    # with the tile-order copies (q4_tile / q8w_tile), which the one-token
+    # decode kernels read
+    tiles = True
     base = device_layer(cfg, tiles=tiles, wfmt=wfmt)
     copies = [base] + [clone_layer(base, tiles=tiles) for _ in range(args.decode_copies - 1)]
     n = args.decode_steps

@@ -21,7 +21,7 @@ import torch
 from . import _lib
 
 __all__ = [
-    "q4_packed_bytes", "q4_pack", "q4_tile", "q8w_pack", "q8_quantize", "MoELayer", "Routing",
+    "q4_packed_bytes", "q4_pack", "q4_tile", "q8w_pack", "q8w_tile", "q8_quantize", "MoELayer", "Routing",
     "moe_q4_route_workspace_bytes", "moe_q4_route",
     "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage",
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
@@ -93,6 +93,19 @@ def q4_tile(q4: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> t
     return out
 
 
+def q8w_tile(q8: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """uint8 [..., rows, K/32*34] Q8_0 blocks -> the same blocks in tile order
+    (q8w_tile in moe_q4.h); rows % 32 == 0, K % 64 == 0."""
+    _dev(q8, "q8")
+    rb = q8.shape[-1]
+    K = rb // 34 * 32
+    rows = q8.numel() // rb
+    if out is None:
+        out = torch.empty_like(q8)
+    _lib.check(_lib.lib().q8w_tile(_p(q8), rows, K, _p(out), _s(stream)), "q8w_tile")
+    return out
+
+
 def q8_quantize(x: torch.Tensor, stream=None):
     """fp32 [..., K] -> (int8 [..., K], fp32 scales [..., K/32])."""
     _dev(x, "x")
@@ -114,9 +127,8 @@ class MoELayer:
     With `tiles` (the default) and H, I multiples of 64 the layer also keeps
     the matrices in grouped-GEMM tile order (q4_tile), which moe_q4_prefill's
     fused GEMM and the one-token decode kernels read; that doubles the
-    resident weight bytes.  wfmt="q8":
-    the matrices are Q8_0 blocks (34 bytes per 32 weights; routing and decode
-    only, no tiles).
+    resident weight bytes.  wfmt="q8": the matrices are Q8_0 blocks (34
+    bytes per 32 weights; routing and decode only), tiles by q8w_tile.
     """
 
     def __init__(self, w_router, gate, up, down, top_k, router_bias=None,
@@ -143,8 +155,9 @@ class MoELayer:
         self.wfmt = wfmt
         st.weight_format = _lib.WEIGHTS_Q8_0 if wfmt == "q8" else _lib.WEIGHTS_Q4_0
         self.tiles = None
-        if tiles and wfmt == "q4" and self.hidden % 64 == 0 and self.inter % 64 == 0:
-            tl = lambda t: None if t is None else q4_tile(t, stream=stream)  # noqa: E731
+        if tiles and self.hidden % 64 == 0 and self.inter % 64 == 0:
+            tile = q8w_tile if wfmt == "q8" else q4_tile
+            tl = lambda t: None if t is None else tile(t, stream=stream)  # noqa: E731
             self.tiles = dict(gate=tl(gate), up=tl(up), down=tl(down),
                               s_gate=tl(s_gate), s_up=tl(s_up), s_down=tl(s_down))
             T_ = self.tiles

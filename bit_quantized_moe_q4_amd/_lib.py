@@ -67,6 +67,7 @@ def _declare(lib):
         "q4_tile": (C.c_int, [P, I64, I64, P, P]),
         "q8w_packed_bytes": (SZ, [I64, I64]),
         "q8w_pack": (C.c_int, [P, I64, I64, P, P]),
+        "q8w_tile": (C.c_int, [P, I64, I64, P, P]),
         "q8_quantize": (C.c_int, [P, I64, I64, P, P, P]),
         "moe_q4_route_workspace_bytes": (SZ, [P, I32]),
         "moe_q4_route": (C.c_int, [P, P, I32, I32, P, P, P, SZ, P]),

@@ -57,8 +57,6 @@ int check_layer(const moe_q4_layer* L) {
   if (L->weight_format != MOE_Q4_WEIGHTS_Q4_0 && L->weight_format != MOE_Q4_WEIGHTS_Q8_0)
     return fail(MOE_Q4_EINVAL, "weight_format=%d must be MOE_Q4_WEIGHTS_Q4_0 or _Q8_0", L->weight_format);
   const bool any_t = L->t_gate || L->t_up || L->t_down || L->ts_gate || L->ts_up || L->ts_down;
-  if (any_t && L->weight_format != MOE_Q4_WEIGHTS_Q4_0)
-    return fail(MOE_Q4_EINVAL, "tile-order matrices exist only for Q4_0 weights");
   if (any_t) {
     const bool routed = L->t_gate && L->t_up && L->t_down;
     const bool shared = L->has_shared ? (L->ts_gate && L->ts_up && L->ts_down)
@@ -203,6 +201,20 @@ int q4_tile(const void* q4, int64_t rows, int64_t K, void* tiled, hipStream_t st
   if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(MOE_Q4_EINVAL, "q4_tile: q4 and tiled overlap");
   hipError_t e = moeq4::launch_q4_tile(q4, rows, K, tiled, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "q4_tile");
+}
+
+int q8w_tile(const void* q8, int64_t rows, int64_t K, void* tiled, hipStream_t stream) {
+  if (rows < 0 || rows % 32 || K <= 0 || K % 64)
+    return fail(MOE_Q4_EINVAL, "q8w_tile: rows=%lld K=%lld (rows %% 32 == 0, K %% 64 == 0)", (long long)rows, (long long)K);
+  if (rows == 0) return MOE_Q4_OK;
+  if (!q8 || !tiled) return fail(MOE_Q4_EINVAL, "q8w_tile: NULL pointer");
+  if (!aligned(q8, 2) || !aligned(tiled, 16)) return fail(MOE_Q4_EINVAL, "q8w_tile: q8 must be 2-byte and tiled 16-byte aligned");
+  if (rows * (K / 32) > ((int64_t)1 << 40)) return fail(MOE_Q4_EINVAL, "q8w_tile: too many blocks");
+  const size_t bytes = (size_t)rows * (size_t)(K / 32) * 34;
+  const uintptr_t a0 = (uintptr_t)q8, b0 = (uintptr_t)tiled;
+  if (a0 < b0 + bytes && b0 < a0 + bytes) return fail(MOE_Q4_EINVAL, "q8w_tile: q8 and tiled overlap");
+  hipError_t e = moeq4::launch_q8w_tile(q8, rows, K, tiled, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "q8w_tile");
 }
 
 int q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d, hipStream_t stream) {

@@ -295,23 +295,55 @@ __global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int l
   gu_epilogue(a, val, slot, i0, publish, ids_l, vals_l, ex_l);
 }
 
-// Gate/up over the tile-order copies (Q4_0, H % 64 == 0; layout at q4_tile
-// in moe_q4.h).  Same blocks, prologue and epilogue as decode_gateup_kernel.
-// The block's W waves split the row's m = next_pow2(H/32) blocks (+0 leaves
-// past H/32) into W aligned runs of 2*SP blocks, SP tile pieces per wave: in
-// piece s, lane l holds block 2s + l/32 of row l%32 of the gate group and of
-// the up group -- one 16-byte and one 2-byte load per lane and matrix, with
-// consecutive lanes on consecutive addresses (a row-major span load touches
-// 64 cache lines per instruction).  The sums follow the row's pairwise tree:
+// Gate/up over the tile-order copies (Q4_0 or Q8_0, H % 64 == 0; layouts at
+// q4_tile and q8w_tile in moe_q4.h).  Same blocks, prologue and epilogue as
+// decode_gateup_kernel.  The block's W waves split the row's m =
+// next_pow2(H/32) blocks (+0 leaves past H/32) into W aligned runs of 2*SP
+// blocks, SP tile pieces per wave: in piece s, lane l holds block 2s + l/32
+// of row l%32 of the gate group and of the up group -- one 16-byte (Q8_0:
+// two) and one 2-byte load per lane and matrix, consecutive lanes on
+// consecutive addresses (a row-major span load touches 64 cache lines per
+// instruction).  The sums follow the row's pairwise tree:
 // blocks 2s and 2s+1 (lanes l and l^32) first, then the lane's pieces
 // pairwise (CH pieces loaded together, then the chunk sums), then the W wave
 // sums pairwise.
 constexpr int kGtWaves = 16, kGtRouteThreads = 512;
 
-template <int SP>
+// Tile order per weight format (q4_tile / q8w_tile in moe_q4.h): bytes of a
+// piece, bytes of a lane's block codes (at lane * code), scale offset.
+template <int FMT> struct TileFmt;
+template <> struct TileFmt<kQ4> { static constexpr int piece = 1152, code = 16, scale = 1024; };
+template <> struct TileFmt<kQ8> { static constexpr int piece = 2176, code = 32, scale = 2048; };
+
+// One lane's block of a piece: its code dwords (Q4_0 nibbles or Q8_0 codes).
+template <int FMT>
+struct TileCodes {
+  uint32_t w[TileFmt<FMT>::code / 4];
+};
+
+template <int FMT>
+__device__ __forceinline__ TileCodes<FMT> tile_codes(const uint8_t* p) {
+  TileCodes<FMT> t;
+#pragma unroll
+  for (int h = 0; h < TileFmt<FMT>::code / 16; h++) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p + 16 * h);
+    t.w[4 * h] = v.x; t.w[4 * h + 1] = v.y; t.w[4 * h + 2] = v.z; t.w[4 * h + 3] = v.w;
+  }
+  return t;
+}
+
+template <int FMT>
+__device__ __forceinline__ int32_t tile_dot(const TileCodes<FMT>& t, const uint32_t (&av)[8], int32_t sa) {
+  if constexpr (FMT == kQ4) return q4_block_dot(t.w, av, sa);
+  else return q8_block_dot(t.w, av);
+}
+
+template <int SP, int FMT>
 __global__ void __launch_bounds__(1024) decode_gateup_tiled_kernel(DecodeArgs a, int P) {
+  using TF = TileFmt<FMT>;
   extern __shared__ __align__(16) uint8_t dyn[];
-  constexpr int CH = SP < 4 ? SP : 4;     // pieces whose loads are issued together
+  constexpr int CHM = FMT == kQ4 ? 4 : 2;  // pieces whose loads are issued together
+  constexpr int CH = SP < CHM ? SP : CHM;
   constexpr int NCH = SP / CH;
   const int H = a.H, I = a.I, nbh = H / BLK, nsteps = H / 64;
   const GuLds l = gu_lds(dyn, nbh, a.E);
@@ -326,7 +358,7 @@ __global__ void __launch_bounds__(1024) decode_gateup_tiled_kernel(DecodeArgs a,
   const bool publish = j == 0;
   decode_gu_prologue(a, l, P, slot < a.k, ids_l, vals_l, publish);
 
-  const size_t gbytes = (size_t)DGU_ROWS * nbh * 18;   // one 32-row group
+  const size_t gbytes = (size_t)DGU_ROWS * nbh * WFmt<FMT>::bytes;   // one 32-row group
   const uint8_t* gb;
   const uint8_t* ub;
   if (slot < a.k) {                      // (clamped: a NaN logit leaves ranks unfilled)
@@ -341,22 +373,22 @@ __global__ void __launch_bounds__(1024) decode_gateup_tiled_kernel(DecodeArgs a,
   float cg[NCH], cu[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; c++) {
-    uint4 gn[CH], un[CH];
+    TileCodes<FMT> gn[CH], un[CH];
     uint32_t gs[CH], us[CH];
     // every load unconditional (pieces past the row re-read its last piece
     // and are zeroed below): branches around loads make each piece wait
     // for the one before
 #pragma unroll
     for (int q = 0; q < CH; q++) {
-      const size_t o = (size_t)min(wave * SP + c * CH + q, nsteps - 1) * 1152;
-      gn[q] = *reinterpret_cast<const uint4*>(gb + o + 16 * lane);
-      un[q] = *reinterpret_cast<const uint4*>(ub + o + 16 * lane);
+      const size_t o = (size_t)min(wave * SP + c * CH + q, nsteps - 1) * TF::piece;
+      gn[q] = tile_codes<FMT>(gb + o + TF::code * lane);
+      un[q] = tile_codes<FMT>(ub + o + TF::code * lane);
     }
 #pragma unroll
     for (int q = 0; q < CH; q++) {
-      const size_t o = (size_t)min(wave * SP + c * CH + q, nsteps - 1) * 1152;
-      gs[q] = *reinterpret_cast<const uint16_t*>(gb + o + 1024 + 2 * lane);
-      us[q] = *reinterpret_cast<const uint16_t*>(ub + o + 1024 + 2 * lane);
+      const size_t o = (size_t)min(wave * SP + c * CH + q, nsteps - 1) * TF::piece;
+      gs[q] = *reinterpret_cast<const uint16_t*>(gb + o + TF::scale + 2 * lane);
+      us[q] = *reinterpret_cast<const uint16_t*>(ub + o + TF::scale + 2 * lane);
     }
     float gv[CH], uv[CH];
 #pragma unroll
@@ -368,10 +400,8 @@ __global__ void __launch_bounds__(1024) decode_gateup_tiled_kernel(DecodeArgs a,
       const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       const float da = l.da[b];
       const int32_t sa = l.sa[b];
-      const uint32_t gw[4] = {gn[q].x, gn[q].y, gn[q].z, gn[q].w};
-      const uint32_t uw[4] = {un[q].x, un[q].y, un[q].z, un[q].w};
-      const int32_t dg = q4_block_dot(gw, av, sa);
-      const int32_t du = q4_block_dot(uw, av, sa);
+      const int32_t dg = tile_dot<FMT>(gn[q], av, sa);
+      const int32_t du = tile_dot<FMT>(un[q], av, sa);
       const bool ok = st < nsteps;
       gv[q] = ok ? (f16_bits_to_f32(gs[q]) * da) * (float)dg : 0.0f;
       uv[q] = ok ? (f16_bits_to_f32(us[q]) * da) * (float)du : 0.0f;
@@ -513,8 +543,8 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
   }
 }
 
-// Down + combine over the tile-order copies (Q4_0, I % 64 == 0; layout at
-// q4_tile in moe_q4.h).  Block: 8 output rows r0..r0+7 (inside one 32-row
+// Down + combine over the tile-order copies (Q4_0 or Q8_0, I % 64 == 0;
+// layouts at q4_tile and q8w_tile in moe_q4.h).  Block: 8 output rows r0..r0+7 (inside one 32-row
 // group) x every slot; wave w serves slots 4w..4w+3.  In piece s of a
 // slot's row group, lane L = 32*half + 8*g + rr loads the piece lane
 // 32*half + (r0 % 32) + rr of slot 4w+g: block 2s + half of row r0 + rr,
@@ -524,10 +554,12 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
 // blocks 2s and 2s+1 (lanes L and L^32) first, then the pieces pairwise
 // (CH loaded together, then the chunk sums).  Then the fixed-order combine.
 constexpr int kDtRows = 8;
-template <int SP>
+template <int SP, int FMT>
 __global__ void __launch_bounds__(1024) decode_down_tiled_kernel(DecodeArgs a) {
+  using TF = TileFmt<FMT>;
   extern __shared__ __align__(16) uint8_t dyn[];
-  constexpr int CH = SP < 8 ? SP : 8;     // pieces whose loads are issued together
+  constexpr int CHM = FMT == kQ4 ? 8 : 4;  // pieces whose loads are issued together
+  constexpr int CH = SP < CHM ? SP : CHM;
   constexpr int NCH = SP / CH;
   const int H = a.H, I = a.I, nbi = I / BLK, nsteps = I / 64;
   const int ns = a.k + (a.has_shared ? 1 : 0);
@@ -561,21 +593,21 @@ __global__ void __launch_bounds__(1024) decode_down_tiled_kernel(DecodeArgs a) {
   const uint4 h1 = reinterpret_cast<const uint4*>(a.qh)[2 * (size_t)i0 + 1];
   const float hd = a.dh[i0];
   const int32_t hs = a.sh[i0];
-  const size_t gbytes = (size_t)nsteps * 1152;                           // one 32-row group
+  const size_t gbytes = (size_t)nsteps * TF::piece;                      // one 32-row group
   const int pl = 32 * half + (r0 % 32) + rr;                             // lane inside a piece
   const size_t G = (size_t)(r0 / 32);
   const uint8_t* base = (sl < a.k) ? a.t_down + ((size_t)min(max(eid, 0), a.E - 1) * (H / 32) + G) * gbytes
                                    : a.ts_down + G * gbytes;
   // pieces past the row re-read its last piece and are zeroed below
-  uint4 wn[CH];
+  TileCodes<FMT> wn[CH];
   uint32_t ws[CH];
   auto load_chunk = [&](int c) {
 #pragma unroll
     for (int q = 0; q < CH; q++)
-      wn[q] = *reinterpret_cast<const uint4*>(base + (size_t)min(c * CH + q, nsteps - 1) * 1152 + 16 * pl);
+      wn[q] = tile_codes<FMT>(base + (size_t)min(c * CH + q, nsteps - 1) * TF::piece + TF::code * pl);
 #pragma unroll
     for (int q = 0; q < CH; q++)
-      ws[q] = *reinterpret_cast<const uint16_t*>(base + (size_t)min(c * CH + q, nsteps - 1) * 1152 + 1024 + 2 * pl);
+      ws[q] = *reinterpret_cast<const uint16_t*>(base + (size_t)min(c * CH + q, nsteps - 1) * TF::piece + TF::scale + 2 * pl);
   };
   load_chunk(0);
   if (tid < nact) {                       // every slot's q8(h) into LDS
@@ -608,8 +640,7 @@ __global__ void __launch_bounds__(1024) decode_down_tiled_kernel(DecodeArgs a) {
       const uint4* qa = reinterpret_cast<const uint4*>(qs + act_off(b));
       const uint4 a0 = qa[0], a1 = qa[1];
       const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const uint32_t wv[4] = {wn[q].x, wn[q].y, wn[q].z, wn[q].w};
-      const int32_t dot = q4_block_dot(wv, av, sh_l[sl * nbi + b]);
+      const int32_t dot = tile_dot<FMT>(wn[q], av, sh_l[sl * nbi + b]);
       v[q] = st < nsteps ? (f16_bits_to_f32(ws[q]) * dh_l[sl * nbi + b]) * (float)dot : 0.0f;
     }
 #pragma unroll
@@ -693,11 +724,11 @@ template <int FMT>
 hipError_t launch_decode_experts(const DecodeArgs& a, const DecodeGeometry& g, hipStream_t stream) {
   hipError_t err = hipSuccess;
   const int ns = a.k + (a.has_shared ? 1 : 0);
-  if (FMT == kQ4 && g.gt_sp > 0 && a.t_gate && a.t_up && (!a.has_shared || (a.ts_gate && a.ts_up))) {
+  if (g.gt_sp > 0 && a.t_gate && a.t_up && (!a.has_shared || (a.ts_gate && a.ts_up))) {
     dim3 grid(a.I / DGU_ROWS * ns);
     dim3 block(g.gt_threads);
 #define MOEQ4_GT(SPV) \
-  hipLaunchKernelGGL((decode_gateup_tiled_kernel<SPV>), grid, block, g.gu_lds, stream, a, g.gt_parts)
+  hipLaunchKernelGGL((decode_gateup_tiled_kernel<SPV, FMT>), grid, block, g.gu_lds, stream, a, g.gt_parts)
     switch (g.gt_sp) {
       case 1: MOEQ4_GT(1); break;
       case 2: MOEQ4_GT(2); break;
@@ -729,11 +760,11 @@ hipError_t launch_decode_experts(const DecodeArgs& a, const DecodeGeometry& g, h
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (FMT == kQ4 && g.dt_sp > 0 && a.t_down && (!a.has_shared || a.ts_down)) {
+  if (g.dt_sp > 0 && a.t_down && (!a.has_shared || a.ts_down)) {
     dim3 grid(a.H / kDtRows);
     dim3 block(g.dt_threads);
 #define MOEQ4_DT(SPV) \
-  hipLaunchKernelGGL((decode_down_tiled_kernel<SPV>), grid, block, g.dt_lds, stream, a)
+  hipLaunchKernelGGL((decode_down_tiled_kernel<SPV, FMT>), grid, block, g.dt_lds, stream, a)
     switch (g.dt_sp) {
       case 1: MOEQ4_DT(1); break;
       case 2: MOEQ4_DT(2); break;

@@ -10,6 +10,7 @@ hipError_t launch_q4_pack(const float* w, int64_t rows, int64_t K, void* packed,
                           hipStream_t stream);
 hipError_t launch_q8w_pack(const float* w, int64_t rows, int64_t K, void* packed, hipStream_t stream);
 hipError_t launch_q4_tile(const void* q4, int64_t rows, int64_t K, void* tiled, hipStream_t stream);
+hipError_t launch_q8w_tile(const void* q8, int64_t rows, int64_t K, void* tiled, hipStream_t stream);
 hipError_t launch_q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d,
                               hipStream_t stream);
 
@@ -84,8 +85,8 @@ struct DecodeArgs {
   const uint8_t* s_gate;
   const uint8_t* s_up;
   const uint8_t* s_down;
-  // tile-order copies (Q4_0), or NULL: the gate/up and down launches then
-  // read these instead of the row-major blocks
+  // tile-order copies (of the layer's weight format), or NULL: the gate/up
+  // and down launches then read these instead of the row-major blocks
   const uint8_t* t_gate;
   const uint8_t* t_up;
   const uint8_t* ts_gate;

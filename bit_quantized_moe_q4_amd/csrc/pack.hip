@@ -163,6 +163,39 @@ hipError_t launch_q4_tile(const void* q4, int64_t rows, int64_t K, void* tiled, 
   return hipGetLastError();
 }
 
+// The same tile order for Q8_0 blocks (layout stated in moe_q4.h at
+// q8w_tile): a step of 32 rows is one 2176-byte piece, lane l's 32 code
+// bytes at 32 * l, its fp16 scale at 2048 + 2 * l.  Source blocks are 2-byte
+// aligned: the codes are read as halfwords and written as two 16-byte stores.
+__global__ void __launch_bounds__(256) q8w_tile_kernel(const uint16_t* __restrict__ q8, int64_t nblocks,
+                                                       int nsteps, uint8_t* __restrict__ tiled) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nblocks) return;
+  const int l = (int)(i & 63);
+  const int64_t gs = i >> 6;                       // G * nsteps + s
+  const int64_t G = gs / nsteps;
+  const int st = (int)(gs - G * nsteps);
+  const int64_t rbh = (int64_t)nsteps * 34;        // row bytes / 2 (halfwords per row)
+  const int64_t row = 32 * G + (l & 31);
+  const int blk = 2 * st + (l >> 5);
+  const uint16_t* src = q8 + row * rbh + (int64_t)blk * 17;
+  uint32_t w[8];
+#pragma unroll
+  for (int c = 0; c < 8; c++) w[c] = (uint32_t)src[1 + 2 * c] | ((uint32_t)src[2 + 2 * c] << 16);
+  uint8_t* piece = tiled + gs * 2176;
+  *reinterpret_cast<uint4*>(piece + 32 * l) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(piece + 32 * l + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  *reinterpret_cast<uint16_t*>(piece + 2048 + 2 * l) = src[0];
+}
+
+hipError_t launch_q8w_tile(const void* q8, int64_t rows, int64_t K, void* tiled, hipStream_t stream) {
+  const int64_t nblocks = rows * (K / BLK);
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(q8w_tile_kernel, dim3((uint32_t)((nblocks + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q8), nblocks, (int)(K / 64), static_cast<uint8_t*>(tiled));
+  return hipGetLastError();
+}
+
 hipError_t launch_q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d,
                               hipStream_t stream) {
   int64_t nblocks = rows * (K / BLK);

@@ -33,7 +33,8 @@ def header_functions():
 
 def test_header_declares_the_api():
     names = header_functions()
-    for n in ["q4_packed_bytes", "q4_pack", "q4_tile", "q8w_packed_bytes", "q8w_pack", "q8_quantize", "moe_q4_route", "moe_q4_prefill",
+    for n in ["q4_packed_bytes", "q4_pack", "q4_tile", "q8w_packed_bytes", "q8w_pack", "q8w_tile", "q8_quantize",
+              "moe_q4_route", "moe_q4_prefill",
               "moe_q4_decode", "moe_q4_decode_batch", "moe_q4_decode_batch_workspace_bytes",
               "moe_q4_decode_stack", "moe_q4_decode_stack_workspace_bytes",
               "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
@@ -131,6 +132,19 @@ def test_q4_tile_argument_checks(lib):
     assert lib.q4_tile(None, 0, 64, None, None) == 0                                        # nothing to do
 
 
+def test_q8w_tile_argument_checks(lib):
+    assert lib.q8w_tile(C.c_void_p(0x1000), 33, 64, C.c_void_p(0x100000), None) == -1     # rows % 32
+    assert lib.q8w_tile(C.c_void_p(0x1000), 32, 96, C.c_void_p(0x100000), None) == -1     # K % 64
+    assert lib.q8w_tile(C.c_void_p(0x1001), 32, 64, C.c_void_p(0x100000), None) == -1     # q8 misaligned
+    assert lib.q8w_tile(C.c_void_p(0x1000), 32, 64, C.c_void_p(0x100008), None) == -1     # tiled misaligned
+    assert "aligned" in _err(lib)
+    # 32 rows x 2 blocks x 34 B = 2176 B: ranges that overlap by one byte
+    assert lib.q8w_tile(C.c_void_p(0x1000), 32, 64, C.c_void_p(0x1000 + 2176 - 16), None) == -1
+    assert "overlap" in _err(lib)
+    assert lib.q8w_tile(None, 32, 64, C.c_void_p(0x100000), None) == -1
+    assert lib.q8w_tile(None, 0, 64, None, None) == 0                                       # nothing to do
+
+
 def test_decode_batch_argument_checks(lib):
     L = _layer()
     ok = C.c_void_p(0x10000)
@@ -159,10 +173,10 @@ def test_q8_weight_checks(lib):
     L.weight_format = 2
     assert lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, 16, None, None, None, 0, None) == -1
     assert "weight_format" in _err(lib)
-    L.weight_format = 1                     # Q8_0 with tile-order copies
-    L.t_gate = L.t_up = L.t_down = 0x20000
+    L.weight_format = 1                     # Q8_0 tile-order copies follow the Q4_0 rules
+    L.t_gate = L.t_up = 0x20000
     assert lib.moe_q4_route(C.byref(L), C.c_void_p(0x1000), 1, 16, None, None, None, 0, None) == -1
-    assert "Q4_0" in _err(lib)
+    assert "together" in _err(lib)
     L = _layer()
     L.weight_format = 1                     # prefill refuses Q8_0 before anything else
     from bit_quantized_moe_q4_amd._lib import Routing

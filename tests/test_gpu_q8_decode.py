@@ -4,8 +4,11 @@ Bars: q8w_pack bytes bit-exact against the oracle's packing (and its
 hand-worked blocks); decode with Q8_0 layers bit-exact in every traced value
 (logits, ids, weights, q8(x), q8(h)) and y within max|dy|/max|y_ref| <= 1e-5
 (0 expected) against the oracle's W8A8 program; the batched decode on Q8_0
-layers bit-identical to one-token decode.  Shapes: the full decode layer,
-small layers on the halfword row program, H = 16384 and I = 8192.
+layers bit-identical to one-token decode; q8w_tile bytes against the tile
+order's byte permutation, and decode over the tile-order copies (the default
+for H, I multiples of 64) bit-identical to the row-major kernels.  Shapes:
+the full decode layer, small layers on the halfword row program, H = 16384,
+I = 8192, ragged and minimal tiled shapes.
 """
 import sys
 
@@ -66,6 +69,61 @@ def _decode_steps(ol, gl, cfg, steps):
         worst = max(worst, err)
         assert err <= DECODE_TOL, (step, err)
     return worst
+
+
+def _q8_tile_reference(packed: np.ndarray, K: int) -> np.ndarray:
+    """The tile order of moe_q4.h (q8w_tile) as a byte permutation of
+    row-major Q8_0 blocks [rows][K/32][34]."""
+    rows = packed.shape[0]
+    nb, ns = K // 32, K // 64
+    blk = packed.reshape(rows // 32, 32, ns, 2, 34)          # group, row, step, block-of-step, byte
+    out = np.empty((rows // 32, ns, 2176), dtype=np.uint8)
+    lanes = blk.transpose(0, 2, 3, 1, 4).reshape(rows // 32, ns, 64, 34)   # lane = 32 * g + n
+    out[:, :, :2048] = lanes[:, :, :, 2:].reshape(rows // 32, ns, 2048)
+    out[:, :, 2048:] = lanes[:, :, :, :2].reshape(rows // 32, ns, 128)
+    return out.reshape(rows, nb * 34)
+
+
+@pytest.mark.parametrize("rows,K", [(32, 64), (96, 128), (512, 2048), (2048, 512)])
+def test_q8w_tile_bytes(rows, K):
+    rng = np.random.default_rng(rows + 3 * K)
+    w = torch.from_numpy(rng.standard_normal((rows, K)).astype(np.float32)).cuda()
+    packed = mq.q8w_pack(w)
+    tiled = mq.q8w_tile(packed)
+    assert np.array_equal(tiled.cpu().numpy(), _q8_tile_reference(packed.cpu().numpy(), K))
+    # spot check: row 37 (group 1, n = 5), block 3 (step 1, g = 1) -> lane 37 of piece (1, 1)
+    if rows >= 64 and K >= 256:
+        pk, tl = packed.cpu().numpy(), tiled.cpu().numpy().reshape(-1)
+        piece = 32 * (K // 32 * 34) + 2176
+        blk = pk[37, 3 * 34:4 * 34]
+        assert bytes(tl[piece + 32 * 37: piece + 32 * 38]) == bytes(blk[2:])
+        assert bytes(tl[piece + 2048 + 2 * 37: piece + 2048 + 2 * 38]) == bytes(blk[:2])
+
+
+@pytest.mark.parametrize("name,H,E,I,k,shared", [
+    ("tiny_shared", 256, 8, 128, 2, True),
+    ("minimal", 64, 4, 64, 2, True),
+    ("ragged_pieces", 192, 16, 128, 4, True),
+    ("wide_hidden", 16384, 8, 64, 2, True),
+    ("ragged_inter", 256, 8, 192, 3, False),
+    ("wide_inter", 128, 8, 2048, 4, True),
+])
+def test_q8_decode_tiled_matches_rowmajor(name, H, E, I, k, shared):
+    # the Q8_0 tile-order decode kernels realise the row-major programs' trees
+    say("q8 decode tiled vs row-major", name)
+    from bit_quantized_moe_q4_amd.synth_layer import device_layer
+    cfg = moe_synth.CONFIGS["tiny"].with_(name=name, H=H, E=E, I=I, k=k, shared=shared, bias="zipf")
+    W = moe_synth.expert_weights(cfg, 0, threads=16)
+    gt = device_layer(cfg, weights=W, tiles=True, wfmt="q8")
+    gr = device_layer(cfg, weights=W, tiles=False, wfmt="q8")
+    assert gt.tiles is not None and gr.tiles is None
+    for step in range(3):
+        x = torch.from_numpy(moe_synth.tokens(cfg, step=step, T=1)[0]).cuda()
+        yt, tt = mq.moe_q4_decode(gt, x, trace=True)
+        yr, trr = mq.moe_q4_decode(gr, x, trace=True)
+        assert np.array_equal(yt.cpu().numpy().view(np.uint32), yr.cpu().numpy().view(np.uint32)), step
+        for key in ("ids", "w", "qh", "dh", "logits"):
+            assert np.array_equal(tt[key].cpu().numpy(), trr[key].cpu().numpy()), (step, key)
 
 
 @pytest.mark.parametrize("name,H,E,I,k,shared,bias", [
