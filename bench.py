@@ -436,8 +436,10 @@ def cpu_baseline(args, pre):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 50 warmup steps (~12 ms) let the clocks settle: after 5 the first timed
+    # steps ran ~5% slower than later ones
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--decode-copies", type=int, default=16)
     ap.add_argument("--decode-reps", type=int, default=3)
