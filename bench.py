@@ -403,7 +403,8 @@ def bench_small_batch(args, torch, mq, moe_synth, dec, pre):
         out["prefill_path_us"].append(round(t_p * 1e6, 2))
         del X, Y, ws, xb, R, rws, pws, yp
     out["note"] = ("per call, graph replay, layer copies rotated: batched = moe_q4_decode_batch (each "
-                   "token bit-identical to one-token decode); one_token_steps = M x the one-token "
+                   "token bit-identical to one-token decode; M <= 2 runs the one-token program per "
+                   "token, M >= 3 the batched kernels); one_token_steps = M x the one-token "
                    "decode step; prefill_path = moe_q4_route + moe_q4_prefill at T = M (bf16 GEMM, "
                    "2 layer copies); weight_gbps = bytes of the experts the call reads / time")
     return out

@@ -1,4 +1,5 @@
-"""GPU parity of the batched decode (moe_q4_decode_batch, up to 32 tokens).
+"""GPU parity of the batched decode (moe_q4_decode_batch, up to 32 tokens;
+batches of 1 or 2 tokens run the one-token program token by token).
 
 Each token of a batch follows the one-token decode program, so the bar is
 bit-exactness twice over: every row of y, and the routing ids and weights,
@@ -134,3 +135,25 @@ def test_decode_batch_empty_and_workspace(decode_layers):
         yb = mq.moe_q4_decode_batch(gl, torch.from_numpy(X).cuda(), ws=ws)
         yr = np.stack([mq.moe_q4_decode(gl, torch.from_numpy(X[t]).cuda()).cpu().numpy() for t in range(M)])
         assert np.array_equal(yb.cpu().numpy(), yr)
+
+
+def test_decode_batch_one_or_two_tokens_use_the_one_token_program(decode_layers):
+    # M <= 2: the one-token program per token, in the one-token workspace;
+    # a workspace sized for 32 tokens serves them too
+    cfg, ol, gl = decode_layers
+    one = mq.decode_workspace(gl).numel()
+    assert mq.moe_q4_decode_batch_workspace_bytes(gl, 1) == one
+    assert mq.moe_q4_decode_batch_workspace_bytes(gl, 2) == one
+    assert mq.moe_q4_decode_batch_workspace_bytes(gl, 3) > one
+    big = torch.empty(mq.moe_q4_decode_batch_workspace_bytes(gl, 32), dtype=torch.uint8, device="cuda")
+    for M in (1, 2):
+        X = _batch_tokens(cfg, M, 5000 + M)
+        xd = torch.from_numpy(X).cuda()
+        exact = torch.empty(mq.moe_q4_decode_batch_workspace_bytes(gl, M), dtype=torch.uint8, device="cuda")
+        for ws in (exact, big):
+            yb, ids, w = mq.moe_q4_decode_batch(gl, xd, ws=ws, routing=True)
+            for t in range(M):
+                y1, tr = mq.moe_q4_decode(gl, xd[t].contiguous(), trace=True)
+                assert np.array_equal(yb[t].cpu().numpy().view(np.uint32), y1.cpu().numpy().view(np.uint32))
+                assert np.array_equal(ids[t].cpu().numpy(), tr["ids"].cpu().numpy())
+                assert np.array_equal(w[t].cpu().numpy().view(np.uint32), tr["w"].cpu().numpy().view(np.uint32))
