@@ -4,8 +4,8 @@ The stack runs each layer's decode with the RMSNorm between layers taken
 inside the next layer's first kernel.  Bars: y bit-identical to the chain of
 moe_q4_decode and moe_q4_rmsnorm calls, and to the oracle's chain of decode
 and rmsnorm (both are the same fp32 programs), on a 6-layer stack of small
-layers (Q4_0 row-major and tile order, Q8_0) and a 4-layer stack at the
-decode layer's shape (both Q4_0 layouts).
+layers (Q4_0 and Q8_0, each row-major and in tile order) and a 4-layer
+stack at the decode layer's shape (both Q4_0 layouts).
 """
 import sys
 
@@ -45,8 +45,8 @@ def _oracle_chain(ols, x):
     return y
 
 
-@pytest.mark.parametrize("wfmt,tiles", [("q4", False), ("q4", True), ("q8", False)],
-                         ids=["q4-rowmajor", "q4-tiled", "q8"])
+@pytest.mark.parametrize("wfmt,tiles", [("q4", False), ("q4", True), ("q8", False), ("q8", True)],
+                         ids=["q4-rowmajor", "q4-tiled", "q8-rowmajor", "q8-tiled"])
 def test_stack_small_layers(wfmt, tiles):
     cfg = moe_synth.CONFIGS["tiny"].with_(name="stack_small", H=256, E=8, I=128, k=2, shared=True)
     pairs = [both_layers(cfg, layer=l, tiles=tiles, wfmt=wfmt) for l in range(6)]
