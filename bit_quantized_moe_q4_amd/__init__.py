@@ -27,7 +27,7 @@ __all__ = [
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
     "moe_q4_decode_batch_workspace_bytes", "moe_q4_decode_batch",
     "LayerStack", "moe_q4_decode_stack_workspace_bytes", "moe_q4_decode_stack",
-    "moe_q4_w4a8_gemv", "moe_q4_rmsnorm", "library_path",
+    "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm", "library_path",
 ]
 
 
@@ -384,6 +384,20 @@ def moe_q4_w4a8_gemv(W: torch.Tensor, N: int, K: int, qa: torch.Tensor, da: torc
     out = torch.empty(N, dtype=torch.float32, device=W.device)
     _lib.check(_lib.lib().moe_q4_w4a8_gemv(_p(W), N, K, _p(qa), _p(da), _p(dots), _p(out), _s(stream)),
                "moe_q4_w4a8_gemv")
+    return dots, out
+
+
+def moe_q4_w4a8_gemm(Wt: torch.Tensor, N: int, K: int, qa: torch.Tensor, da: torch.Tensor,
+                     with_dots: bool = False, stream=None):
+    """The row program for M tokens on int8 MFMA: Wt (tile order, q4_tile), qa
+    int8 [M, K], da fp32 [M, K/32] -> (dots int32 [M, N, K/32] | None, out fp32 [M, N])."""
+    for n, t in (("Wt", Wt), ("qa", qa), ("da", da)):
+        _dev(t, n)
+    M = int(qa.shape[0])
+    dots = torch.empty((M, N, K // 32), dtype=torch.int32, device=Wt.device) if with_dots else None
+    out = torch.empty((M, N), dtype=torch.float32, device=Wt.device)
+    _lib.check(_lib.lib().moe_q4_w4a8_gemm(_p(Wt), N, K, _p(qa), _p(da), M, _p(dots), _p(out), _s(stream)),
+               "moe_q4_w4a8_gemm")
     return dots, out
 
 

@@ -537,6 +537,19 @@ int moe_q4_w4a8_gemv(const void* W, int32_t N, int32_t K, const int8_t* qa, cons
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_w4a8_gemv");
 }
 
+int moe_q4_w4a8_gemm(const void* Wt, int32_t N, int32_t K, const int8_t* qa, const float* da, int32_t M,
+                     int32_t* dots, float* out, hipStream_t stream) {
+  if (N < 0 || N % 32 || K < 64 || K % 64 || K > 4096 || M < 0)
+    return fail(MOE_Q4_EINVAL, "moe_q4_w4a8_gemm: N=%d K=%d M=%d (N %% 32 == 0, K %% 64 == 0, 64 <= K <= 4096)",
+                N, K, M);
+  if (N == 0 || M == 0) return MOE_Q4_OK;
+  if (!Wt || !qa || !da || !out) return fail(MOE_Q4_EINVAL, "moe_q4_w4a8_gemm: NULL pointer");
+  if (!aligned(Wt, 16) || !aligned(qa, 16) || !aligned(da, 4) || !aligned(out, 4) || !aligned(dots, 4))
+    return fail(MOE_Q4_EINVAL, "moe_q4_w4a8_gemm: Wt and qa 16-byte, da, dots and out 4-byte alignment");
+  hipError_t e = moeq4::launch_w4a8_gemm(static_cast<const uint8_t*>(Wt), N, K, qa, da, M, dots, out, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_w4a8_gemm");
+}
+
 int moe_q4_rmsnorm(const float* y, int32_t T, int32_t H, float eps, float* out_f32,
                    uint16_t* out_bf16, hipStream_t stream) {
   if (T < 0 || H <= 0 || H % 32 || H > kMaxDim)

@@ -11,6 +11,10 @@ hipError_t launch_q4_pack(const float* w, int64_t rows, int64_t K, void* packed,
 hipError_t launch_q8w_pack(const float* w, int64_t rows, int64_t K, void* packed, hipStream_t stream);
 hipError_t launch_q4_tile(const void* q4, int64_t rows, int64_t K, void* tiled, hipStream_t stream);
 hipError_t launch_q8w_tile(const void* q8, int64_t rows, int64_t K, void* tiled, hipStream_t stream);
+// W4A8 row program for M tokens on int8 MFMA (weights in q4_tile order).
+size_t w4a8_gemm_lds_bytes(int K);
+hipError_t launch_w4a8_gemm(const uint8_t* Wt, int N, int K, const int8_t* qa, const float* da, int M,
+                            int32_t* dots, float* out, hipStream_t stream);
 hipError_t launch_q8_quantize(const float* x, int64_t rows, int64_t K, int8_t* q, float* d,
                               hipStream_t stream);
 

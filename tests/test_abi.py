@@ -38,7 +38,7 @@ def test_header_declares_the_api():
               "moe_q4_decode", "moe_q4_decode_batch", "moe_q4_decode_batch_workspace_bytes",
               "moe_q4_decode_stack", "moe_q4_decode_stack_workspace_bytes",
               "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
-              "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_rmsnorm",
+              "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm",
               "moe_q4_last_error"]:
         assert n in names, n
 
@@ -143,6 +143,18 @@ def test_q8w_tile_argument_checks(lib):
     assert "overlap" in _err(lib)
     assert lib.q8w_tile(None, 32, 64, C.c_void_p(0x100000), None) == -1
     assert lib.q8w_tile(None, 0, 64, None, None) == 0                                       # nothing to do
+
+
+def test_w4a8_gemm_argument_checks(lib):
+    ok = C.c_void_p(0x100000)
+    assert lib.moe_q4_w4a8_gemm(ok, 48, 128, ok, ok, 4, None, ok, None) == -1       # N % 32
+    assert lib.moe_q4_w4a8_gemm(ok, 64, 96, ok, ok, 4, None, ok, None) == -1        # K % 64
+    assert lib.moe_q4_w4a8_gemm(ok, 64, 8192, ok, ok, 4, None, ok, None) == -1      # K > 4096
+    assert "4096" in _err(lib)
+    assert lib.moe_q4_w4a8_gemm(ok, 64, 128, ok, ok, -1, None, ok, None) == -1      # M < 0
+    assert lib.moe_q4_w4a8_gemm(C.c_void_p(0x100008), 64, 128, ok, ok, 4, None, ok, None) == -1   # Wt alignment
+    assert lib.moe_q4_w4a8_gemm(ok, 64, 128, None, ok, 4, None, ok, None) == -1     # NULL
+    assert lib.moe_q4_w4a8_gemm(None, 64, 128, None, None, 0, None, None, None) == 0   # nothing to do
 
 
 def test_decode_batch_argument_checks(lib):

@@ -457,6 +457,30 @@ def test_w4a8_dots_of_decode_layer_rows():
     assert np.array_equal(out.cpu().numpy(), out_o)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 32, 64), (37, 96, 192), (64, 128, 2048), (130, 512, 2048), (33, 64, 4096)])
+def test_w4a8_gemm_is_the_row_program(M, N, K):
+    # int8 MFMA block dots bit-exact against the oracle's, and every output
+    # row bit-identical to the one-token GEMV of the same token
+    rng = np.random.default_rng(M * 131 + N + K)
+    w = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).cuda()
+    W = mq.q4_pack(w)
+    Wt = mq.q4_tile(W)
+    x = (rng.standard_normal((M, K)) * rng.choice([0.1, 1.0, 30.0], size=(M, 1))).astype(np.float32)
+    x[0, :32] = 0.0                                   # an all-zero activation block
+    qa, da = oracle.q8_quantize(x)
+    qad, dad = torch.from_numpy(qa).cuda(), torch.from_numpy(da).cuda()
+    dots, out = mq.moe_q4_w4a8_gemm(Wt, N, K, qad, dad, with_dots=True)
+    dots, out = dots.cpu().numpy(), out.cpu().numpy()
+    Wn = W.cpu().numpy()
+    for m in sorted({0, M // 2, M - 1}):
+        dots_o, out_o = oracle.w4a8_gemv(Wn, K, qa[m], da[m])
+        assert np.array_equal(dots[m], dots_o), m
+        assert np.array_equal(out[m].view(np.uint32), out_o.astype(np.float32).view(np.uint32)), m
+    for m in range(M):
+        _, o1 = mq.moe_q4_w4a8_gemv(W, N, K, qad[m].contiguous(), dad[m].contiguous(), with_dots=False)
+        assert np.array_equal(out[m].view(np.uint32), o1.cpu().numpy().view(np.uint32)), m
+
+
 # ---------------------------------------------------------------- glue
 @pytest.mark.parametrize("T,H", [(1, 2048), (9, 96), (64, 256)])
 def test_rmsnorm_bit_exact(T, H):
