@@ -44,6 +44,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E peak
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 matrix peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -355,6 +356,35 @@ def _graph_time(torch, calls, reps):
     return (time.perf_counter() - t0) / (reps * len(calls))
 
 
+def bench_w4a8_gemm(args, torch, mq, bf16_tflops):
+    """The W4A8 row program in GEMM form on int8 MFMA (moe_q4_w4a8_gemm):
+    2048 tokens against the shared expert's gate and up rows (N = 2I = 1024,
+    K = H = 2048), the same algorithmic work per token as the bf16 grouped
+    GEMM's gate/up; back-to-back calls between two events."""
+    M, N, K = 2048, 1024, 2048
+    g = torch.Generator(device="cuda").manual_seed(7)
+    Wt = mq.q4_tile(mq.q4_pack(torch.randn((N, K), generator=g, device="cuda") * 0.02))
+    qa, da = mq.q8_quantize(torch.randn((M, K), generator=g, device="cuda"))
+    for _ in range(3):
+        mq.moe_q4_w4a8_gemm(Wt, N, K, qa, da)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        mq.moe_q4_w4a8_gemm(Wt, N, K, qa, da)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    tops = 2.0 * M * N * K / t / 1e12
+    return {"workload": "moe_q4_w4a8_gemm: %d tokens x %d Q4_0 weight rows (tile order) x K %d, int8 MFMA "
+                        "block dots, per-block fp32 rescale and the pinned tree (bit-identical to the "
+                        "one-token GEMV)" % (M, N, K),
+            "us": round(t * 1e6, 2), "tops": round(tops, 2), "peak_int8_tops": PEAK_INT8_TOPS,
+            "frac": round(tops / PEAK_INT8_TOPS, 4), "bf16_grouped_gemm_tflops": round(bf16_tflops, 2),
+            "ratio_to_bf16_path": round(tops / bf16_tflops, 4)}
+
+
 def bench_small_batch(args, torch, mq, moe_synth, dec, pre):
     """Decode of M = 1..32 tokens: one batched W4A8 call (weights of an expert
     read once per call) against M one-token steps and against the prefill
@@ -449,6 +479,7 @@ def main():
     ap.add_argument("--no-small-batch", action="store_true", help="skip the 1..32-token decode comparison")
     ap.add_argument("--no-q8", action="store_true", help="skip the Q8_0-weight decode comparison")
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer stack decode")
+    ap.add_argument("--no-w4a8-gemm", action="store_true", help="skip the int8-MFMA W4A8 GEMM leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -546,6 +577,7 @@ def main():
     }
     out["small_batch_decode"] = small
     out["stack_decode"] = stackr
+    out["w4a8_gemm"] = None if args.no_w4a8_gemm else bench_w4a8_gemm(args, torch, mq, ach)
     if dec8 is not None:
         g8 = dec8["bytes_step"] / dec8["step_s"] / 1e9
         out["decode_q8_0"] = {
