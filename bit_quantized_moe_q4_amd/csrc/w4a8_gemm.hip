@@ -33,8 +33,8 @@
 // bytes of block b0 + g of its token row (whole cache lines), and a 4 x 4
 // transpose across the lane quarters (two rounds of permlane swaps) leaves
 // quarter g holding elements 8 g .. +7 of each of the four blocks.  The code
-// sums for the -8 correction come from a second MFMA against all-ones
-// weights, already in the output layout.  The next four blocks' operands are
+// sums for the -8 correction come from a second MFMA against weights that
+// are all 8, so it yields 8 x the sum, already in the output layout.  The next four blocks' operands are
 // in flight while the current four are reduced.
 #include "launch.hpp"
 #include "device_math.hpp"
@@ -44,7 +44,7 @@ namespace moeq4 {
 typedef int w8_v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kW8Levels = 8;                 // tree levels: up to 128 blocks (K <= 4096)
-constexpr long kW8Ones = 0x0101010101010101L;
+constexpr long kW8Eights = 0x0808080808080808L;     // B operand of the code-sum MFMA: 8 x the sum
 
 struct W8Quad {
   uint4 a0, a1;                              // 32 activation bytes: block b0 + g of the lane's token row
@@ -132,7 +132,7 @@ __device__ __forceinline__ void w8_leaf(float (&st)[4][kW8Levels], const float (
 // One block of the row: the MFMAs, the correction and rescale of the four
 // dots, and the leaf's merge.  LIVE = false: b may lie past the row (then the
 // leaf is +0 and no dot is written).
-template <int LG, bool LIVE>
+template <int LG, bool LIVE, bool DOTS>
 __device__ __forceinline__ void w8_block(float (&st)[4][kW8Levels], long a, long w, uint32_t sc, int b, int nb,
                                          int i, int grp, const float* da_l, int t0, int sh, int m0, int M, int N,
                                          int n, int32_t* dots) {
@@ -140,7 +140,7 @@ __device__ __forceinline__ void w8_block(float (&st)[4][kW8Levels], long a, long
   const uint32_t lo = (uint32_t)w, hi = (uint32_t)((unsigned long)w >> 32);
   const long bw = (long)(((unsigned long)((hi >> sh) & 0x0f0f0f0fu) << 32) | ((lo >> sh) & 0x0f0f0f0fu));
   const w8_v4i acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw, zero, 0, 0, 0);
-  const w8_v4i sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, kW8Ones, zero, 0, 0, 0);
+  const w8_v4i sum8 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, kW8Eights, zero, 0, 0, 0);
   const float dw = f16_bits_to_f32(sc);
   const int bc = LIVE ? b : min(b, nb - 1);
   const float4 d4 = *reinterpret_cast<const float4*>(da_l + bc * 32 + t0);
@@ -149,8 +149,8 @@ __device__ __forceinline__ void w8_block(float (&st)[4][kW8Levels], long a, long
   float v[4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    const int32_t dot = acc[r] - 8 * sum[r];
-    if (dots && live) {
+    const int32_t dot = acc[r] - sum8[r];
+    if (DOTS && live) {
       const int m = m0 + t0 + r;
       if (m < M) dots[((size_t)m * N + n) * nb + b] = dot;
     }
@@ -160,8 +160,8 @@ __device__ __forceinline__ void w8_block(float (&st)[4][kW8Levels], long a, long
   w8_leaf<LG>(st, v, i, grp);
 }
 
-template <int LG>
-__global__ void __launch_bounds__(256, 3) w4a8_gemm_kernel(const uint8_t* __restrict__ Wt, int N, int K,
+template <int LG, bool DOTS>
+__global__ void __launch_bounds__(256, 2) w4a8_gemm_kernel(const uint8_t* __restrict__ Wt, int N, int K,
                                                        const int8_t* __restrict__ qa,
                                                        const float* __restrict__ da, int M,
                                                        int32_t* __restrict__ dots, float* __restrict__ out) {
@@ -215,7 +215,7 @@ __global__ void __launch_bounds__(256, 3) w4a8_gemm_kernel(const uint8_t* __rest
         w8_transpose(cur, R);
 #pragma unroll
         for (int t = 0; t < TQ; t++)
-          w8_block<LG, true>(st, R[t], cur.w[t], cur.sc[t], c + 4 * qd + t, nb, 4 * qd + t, c >> LG, da_l, t0,
+          w8_block<LG, true, DOTS>(st, R[t], cur.w[t], cur.sc[t], c + 4 * qd + t, nb, 4 * qd + t, c >> LG, da_l, t0,
                              sh, m0, M, N, n, dots);
       }
     } else {                                                 // the row's end: clamped loads, +0 leaves
@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(256, 3) w4a8_gemm_kernel(const uint8_t* __rest
         w8_transpose(cur, R);
 #pragma unroll
         for (int t = 0; t < TQ; t++)
-          w8_block<LG, false>(st, R[t], cur.w[t], cur.sc[t], c + 4 * qd + t, nb, 4 * qd + t, c >> LG, da_l, t0,
+          w8_block<LG, false, DOTS>(st, R[t], cur.w[t], cur.sc[t], c + 4 * qd + t, nb, 4 * qd + t, c >> LG, da_l, t0,
                               sh, m0, M, N, n, dots);
       }
     }
@@ -253,12 +253,18 @@ hipError_t launch_w4a8_gemm(const uint8_t* Wt, int N, int K, const int8_t* qa, c
   int m2 = 1;
   while (m2 < K / 32) m2 <<= 1;                              // K >= 64: m2 >= 2
   const size_t lds = w4a8_gemm_lds_bytes(K);
-  if (m2 >= 8)
-    hipLaunchKernelGGL(w4a8_gemm_kernel<3>, grid, dim3(256), lds, stream, Wt, N, K, qa, da, M, dots, out);
-  else if (m2 == 4)
-    hipLaunchKernelGGL(w4a8_gemm_kernel<2>, grid, dim3(256), lds, stream, Wt, N, K, qa, da, M, dots, out);
-  else
-    hipLaunchKernelGGL(w4a8_gemm_kernel<1>, grid, dim3(256), lds, stream, Wt, N, K, qa, da, M, dots, out);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), lds, stream, Wt, N, K, qa, da, M, dots, out);
+  };
+  if (dots) {
+    if (m2 >= 8) go(w4a8_gemm_kernel<3, true>);
+    else if (m2 == 4) go(w4a8_gemm_kernel<2, true>);
+    else go(w4a8_gemm_kernel<1, true>);
+  } else {
+    if (m2 >= 8) go(w4a8_gemm_kernel<3, false>);
+    else if (m2 == 4) go(w4a8_gemm_kernel<2, false>);
+    else go(w4a8_gemm_kernel<1, false>);
+  }
   return hipGetLastError();
 }
 
