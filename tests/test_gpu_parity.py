@@ -457,7 +457,11 @@ def test_w4a8_dots_of_decode_layer_rows():
     assert np.array_equal(out.cpu().numpy(), out_o)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 32, 64), (37, 96, 192), (64, 128, 2048), (130, 512, 2048), (33, 64, 4096)])
+# K/32 blocks per row: 2 and 4 (a single group of 2 or 4 leaves), 6 (one
+# group of 8 with +0 leaves), 20 and 34 (groups of 8 taken four blocks at a
+# time, then a ragged group and groups of +0 leaves), 64 and 128
+@pytest.mark.parametrize("M,N,K", [(1, 32, 64), (5, 32, 128), (37, 96, 192), (31, 160, 640), (70, 96, 1088),
+                                   (64, 128, 2048), (130, 512, 2048), (33, 64, 4096)])
 def test_w4a8_gemm_is_the_row_program(M, N, K):
     # int8 MFMA block dots bit-exact against the oracle's, and every output
     # row bit-identical to the one-token GEMV of the same token
@@ -471,6 +475,8 @@ def test_w4a8_gemm_is_the_row_program(M, N, K):
     qad, dad = torch.from_numpy(qa).cuda(), torch.from_numpy(da).cuda()
     dots, out = mq.moe_q4_w4a8_gemm(Wt, N, K, qad, dad, with_dots=True)
     dots, out = dots.cpu().numpy(), out.cpu().numpy()
+    _, out_nd = mq.moe_q4_w4a8_gemm(Wt, N, K, qad, dad, with_dots=False)
+    assert np.array_equal(out_nd.cpu().numpy().view(np.uint32), out.view(np.uint32))   # the kernel without the export
     Wn = W.cpu().numpy()
     for m in sorted({0, M // 2, M - 1}):
         dots_o, out_o = oracle.w4a8_gemv(Wn, K, qa[m], da[m])
