@@ -539,8 +539,9 @@ int moe_q4_w4a8_gemv(const void* W, int32_t N, int32_t K, const int8_t* qa, cons
 
 int moe_q4_w4a8_gemm(const void* Wt, int32_t N, int32_t K, const int8_t* qa, const float* da, int32_t M,
                      int32_t* dots, float* out, hipStream_t stream) {
-  if (N < 0 || N % 32 || K < 64 || K % 64 || K > 4096 || M < 0)
-    return fail(MOE_Q4_EINVAL, "moe_q4_w4a8_gemm: N=%d K=%d M=%d (N %% 32 == 0, K %% 64 == 0, 64 <= K <= 4096)",
+  if (N < 0 || N % 32 || N / 32 > 65535 || K < 64 || K % 64 || K > 4096 || M < 0)
+    return fail(MOE_Q4_EINVAL,
+                "moe_q4_w4a8_gemm: N=%d K=%d M=%d (N %% 32 == 0, N <= 2097120, K %% 64 == 0, 64 <= K <= 4096)",
                 N, K, M);
   if (N == 0 || M == 0) return MOE_Q4_OK;
   if (!Wt || !qa || !da || !out) return fail(MOE_Q4_EINVAL, "moe_q4_w4a8_gemm: NULL pointer");

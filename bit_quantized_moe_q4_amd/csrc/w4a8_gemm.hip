@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(256, 2) w4a8_gemm_kernel(const uint8_t* __rest
   float* da_l = reinterpret_cast<float*>(dyn);               // [nb][32] activation block scales per token
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int m0 = blockIdx.y * 32;
+  const int m0 = blockIdx.x * 32;
   for (int i0 = tid; i0 < nb * 32; i0 += 4 * 256) {
     float x[4];
 #pragma unroll
@@ -189,8 +189,8 @@ __global__ void __launch_bounds__(256, 2) w4a8_gemm_kernel(const uint8_t* __rest
 
   const int j = lane % 16, g = lane / 16;
   const int tw = 16 * (wave & 1), rw = 16 * (wave >> 1);    // the wave's token and weight-row offsets
-  const int n = blockIdx.x * 32 + rw + j;                    // this lane's weight row (N % 32 == 0: in range)
-  const uint8_t* grp = Wt + (size_t)blockIdx.x * (size_t)nsteps * 1152;
+  const int n = blockIdx.y * 32 + rw + j;                    // this lane's weight row (N % 32 == 0: in range)
+  const uint8_t* grp = Wt + (size_t)blockIdx.y * (size_t)nsteps * 1152;
   const uint8_t* wrow = grp + 16 * (rw + j) + 8 * (g & 1);
   const uint8_t* srow = grp + 1024 + 2 * (rw + j);
   const int8_t* arow = qa + (size_t)min(m0 + tw + j, M - 1) * K;
@@ -249,7 +249,9 @@ size_t w4a8_gemm_lds_bytes(int K) { return (size_t)(K / 32) * 32 * 4; }
 
 hipError_t launch_w4a8_gemm(const uint8_t* Wt, int N, int K, const int8_t* qa, const float* da, int M,
                             int32_t* dots, float* out, hipStream_t stream) {
-  dim3 grid(N / 32, (M + 31) / 32);
+  // token tiles along x: consecutive blocks go to different XCDs, so each
+  // XCD's L2 holds its own token tiles' activations (N / 32 <= 65535)
+  dim3 grid((M + 31) / 32, N / 32);
   int m2 = 1;
   while (m2 < K / 32) m2 <<= 1;                              // K >= 64: m2 >= 2
   const size_t lds = w4a8_gemm_lds_bytes(K);

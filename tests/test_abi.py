@@ -148,6 +148,7 @@ def test_q8w_tile_argument_checks(lib):
 def test_w4a8_gemm_argument_checks(lib):
     ok = C.c_void_p(0x100000)
     assert lib.moe_q4_w4a8_gemm(ok, 48, 128, ok, ok, 4, None, ok, None) == -1       # N % 32
+    assert lib.moe_q4_w4a8_gemm(ok, 2097152, 128, ok, ok, 4, None, ok, None) == -1  # N / 32 > 65535
     assert lib.moe_q4_w4a8_gemm(ok, 64, 96, ok, ok, 4, None, ok, None) == -1        # K % 64
     assert lib.moe_q4_w4a8_gemm(ok, 64, 8192, ok, ok, 4, None, ok, None) == -1      # K > 4096
     assert "4096" in _err(lib)
