@@ -23,7 +23,7 @@ from . import _lib
 __all__ = [
     "q4_packed_bytes", "q4_pack", "q4_tile", "q8w_pack", "q8w_tile", "q8_quantize", "MoELayer", "Routing",
     "moe_q4_route_workspace_bytes", "moe_q4_route",
-    "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage",
+    "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage", "moe_q4_prefill_status",
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
     "moe_q4_decode_batch_workspace_bytes", "moe_q4_decode_batch",
     "LayerStack", "moe_q4_decode_stack_workspace_bytes", "moe_q4_decode_stack",
@@ -268,6 +268,15 @@ def moe_q4_prefill_stage(layer: MoELayer, x_bf16: torch.Tensor, routing: Routing
                                                _p(ws), ws.numel(), int(stages), _s(stream)),
                "moe_q4_prefill_stage")
     return y
+
+
+def moe_q4_prefill_status(layer: MoELayer, T: int, ws: torch.Tensor, stream=None) -> int:
+    """Down units of the last fused prefill launch on `ws` whose bounded wait
+    gave up (0: all waits ended normally).  Waits for the stream."""
+    n = C.c_int32(-1)
+    _lib.check(_lib.lib().moe_q4_prefill_status(layer.struct_ptr(), int(T), _p(ws), ws.numel(), C.byref(n),
+                                                _s(stream)), "moe_q4_prefill_status")
+    return int(n.value)
 
 
 # ------------------------------------------------------------------ decode

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(PKG, "libmoe_q4.so")
 MOE_Q4_OK, MOE_Q4_EINVAL, MOE_Q4_EWORKSPACE, MOE_Q4_EHIP = 0, -1, -2, -3
 MOE_Q4_F32, MOE_Q4_BF16 = 0, 1
 STAGE_GATEUP, STAGE_DOWN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
+STAGE_TEST_WAIT_FAIL = 16
 
 EXPORTS = [
     "q4_packed_bytes", "q4_pack", "q8_quantize",
@@ -74,6 +75,7 @@ def _declare(lib):
         "moe_q4_prefill_workspace_bytes": (SZ, [P, I32]),
         "moe_q4_prefill": (C.c_int, [P, P, I32, P, P, P, SZ, P]),
         "moe_q4_prefill_stage": (C.c_int, [P, P, I32, P, P, P, SZ, I32, P]),
+        "moe_q4_prefill_status": (C.c_int, [P, I32, P, SZ, P, P]),
         "moe_q4_decode_workspace_bytes": (SZ, [P]),
         "moe_q4_decode_batch_workspace_bytes": (SZ, [P, I32]),
         "moe_q4_decode_stack_workspace_bytes": (SZ, [P, I32]),

@@ -96,7 +96,8 @@ PrefillWs prefill_ws(const moe_q4_layer* L, int32_t T) {
   w.h = 0;
   w.o = w.h + up256(rows * L->inter * 2);
   w.tile_done = w.o + up256((size_t)T * L->top_k * L->hidden * 2);
-  w.total = w.tile_done + up256((size_t)moeq4::prefill_tile_bound(T, L->top_k, L->n_experts, L->has_shared) * 4);
+  // per-tile counters of the fused launch, then the count of waits that gave up
+  w.total = w.tile_done + up256(((size_t)moeq4::prefill_tile_bound(T, L->top_k, L->n_experts, L->has_shared) + 1) * 4);
   return w;
 }
 
@@ -323,8 +324,10 @@ int moe_q4_prefill(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T,
 int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T,
                          const moe_q4_routing* routing, float* y, void* ws, size_t ws_bytes,
                          int32_t stages, hipStream_t stream) {
+  const int test_wait_fail = (stages & MOE_Q4_STAGE_TEST_WAIT_FAIL) != 0;
+  stages &= ~MOE_Q4_STAGE_TEST_WAIT_FAIL;
   if (stages <= 0 || stages > MOE_Q4_STAGE_ALL)
-    return fail(MOE_Q4_EINVAL, "moe_q4_prefill_stage: stages=%d must be a non-empty mask of 1|2|4", stages);
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill_stage: stages=%d must be a non-empty mask of 1|2|4 (| 16)", stages);
   int rc = check_layer(L);
   if (rc) return rc;
   if (T < 0) return fail(MOE_Q4_EINVAL, "moe_q4_prefill: T=%d < 0", T);
@@ -366,9 +369,31 @@ int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t 
   a.h = at<uint16_t>(ws, W.h);
   a.o_perm = at<uint16_t>(ws, W.o);
   a.tile_done = at<int32_t>(ws, W.tile_done);
+  a.test_wait_fail = test_wait_fail;
   a.y = y;
   hipError_t e = moeq4::launch_prefill(a, stages, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_prefill");
+}
+
+int moe_q4_prefill_status(const moe_q4_layer* L, int32_t T, const void* ws, size_t ws_bytes,
+                          int32_t* failed_waits, hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0 || !failed_waits) return fail(MOE_Q4_EINVAL, "moe_q4_prefill_status: T=%d, failed_waits=%p", T,
+                                          (void*)failed_waits);
+  *failed_waits = 0;
+  if (T == 0) return MOE_Q4_OK;
+  const PrefillWs W = prefill_ws(L, T);
+  rc = check_ws(const_cast<void*>(ws), ws_bytes, W.total);
+  if (rc) return rc;
+  const size_t n_tiles = (size_t)moeq4::prefill_tile_bound(T, L->top_k, L->n_experts, L->has_shared);
+  const char* src = static_cast<const char*>(ws) + W.tile_done + n_tiles * 4;
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, src, 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_q4_prefill_status");
+  *failed_waits = v;
+  return MOE_Q4_OK;
 }
 
 // Batches of up to this many tokens run the one-token program token by

@@ -693,10 +693,12 @@ __global__ void __launch_bounds__(256, 2) gemm_g2_kernel(PrefillArgs a, int ncb)
 // gate/up unit ends with an agent-scope release increment of tile_done[tile],
 // and the down unit's thread 0 polls it and takes an acquire fence.  Down
 // work thus fills the CUs that the last gate/up units leave idle, and the
-// other way round.  The wait always ends: every gate/up block has a lower
-// index than every down block, so it is dispatched first, and it waits on
-// nothing; the poll is bounded all the same.  tile_done is zeroed by a fill
-// launch just before.
+// other way round.  The wait ends: every gate/up block has a lower index than
+// every down block, so it is dispatched first, and it waits on nothing.  The
+// poll is bounded all the same (spin_max polls); a down unit whose wait gives
+// up stores nothing and counts itself in tile_done[n_tiles], which the host
+// reads back (moe_q4_prefill_status).  tile_done, that count included, is
+// zeroed by a fill launch just before.
 constexpr int kTileSpinMax = 1 << 22;
 
 __global__ void __launch_bounds__(256) fill_zero_kernel(int32_t* __restrict__ p, int n) {
@@ -704,8 +706,10 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(int32_t* __restrict__ p,
   if (i < n) p[i] = 0;
 }
 
-__global__ void __launch_bounds__(256, 2) gemm_ffn_kernel(PrefillArgs a, int ncb_gu, int ncb_dn, int n_gu) {
+__global__ void __launch_bounds__(256, 2) gemm_ffn_kernel(PrefillArgs a, int ncb_gu, int ncb_dn, int n_gu,
+                                                          int n_tiles, int need, int spin_max) {
   __shared__ __attribute__((aligned(16))) G2Smem sm;
+  __shared__ int gave_up;
   const bool gu = (int)blockIdx.x < n_gu;
   const int b = gu ? (int)blockIdx.x : (int)blockIdx.x - n_gu;   // n_gu % 8 == 0: same XCD mapping
   const int ncb = gu ? ncb_gu : ncb_dn;
@@ -732,13 +736,16 @@ __global__ void __launch_bounds__(256, 2) gemm_ffn_kernel(PrefillArgs a, int ncb
   }
   if (threadIdx.x == 0) {
     int n = __hip_atomic_load(a.tile_done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int it = 0; n < ncb_gu && it < kTileSpinMax; it++) {
+    for (int it = 0; n < need && it < spin_max; it++) {
       __builtin_amdgcn_s_sleep(8);
       n = __hip_atomic_load(a.tile_done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    gave_up = n < need;
+    if (n < need) __hip_atomic_fetch_add(a.tile_done + n_tiles, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  if (gave_up) return;                    // h of this tile may be incomplete: store nothing
   switch (S) {
     case 1: g2_tile<1, false>(a, t, cb, sm); break;
     case 2: g2_tile<2, false>(a, t, cb, sm); break;
@@ -816,15 +823,24 @@ hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream) 
   const int vec_d = ((a.I / BLK) % 4 == 0) && ((uintptr_t)a.w_down % 8 == 0) &&
                     (!a.has_shared || ((uintptr_t)a.s_down % 8 == 0));
   const bool tiled = a.t_gate && a.t_up && a.t_down && (!a.has_shared || (a.ts_gate && a.ts_up && a.ts_down));
-  const bool g2_g = tiled && a.H % G2K == 0 && ((uintptr_t)a.x % 16 == 0);
+  // (g2 addresses x through one buffer descriptor of T*H*2 bytes, a 32-bit
+  // count: larger batches take the generic kernels)
+  const bool g2_g = tiled && a.H % G2K == 0 && ((uintptr_t)a.x % 16 == 0) &&
+                    (uint64_t)a.T * (uint64_t)a.H * 2u <= 0xffffffffull;
   const bool g2_d = tiled && a.I % G2K == 0 && ((uintptr_t)a.h % 16 == 0);
   const int g2_groups = (btiles + 7) / 8;
   hipError_t err = hipSuccess;
   if ((stages & 3) == 3 && g2_g && g2_d && a.tile_done) {
     const int ncb_gu = (a.I + 127) / 128, ncb_dn = (a.H + 255) / 256;
     const int n_gu = g2_groups * 8 * ncb_gu, n_dn = g2_groups * 8 * ncb_dn;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((btiles + 255) / 256), dim3(256), 0, stream, a.tile_done, btiles);
-    hipLaunchKernelGGL(gemm_ffn_kernel, dim3(n_gu + n_dn), dim3(256), 0, stream, a, ncb_gu, ncb_dn, n_gu);
+    // (a test of the failure path asks for one gate/up unit more than a tile
+    // has, with a short spin: every wait then gives up)
+    const int need = ncb_gu + (a.test_wait_fail ? 1 : 0);
+    const int spin = a.test_wait_fail ? 16 : kTileSpinMax;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((btiles + 1 + 255) / 256), dim3(256), 0, stream, a.tile_done,
+                       btiles + 1);
+    hipLaunchKernelGGL(gemm_ffn_kernel, dim3(n_gu + n_dn), dim3(256), 0, stream, a, ncb_gu, ncb_dn, n_gu,
+                       btiles, need, spin);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     stages &= ~3;

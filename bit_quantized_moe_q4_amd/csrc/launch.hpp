@@ -62,7 +62,9 @@ struct PrefillArgs {
   uint16_t* h;              // [(T*k + T*S)][I] bf16
   uint16_t* o_perm;         // [T*k][H] bf16
   float* y;                 // [T][H] fp32
-  int32_t* tile_done;       // [prefill_tile_bound] gate/up units finished per tile (fused launch)
+  int32_t* tile_done;       // [prefill_tile_bound + 1] gate/up units finished per tile (fused
+                            // launch), then the count of down units whose wait gave up
+  int test_wait_fail;       // test only: make every wait of the fused launch give up
 };
 hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream);
 

@@ -15,6 +15,7 @@ import ctypes as C
 import os
 import subprocess
 import threading
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -345,22 +346,32 @@ def route(layer: PackedLayer, x, lib=None) -> dict:
                 offsets=offsets, perm=perm, inv_perm=inv)
 
 
-def prefill_ref(layer: PackedLayer, x, ids, w64, tokens=None, lib=None) -> np.ndarray:
-    """``orc_prefill_ref``: binary64 y for the listed tokens -> [n, H] fp64."""
+def prefill_ref(layer: PackedLayer, x, ids, w64, tokens=None, lib=None, threads: int = 1) -> np.ndarray:
+    """``orc_prefill_ref``: binary64 y for the listed tokens -> [n, H] fp64.
+
+    ``threads`` > 1 runs the same single-threaded C function on disjoint
+    slices of the token list concurrently (the layer is a per-token function,
+    so each token's row is the same whatever the split)."""
     assert layer.wfmt == Q4_0, "the prefill reference is defined for Q4_0 layers"
     lib = lib or load()
     x = _c(x, np.float32)
     ids = _c(ids, np.int32)
     w64 = _c(w64, np.float64)
     T = x.shape[0]
-    if tokens is None:
-        tok, n = None, T
-    else:
-        tok = _c(tokens, np.int64)
-        n = tok.size
+    tok = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    n = tok.size
     y = np.empty((n, layer.H), dtype=np.float64)
     L = layer.cstruct()
-    lib.orc_prefill_ref(C.byref(L), _p(x), _p(ids), _p(w64), _p(tok), n, _p(y))
+
+    def run(lo, hi):
+        if hi > lo:
+            lib.orc_prefill_ref(C.byref(L), _p(x), _p(ids), _p(w64), _p(tok[lo:hi]), hi - lo, _p(y[lo:hi]))
+    if threads <= 1 or n < 2 * threads:
+        run(0, n)
+        return y
+    step = (n + threads - 1) // threads
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda i: run(i, min(i + step, n)), range(0, n, step)))
     return y
 
 

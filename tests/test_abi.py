@@ -39,7 +39,7 @@ def test_header_declares_the_api():
               "moe_q4_decode_stack", "moe_q4_decode_stack_workspace_bytes",
               "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
               "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm",
-              "moe_q4_last_error"]:
+              "moe_q4_prefill_status", "moe_q4_last_error"]:
         assert n in names, n
 
 
@@ -247,6 +247,20 @@ def test_workspace_checks(lib):
     rc = lib.moe_q4_decode(C.byref(L), C.c_void_p(0x1000), C.c_void_p(0x2000), None,
                            C.c_void_p(0x100000), dneed - 1, None)
     assert rc == -2
+
+
+def test_prefill_status_checks(lib):
+    L = _layer()
+    n = C.c_int32(-7)
+    # no tokens: nothing was launched, nothing to report (no device access)
+    assert lib.moe_q4_prefill_status(C.byref(L), 0, None, 0, C.byref(n), None) == 0 and n.value == 0
+    assert lib.moe_q4_prefill_status(C.byref(L), -1, None, 0, C.byref(n), None) == -1
+    assert lib.moe_q4_prefill_status(C.byref(L), 8, None, 0, None, None) == -1
+    pneed = lib.moe_q4_prefill_workspace_bytes(C.byref(L), 8)
+    assert lib.moe_q4_prefill_status(C.byref(L), 8, C.c_void_p(0x100000), pneed - 1, C.byref(n), None) == -2
+    # the bit of the test-only forced wait failure is accepted on top of a stage mask
+    assert lib.moe_q4_prefill_stage(C.byref(L), None, 0, None, None, None, 0, 3 | 16, None) == 0
+    assert lib.moe_q4_prefill_stage(C.byref(L), None, 0, None, None, None, 0, 16, None) == -1
 
 
 def test_gemv_and_rmsnorm_checks(lib):

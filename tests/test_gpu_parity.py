@@ -233,8 +233,10 @@ def _prefill_err(ol, gl, cfg, T, sample=None, step=0):
     y = mq.moe_q4_prefill(gl, xbd, r).cpu().numpy().astype(np.float64)
     ref_route = oracle.route(ol, xw)
     assert np.array_equal(r.topk_ids.cpu().numpy(), ref_route["ids"])
+    if callable(sample):
+        sample = sample(ref_route)
     toks = np.arange(T) if sample is None else np.asarray(sample)
-    yref = oracle.prefill_ref(ol, xw, ref_route["ids"], ref_route["w64"], tokens=toks)
+    yref = oracle.prefill_ref(ol, xw, ref_route["ids"], ref_route["w64"], tokens=toks, threads=8)
     ys = y[toks]
     assert np.all(np.isfinite(ys))
     rel = np.linalg.norm(ys - yref) / np.linalg.norm(yref)
@@ -270,12 +272,32 @@ def prefill_layer():
     return cfg, both_layers(cfg)
 
 
+def _cover_sample(rr, T, k, extra=0, seed=0):
+    """Tokens such that every 32-row subtile of every expert segment (the
+    grouped GEMM's unit of rows) and of the shared expert's rows holds at
+    least one sampled row: segment positions 0, 32, 64, ... and the last of
+    each non-empty segment, mapped to their tokens through the oracle's perm,
+    plus tokens 0, 32, ..., T-1 (the shared expert's rows are in token order)
+    and `extra` random tokens."""
+    off, perm = rr["offsets"], rr["perm"]
+    pos = []
+    for e in range(len(off) - 1):
+        if off[e + 1] > off[e]:
+            pos.extend(range(off[e], off[e + 1], 32))
+            pos.append(off[e + 1] - 1)
+    toks = [perm[np.asarray(pos)] // k, np.arange(0, T, 32), [T - 1]]
+    if extra:
+        toks.append(np.random.default_rng(seed).choice(T, extra, replace=False))
+    return np.unique(np.concatenate(toks))
+
+
 def test_prefill_2k_sampled(prefill_layer):
     cfg, (ol, gl) = prefill_layer
-    rng = np.random.default_rng(1)
-    sample = np.unique(np.concatenate([[0, 1, cfg.T - 1], rng.choice(cfg.T, 45, replace=False)]))
-    rel, per_tok, y, rr = _prefill_err(ol, gl, cfg, cfg.T, sample=sample)
+    rel, per_tok, y, rr = _prefill_err(ol, gl, cfg, cfg.T,
+                                       sample=lambda rr: _cover_sample(rr, cfg.T, cfg.k, extra=45, seed=1))
+    say("sampled %d tokens" % per_tok.size)
     assert rel <= PREFILL_TOL
+    assert per_tok.max() <= 3 * PREFILL_TOL
     # every expert segment is non-empty at this size; the y rows exist for all tokens
     assert np.all(np.diff(rr["offsets"]) > 0)
     assert np.all(np.isfinite(y))
@@ -318,13 +340,44 @@ def test_prefill_skewed_10k_sampled():
     counts = np.diff(ref["offsets"])
     say("skew: hottest expert %d rows, empty experts %d" % (counts.max(), (counts == 0).sum()))
     y = mq.moe_q4_prefill(gl, xbd, r).cpu().numpy().astype(np.float64)
-    rng = np.random.default_rng(3)
-    sample = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 30, replace=False)]))
-    yref = oracle.prefill_ref(ol, xw, ref["ids"], ref["w64"], tokens=sample)
+    # every 32-row subtile of every non-empty segment (the hot expert's 10k
+    # rows included) and of the shared expert contributes a sampled token
+    sample = _cover_sample(ref, cfg.T, cfg.k, extra=30, seed=3)
+    yref = oracle.prefill_ref(ol, xw, ref["ids"], ref["w64"], tokens=sample, threads=16)
     rel = np.linalg.norm(y[sample] - yref) / np.linalg.norm(yref)
-    say("skew prefill rel-L2 %.3e" % rel)
+    per_tok = np.linalg.norm(y[sample] - yref, axis=1) / np.linalg.norm(yref, axis=1)
+    say("skew prefill rel-L2 %.3e over %d tokens, worst token %.3e" % (rel, sample.size, per_tok.max()))
     assert rel <= PREFILL_TOL
+    assert per_tok.max() <= 3 * PREFILL_TOL
     assert np.all(np.isfinite(y))
+
+
+def test_prefill_wait_failure_is_reported():
+    """The fused launch's bounded wait: forced to give up from the host (a
+    tile count that is never reached, a 16-poll bound), every down unit
+    stores nothing and is counted, and the kernels still end; the next normal
+    call on the same workspace reports 0 and is correct again."""
+    cfg = moe_synth.CONFIGS["tiny"].with_(name="waitfail", T=300, H=256, E=16, I=128, k=4, shared=True)
+    ol, gl = both_layers(cfg)
+    assert gl.tiles is not None
+    x, bits, xw, xd, xbd = tokens(cfg, T=cfg.T)
+    r = mq.moe_q4_route(gl, xbd)
+    ws = torch.empty(mq.moe_q4_prefill_workspace_bytes(gl, cfg.T), dtype=torch.uint8, device="cuda")
+    y = torch.zeros((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+    S = mq._lib
+    mq.moe_q4_prefill_stage(gl, xbd, r, y, ws, S.STAGE_GATEUP | S.STAGE_DOWN | S.STAGE_TEST_WAIT_FAIL)
+    torch.cuda.synchronize()
+    failed = mq.moe_q4_prefill_status(gl, cfg.T, ws)
+    say("forced give-ups:", failed)
+    assert failed > 0
+    # down units that gave up stored nothing: the shared expert's rows of y stay 0
+    assert torch.count_nonzero(y).item() == 0
+    y = mq.moe_q4_prefill(gl, xbd, r, ws=ws)
+    assert mq.moe_q4_prefill_status(gl, cfg.T, ws) == 0
+    ref = oracle.route(ol, xw)
+    yref = oracle.prefill_ref(ol, xw, ref["ids"], ref["w64"])
+    yy = y.cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(yy - yref) / np.linalg.norm(yref) <= PREFILL_TOL
 
 
 # ---------------------------------------------------------------- decode
