@@ -24,7 +24,7 @@ __all__ = [
     "q4_packed_bytes", "q4_pack", "q4_tile", "q8w_pack", "q8w_tile", "q8_quantize", "MoELayer", "Routing",
     "moe_q4_route_workspace_bytes", "moe_q4_route",
     "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage", "moe_q4_prefill_status",
-    "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace",
+    "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace", "moe_q4_decode_noalloc",
     "moe_q4_decode_batch_workspace_bytes", "moe_q4_decode_batch",
     "LayerStack", "moe_q4_decode_stack_workspace_bytes", "moe_q4_decode_stack",
     "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm", "library_path",
@@ -317,6 +317,18 @@ def moe_q4_decode(layer: MoELayer, x: torch.Tensor, y: torch.Tensor | None = Non
                                         C.byref(tc) if tc is not None else None,
                                         _p(ws), ws.numel(), _s(stream)), "moe_q4_decode")
     return (y, tr) if trace else y
+
+
+def moe_q4_decode_noalloc(layer: MoELayer, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """One-token decode into the caller's y [H] fp32 with the library's fixed
+    per-GPU scratch array (no workspace, nothing allocated)."""
+    _dev(x, "x")
+    _dev(y, "y")
+    if x.dtype != torch.float32 or y.dtype != torch.float32:
+        raise ValueError("x and y must be float32")
+    _lib.check(_lib.lib().moe_q4_decode_noalloc(layer.struct_ptr(), _p(x), _p(y), _s(stream)),
+               "moe_q4_decode_noalloc")
+    return y
 
 
 class LayerStack:

@@ -7,7 +7,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "launch.hpp"
+
+// Scratch of moe_q4_decode_noalloc: one array on every GPU the library runs
+// on, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: host code uses only the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[MOE_Q4_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -190,6 +198,26 @@ moeq4::DecodeArgs decode_args(const moe_q4_layer* L, void* ws) {
   a.dh = at<float>(ws, W.dh);
   a.sh = at<int32_t>(ws, W.sh);
   return a;
+}
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int noalloc_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_Q4_EINVAL, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "moe_q4_decode_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(MOE_Q4_EHIP, "moe_q4_decode_noalloc: scratch at %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_Q4_OK;
 }
 
 }  // namespace
@@ -502,6 +530,39 @@ int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_
   }
   hipError_t e = moeq4::launch_decode(a, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_decode");
+}
+
+int moe_q4_decode_noalloc(const moe_q4_layer* L, const float* x, float* y, hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!x || !y) return fail(MOE_Q4_EINVAL, "moe_q4_decode_noalloc: NULL pointer");
+  if (!aligned(x, 16) || !aligned(y, 4)) return fail(MOE_Q4_EINVAL, "moe_q4_decode_noalloc: x must be 16-byte aligned");
+  const size_t need = decode_ws(L).total;
+  if (need > (size_t)MOE_Q4_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_Q4_EWORKSPACE,
+                "moe_q4_decode_noalloc: this layer needs %zu bytes of scratch, the fixed array holds %zu "
+                "(use moe_q4_decode with a workspace)", need, (size_t)MOE_Q4_NOALLOC_SCRATCH_BYTES);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "moe_q4_decode_noalloc: hipGetDevice");
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "moe_q4_decode_noalloc: hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(MOE_Q4_EINVAL, "moe_q4_decode_noalloc: the stream belongs to device %d, the current device is %d",
+                  sdev, dev);
+  }
+  void* ws = nullptr;
+  rc = noalloc_scratch(dev, &ws);
+  if (rc) return rc;
+  // the three decode kernels write every scratch piece before reading it, so
+  // nothing needs clearing between calls
+  moeq4::DecodeArgs a = decode_args(L, ws);
+  a.x = x;
+  a.y = y;
+  e = moeq4::launch_decode(a, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_decode_noalloc");
 }
 
 size_t moe_q4_decode_stack_workspace_bytes(const moe_q4_layer* layers, int32_t n_layers) {

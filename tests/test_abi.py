@@ -263,6 +263,17 @@ def test_prefill_status_checks(lib):
     assert lib.moe_q4_prefill_stage(C.byref(L), None, 0, None, None, None, 0, 16, None) == -1
 
 
+def test_decode_noalloc_checks(lib):
+    # a layer whose decode scratch exceeds the fixed array is refused before any device call
+    L = _layer(hidden=8192, inter=64, E=1024, k=2)
+    assert lib.moe_q4_decode_workspace_bytes(C.byref(L)) > (1 << 20)
+    rc = lib.moe_q4_decode_noalloc(C.byref(L), C.c_void_p(0x1000), C.c_void_p(0x2000), None)
+    assert rc == -2 and "fixed array" in _err(lib)
+    assert lib.moe_q4_decode_noalloc(C.byref(L), None, C.c_void_p(0x2000), None) == -1
+    assert lib.moe_q4_decode_noalloc(C.byref(L), C.c_void_p(0x1008), C.c_void_p(0x2000), None) == -1
+    assert "MOE_Q4_NOALLOC_SCRATCH_BYTES (1u << 20)" in open(HEADER).read()
+
+
 def test_gemv_and_rmsnorm_checks(lib):
     assert lib.moe_q4_w4a8_gemv(C.c_void_p(0x1000), 4, 48, C.c_void_p(0x2000), C.c_void_p(0x3000),
                                 None, C.c_void_p(0x4000), None) == -1
