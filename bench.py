@@ -306,7 +306,7 @@ def bench_stack(args, torch, mq, moe_synth, dec):
     ntok = 10
     X = torch.from_numpy(moe_synth.tokens(cfg, step=9000, T=ntok)).cuda()
     Y = torch.empty((ntok, cfg.H), dtype=torch.float32, device="cuda")
-    ws = torch.empty(mq.moe_q4_decode_stack_workspace_bytes(stack), dtype=torch.uint8, device="cuda")
+    ws = mq.stack_workspace(stack)
     dws = mq.decode_workspace(seq[0])
     yb = torch.empty(cfg.H, dtype=torch.float32, device="cuda")
     xb = torch.empty((1, cfg.H), dtype=torch.float32, device="cuda")
@@ -399,7 +399,7 @@ def bench_small_batch(args, torch, mq, moe_synth, dec, pre):
     for M in SMALL_M:
         X = torch.from_numpy(moe_synth.tokens(cfg, step=5000 + 100 * M, T=ncall * M)).cuda().view(ncall, M, cfg.H)
         Y = torch.empty((ncall, M, cfg.H), dtype=torch.float32, device="cuda")
-        ws = torch.empty(mq.moe_q4_decode_batch_workspace_bytes(copies[0], M), dtype=torch.uint8, device="cuda")
+        ws = mq.batch_workspace(copies[0], M)
         uniq = 0
         for i in range(ncall):              # eager pass: warm-up and the experts each call reads
             _, ids, _ = mq.moe_q4_decode_batch(copies[i % len(copies)], X[i], y=Y[i], ws=ws, routing=True)

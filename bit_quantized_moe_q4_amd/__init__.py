@@ -24,9 +24,10 @@ __all__ = [
     "q4_packed_bytes", "q4_pack", "q4_tile", "q8w_pack", "q8w_tile", "q8_quantize", "MoELayer", "Routing",
     "moe_q4_route_workspace_bytes", "moe_q4_route",
     "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage", "moe_q4_prefill_status",
-    "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace", "moe_q4_decode_noalloc",
+    "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace", "moe_q4_decode_noalloc", "moe_q4_decode_status",
     "moe_q4_decode_batch_workspace_bytes", "moe_q4_decode_batch",
-    "LayerStack", "moe_q4_decode_stack_workspace_bytes", "moe_q4_decode_stack",
+    "LayerStack", "moe_q4_decode_stack_workspace_bytes", "moe_q4_decode_stack", "stack_workspace",
+    "batch_workspace",
     "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm", "library_path",
 ]
 
@@ -285,9 +286,20 @@ def moe_q4_decode_workspace_bytes(layer: MoELayer) -> int:
 
 
 def decode_workspace(layer: MoELayer, device=None) -> torch.Tensor:
-    """A decode workspace (its contents need no initialisation)."""
+    """A decode workspace, zero-filled (the one-launch step keeps its call
+    counter in it; each call leaves it ready for the next)."""
     dev = device if device is not None else layer.w_router.device
-    return torch.empty(max(moe_q4_decode_workspace_bytes(layer), 1), dtype=torch.uint8, device=dev)
+    return torch.zeros(max(moe_q4_decode_workspace_bytes(layer), 1), dtype=torch.uint8, device=dev)
+
+
+def moe_q4_decode_status(layer: MoELayer, ws: torch.Tensor, stream=None) -> int:
+    """Waits of the one-launch decode on `ws` that gave up since the last
+    query (0: every step completed normally); resets the count.  Waits for the
+    stream."""
+    n = C.c_int32(-1)
+    _lib.check(_lib.lib().moe_q4_decode_status(layer.struct_ptr(), _p(ws), ws.numel(), C.byref(n), _s(stream)),
+               "moe_q4_decode_status")
+    return int(n.value)
 
 
 def moe_q4_decode(layer: MoELayer, x: torch.Tensor, y: torch.Tensor | None = None,
@@ -354,6 +366,12 @@ def moe_q4_decode_stack_workspace_bytes(stack: LayerStack) -> int:
     return int(_lib.lib().moe_q4_decode_stack_workspace_bytes(stack.ptr(), len(stack)))
 
 
+def stack_workspace(stack: LayerStack, device=None) -> torch.Tensor:
+    """A zero-filled workspace for moe_q4_decode_stack."""
+    dev = device if device is not None else stack.layers[0].w_router.device
+    return torch.zeros(max(1, moe_q4_decode_stack_workspace_bytes(stack)), dtype=torch.uint8, device=dev)
+
+
 def moe_q4_decode_stack(stack: LayerStack, x: torch.Tensor, eps: float = 1e-6,
                         y: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
     """One decode step through the stack: x [H] fp32 -> y [H] fp32, the last
@@ -362,8 +380,7 @@ def moe_q4_decode_stack(stack: LayerStack, x: torch.Tensor, eps: float = 1e-6,
     if y is None:
         y = torch.empty(stack.hidden, dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = torch.empty(max(1, moe_q4_decode_stack_workspace_bytes(stack)), dtype=torch.uint8,
-                         device=x.device)
+        ws = stack_workspace(stack, x.device)
     _lib.check(_lib.lib().moe_q4_decode_stack(stack.ptr(), len(stack), _p(x), _p(y), float(eps), _p(ws),
                                               ws.numel(), _s(stream)), "moe_q4_decode_stack")
     return y
@@ -371,6 +388,12 @@ def moe_q4_decode_stack(stack: LayerStack, x: torch.Tensor, eps: float = 1e-6,
 
 def moe_q4_decode_batch_workspace_bytes(layer: MoELayer, M: int) -> int:
     return int(_lib.lib().moe_q4_decode_batch_workspace_bytes(layer.struct_ptr(), int(M)))
+
+
+def batch_workspace(layer: MoELayer, M: int, device=None) -> torch.Tensor:
+    """A zero-filled workspace for moe_q4_decode_batch of M tokens."""
+    dev = device if device is not None else layer.w_router.device
+    return torch.zeros(max(1, moe_q4_decode_batch_workspace_bytes(layer, M)), dtype=torch.uint8, device=dev)
 
 
 def moe_q4_decode_batch(layer: MoELayer, x: torch.Tensor, y: torch.Tensor | None = None,
@@ -385,8 +408,7 @@ def moe_q4_decode_batch(layer: MoELayer, x: torch.Tensor, y: torch.Tensor | None
     if y is None:
         y = torch.empty((M, layer.hidden), dtype=torch.float32, device=x.device)
     if ws is None:
-        ws = torch.empty(max(1, moe_q4_decode_batch_workspace_bytes(layer, M)), dtype=torch.uint8,
-                         device=x.device)
+        ws = batch_workspace(layer, M, x.device)
     ids = w = None
     if routing:
         ids = torch.empty((M, layer.top_k), dtype=torch.int32, device=x.device)

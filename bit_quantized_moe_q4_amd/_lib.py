@@ -83,6 +83,8 @@ def _declare(lib):
         "moe_q4_decode_batch": (C.c_int, [P, P, I32, P, P, P, P, SZ, P]),
         "moe_q4_decode": (C.c_int, [P, P, P, P, P, SZ, P]),
         "moe_q4_decode_noalloc": (C.c_int, [P, P, P, P]),
+        "moe_q4_decode_status": (C.c_int, [P, P, SZ, P, P]),
+        "moe_q4_test_decode_wait_fail": (None, [I32]),
         "moe_q4_w4a8_gemv": (C.c_int, [P, I32, I32, P, P, P, P, P]),
         "moe_q4_w4a8_gemm": (C.c_int, [P, I32, I32, P, P, I32, P, P, P]),
         "moe_q4_rmsnorm": (C.c_int, [P, I32, I32, C.c_float, P, P, P]),

@@ -36,8 +36,8 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-SOURCES = ["abi.cpp", "pack.hip", "router.hip", "gemm.hip", "decode.hip", "decode_batch.hip", "rmsnorm.hip",
-           "w4a8_gemm.hip"]
+SOURCES = ["abi.cpp", "pack.hip", "router.hip", "gemm.hip", "decode.hip", "decode_fused.hip", "decode_batch.hip",
+           "rmsnorm.hip", "w4a8_gemm.hip"]
 
 
 def _compile(src: str) -> str:

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "launch.hpp"
@@ -109,14 +110,22 @@ PrefillWs prefill_ws(const moe_q4_layer* L, int32_t T) {
   return w;
 }
 
+// Decode workspace: a header (the one-launch decode's failure count and epoch
+// slots), the one-launch path's handoff words, then the three-launch path's
+// pieces.
 struct DecodeWs {
-  size_t partials, ids, w, qx, dx, sx, qh, dh, sh, total;
+  size_t hdr, ll_leaf, ll_route, ll_qh, partials, ids, w, qx, dx, sx, qh, dh, sh, total;
 };
 DecodeWs decode_ws(const moe_q4_layer* L) {
   DecodeWs w;
   const size_t ns = (size_t)L->top_k + (L->has_shared ? 1 : 0);
   const size_t H = L->hidden, I = L->inter;
-  w.partials = 0;
+  const moeq4::FusedGeometry fg = moeq4::fused_geometry(L->hidden, L->inter, L->n_experts, L->top_k, L->has_shared);
+  w.hdr = 0;
+  w.ll_leaf = up256(moeq4::kFuHeaderBytes);
+  w.ll_route = w.ll_leaf + (fg.ok ? up256((size_t)fg.n_cg * L->n_experts * 8) : 0);
+  w.ll_qh = w.ll_route + (fg.ok ? up256((size_t)L->top_k * 2 * 8) : 0);
+  w.partials = w.ll_qh + (fg.ok ? up256(ns * I / 32 * 10 * 8) : 0);
   w.ids = w.partials + up256(H / 32 * (size_t)L->n_experts * 4);
   w.w = w.ids + up256((size_t)L->top_k * 4);
   w.qx = w.w + up256((size_t)L->top_k * 4);
@@ -137,7 +146,8 @@ DecodeBatchWs decode_batch_ws(const moe_q4_layer* L, int32_t M) {
   const size_t m = (size_t)M, k = (size_t)L->top_k, E = (size_t)L->n_experts;
   const size_t H = L->hidden, I = L->inter, nc = H / 32;
   const size_t np = m * k + (L->has_shared ? m : 0);
-  w.partials = 0;
+  // after the one-token layout, which M <= 2 uses on the same workspace
+  w.partials = decode_ws(L).total;
   w.qx = w.partials + up256(m * nc * E * 4);
   w.dx = w.qx + up256(m * H);
   w.sx = w.dx + up256(m * nc * 4);
@@ -197,7 +207,26 @@ moeq4::DecodeArgs decode_args(const moe_q4_layer* L, void* ws) {
   a.qh = at<int8_t>(ws, W.qh);
   a.dh = at<float>(ws, W.dh);
   a.sh = at<int32_t>(ws, W.sh);
+  a.hdr = at<uint64_t>(ws, W.hdr);
+  a.ll_leaf = at<uint64_t>(ws, W.ll_leaf);
+  a.ll_route = at<uint64_t>(ws, W.ll_route);
+  a.ll_qh = at<uint64_t>(ws, W.ll_qh);
   return a;
+}
+
+// One decode step: the one-launch kernel when the layer and the GPU allow it
+// (tile-order copies, covered shape, grid resident at once), else the three
+// launches.  Both give the same y bit for bit.
+std::atomic<int> g_test_decode_wait_fail{0};
+
+hipError_t decode_step(const moeq4::DecodeArgs& a, hipStream_t stream) {
+  if (moeq4::fused_decode_available(a)) {
+    moeq4::DecodeArgs b = a;
+    b.test_wait_fail = g_test_decode_wait_fail.load();
+    b.spin_max = b.test_wait_fail ? 16 : (1 << 20);
+    return moeq4::launch_decode_fused(b, stream);
+  }
+  return moeq4::launch_decode(a, stream);
 }
 
 // Device address of `scratch` on each device, looked up once per device with
@@ -457,7 +486,7 @@ int moe_q4_decode_batch(const moe_q4_layer* L, const float* x, int32_t M, float*
       a.y = y + t * H;
       a.t_ids = ids_out ? ids_out + t * k : nullptr;
       a.t_w = w_out ? w_out + t * k : nullptr;
-      hipError_t e = moeq4::launch_decode(a, stream);
+      hipError_t e = decode_step(a, stream);
       if (e != hipSuccess) return hip_fail(e, "moe_q4_decode_batch");
     }
     return MOE_Q4_OK;
@@ -528,7 +557,7 @@ int moe_q4_decode(const moe_q4_layer* L, const float* x, float* y, const moe_q4_
     a.t_qh = tr->qh;
     a.t_dh = tr->dh;
   }
-  hipError_t e = moeq4::launch_decode(a, stream);
+  hipError_t e = decode_step(a, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_decode");
 }
 
@@ -563,6 +592,28 @@ int moe_q4_decode_noalloc(const moe_q4_layer* L, const float* x, float* y, hipSt
   a.y = y;
   e = moeq4::launch_decode(a, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_decode_noalloc");
+}
+
+void moe_q4_test_decode_wait_fail(int32_t on) { g_test_decode_wait_fail.store(on ? 1 : 0); }
+
+int moe_q4_decode_status(const moe_q4_layer* L, const void* ws, size_t ws_bytes, int32_t* failed_waits,
+                         hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!failed_waits) return fail(MOE_Q4_EINVAL, "moe_q4_decode_status: failed_waits is NULL");
+  rc = check_ws(const_cast<void*>(ws), ws_bytes, decode_ws(L).total);
+  if (rc) return rc;
+  uint32_t* word = reinterpret_cast<uint32_t*>(const_cast<void*>(ws));
+  uint32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, word, 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess && v != 0) {
+    e = hipMemsetAsync(word, 0, 4, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "moe_q4_decode_status");
+  *failed_waits = (int32_t)v;
+  return MOE_Q4_OK;
 }
 
 size_t moe_q4_decode_stack_workspace_bytes(const moe_q4_layer* layers, int32_t n_layers) {
@@ -605,7 +656,7 @@ int moe_q4_decode_stack(const moe_q4_layer* layers, int32_t n_layers, const floa
     a.norm_eps = eps;
     a.x = l == 0 ? x : ybuf[(l - 1) & 1];
     a.y = l == n_layers - 1 ? y : ybuf[l & 1];
-    hipError_t e = moeq4::launch_decode(a, stream);
+    hipError_t e = decode_step(a, stream);
     if (e != hipSuccess) return hip_fail(e, "moe_q4_decode_stack");
   }
   return MOE_Q4_OK;

@@ -31,6 +31,7 @@
 #include "launch.hpp"
 #include "w4a8.hpp"
 #include "decode_common.hpp"
+#include "decode_tile.hpp"
 
 namespace moeq4 {
 
@@ -82,7 +83,6 @@ __global__ void __launch_bounds__(1024) decode_router_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------- gate/up
 // Block: 32 values of i; rows 0..31 gate, 32..63 up, LPR lanes per row.
-constexpr int DGU_ROWS = 32;
 
 // Router completion inside a gate/up block.  The nc leaves of expert e
 // (padded with +0 to m = next_pow2(nc)) are split into P aligned runs of
@@ -174,41 +174,7 @@ __device__ void decode_gu_prologue(const DecodeArgs& a, const GuLds& l, int P, b
     }
   }
   __syncthreads();
-  // Rank pass.  A wave task is (64 experts, one range of Q equal key ranges):
-  // every lane compares its expert's key against the range's keys, all lanes
-  // reading the same key at once (an LDS broadcast, no bank conflicts).  The
-  // Q partial counts of an expert are then summed by one thread.
-  __shared__ int32_t rpart[1024];         // [Q][E]; Q * E <= max(E, 64 * waves) <= 1024
-  const int nw = nt / 64, lane = tid % 64;
-  const int nchunk = (E + 63) / 64;
-  const int Q = nw / nchunk > 1 ? nw / nchunk : 1;
-  const int span = ((E + Q - 1) / Q + 1) & ~1;          // even: 16-byte key pairs
-  const ulonglong2* K2 = reinterpret_cast<const ulonglong2*>(l.key);
-  for (int task = tid / 64; task < nchunk * Q; task += nw) {
-    const int e = (task % nchunk) * 64 + lane, q = task / nchunk;
-    const uint64_t ke = l.key[e < E ? e : 0];
-    const int j0 = min(q * span, E), j1 = min(j0 + span, E);
-    int rank = 0;
-    int j = j0;                           // j0 is even
-#pragma unroll 8
-    for (; j + 2 <= j1; j += 2) {
-      const ulonglong2 kk = K2[j >> 1];
-      rank += (kk.x > ke) ? 1 : 0;
-      rank += (kk.y > ke) ? 1 : 0;
-    }
-    if (j < j1) rank += (l.key[j] > ke) ? 1 : 0;
-    if (e < E) rpart[q * E + e] = rank;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += nt) {
-    int rank = 0;
-    for (int q = 0; q < Q; q++) rank += rpart[q * E + e];
-    if (rank < a.k) {
-      ids_l[rank] = e;
-      vals_l[rank] = l.logit[e];
-    }
-  }
-  __syncthreads();
+  rank_topk(l.key, l.logit, E, a.k, ids_l, vals_l);
 }
 
 // h = silu(g) * u of the block's 32-group from val[0..31] (gate) and
@@ -308,35 +274,6 @@ __global__ void __launch_bounds__(1024) decode_gateup_kernel(DecodeArgs a, int l
 // pairwise (CH pieces loaded together, then the chunk sums), then the W wave
 // sums pairwise.
 constexpr int kGtWaves = 16, kGtRouteThreads = 512;
-
-// Tile order per weight format (q4_tile / q8w_tile in moe_q4.h): bytes of a
-// piece, bytes of a lane's block codes (at lane * code), scale offset.
-template <int FMT> struct TileFmt;
-template <> struct TileFmt<kQ4> { static constexpr int piece = 1152, code = 16, scale = 1024; };
-template <> struct TileFmt<kQ8> { static constexpr int piece = 2176, code = 32, scale = 2048; };
-
-// One lane's block of a piece: its code dwords (Q4_0 nibbles or Q8_0 codes).
-template <int FMT>
-struct TileCodes {
-  uint32_t w[TileFmt<FMT>::code / 4];
-};
-
-template <int FMT>
-__device__ __forceinline__ TileCodes<FMT> tile_codes(const uint8_t* p) {
-  TileCodes<FMT> t;
-#pragma unroll
-  for (int h = 0; h < TileFmt<FMT>::code / 16; h++) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p + 16 * h);
-    t.w[4 * h] = v.x; t.w[4 * h + 1] = v.y; t.w[4 * h + 2] = v.z; t.w[4 * h + 3] = v.w;
-  }
-  return t;
-}
-
-template <int FMT>
-__device__ __forceinline__ int32_t tile_dot(const TileCodes<FMT>& t, const uint32_t (&av)[8], int32_t sa) {
-  if constexpr (FMT == kQ4) return q4_block_dot(t.w, av, sa);
-  else return q8_block_dot(t.w, av);
-}
 
 template <int SP, int FMT>
 __global__ void __launch_bounds__(1024) decode_gateup_tiled_kernel(DecodeArgs a, int P) {
@@ -553,7 +490,6 @@ __global__ void __launch_bounds__(1024) decode_down_kernel(DecodeArgs a, int lpr
 // pieces, +0 leaves past I/32); the sums follow the row's pairwise tree:
 // blocks 2s and 2s+1 (lanes L and L^32) first, then the pieces pairwise
 // (CH loaded together, then the chunk sums).  Then the fixed-order combine.
-constexpr int kDtRows = 8;
 template <int SP, int FMT>
 __global__ void __launch_bounds__(1024) decode_down_tiled_kernel(DecodeArgs a) {
   using TF = TileFmt<FMT>;

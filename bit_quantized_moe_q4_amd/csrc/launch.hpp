@@ -110,6 +110,13 @@ struct DecodeArgs {
   int8_t* qh;               // [k+S][I]    (16-byte aligned)
   float* dh;                // [(k+S) I/32]
   int32_t* sh;              // [(k+S) I/32]
+  // the one-launch decode's handoff words (workspace; see decode_fused.hip)
+  uint64_t* hdr;            // [0] low 32 bits: waits that gave up; then kFuSlots uint32 epoch slots
+  uint64_t* ll_leaf;        // [n_cg][E] router subtree values
+  uint64_t* ll_route;       // [2k] ids, then weights
+  uint64_t* ll_qh;          // [(k+S) * I/32][10] q8(h) groups: 8 code dwords, d, code sum
+  int spin_max;             // polls of one wait before it gives up
+  int test_wait_fail;       // test only: every wait looks for a tag no word carries
   // optional trace
   float* t_logits;
   int32_t* t_ids;
@@ -135,6 +142,26 @@ struct DecodeGeometry {
 };
 DecodeGeometry decode_geometry(int H, int I, int E, int k, int has_shared);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// The one-launch decode (decode_fused.hip): block roles, their counts and
+// split parameters; ok = 0 when the shape is not covered (the three-launch
+// path then runs).
+constexpr int kFuSlots = 2048;            // epoch slots = the largest one-launch grid
+constexpr size_t kFuHeaderBytes = 8 + 4 * kFuSlots;
+struct FusedGeometry {
+  int ok;
+  int cpb, eb, n_eg, n_cg, nR;   // router: chunks and experts per block, expert and chunk groups, blocks
+  int P, L;                 // logit tree: lanes per expert, subtree values per lane
+  int gu_waves, gu_sp, n_gu;
+  int dn_nh, dn_sp, n_dn;    // down: step halves per row, pieces per lane and task, units
+  int base_dn, nblocks;
+  size_t lds;
+};
+FusedGeometry fused_geometry(int H, int I, int E, int k, int has_shared);
+// true if the layer (tile-order copies, shape) and the GPU's resident block
+// count allow the one-launch decode with the given workspace words
+bool fused_decode_available(const DecodeArgs& a);
+hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream);
 
 // Batched decode: M <= kDecodeBatchMax tokens, each through the single-token
 // program; the selected experts' weights are read once per call.

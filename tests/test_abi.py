@@ -39,7 +39,8 @@ def test_header_declares_the_api():
               "moe_q4_decode_stack", "moe_q4_decode_stack_workspace_bytes",
               "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
               "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm",
-              "moe_q4_prefill_status", "moe_q4_last_error"]:
+              "moe_q4_prefill_status", "moe_q4_decode_status", "moe_q4_test_decode_wait_fail",
+              "moe_q4_last_error"]:
         assert n in names, n
 
 

@@ -129,7 +129,7 @@ def test_decode_batch_empty_and_workspace(decode_layers):
     assert y0.shape == (0, cfg.H)
     assert mq.moe_q4_decode_batch_workspace_bytes(gl, 33) == 0
     # one workspace reused across batch sizes: calls on one stream are ordered
-    ws = torch.empty(mq.moe_q4_decode_batch_workspace_bytes(gl, 32), dtype=torch.uint8, device="cuda")
+    ws = mq.batch_workspace(gl, 32)
     for M in (32, 3, 32):
         X = _batch_tokens(cfg, M, 3000 + M)
         yb = mq.moe_q4_decode_batch(gl, torch.from_numpy(X).cuda(), ws=ws)
@@ -145,11 +145,11 @@ def test_decode_batch_one_or_two_tokens_use_the_one_token_program(decode_layers)
     assert mq.moe_q4_decode_batch_workspace_bytes(gl, 1) == one
     assert mq.moe_q4_decode_batch_workspace_bytes(gl, 2) == one
     assert mq.moe_q4_decode_batch_workspace_bytes(gl, 3) > one
-    big = torch.empty(mq.moe_q4_decode_batch_workspace_bytes(gl, 32), dtype=torch.uint8, device="cuda")
+    big = mq.batch_workspace(gl, 32)
     for M in (1, 2):
         X = _batch_tokens(cfg, M, 5000 + M)
         xd = torch.from_numpy(X).cuda()
-        exact = torch.empty(mq.moe_q4_decode_batch_workspace_bytes(gl, M), dtype=torch.uint8, device="cuda")
+        exact = mq.batch_workspace(gl, M)
         for ws in (exact, big):
             yb, ids, w = mq.moe_q4_decode_batch(gl, xd, ws=ws, routing=True)
             for t in range(M):

@@ -70,7 +70,7 @@ def test_stack_decode_layers(tiles):
     from bit_quantized_moe_q4_amd.synth_layer import device_layer
     gls = [device_layer(cfg, layer=l, tiles=tiles) for l in range(4)]
     stack = mq.LayerStack(gls)
-    ws = torch.empty(mq.moe_q4_decode_stack_workspace_bytes(stack), dtype=torch.uint8, device="cuda")
+    ws = mq.stack_workspace(stack)
     for step in range(3):
         xd = torch.from_numpy(moe_synth.tokens(cfg, step=700 + step, T=1)[0]).cuda()
         ys = mq.moe_q4_decode_stack(stack, xd, EPS, ws=ws).cpu().numpy()

@@ -461,6 +461,38 @@ def test_decode_tiled_matches_rowmajor(name, H, E, I, k, shared):
             assert np.array_equal(tt[key].cpu().numpy(), trr[key].cpu().numpy()), (step, key)
 
 
+@pytest.mark.parametrize("cfgname", ["tiny_shared", "decode"])
+def test_decode_wait_failure_is_reported(cfgname):
+    """The one-launch decode's bounded waits: with the test switch every wait
+    looks for a tag no word carries and gives up after 16 polls; the kernel
+    ends, moe_q4_decode_status counts the failures (the three-launch path has
+    no waits, so a count > 0 also shows the one-launch kernel ran), and the
+    next normal step on the same workspace is exact again."""
+    cfg = (moe_synth.CONFIGS["tiny"].with_(name="tiny_shared", shared=True) if cfgname == "tiny_shared"
+           else moe_synth.CONFIGS["decode"])
+    ol, gl = both_layers(cfg)
+    ws = mq.decode_workspace(gl)
+    x = moe_synth.tokens(cfg, step=3, T=1)[0]
+    xd = torch.from_numpy(x).cuda()
+    y0 = mq.moe_q4_decode(gl, xd, ws=ws)
+    assert mq.moe_q4_decode_status(gl, ws) == 0
+    lib = mq._lib.lib()
+    try:
+        lib.moe_q4_test_decode_wait_fail(1)
+        mq.moe_q4_decode(gl, xd, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        lib.moe_q4_test_decode_wait_fail(0)
+    failed = mq.moe_q4_decode_status(gl, ws)
+    say("forced decode give-ups:", failed)
+    assert failed > 0
+    assert mq.moe_q4_decode_status(gl, ws) == 0          # the query resets the count
+    y1 = mq.moe_q4_decode(gl, xd, ws=ws)
+    assert torch.equal(y0, y1)
+    assert np.array_equal(y1.cpu().numpy(), oracle.decode(ol, x))
+    assert mq.moe_q4_decode_status(gl, ws) == 0
+
+
 def test_decode_tied_logits():
     # experts 2j and 2j+1 share a router column, so every logit ties with its
     # pair: the choice takes the lower index first (k rounds of "first maximum
