@@ -24,6 +24,7 @@ __all__ = [
     "q4_packed_bytes", "q4_pack", "q4_tile", "q8w_pack", "q8w_tile", "q8_quantize", "MoELayer", "Routing",
     "moe_q4_route_workspace_bytes", "moe_q4_route",
     "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage", "moe_q4_prefill_status",
+    "moe_q4_prefill_w4a8",
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace", "moe_q4_decode_noalloc", "moe_q4_decode_status",
     "moe_q4_decode_batch_workspace_bytes", "moe_q4_decode_batch",
     "LayerStack", "moe_q4_decode_stack_workspace_bytes", "moe_q4_decode_stack", "stack_workspace",
@@ -278,6 +279,31 @@ def moe_q4_prefill_status(layer: MoELayer, T: int, ws: torch.Tensor, stream=None
     _lib.check(_lib.lib().moe_q4_prefill_status(layer.struct_ptr(), int(T), _p(ws), ws.numel(), C.byref(n),
                                                 _s(stream)), "moe_q4_prefill_status")
     return int(n.value)
+
+
+def moe_q4_prefill_w4a8(layer: MoELayer, x_bf16: torch.Tensor, routing: Routing,
+                        y: torch.Tensor | None = None, gate_dots: torch.Tensor | None = None,
+                        ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Grouped prefill in the W4A8 form (int8 block dots): y [T, H] fp32.
+    gate_dots: None, or int32 [T*k + T*S, I, H/32] receiving every gate block dot."""
+    _dev(x_bf16, "x_bf16")
+    if x_bf16.dtype != torch.bfloat16:
+        raise ValueError("x_bf16 must be bfloat16")
+    T = int(x_bf16.shape[0])
+    if y is None:
+        y = torch.empty((T, layer.hidden), dtype=torch.float32, device=x_bf16.device)
+    if gate_dots is not None:
+        rows = T * layer.top_k + (T if layer.has_shared else 0)
+        if gate_dots.dtype != torch.int32 or gate_dots.numel() < rows * layer.inter * (layer.hidden // 32):
+            raise ValueError("gate_dots must be int32 with [T*k + T*S, I, H/32] elements")
+        _dev(gate_dots, "gate_dots")
+    nb = moe_q4_prefill_workspace_bytes(layer, T)
+    w = _ws(nb, x_bf16.device, ws)
+    rs = routing.cstruct()
+    _lib.check(_lib.lib().moe_q4_prefill_w4a8(layer.struct_ptr(), _p(x_bf16), T, C.byref(rs), _p(y),
+                                              _p(gate_dots), _p(w), w.numel(), _s(stream)),
+               "moe_q4_prefill_w4a8")
+    return y
 
 
 # ------------------------------------------------------------------ decode

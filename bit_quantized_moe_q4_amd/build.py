@@ -37,7 +37,7 @@ FLAGS = [
 ]
 
 SOURCES = ["abi.cpp", "pack.hip", "router.hip", "gemm.hip", "decode.hip", "decode_fused.hip", "decode_batch.hip",
-           "rmsnorm.hip", "w4a8_gemm.hip"]
+           "rmsnorm.hip", "w4a8_gemm.hip", "w4a8_prefill.hip"]
 
 
 def _compile(src: str) -> str:

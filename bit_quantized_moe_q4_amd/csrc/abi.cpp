@@ -96,17 +96,28 @@ RouteWs route_ws(const moe_q4_layer* L, int32_t T, const moeq4::RouterSplit& sp)
   return w;
 }
 
+// Prefill workspace, one size for both forms.  bf16 form: h, the routed
+// expert outputs (o), the fused launch's tile counters.  W4A8 form: the same
+// o, then q8(h) codes and scales, then q8(x) codes and scales.
 struct PrefillWs {
-  size_t h, o, tile_done, total;
+  size_t h, o, tile_done, qh, dh, qx, dx, total;
 };
 PrefillWs prefill_ws(const moe_q4_layer* L, int32_t T) {
   PrefillWs w;
   const size_t rows = (size_t)T * L->top_k + (L->has_shared ? (size_t)T : 0);
+  const size_t H = L->hidden, I = L->inter;
   w.h = 0;
-  w.o = w.h + up256(rows * L->inter * 2);
-  w.tile_done = w.o + up256((size_t)T * L->top_k * L->hidden * 2);
+  w.o = w.h + up256(rows * I * 2);
+  w.tile_done = w.o + up256((size_t)T * L->top_k * H * 2);
   // per-tile counters of the fused launch, then the count of waits that gave up
-  w.total = w.tile_done + up256(((size_t)moeq4::prefill_tile_bound(T, L->top_k, L->n_experts, L->has_shared) + 1) * 4);
+  const size_t bf16_total =
+      w.tile_done + up256(((size_t)moeq4::prefill_tile_bound(T, L->top_k, L->n_experts, L->has_shared) + 1) * 4);
+  w.qh = w.tile_done;
+  w.dh = w.qh + up256(rows * I);
+  w.qx = w.dh + up256(rows * (I / 32) * 4);
+  w.dx = w.qx + up256((size_t)T * H);
+  const size_t w4a8_total = w.dx + up256((size_t)T * (H / 32) * 4);
+  w.total = bf16_total > w4a8_total ? bf16_total : w4a8_total;
   return w;
 }
 
@@ -430,6 +441,71 @@ int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t 
   a.y = y;
   hipError_t e = moeq4::launch_prefill(a, stages, stream);
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_prefill");
+}
+
+int moe_q4_prefill_w4a8(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T, const moe_q4_routing* routing,
+                        float* y, int32_t* gate_dots, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_Q4_EINVAL, "moe_q4_prefill_w4a8: T=%d < 0", T);
+  if ((int64_t)T * L->top_k > 0x7fffffff) return fail(MOE_Q4_EINVAL, "moe_q4_prefill_w4a8: T*k exceeds int32");
+  if (L->weight_format != MOE_Q4_WEIGHTS_Q4_0)
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill_w4a8: Q4_0 weights only (weight_format=%d)", L->weight_format);
+  if (!L->t_gate) return fail(MOE_Q4_EINVAL, "moe_q4_prefill_w4a8: needs the tile-order copies (q4_tile)");
+  if (L->hidden > 4096 || L->inter > 4096)
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill_w4a8: hidden=%d inter=%d (each <= 4096)", L->hidden, L->inter);
+  if (T == 0) return MOE_Q4_OK;
+  if (!x_bf16 || !routing || !y || !routing->topk_w || !routing->expert_offsets || !routing->perm ||
+      !routing->inv_perm)
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill_w4a8: NULL pointer");
+  if (!aligned(x_bf16, 16) || !aligned(y, 16) || !aligned(gate_dots, 4))
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill_w4a8: x_bf16 and y 16-byte, gate_dots 4-byte aligned");
+  const PrefillWs W = prefill_ws(L, T);
+  rc = check_ws(ws, ws_bytes, W.total);
+  if (rc) return rc;
+  moeq4::W4A8PrefillArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x_bf16;
+  a.T = T;
+  a.H = L->hidden;
+  a.I = L->inter;
+  a.E = L->n_experts;
+  a.k = L->top_k;
+  a.has_shared = L->has_shared;
+  a.perm = routing->perm;
+  a.offsets = routing->expert_offsets;
+  a.t_gate = static_cast<const uint8_t*>(L->t_gate);
+  a.t_up = static_cast<const uint8_t*>(L->t_up);
+  a.t_down = static_cast<const uint8_t*>(L->t_down);
+  a.ts_gate = static_cast<const uint8_t*>(L->ts_gate);
+  a.ts_up = static_cast<const uint8_t*>(L->ts_up);
+  a.ts_down = static_cast<const uint8_t*>(L->ts_down);
+  a.qx = at<int8_t>(ws, W.qx);
+  a.dx = at<float>(ws, W.dx);
+  a.qh = at<int8_t>(ws, W.qh);
+  a.dh = at<float>(ws, W.dh);
+  a.o_perm = at<uint16_t>(ws, W.o);
+  a.y = y;
+  hipError_t e = moeq4::launch_prefill_w4a8(a, gate_dots, stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_q4_prefill_w4a8");
+  // the weighted combine of the routed outputs into y (the bf16 form's)
+  moeq4::PrefillArgs c;
+  memset(&c, 0, sizeof c);
+  c.x = x_bf16;
+  c.T = T;
+  c.H = L->hidden;
+  c.I = L->inter;
+  c.E = L->n_experts;
+  c.k = L->top_k;
+  c.has_shared = L->has_shared;
+  c.perm = routing->perm;
+  c.offsets = routing->expert_offsets;
+  c.inv_perm = routing->inv_perm;
+  c.topk_w = routing->topk_w;
+  c.o_perm = a.o_perm;
+  c.y = y;
+  e = moeq4::launch_prefill(c, MOE_Q4_STAGE_COMBINE, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_prefill_w4a8/combine");
 }
 
 int moe_q4_prefill_status(const moe_q4_layer* L, int32_t T, const void* ws, size_t ws_bytes,

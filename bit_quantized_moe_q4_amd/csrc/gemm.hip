@@ -35,6 +35,7 @@
 #include "launch.hpp"
 #include "device_math.hpp"
 #include "w4a8.hpp"
+#include "tiles.hpp"
 
 namespace moeq4 {
 
@@ -46,13 +47,6 @@ constexpr int GLDA = GKB + 8;     // LDS row stride in bf16 elements (16-byte pa
 constexpr int GBN = 128;          // output columns per block (4 waves x 32)
 constexpr int GMaxE = 1024;
 
-struct Tile {
-  int valid;     // 0: no work for this block
-  int rows;      // valid rows in the tile (1..BM)
-  int pos0;      // row position of the tile's first row in h / o_perm
-  int expert;    // routed expert, or -1 for the shared expert
-  int m0;        // first row inside the expert segment (token index for shared)
-};
 
 // pref[e] = tiles of experts < e (pref[E] = routed total), computed by wave 0.
 template <int BM>
@@ -362,61 +356,6 @@ constexpr int FMAXS = 5;                 // max 32-row subtiles per tile
 constexpr int FMAXR = 32 * FMAXS;        // max rows per tile
 static_assert(FMAXR == kPrefillTileRows, "tile rows shared with the workspace bound");
 
-// Tile mt, found by every wave on its own (registers only, no LDS): the
-// shared expert's ceil(T / FMAXR) tiles come first (its dense M = T tiles
-// are the largest units and their down work the longest chain), then
-// expert e owns ceil(c_e / FMAXR) consecutive tile indices, experts in order.
-__device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offsets, int E, int T,
-                                              int k, int has_shared, int mt) {
-  const int lane = threadIdx.x % 64;
-  Tile t;
-  t.valid = 0;
-  t.rows = 0;
-  t.pos0 = 0;
-  t.expert = -1;
-  t.m0 = 0;
-  int c = -1, q = 0;
-  const int n_sh = has_shared ? (T + FMAXR - 1) / FMAXR : 0;
-  if (mt < n_sh) {                        // (uniform per wave)
-    c = T;
-    q = mt;
-  } else {
-    const int mr = mt - n_sh;
-    int carry = 0;
-    for (int base = 0; base < E; base += 64) {
-      const int e = base + lane;
-      int ce = 0;
-      if (e < E) ce = offsets[e + 1] - offsets[e];
-      const int nt = (ce + FMAXR - 1) / FMAXR;
-      int incl = nt;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += o;
-      }
-      const unsigned long long hit = __ballot(carry + incl > mr);
-      if (hit) {
-        const int f = __builtin_ctzll(hit);
-        t.expert = base + f;
-        c = __shfl(ce, f, 64);
-        q = mr - (carry + __shfl(incl, f, 64) - __shfl(nt, f, 64));
-        break;
-      }
-      carry += __shfl(incl, 63, 64);
-    }
-    if (c < 0) return t;
-  }
-  const int nt = (c + FMAXR - 1) / FMAXR;
-  if (q < 0 || q >= nt) return t;
-  const int tr = 32 * (((c + nt - 1) / nt + 31) / 32);   // rows per tile, <= FMAXR
-  t.m0 = q * tr;
-  t.rows = min(tr, c - t.m0);
-  if (t.rows <= 0) return t;
-  t.valid = 1;
-  t.pos0 = (t.expert >= 0) ? offsets[t.expert] + t.m0 : T * k + t.m0;
-  return t;
-}
-
 __device__ __forceinline__ void lds_load16(const void* g, uint16_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
@@ -674,7 +613,7 @@ __global__ void __launch_bounds__(256, 2) gemm_g2_kernel(PrefillArgs a, int ncb)
   __shared__ __attribute__((aligned(16))) G2Smem sm;
   const int b = blockIdx.x, q = b / 8;
   const int tile = 8 * (q / ncb) + b % 8, cb = q % ncb;
-  const Tile t = find_tile_bal(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
+  const Tile t = find_tile_bal<FMAXR>(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
   if (!t.valid) return;
   switch ((t.rows + 31) / 32) {
     case 1: g2_tile<1, GATEUP>(a, t, cb, sm); break;
@@ -715,7 +654,7 @@ __global__ void __launch_bounds__(256, 2) gemm_ffn_kernel(PrefillArgs a, int ncb
   const int ncb = gu ? ncb_gu : ncb_dn;
   const int q = b / 8;
   const int tile = 8 * (q / ncb) + b % 8, cb = q % ncb;
-  const Tile t = find_tile_bal(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
+  const Tile t = find_tile_bal<FMAXR>(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
   if (!t.valid) return;
   const int S = (t.rows + 31) / 32;
   if (gu) {

@@ -68,6 +68,29 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, int stages, hipStream_t stream);
 
+// The W4A8 form of the batched prefill (w4a8_prefill.hip): int8 MFMA block
+// dots over 8-bit tokens and 8-bit h, one fp32 FMA per block dot.
+struct W4A8PrefillArgs {
+  const uint16_t* x;        // [T][H] bf16
+  int T, H, I, E, k, has_shared;
+  const int32_t* perm;      // [T*k]
+  const int32_t* offsets;   // [E+1]
+  const uint8_t* t_gate;    // tile-order matrices (q4_tile)
+  const uint8_t* t_up;
+  const uint8_t* t_down;
+  const uint8_t* ts_gate;
+  const uint8_t* ts_up;
+  const uint8_t* ts_down;
+  int8_t* qx;               // [T][H]        q8 codes of x
+  float* dx;                // [T][H/32]     their scales
+  int8_t* qh;               // [T*k + T*S][I] q8 codes of h, segment order (shared rows last)
+  float* dh;                // [T*k + T*S][I/32]
+  uint16_t* o_perm;         // [T*k][H] bf16 routed expert outputs, segment order
+  float* y;                 // [T][H]
+};
+int64_t w4a8_prefill_tile_bound(int64_t T, int k, int E, int has_shared);
+hipError_t launch_prefill_w4a8(const W4A8PrefillArgs& a, int32_t* gate_dots, hipStream_t stream);
+
 // Rows per tile of the grouped GEMMs (an expert segment of c rows is cut into
 // ceil(c / kPrefillTileRows) tiles) and an upper bound of the tile count.
 constexpr int kPrefillTileRows = 160;

@@ -39,7 +39,8 @@ def test_header_declares_the_api():
               "moe_q4_decode_stack", "moe_q4_decode_stack_workspace_bytes",
               "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
               "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm",
-              "moe_q4_prefill_status", "moe_q4_decode_status", "moe_q4_test_decode_wait_fail",
+              "moe_q4_prefill_status", "moe_q4_prefill_w4a8", "moe_q4_decode_status",
+              "moe_q4_test_decode_wait_fail",
               "moe_q4_last_error"]:
         assert n in names, n
 
@@ -262,6 +263,37 @@ def test_prefill_status_checks(lib):
     # the bit of the test-only forced wait failure is accepted on top of a stage mask
     assert lib.moe_q4_prefill_stage(C.byref(L), None, 0, None, None, None, 0, 3 | 16, None) == 0
     assert lib.moe_q4_prefill_stage(C.byref(L), None, 0, None, None, None, 0, 16, None) == -1
+
+
+def test_prefill_w4a8_checks(lib):
+    L = _layer()
+    x, y, ws = C.c_void_p(0x1000), C.c_void_p(0x2000), C.c_void_p(0x100000)
+    from bit_quantized_moe_q4_amd._lib import Routing
+    R = Routing()
+    R.topk_ids = R.topk_w = R.expert_offsets = R.perm = R.inv_perm = 0x3000
+    # row-major layer: the W4A8 form needs the tile-order copies
+    assert lib.moe_q4_prefill_w4a8(C.byref(L), x, 8, C.byref(R), y, None, ws, 1 << 30, None) == -1
+    assert "tile-order" in _err(lib)
+    L.t_gate = L.t_up = L.t_down = 0x20000
+    assert lib.moe_q4_prefill_w4a8(C.byref(L), x, -1, C.byref(R), y, None, ws, 1 << 30, None) == -1
+    # no tokens: valid, nothing enqueued
+    assert lib.moe_q4_prefill_w4a8(C.byref(L), None, 0, None, None, None, None, 0, None) == 0
+    assert lib.moe_q4_prefill_w4a8(C.byref(L), x, 8, None, y, None, ws, 1 << 30, None) == -1
+    # one workspace size serves both prefill forms
+    pneed = lib.moe_q4_prefill_workspace_bytes(C.byref(L), 100)
+    rows = 100 * 2
+    assert pneed >= rows * 128 * 2 + rows * 256 * 2                    # bf16 h + routed outputs
+    assert pneed >= rows * 256 * 2 + rows * 128 + rows * 4 * 4 + 100 * 256 + 100 * 8 * 4
+    rc = lib.moe_q4_prefill_w4a8(C.byref(L), x, 100, C.byref(R), y, None, ws, pneed - 1, None)
+    assert rc == -2
+    assert lib.moe_q4_prefill_w4a8(C.byref(L), C.c_void_p(0x1008), 100, C.byref(R), y, None, ws, pneed,
+                                   None) == -1 and "aligned" in _err(lib)
+    big = _layer(hidden=8192, inter=128)
+    big.t_gate = big.t_up = big.t_down = 0x20000
+    assert lib.moe_q4_prefill_w4a8(C.byref(big), x, 8, C.byref(R), y, None, ws, 1 << 40, None) == -1
+    assert "4096" in _err(lib)
+    L.weight_format = 1
+    assert lib.moe_q4_prefill_w4a8(C.byref(L), x, 8, C.byref(R), y, None, ws, 1 << 30, None) == -1
 
 
 def test_decode_noalloc_checks(lib):
