@@ -21,9 +21,16 @@ in HBM when timing starts:
   launch (and the tiny counter fill before it) on the stream it runs on.
   `traffic` is the HBM bytes per launch from rocprofv3 FETCH_SIZE and
   WRITE_SIZE counters, calibrated against a plain 1 GiB device copy, read
-  from profiles/traffic_*.json while the kernel sources are unchanged.
-- cpu_baseline: the CPU oracle (single-threaded C) on a bounded token sample
-  of the same workload, scaled to tokens/s.
+  from profiles/traffic_*.json while the kernel sources are unchanged;
+  `algorithmic_bytes` the least a launch must move (prefill_algorithmic_bytes).
+- prefill_w4a8: the same step in the W4A8 form (int8 MFMA), with its own
+  int8 roofline.
+- prefill_skewed_10k: 10240 tokens with Zipf-like routing, both forms.
+- full_depth_40_layers: 40 distinct 256-expert layers, an 8192-token prefill
+  and 256 one-token decode steps through all of them.
+- small_batch_decode, stack_decode, decode_q8_0, w4a8_gemm: comparisons.
+- cpu_baseline: the CPU oracle (single-threaded C functions) on bounded token
+  samples, prefill and decode, on one core and on N threads.
 
 Counter collection (two rocprofv3 --pmc runs of this script with
 --copy-probe, then `python bench.py --traffic-from FETCH.csv WRITE.csv`):
@@ -73,9 +80,11 @@ def _traffic(unit):
 # kernels whose HBM traffic is recorded: name -> (kernel-name substrings
 # counted per unit, sources the record is valid for)
 TRAFFIC_KERNELS = {
-    "gemm": (["gemm_ffn_kernel"], ["gemm.hip", "launch.hpp", "device_math.hpp"]),
-    "decode": (["decode_router_kernel", "decode_gateup_tiled_kernel", "decode_down_tiled_kernel"],
-               ["decode.hip", "launch.hpp", "w4a8.hpp", "device_math.hpp"]),
+    "gemm": (["gemm_ffn_kernel"], ["gemm.hip", "tiles.hpp", "launch.hpp", "device_math.hpp"]),
+    "decode": (["decode_fused_kernel"],
+               ["decode_fused.hip", "decode_tile.hpp", "launch.hpp", "w4a8.hpp", "device_math.hpp"]),
+    "w4a8_prefill": (["w8_gateup_kernel", "w8_down_kernel"],
+                     ["w4a8_prefill.hip", "tiles.hpp", "launch.hpp", "device_math.hpp"]),
 }
 COPY_PROBE_BYTES = 1 << 30
 
@@ -223,8 +232,217 @@ def bench_prefill(args, torch, mq, moe_synth, device_layer):
     fl_dn = 2.0 * rows * cfg.I * cfg.H
     fl_total = fl_gu + fl_dn
     assert torch.isfinite(y).all().item()
+    import numpy as np
+    counts = np.diff(routing.expert_offsets.cpu().numpy())
     return dict(cfg=cfg, W=W, step_s=step_s, t_route=t_route, t_gemm=t_gemm, t_gemm_split=t_gemm_split, t_cb=t_cb,
-                fl_gu=fl_gu, fl_dn=fl_dn, fl_total=fl_total, layers=layers)
+                fl_gu=fl_gu, fl_dn=fl_dn, fl_total=fl_total, layers=layers, xb=xb, y=y, routing=routing,
+                rws=rws, pws=pws, counts=counts)
+
+
+def _stage_time(torch, call, n):
+    """Mean seconds of `call(i)` over n back-to-back calls between two events
+    on the current stream (the one the library launches on)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / n
+
+
+def prefill_algorithmic_bytes(cfg, T, counts, form="bf16"):
+    """HBM bytes a grouped prefill launch must move at least: every expert
+    matrix with at least one routed row (and the shared expert's) read once,
+    the tokens read once, h written and read once (the down GEMM's input),
+    the routed outputs (bf16) and the shared expert's rows of y (fp32)
+    written once.  W4A8 form: h as int8 codes + a scale per 32, and x read
+    as int8 codes + scales by the GEMM after q8(x)."""
+    mat = cfg.I * (cfg.H // 32) * 18
+    S = 1 if cfg.shared else 0
+    live = int((counts > 0).sum()) + S
+    rows = T * cfg.k + T * S
+    w = 3 * live * mat
+    if form == "bf16":
+        xb = T * cfg.H * 2
+        hb = 2 * rows * cfg.I * 2
+    else:
+        xb = T * cfg.H + T * (cfg.H // 32) * 4
+        hb = 2 * (rows * cfg.I + rows * (cfg.I // 32) * 4)
+    ob = T * cfg.k * cfg.H * 2 + S * T * cfg.H * 4
+    return w + xb + hb + ob
+
+
+def bench_prefill_w4a8(args, torch, mq, pre):
+    """The W4A8 form of the same prefill step (moe_q4_route +
+    moe_q4_prefill_w4a8: q8(x), int8-MFMA gate/up with SwiGLU and q8(h),
+    int8-MFMA down, combine) on the same layers and tokens."""
+    cfg, layers, xb, y = pre["cfg"], pre["layers"], pre["xb"], pre["y"]
+    T = cfg.T
+    routing, rws, pws = pre["routing"], pre["rws"], pre["pws"]
+    S = mq._lib
+
+    def step(i):
+        L = layers[i % len(layers)]
+        mq.moe_q4_route(L, xb, out=routing, ws=rws)
+        mq.moe_q4_prefill_w4a8(L, xb, routing, y=y, ws=pws)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    n = args.steps
+    st = lambda m: (lambda i: mq.moe_q4_prefill_w4a8_stage(layers[i % len(layers)], xb, routing, y, pws, m))  # noqa
+    t_gu = _stage_time(torch, st(S.STAGE_GATEUP), n)
+    t_dn = _stage_time(torch, st(S.STAGE_DOWN), n)
+    t_cb = _stage_time(torch, st(S.STAGE_COMBINE), n)
+    assert torch.isfinite(y).all().item()
+    return dict(step_s=step_s, t_gu=t_gu, t_dn=t_dn, t_cb=t_cb)
+
+
+def bench_skew(args, torch, mq, moe_synth, device_layer):
+    """The long-context prefill with skewed routing: 10240 tokens, the same
+    layer shape with the Zipf-like router bias (hottest expert ~10x the mean
+    load, some experts near-empty); both prefill forms, two layer copies
+    alternating."""
+    import numpy as np
+    cfg = moe_synth.CONFIGS["skew"]
+    base = device_layer(cfg, threads=16)
+    layers = [base, clone_layer(base)]
+    x = moe_synth.tokens(cfg)
+    xb = torch.from_numpy(moe_synth.to_bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+    T = cfg.T
+    routing = mq.Routing.empty(T, cfg.k, cfg.E, xb.device)
+    rws = torch.empty(mq.moe_q4_route_workspace_bytes(base, T), dtype=torch.uint8, device="cuda")
+    pws = torch.empty(mq.moe_q4_prefill_workspace_bytes(base, T), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, cfg.H), dtype=torch.float32, device="cuda")
+    steps = max(5, args.steps // 4)
+
+    def run(fn):
+        for i in range(max(3, args.warmup // 4)):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def bf16(i):
+        L = layers[i % 2]
+        mq.moe_q4_route(L, xb, out=routing, ws=rws)
+        mq.moe_q4_prefill(L, xb, routing, y=y, ws=pws)
+
+    def w4a8(i):
+        L = layers[i % 2]
+        mq.moe_q4_route(L, xb, out=routing, ws=rws)
+        mq.moe_q4_prefill_w4a8(L, xb, routing, y=y, ws=pws)
+    t16 = run(bf16)
+    S = mq._lib
+    t_gemm = _stage_time(torch, lambda i: mq.moe_q4_prefill_stage(layers[i % 2], xb, routing, y, pws,
+                                                                  S.STAGE_GATEUP | S.STAGE_DOWN), steps)
+    t8 = run(w4a8)
+    counts = np.diff(routing.expert_offsets.cpu().numpy())
+    rows = T * cfg.k + T
+    fl = 2.0 * rows * 3 * cfg.I * cfg.H
+    assert torch.isfinite(y).all().item()
+    return {
+        "workload": "one MoE FFN layer, prefill of 10240 tokens with skewed routing (router bias "
+                    "1.5 log(1/(rank+1))): hidden 2048, 128 routed experts + 1 shared, intermediate 512, "
+                    "top-8, Q4_0 weights; route + grouped GEMM + combine",
+        "tok_s": round(T / t16, 1), "ms_per_step": round(t16 * 1e3, 4),
+        "gemm_us": round(t_gemm * 1e6, 2), "gemm_tflops": round(fl / t_gemm / 1e12, 2),
+        "gemm_mfma_frac": round(fl / t_gemm / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "w4a8_tok_s": round(T / t8, 1), "w4a8_ms_per_step": round(t8 * 1e3, 4),
+        "hottest_expert_rows": int(counts.max()), "mean_expert_rows": round(float(counts.mean()), 1),
+        "empty_experts": int((counts == 0).sum()), "steps": steps, "layer_copies_rotated": 2,
+    }
+
+
+C5_LAYERS = 40
+
+
+def bench_full_depth(args, torch, mq, moe_synth):
+    """The full-depth sweep: 40 distinct layers of 256 routed experts + 1
+    shared (hidden 2048, intermediate 512, top-8, Q4_0; ~18 GB resident),
+    an 8192-token prefill through all 40 (RMSNorm, unit gain, eps 1e-6,
+    between layers, bf16 into the next prefill layer), then 256 one-token
+    decode steps through all 40 (moe_q4_decode_stack: the RMSNorm fused into
+    each next layer).  Expert weights are drawn on the device (N(0, 0.02),
+    seeded torch generator) to keep set-up to seconds; router weights and
+    tokens are the seeded synthetic ones."""
+    import numpy as np
+    cfg = moe_synth.CONFIGS["stack"]
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    H, I, E = cfg.H, cfg.I, cfg.E
+    layers = []
+    for l in range(C5_LAYERS):
+        pk = lambda *shape: mq.q4_pack(torch.randn(shape, generator=g, device="cuda") * 0.02)  # noqa: E731
+        wr = torch.from_numpy(moe_synth.router(cfg, l)).cuda()
+        layers.append(mq.MoELayer(wr, pk(E, I, H), pk(E, I, H), pk(E, H, I), cfg.k,
+                                  s_gate=pk(I, H), s_up=pk(I, H), s_down=pk(H, I)))
+    torch.cuda.synchronize()
+    resident = sum(L.resident_bytes() for L in layers)
+    T = cfg.T
+    x = moe_synth.tokens(cfg)
+    xb0 = torch.from_numpy(moe_synth.to_bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16)
+    routing = mq.Routing.empty(T, cfg.k, E, xb0.device)
+    rws = torch.empty(mq.moe_q4_route_workspace_bytes(layers[0], T), dtype=torch.uint8, device="cuda")
+    pws = torch.empty(mq.moe_q4_prefill_workspace_bytes(layers[0], T), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    xn = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def prefill_pass():
+        xb = xb0
+        for L in layers:
+            mq.moe_q4_route(L, xb, out=routing, ws=rws)
+            mq.moe_q4_prefill(L, xb, routing, y=y, ws=pws)
+            mq.moe_q4_rmsnorm(y, 1e-6, f32=False, out_bf16=xn)
+            xb = xn
+    prefill_pass()
+    torch.cuda.synchronize()
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        prefill_pass()
+    torch.cuda.synchronize()
+    t_pre = (time.perf_counter() - t0) / reps
+    assert torch.isfinite(y).all().item()
+    # decode: 256 steps = 8 replays of a graph of 32 one-token steps (fresh
+    # seeded x per step), each step through all 40 layers
+    stack = mq.LayerStack(layers)
+    ws = mq.stack_workspace(stack)
+    nt = 32
+    X = torch.from_numpy(moe_synth.tokens(cfg, step=1000, T=nt)).cuda()
+    Y = torch.empty((nt, H), dtype=torch.float32, device="cuda")
+    calls = [(lambda i=i: mq.moe_q4_decode_stack(stack, X[i], 1e-6, y=Y[i], ws=ws)) for i in range(nt)]
+    for c in calls[:2]:
+        c()
+    torch.cuda.synchronize()
+    t_dec = _graph_time(torch, calls, cfg.steps // nt)
+    assert torch.isfinite(Y).all().item()
+    per_layer = 3 * (cfg.k + 1) * I * (H // 32) * 18 + H * E * 4
+    del layers, stack, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": "40 stacked MoE FFN layers (256 routed experts + 1 shared, hidden 2048, "
+                    "intermediate 512, top-8, Q4_0), 8192-token prefill then 256 one-token decode "
+                    "steps, RMSNorm (unit gain, eps 1e-6) between layers",
+        "prefill_tok_s": round(T / t_pre, 1), "prefill_ms_40_layers": round(t_pre * 1e3, 3),
+        "prefill_layer_tok_s": round(T * C5_LAYERS / t_pre, 1),
+        "decode_us_per_token_40_layers": round(t_dec * 1e6, 2),
+        "decode_us_per_layer": round(t_dec * 1e6 / C5_LAYERS, 3),
+        "decode_weight_gbps": round(per_layer * C5_LAYERS / t_dec / 1e9, 1),
+        "total_s": round(t_pre + cfg.steps * t_dec, 4),
+        "resident_bytes": resident,
+        "note": "prefill: route + fused grouped GEMM + combine + RMSNorm per layer, eager launches, "
+                "mean of 3 passes; decode: moe_q4_decode_stack, HIP graph of 32 steps replayed 8 times; "
+                "every step streams its 9 experts per layer from HBM (40 layers x 17 MB > the 256 MB "
+                "last-level cache)",
+    }
 
 
 def bench_decode(args, torch, mq, moe_synth, device_layer, wfmt="q4"):
@@ -440,28 +658,85 @@ def bench_small_batch(args, torch, mq, moe_synth, dec, pre):
     return out
 
 
+def cpu_info():
+    """Host CPU model, physical cores, logical CPUs, the CPUs this process may
+    use, and whether SMT is active (None where the system does not say)."""
+    model, phys, cur = None, set(), {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if ":" in line:
+                    k, v = (t.strip() for t in line.split(":", 1))
+                    if k == "model name" and model is None:
+                        model = v
+                    elif k in ("physical id", "core id"):
+                        cur[k] = v
+                elif not line.strip() and cur:
+                    phys.add((cur.get("physical id"), cur.get("core id")))
+                    cur = {}
+        if cur:
+            phys.add((cur.get("physical id"), cur.get("core id")))
+    except OSError:
+        pass
+    smt = None
+    try:
+        with open("/sys/devices/system/cpu/smt/active") as f:
+            smt = f.read().strip() == "1"
+    except OSError:
+        pass
+    return {"model": model, "physical_cores": len(phys) or None, "logical_cpus": os.cpu_count(),
+            "cpus_allowed": len(os.sched_getaffinity(0)), "smt_active": smt}
+
+
 def cpu_baseline(args, pre):
-    """The oracle as it stands, single-threaded, on a bounded token sample."""
+    """The oracle as it stands (single-threaded C functions) on bounded token
+    samples of the prefill workload: its binary64 prefill reference (with the
+    fp32 routing program) and its one-token W4A8 decode program, each on one
+    core and on N cores (N threads, each running the same C function on its
+    own slice of tokens)."""
+    from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import moe_synth
     import oracle
     cfg, W = pre["cfg"], pre["W"]
+    info = cpu_info()
+    nthr = max(1, min(16, info["cpus_allowed"]))
     ol = oracle.PackedLayer.from_float(moe_synth.router(cfg), moe_synth.router_bias(cfg), W["gate"],
                                        W["up"], W["down"], W["s_gate"], W["s_up"], W["s_down"],
-                                       k=cfg.k, threads=16)
+                                       k=cfg.k, threads=nthr)
     x = moe_synth.tokens(cfg)
     xw = moe_synth.bf16_bits_to_f32(moe_synth.to_bf16_bits(x))
-    n = args.cpu_sample_tokens
-    sample = np.arange(n)
-    t0 = time.perf_counter()
-    r = oracle.route(ol, xw[:n])
-    t1 = time.perf_counter()
-    oracle.prefill_ref(ol, xw[:n], r["ids"], r["w64"], tokens=sample)
-    t2 = time.perf_counter()
-    per_tok = (t2 - t0) / n
-    return {"value": round(1.0 / per_tok, 3), "unit": "tok/s", "cores": 1, "kind": "oracle",
-            "sample": "first %d tokens of the 2048-token batch: routing (fp32 program) + binary64 "
-                      "expert FFN reference; %.1f s of CPU time" % (n, t2 - t0)}
+    n1 = args.cpu_sample_tokens
+    nn = min(cfg.T, n1 * nthr)
+
+    def prefill(n, threads):
+        t0 = time.perf_counter()
+        r = oracle.route(ol, xw[:n])
+        oracle.prefill_ref(ol, xw[:n], r["ids"], r["w64"], tokens=np.arange(n), threads=threads)
+        return n / (time.perf_counter() - t0)
+
+    def decode(n, threads):
+        t0 = time.perf_counter()
+        if threads == 1:
+            for i in range(n):
+                oracle.decode(ol, xw[i])
+        else:
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                list(ex.map(lambda i: oracle.decode(ol, xw[i]), range(n)))
+        return n / (time.perf_counter() - t0)
+    t_start = time.perf_counter()
+    p1, pn = prefill(n1, 1), prefill(nn, nthr)
+    d1, dn = decode(n1, 1), decode(nn, nthr)
+    wall = time.perf_counter() - t_start
+    return {"value": round(pn, 2), "unit": "tok/s", "cores": nthr, "kind": "oracle",
+            "sample": "prefill: first %d tokens of the 2048-token batch, routing (fp32 program) + the "
+                      "binary64 expert FFN reference; %d threads on disjoint token slices" % (nn, nthr),
+            "one_core": {"prefill_tok_s": round(p1, 3), "decode_tok_s": round(d1, 3), "tokens": n1},
+            "n_core": {"prefill_tok_s": round(pn, 2), "decode_tok_s": round(dn, 2), "tokens": nn,
+                       "threads": nthr},
+            "decode_note": "decode: the oracle's one-token W4A8 program (routing, q8, int32 block dots, "
+                           "pinned fp32 sums) on the same layer, one token per call",
+            "cpu": info, "wall_s": round(wall, 1)}
 
 
 def main():
@@ -474,12 +749,16 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--decode-copies", type=int, default=16)
     ap.add_argument("--decode-reps", type=int, default=3)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=768)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=96,
+                    help="tokens per core of the CPU oracle samples")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true", help="skip the 1..32-token decode comparison")
     ap.add_argument("--no-q8", action="store_true", help="skip the Q8_0-weight decode comparison")
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer stack decode")
     ap.add_argument("--no-w4a8-gemm", action="store_true", help="skip the int8-MFMA W4A8 GEMM leg")
+    ap.add_argument("--no-w4a8-prefill", action="store_true", help="skip the W4A8-form prefill leg")
+    ap.add_argument("--no-skew", action="store_true", help="skip the 10240-token skewed prefill leg")
+    ap.add_argument("--no-full-depth", action="store_true", help="skip the 40-layer full-depth leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -504,6 +783,9 @@ def main():
     torch.cuda.set_device(0)
 
     pre = bench_prefill(args, torch, mq, moe_synth, device_layer)
+    w8 = None if args.no_w4a8_prefill else bench_prefill_w4a8(args, torch, mq, pre)
+    for k_ in ("xb", "y", "routing", "rws", "pws"):
+        pre.pop(k_)
     dec = bench_decode(args, torch, mq, moe_synth, device_layer)
     small = None if args.no_small_batch else bench_small_batch(args, torch, mq, moe_synth, dec, pre)
     stackr = None if args.no_stack else bench_stack(args, torch, mq, moe_synth, dec)
@@ -512,12 +794,18 @@ def main():
     if not args.no_q8:
         dec8 = bench_decode(args, torch, mq, moe_synth, device_layer, wfmt="q8")
         dec8.pop("layers")
+    skew = None if args.no_skew else bench_skew(args, torch, mq, moe_synth, device_layer)
+    torch.cuda.empty_cache()
+    full = None if args.no_full_depth else bench_full_depth(args, torch, mq, moe_synth)
+    torch.cuda.empty_cache()
     copy_gbps = hbm_copy_gbps(torch)
     cfg = pre["cfg"]
     tok_s = cfg.T / pre["step_s"]
     fl_gemm = pre["fl_gu"] + pre["fl_dn"]
     ach = fl_gemm / pre["t_gemm"] / 1e12
     dec_gbps = dec["bytes_step"] / dec["step_s"] / 1e9
+    alg_gemm = prefill_algorithmic_bytes(cfg, cfg.T, pre["counts"])
+    alg_dec = dec["bytes_step"] + 2 * cfg.H * 4
     out = {
         "metric": "MoE-layer tok/s at 2k prefill; decode weight GB/s; % of HBM/MFMA roofline",
         "value": round(tok_s, 1),
@@ -545,6 +833,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": _traffic("gemm"),
+            "algorithmic_bytes": alg_gemm,
+            "traffic_over_algorithmic": None if _traffic("gemm") is None else round(_traffic("gemm") / alg_gemm, 3),
             "flop_per_launch": fl_gemm,
             "avg_launch_us": round(pre["t_gemm"] * 1e6, 2),
             "timing": "%d back-to-back fused GEMM calls (counter fill + gemm_ffn_kernel) between two "
@@ -572,9 +862,37 @@ def main():
             "workload": "one-token W4A8 decode, same layer shape, fresh x per step, HIP graph replay",
             "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
-                         "traffic": _traffic("decode")},
+                         "kernel": "decode_fused_kernel (routing, gate/up + SwiGLU + q8(h), down and "
+                                   "combine in one launch)",
+                         "traffic": _traffic("decode"),
+                         "algorithmic_bytes": alg_dec,
+                         "traffic_over_algorithmic": None if _traffic("decode") is None
+                         else round(_traffic("decode") / alg_dec, 3)},
         },
     }
+    if w8 is not None:
+        t8 = w8["t_gu"] + w8["t_dn"]
+        ops8 = pre["fl_gu"] + pre["fl_dn"]
+        alg8 = prefill_algorithmic_bytes(cfg, cfg.T, pre["counts"], form="w4a8")
+        tr8 = _traffic("w4a8_prefill")
+        out["prefill_w4a8"] = {
+            "workload": "the same 2048-token prefill step in the W4A8 form: moe_q4_route + "
+                        "moe_q4_prefill_w4a8 (q8(x), int8-MFMA grouped gate/up with SwiGLU and q8(h), "
+                        "int8-MFMA grouped down, combine)",
+            "tok_s": round(cfg.T / w8["step_s"], 1), "ms_per_step": round(w8["step_s"] * 1e3, 4),
+            "stages_us": {"q8x_gateup": round(w8["t_gu"] * 1e6, 2), "down": round(w8["t_dn"] * 1e6, 2),
+                          "combine": round(w8["t_cb"] * 1e6, 2)},
+            "roofline": {"kernel": "w8_gateup_kernel + w8_down_kernel (q8x_kernel included in the time)",
+                         "bound": "mfma", "achieved": round(ops8 / t8 / 1e12, 2), "peak": PEAK_INT8_TOPS,
+                         "unit": "TOPS", "frac": round(ops8 / t8 / 1e12 / PEAK_INT8_TOPS, 4),
+                         "ops_per_step": ops8, "traffic": tr8, "algorithmic_bytes": alg8,
+                         "traffic_over_algorithmic": None if tr8 is None else round(tr8 / alg8, 3),
+                         "note": "int8 matrix-core peak; each block dot needs its own fp32 rescale, so "
+                                 "the kernels are bound by VALU issue well below it"},
+            "bf16_form_gemm_tflops": round(ach, 2),
+        }
+    out["prefill_skewed_10k"] = skew
+    out["full_depth_40_layers"] = full
     out["small_batch_decode"] = small
     out["stack_decode"] = stackr
     out["w4a8_gemm"] = None if args.no_w4a8_gemm else bench_w4a8_gemm(args, torch, mq, ach)

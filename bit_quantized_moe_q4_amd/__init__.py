@@ -24,7 +24,7 @@ __all__ = [
     "q4_packed_bytes", "q4_pack", "q4_tile", "q8w_pack", "q8w_tile", "q8_quantize", "MoELayer", "Routing",
     "moe_q4_route_workspace_bytes", "moe_q4_route",
     "moe_q4_prefill_workspace_bytes", "moe_q4_prefill", "moe_q4_prefill_stage", "moe_q4_prefill_status",
-    "moe_q4_prefill_w4a8",
+    "moe_q4_prefill_w4a8", "moe_q4_prefill_w4a8_stage",
     "moe_q4_decode_workspace_bytes", "moe_q4_decode", "decode_workspace", "moe_q4_decode_noalloc", "moe_q4_decode_status",
     "moe_q4_decode_batch_workspace_bytes", "moe_q4_decode_batch",
     "LayerStack", "moe_q4_decode_stack_workspace_bytes", "moe_q4_decode_stack", "stack_workspace",
@@ -179,6 +179,13 @@ class MoELayer:
     def struct_ptr(self):
         return C.byref(self._c)
 
+    def resident_bytes(self) -> int:
+        """Device bytes the layer holds (router, packed matrices, tile-order copies)."""
+        ts = [self.w_router, self.router_bias, self.gate, self.up, self.down, self.s_gate, self.s_up, self.s_down]
+        if self.tiles:
+            ts += list(self.tiles.values())
+        return sum(t.numel() * t.element_size() for t in ts if t is not None)
+
 
 @dataclass
 class Routing:
@@ -303,6 +310,20 @@ def moe_q4_prefill_w4a8(layer: MoELayer, x_bf16: torch.Tensor, routing: Routing,
     _lib.check(_lib.lib().moe_q4_prefill_w4a8(layer.struct_ptr(), _p(x_bf16), T, C.byref(rs), _p(y),
                                               _p(gate_dots), _p(w), w.numel(), _s(stream)),
                "moe_q4_prefill_w4a8")
+    return y
+
+
+def moe_q4_prefill_w4a8_stage(layer: MoELayer, x_bf16: torch.Tensor, routing: Routing, y: torch.Tensor,
+                              ws: torch.Tensor, stages: int, gate_dots: torch.Tensor | None = None,
+                              stream=None) -> torch.Tensor:
+    """Some stages of moe_q4_prefill_w4a8 (mask of _lib.STAGE_GATEUP | _DOWN | _COMBINE)
+    with a caller-held workspace."""
+    _dev(x_bf16, "x_bf16")
+    T = int(x_bf16.shape[0])
+    rs = routing.cstruct()
+    _lib.check(_lib.lib().moe_q4_prefill_w4a8_stage(layer.struct_ptr(), _p(x_bf16), T, C.byref(rs), _p(y),
+                                                    _p(gate_dots), _p(ws), ws.numel(), int(stages), _s(stream)),
+               "moe_q4_prefill_w4a8_stage")
     return y
 
 

@@ -77,6 +77,7 @@ def _declare(lib):
         "moe_q4_prefill_stage": (C.c_int, [P, P, I32, P, P, P, SZ, I32, P]),
         "moe_q4_prefill_status": (C.c_int, [P, I32, P, SZ, P, P]),
         "moe_q4_prefill_w4a8": (C.c_int, [P, P, I32, P, P, P, P, SZ, P]),
+        "moe_q4_prefill_w4a8_stage": (C.c_int, [P, P, I32, P, P, P, P, SZ, I32, P]),
         "moe_q4_decode_workspace_bytes": (SZ, [P]),
         "moe_q4_decode_batch_workspace_bytes": (SZ, [P, I32]),
         "moe_q4_decode_stack_workspace_bytes": (SZ, [P, I32]),

@@ -445,6 +445,15 @@ int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t 
 
 int moe_q4_prefill_w4a8(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T, const moe_q4_routing* routing,
                         float* y, int32_t* gate_dots, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_q4_prefill_w4a8_stage(L, x_bf16, T, routing, y, gate_dots, ws, ws_bytes, MOE_Q4_STAGE_ALL, stream);
+}
+
+int moe_q4_prefill_w4a8_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T,
+                              const moe_q4_routing* routing, float* y, int32_t* gate_dots, void* ws,
+                              size_t ws_bytes, int32_t stages, hipStream_t stream) {
+  if (stages & ~MOE_Q4_STAGE_ALL || !stages)
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill_w4a8_stage: stages=%d (a nonzero mask of GATEUP, DOWN, COMBINE)",
+                stages);
   int rc = check_layer(L);
   if (rc) return rc;
   if (T < 0) return fail(MOE_Q4_EINVAL, "moe_q4_prefill_w4a8: T=%d < 0", T);
@@ -486,8 +495,12 @@ int moe_q4_prefill_w4a8(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t T
   a.dh = at<float>(ws, W.dh);
   a.o_perm = at<uint16_t>(ws, W.o);
   a.y = y;
-  hipError_t e = moeq4::launch_prefill_w4a8(a, gate_dots, stream);
-  if (e != hipSuccess) return hip_fail(e, "moe_q4_prefill_w4a8");
+  hipError_t e = hipSuccess;
+  if (stages & (MOE_Q4_STAGE_GATEUP | MOE_Q4_STAGE_DOWN)) {
+    e = moeq4::launch_prefill_w4a8(a, gate_dots, stages & 3, stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_q4_prefill_w4a8");
+  }
+  if (!(stages & MOE_Q4_STAGE_COMBINE)) return MOE_Q4_OK;
   // the weighted combine of the routed outputs into y (the bf16 form's)
   moeq4::PrefillArgs c;
   memset(&c, 0, sizeof c);

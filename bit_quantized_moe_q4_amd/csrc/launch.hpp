@@ -89,7 +89,8 @@ struct W4A8PrefillArgs {
   float* y;                 // [T][H]
 };
 int64_t w4a8_prefill_tile_bound(int64_t T, int k, int E, int has_shared);
-hipError_t launch_prefill_w4a8(const W4A8PrefillArgs& a, int32_t* gate_dots, hipStream_t stream);
+// stages: 1 = q8(x) + gate/up, 2 = down (the combine is the bf16 form's)
+hipError_t launch_prefill_w4a8(const W4A8PrefillArgs& a, int32_t* gate_dots, int stages, hipStream_t stream);
 
 // Rows per tile of the grouped GEMMs (an expert segment of c rows is cut into
 // ceil(c / kPrefillTileRows) tiles) and an upper bound of the tile count.

@@ -303,24 +303,30 @@ int64_t w4a8_prefill_tile_bound(int64_t T, int k, int E, int has_shared) {
   return T * k / kW8Rows + E + (has_shared ? (T + kW8Rows - 1) / kW8Rows : 0);
 }
 
-hipError_t launch_prefill_w4a8(const W4A8PrefillArgs& a, int32_t* gate_dots, hipStream_t stream) {
-  const int64_t nblk = (int64_t)a.T * (a.H / BLK);
-  hipLaunchKernelGGL(w8_q8x_kernel, dim3((unsigned)((nblk * 8 + 255) / 256)), dim3(256), 0, stream, a.x, nblk,
-                     a.qx, a.dx);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+hipError_t launch_prefill_w4a8(const W4A8PrefillArgs& a, int32_t* gate_dots, int stages, hipStream_t stream) {
   const int groups = (int)((w4a8_prefill_tile_bound(a.T, a.k, a.E, a.has_shared) + 7) / 8);
   const int ncb_gu = a.I / 32, ncb_dn = a.H / kW8DnCols;
-  const size_t lds_gu = (size_t)(a.H / BLK) * kW8Rows * 4 + 4 * 1024;
-  const size_t lds_dn = (size_t)(a.I / BLK) * kW8Rows * 4;
-  if (gate_dots)
-    hipLaunchKernelGGL(w8_gateup_kernel<true>, dim3(groups * 8 * ncb_gu), dim3(256), lds_gu, stream, a, gate_dots);
-  else
-    hipLaunchKernelGGL(w8_gateup_kernel<false>, dim3(groups * 8 * ncb_gu), dim3(256), lds_gu, stream, a, gate_dots);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(w8_down_kernel, dim3(groups * 8 * ncb_dn), dim3(256), lds_dn, stream, a);
-  return hipGetLastError();
+  hipError_t err = hipSuccess;
+  if (stages & 1) {                      // q8(x), then gate/up + SwiGLU + q8(h)
+    const int64_t nblk = (int64_t)a.T * (a.H / BLK);
+    hipLaunchKernelGGL(w8_q8x_kernel, dim3((unsigned)((nblk * 8 + 255) / 256)), dim3(256), 0, stream, a.x, nblk,
+                       a.qx, a.dx);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const size_t lds_gu = (size_t)(a.H / BLK) * kW8Rows * 4 + 4 * 1024;
+    if (gate_dots)
+      hipLaunchKernelGGL(w8_gateup_kernel<true>, dim3(groups * 8 * ncb_gu), dim3(256), lds_gu, stream, a, gate_dots);
+    else
+      hipLaunchKernelGGL(w8_gateup_kernel<false>, dim3(groups * 8 * ncb_gu), dim3(256), lds_gu, stream, a, gate_dots);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (stages & 2) {
+    const size_t lds_dn = (size_t)(a.I / BLK) * kW8Rows * 4;
+    hipLaunchKernelGGL(w8_down_kernel, dim3(groups * 8 * ncb_dn), dim3(256), lds_dn, stream, a);
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 }  // namespace moeq4

@@ -39,7 +39,8 @@ def test_header_declares_the_api():
               "moe_q4_decode_stack", "moe_q4_decode_stack_workspace_bytes",
               "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
               "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm",
-              "moe_q4_prefill_status", "moe_q4_prefill_w4a8", "moe_q4_decode_status",
+              "moe_q4_prefill_status", "moe_q4_prefill_w4a8", "moe_q4_prefill_w4a8_stage",
+              "moe_q4_decode_status",
               "moe_q4_test_decode_wait_fail",
               "moe_q4_last_error"]:
         assert n in names, n
@@ -294,6 +295,10 @@ def test_prefill_w4a8_checks(lib):
     assert "4096" in _err(lib)
     L.weight_format = 1
     assert lib.moe_q4_prefill_w4a8(C.byref(L), x, 8, C.byref(R), y, None, ws, 1 << 30, None) == -1
+    L.weight_format = 0
+    for bad in (0, 8, 16, -1):
+        assert lib.moe_q4_prefill_w4a8_stage(C.byref(L), x, 8, C.byref(R), y, None, ws, 1 << 30, bad, None) == -1
+    assert lib.moe_q4_prefill_w4a8_stage(C.byref(L), None, 0, None, None, None, None, 0, 3, None) == 0
 
 
 def test_decode_noalloc_checks(lib):
