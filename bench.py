@@ -251,26 +251,16 @@ def _stage_time(torch, call, n):
     return e0.elapsed_time(e1) * 1e-3 / n
 
 
-def prefill_algorithmic_bytes(cfg, T, counts, form="bf16"):
-    """HBM bytes a grouped prefill launch must move at least: every expert
+def prefill_algorithmic_bytes(cfg, T, counts):
+    """HBM bytes a prefill GEMM launch must move at least: every expert
     matrix with at least one routed row (and the shared expert's) read once,
-    the tokens read once, h written and read once (the down GEMM's input),
-    the routed outputs (bf16) and the shared expert's rows of y (fp32)
-    written once.  W4A8 form: h as int8 codes + a scale per 32, and x read
-    as int8 codes + scales by the GEMM after q8(x)."""
+    the bf16 tokens read once and the fp32 y written once; scratch (h, the
+    routed outputs, q8 codes) and tile padding are not counted.  The same
+    figure serves both forms."""
     mat = cfg.I * (cfg.H // 32) * 18
     S = 1 if cfg.shared else 0
     live = int((counts > 0).sum()) + S
-    rows = T * cfg.k + T * S
-    w = 3 * live * mat
-    if form == "bf16":
-        xb = T * cfg.H * 2
-        hb = 2 * rows * cfg.I * 2
-    else:
-        xb = T * cfg.H + T * (cfg.H // 32) * 4
-        hb = 2 * (rows * cfg.I + rows * (cfg.I // 32) * 4)
-    ob = T * cfg.k * cfg.H * 2 + S * T * cfg.H * 4
-    return w + xb + hb + ob
+    return 3 * live * mat + T * cfg.H * 2 + T * cfg.H * 4
 
 
 def bench_prefill_w4a8(args, torch, mq, pre):
@@ -873,7 +863,7 @@ def main():
     if w8 is not None:
         t8 = w8["t_gu"] + w8["t_dn"]
         ops8 = pre["fl_gu"] + pre["fl_dn"]
-        alg8 = prefill_algorithmic_bytes(cfg, cfg.T, pre["counts"], form="w4a8")
+        alg8 = prefill_algorithmic_bytes(cfg, cfg.T, pre["counts"])
         tr8 = _traffic("w4a8_prefill")
         out["prefill_w4a8"] = {
             "workload": "the same 2048-token prefill step in the W4A8 form: moe_q4_route + "

@@ -21,7 +21,9 @@ struct Tile {
 // shared expert's ceil(T / FMAXR) tiles come first (its dense M = T tiles
 // are the largest units and their down work the longest chain), then
 // expert e owns ceil(c_e / FMAXR) consecutive tile indices, experts in order.
-template <int FMAXR>
+// BAL = false: greedy tiles instead, FMAXR rows each but the segment's last
+// (fewest 32-row groups per expert; for kernels that skip idle 32-row groups).
+template <int FMAXR, bool BAL = true>
 __device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offsets, int E, int T,
                                               int k, int has_shared, int mt) {
   const int lane = threadIdx.x % 64;
@@ -64,7 +66,7 @@ __device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offset
   }
   const int nt = (c + FMAXR - 1) / FMAXR;
   if (q < 0 || q >= nt) return t;
-  const int tr = 32 * (((c + nt - 1) / nt + 31) / 32);   // rows per tile, <= FMAXR
+  const int tr = BAL ? 32 * (((c + nt - 1) / nt + 31) / 32) : FMAXR;   // rows per tile, <= FMAXR
   t.m0 = q * tr;
   t.rows = min(tr, c - t.m0);
   if (t.rows <= 0) return t;

@@ -28,7 +28,8 @@
 // Kernels (all on the caller's stream):
 //   q8x   x bf16 [T][H] -> codes [T][H] int8, scales [T][H/32] fp32
 //   gate/up   unit = (tile of <= 128 rows of one expert segment, 32 columns
-//         of I); wave w: rows 32w .. 32w+31, gate and up of the 32 columns;
+//         of I); wave w of 4: rows 32w .. 32w+31, gate and up of the 32
+//         columns (a wave past the tile's rows idles);
 //         h = silu(g) * u and its q8 (the unit holds whole 32-groups of I)
 //   down  unit = (tile, 64 columns of H); wave w: rows 32w .. +31, two
 //         groups of 32 columns; routed rows -> bf16 expert outputs in segment
@@ -45,7 +46,9 @@ namespace moeq4 {
 typedef int w8v4 __attribute__((ext_vector_type(4)));
 typedef int w8v16 __attribute__((ext_vector_type(16)));
 
-constexpr int kW8Rows = 128;           // rows per tile (4 waves x 32)
+constexpr int kW8Rows = 128;           // rows per tile (4 waves x 32), greedy tiles
+constexpr int kW8Waves = kW8Rows / 32;
+constexpr int kW8Threads = 64 * kW8Waves;
 constexpr int kW8DnCols = 64;          // columns of H per down unit
 
 // ---------------------------------------------------------------- q8 of x
@@ -110,32 +113,42 @@ __device__ __forceinline__ void w8_accumulate(float (&acc)[16], const w8v16& dot
 }
 
 // ---------------------------------------------------------------- gate/up
-// LDS: activation scales of the tile's rows [nb][128], then the wave's q8(h)
-// codes [4][32][32] for the coalesced store.
+// LDS: activation scales of the tile's rows [nb][kW8Rows], the wave's q8(h)
+// codes [waves][32][32] for the coalesced store, the tile rows' tokens.
 template <bool DOTS>
-__global__ void __launch_bounds__(256, 2) w8_gateup_kernel(W4A8PrefillArgs a, int32_t* __restrict__ gate_dots) {
+__global__ void __launch_bounds__(kW8Threads, 2) w8_gateup_kernel(W4A8PrefillArgs a, int32_t* __restrict__ gate_dots) {
   extern __shared__ __align__(16) uint8_t dyn[];
   const int H = a.H, I = a.I, nb = H / BLK, nsteps = H / 64, ncb = I / 32;
-  float* da_l = reinterpret_cast<float*>(dyn);                              // [nb][128]
-  uint8_t* qo_l = dyn + (size_t)nb * kW8Rows * 4;                           // [4][32][32]
+  float* da_l = reinterpret_cast<float*>(dyn);                              // [nb][kW8Rows]
+  uint8_t* qo_l = dyn + (size_t)nb * kW8Rows * 4;                           // [waves][32][32]
+  int* tok_l = reinterpret_cast<int*>(qo_l + 1024 * kW8Waves);              // [kW8Rows]
   const int b = blockIdx.x, qq = b / 8;
   const int tile = 8 * (qq / ncb) + b % 8, cb = qq % ncb;
-  const Tile t = find_tile_bal<kW8Rows>(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
+  const Tile t = find_tile_bal<kW8Rows, false>(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
   if (!t.valid) return;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   // token of each tile row (rows past the tile repeat its first row)
-  auto token = [&](int row) {
-    const int r = row < t.rows ? row : 0;
-    return t.expert >= 0 ? min(max(a.perm[t.pos0 + r] / a.k, 0), a.T - 1) : t.m0 + r;
-  };
-  for (int i = tid; i < nb * kW8Rows; i += 256) {        // da_l[bb][row]
-    const int row = i % kW8Rows, bb = i / kW8Rows;
-    da_l[i] = a.dx[(size_t)token(row) * nb + bb];
+  if (tid < kW8Rows) {
+    const int r = tid < t.rows ? tid : 0;
+    tok_l[tid] = t.expert >= 0 ? min(max(a.perm[t.pos0 + r] / a.k, 0), a.T - 1) : t.m0 + r;
+  }
+  __syncthreads();
+  {                                                          // da_l[bb][row], 4 independent loads per round
+    const int row = tid % kW8Rows, b0 = tid / kW8Rows;       // (2 x kW8Rows threads: 2 blocks per round)
+    const float* src = a.dx + (size_t)tok_l[row] * nb;
+    for (int bb = b0; bb < nb; bb += 8) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) v[u] = src[min(bb + 2 * u, nb - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        if (bb + 2 * u < nb) da_l[(bb + 2 * u) * kW8Rows + row] = v[u];
+    }
   }
   const int n = lane % 32, h = lane / 32, shl = 4 * (1 - h);
   const int row_a = 32 * wave + n;                          // the lane's A row (token)
-  const int8_t* arow = a.qx + (size_t)token(row_a) * H + 16 * h;
+  const int8_t* arow = a.qx + (size_t)tok_l[row_a] * H + 16 * h;
   const size_t gbytes = (size_t)nsteps * 1152;              // one 32-row group of a matrix
   const uint8_t* gw = (t.expert >= 0 ? a.t_gate + ((size_t)t.expert * ncb + cb) * gbytes : a.ts_gate + cb * gbytes);
   const uint8_t* uw = (t.expert >= 0 ? a.t_up + ((size_t)t.expert * ncb + cb) * gbytes : a.ts_up + cb * gbytes);
@@ -144,7 +157,10 @@ __global__ void __launch_bounds__(256, 2) w8_gateup_kernel(W4A8PrefillArgs a, in
 #pragma unroll
   for (int r = 0; r < 16; r++) accg[r] = accu[r] = 0.0f;
   const w8v16 zero = {};
-  const float* da_w = da_l + 32 * wave + 4 * h;             // + bb * 128 + 8 q
+  const float* da_w = da_l + 32 * wave + 4 * h;             // + bb * kW8Rows + 8 q
+  // a wave whose 32 rows all lie past the tile computes nothing (it still
+  // takes part in the barriers)
+  const int nsteps_w = __builtin_amdgcn_readfirstlane((32 * wave < t.rows) ? nsteps : 0);
   // operands of a step (blocks 2s, 2s+1), one step ahead in registers
   auto load = [&](int s, uint4 (&A)[2], uint4 (&G)[2], uint4 (&U)[2], uint32_t (&sg)[2], uint32_t (&su)[2]) {
     const uint8_t* gp = gw + (size_t)s * 1152;
@@ -158,13 +174,8 @@ __global__ void __launch_bounds__(256, 2) w8_gateup_kernel(W4A8PrefillArgs a, in
       su[j] = *reinterpret_cast<const uint16_t*>(up + 1024 + 2 * (32 * j + n));
     }
   };
-  uint4 A[2], G[2], U[2];
-  uint32_t sg[2], su[2];
-  load(0, A, G, U, sg, su);
-  for (int s = 0; s < nsteps; s++) {
-    uint4 An[2], Gn[2], Un[2];
-    uint32_t sgn[2], sun[2];
-    load(min(s + 1, nsteps - 1), An, Gn, Un, sgn, sun);     // (the last step re-reads its own, unused)
+  auto compute = [&](int s, const uint4 (&A)[2], const uint4 (&G)[2], const uint4 (&U)[2], const uint32_t (&sg)[2],
+                     const uint32_t (&su)[2]) {
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int bb = 2 * s + j;
@@ -186,6 +197,17 @@ __global__ void __launch_bounds__(256, 2) w8_gateup_kernel(W4A8PrefillArgs a, in
         }
       }
     }
+  };
+  // the next step's operands are loaded while this step computes (the last
+  // step re-reads its own, unused)
+  uint4 A[2], G[2], U[2];
+  uint32_t sg[2], su[2];
+  load(0, A, G, U, sg, su);
+  for (int s = 0; s < nsteps_w; s++) {
+    uint4 An[2], Gn[2], Un[2];
+    uint32_t sgn[2], sun[2];
+    load(min(s + 1, nsteps - 1), An, Gn, Un, sgn, sun);
+    compute(s, A, G, U, sg, su);
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       A[j] = An[j]; G[j] = Gn[j]; U[j] = Un[j]; sg[j] = sgn[j]; su[j] = sun[j];
@@ -219,20 +241,28 @@ __global__ void __launch_bounds__(256, 2) w8_gateup_kernel(W4A8PrefillArgs a, in
 }
 
 // ---------------------------------------------------------------- down
-// LDS: q8(h) scales of the tile's rows [I/32][128].
-__global__ void __launch_bounds__(256, 2) w8_down_kernel(W4A8PrefillArgs a) {
+// LDS: q8(h) scales of the tile's rows [I/32][kW8Rows].
+__global__ void __launch_bounds__(kW8Threads, 2) w8_down_kernel(W4A8PrefillArgs a) {
   extern __shared__ __align__(16) uint8_t dyn[];
   const int H = a.H, I = a.I, nb = I / BLK, nsteps = I / 64, ncb = H / kW8DnCols;
-  float* da_l = reinterpret_cast<float*>(dyn);                              // [nb][128]
+  float* da_l = reinterpret_cast<float*>(dyn);                              // [nb][kW8Rows]
   const int b = blockIdx.x, qq = b / 8;
   const int tile = 8 * (qq / ncb) + b % 8, cb = qq % ncb;
-  const Tile t = find_tile_bal<kW8Rows>(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
+  const Tile t = find_tile_bal<kW8Rows, false>(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
   if (!t.valid) return;
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  for (int i = tid; i < nb * kW8Rows; i += 256) {
-    const int row = i % kW8Rows, bb = i / kW8Rows;
-    da_l[i] = a.dh[(size_t)(t.pos0 + (row < t.rows ? row : 0)) * nb + bb];
+  {                                                          // da_l[bb][row], 4 independent loads per round
+    const int row = tid % kW8Rows, b0 = tid / kW8Rows;
+    const float* src = a.dh + (size_t)(t.pos0 + (row < t.rows ? row : 0)) * nb;
+    for (int bb = b0; bb < nb; bb += 8) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) v[u] = src[min(bb + 2 * u, nb - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        if (bb + 2 * u < nb) da_l[(bb + 2 * u) * kW8Rows + row] = v[u];
+    }
   }
   const int n = lane % 32, h = lane / 32, shl = 4 * (1 - h);
   const int row_a = 32 * wave + n;
@@ -247,6 +277,8 @@ __global__ void __launch_bounds__(256, 2) w8_down_kernel(W4A8PrefillArgs a) {
   for (int r = 0; r < 16; r++) acc0[r] = acc1[r] = 0.0f;
   const w8v16 zero = {};
   const float* da_w = da_l + 32 * wave + 4 * h;
+  // (waves past the tile compute nothing)
+  const int nsteps_w = __builtin_amdgcn_readfirstlane((32 * wave < t.rows) ? nsteps : 0);
   auto load = [&](int s, uint4 (&A)[2], uint4 (&B0)[2], uint4 (&B1)[2], uint32_t (&s0)[2], uint32_t (&s1)[2]) {
     const uint8_t* p0 = w0 + (size_t)s * 1152;
     const uint8_t* p1 = w1 + (size_t)s * 1152;
@@ -259,13 +291,8 @@ __global__ void __launch_bounds__(256, 2) w8_down_kernel(W4A8PrefillArgs a) {
       s1[j] = *reinterpret_cast<const uint16_t*>(p1 + 1024 + 2 * (32 * j + n));
     }
   };
-  uint4 A[2], B0[2], B1[2];
-  uint32_t s0[2], s1[2];
-  load(0, A, B0, B1, s0, s1);
-  for (int s = 0; s < nsteps; s++) {
-    uint4 An[2], B0n[2], B1n[2];
-    uint32_t s0n[2], s1n[2];
-    load(min(s + 1, nsteps - 1), An, B0n, B1n, s0n, s1n);
+  auto compute = [&](int s, const uint4 (&A)[2], const uint4 (&B0)[2], const uint4 (&B1)[2], const uint32_t (&s0)[2],
+                     const uint32_t (&s1)[2]) {
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int bb = 2 * s + j;
@@ -278,6 +305,15 @@ __global__ void __launch_bounds__(256, 2) w8_down_kernel(W4A8PrefillArgs a) {
       w8_accumulate(acc0, d0, f16_bits_to_f32(s0[j]) * 0.0625f, da4);
       w8_accumulate(acc1, d1, f16_bits_to_f32(s1[j]) * 0.0625f, da4);
     }
+  };
+  uint4 A[2], B0[2], B1[2];
+  uint32_t s0[2], s1[2];
+  load(0, A, B0, B1, s0, s1);
+  for (int s = 0; s < nsteps_w; s++) {
+    uint4 An[2], B0n[2], B1n[2];
+    uint32_t s0n[2], s1n[2];
+    load(min(s + 1, nsteps - 1), An, B0n, B1n, s0n, s1n);
+    compute(s, A, B0, B1, s0, s1);
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       A[j] = An[j]; B0[j] = B0n[j]; B1[j] = B1n[j]; s0[j] = s0n[j]; s1[j] = s1n[j];
@@ -300,6 +336,7 @@ __global__ void __launch_bounds__(256, 2) w8_down_kernel(W4A8PrefillArgs a) {
 
 // ---------------------------------------------------------------- launch
 int64_t w4a8_prefill_tile_bound(int64_t T, int k, int E, int has_shared) {
+  // sum over experts of ceil(c_e / kW8Rows) <= T k / kW8Rows + E
   return T * k / kW8Rows + E + (has_shared ? (T + kW8Rows - 1) / kW8Rows : 0);
 }
 
@@ -313,17 +350,17 @@ hipError_t launch_prefill_w4a8(const W4A8PrefillArgs& a, int32_t* gate_dots, int
                        a.qx, a.dx);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t lds_gu = (size_t)(a.H / BLK) * kW8Rows * 4 + 4 * 1024;
+    const size_t lds_gu = (size_t)(a.H / BLK) * kW8Rows * 4 + 1024 * kW8Waves + kW8Rows * 4;
     if (gate_dots)
-      hipLaunchKernelGGL(w8_gateup_kernel<true>, dim3(groups * 8 * ncb_gu), dim3(256), lds_gu, stream, a, gate_dots);
+      hipLaunchKernelGGL(w8_gateup_kernel<true>, dim3(groups * 8 * ncb_gu), dim3(kW8Threads), lds_gu, stream, a, gate_dots);
     else
-      hipLaunchKernelGGL(w8_gateup_kernel<false>, dim3(groups * 8 * ncb_gu), dim3(256), lds_gu, stream, a, gate_dots);
+      hipLaunchKernelGGL(w8_gateup_kernel<false>, dim3(groups * 8 * ncb_gu), dim3(kW8Threads), lds_gu, stream, a, gate_dots);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (stages & 2) {
     const size_t lds_dn = (size_t)(a.I / BLK) * kW8Rows * 4;
-    hipLaunchKernelGGL(w8_down_kernel, dim3(groups * 8 * ncb_dn), dim3(256), lds_dn, stream, a);
+    hipLaunchKernelGGL(w8_down_kernel, dim3(groups * 8 * ncb_dn), dim3(kW8Threads), lds_dn, stream, a);
     err = hipGetLastError();
   }
   return err;
