@@ -400,6 +400,11 @@ constexpr int G2K = 64;                 // K per step
 
 struct G2Smem {
   uint16_t a[2][G2R * G2K];
+  // the fused launch's wait result, read by every wave after a barrier (kept
+  // in the tile's LDS object: a second __shared__ object made the compiler
+  // wait for every load in flight, the next step's included, before each
+  // fragment read of the step loop)
+  int gave_up;
 };
 
 __device__ __forceinline__ int g2_slot(int cc, int m) { return cc ^ (m & 7) ^ ((m >> 3) & 1); }
@@ -648,7 +653,6 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(int32_t* __restrict__ p,
 __global__ void __launch_bounds__(256, 2) gemm_ffn_kernel(PrefillArgs a, int ncb_gu, int ncb_dn, int n_gu,
                                                           int n_tiles, int need, int spin_max) {
   __shared__ __attribute__((aligned(16))) G2Smem sm;
-  __shared__ int gave_up;
   const bool gu = (int)blockIdx.x < n_gu;
   const int b = gu ? (int)blockIdx.x : (int)blockIdx.x - n_gu;   // n_gu % 8 == 0: same XCD mapping
   const int ncb = gu ? ncb_gu : ncb_dn;
@@ -680,11 +684,11 @@ __global__ void __launch_bounds__(256, 2) gemm_ffn_kernel(PrefillArgs a, int ncb
       n = __hip_atomic_load(a.tile_done + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    gave_up = n < need;
+    sm.gave_up = n < need;
     if (n < need) __hip_atomic_fetch_add(a.tile_done + n_tiles, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  if (gave_up) return;                    // h of this tile may be incomplete: store nothing
+  if (sm.gave_up) return;                 // h of this tile may be incomplete: store nothing
   switch (S) {
     case 1: g2_tile<1, false>(a, t, cb, sm); break;
     case 2: g2_tile<2, false>(a, t, cb, sm); break;
