@@ -166,10 +166,7 @@ def copy_probe(torch):
 
 
 def clone_layer(L, tiles=True):
-    import bit_quantized_moe_q4_amd as mq
-    c = lambda t: None if t is None else t.clone()  # noqa: E731
-    return mq.MoELayer(c(L.w_router), c(L.gate), c(L.up), c(L.down), L.top_k, c(L.router_bias),
-                       c(L.s_gate), c(L.s_up), c(L.s_down), tiles=tiles, wfmt=L.wfmt)
+    return L.clone()
 
 
 def setup_prefill(torch, mq, moe_synth, device_layer):

@@ -126,19 +126,24 @@ class MoELayer:
     w_router fp32 [H, E]; gate/up uint8 [E, I, H/32*18]; down uint8
     [E, H, I/32*18]; optional router_bias fp32 [E] and shared expert
     s_gate/s_up uint8 [I, H/32*18], s_down uint8 [H, I/32*18].
-    With `tiles` (the default) and H, I multiples of 64 the layer also keeps
-    the matrices in grouped-GEMM tile order (q4_tile), which moe_q4_prefill's
-    fused GEMM and the one-token decode kernels read; that doubles the
-    resident weight bytes.  wfmt="q8": the matrices are Q8_0 blocks (34
-    bytes per 32 weights; routing and decode only), tiles by q8w_tile.
+    With `tiles` (the default) and H, I multiples of 64 the matrices are
+    regrouped into the tile order (q4_tile), which every kernel reads; the
+    row-major copies are then released (one resident copy of the weights)
+    unless `rowmajor` is True or the library does not cover the shape
+    without them (moe_q4_check_layer); `rowmajor=False` makes that an error.
+    wfmt="q8": the matrices are Q8_0 blocks (34 bytes per 32 weights;
+    routing and decode only), tiles by q8w_tile.
     """
 
     def __init__(self, w_router, gate, up, down, top_k, router_bias=None,
-                 s_gate=None, s_up=None, s_down=None, tiles=True, stream=None, wfmt="q4"):
+                 s_gate=None, s_up=None, s_down=None, tiles=True, stream=None, wfmt="q4",
+                 rowmajor=None):
         for n, t in (("w_router", w_router), ("gate", gate), ("up", up), ("down", down),
                      ("router_bias", router_bias), ("s_gate", s_gate), ("s_up", s_up),
                      ("s_down", s_down)):
             _dev(t, n)
+        if wfmt not in ("q4", "q8"):
+            raise ValueError("wfmt must be 'q4' or 'q8'")
         self.w_router, self.router_bias = w_router, router_bias
         self.gate, self.up, self.down = gate, up, down
         self.s_gate, self.s_up, self.s_down = s_gate, s_up, s_down
@@ -146,35 +151,70 @@ class MoELayer:
         self.inter = int(gate.shape[1])
         self.top_k = int(top_k)
         self.has_shared = s_gate is not None
-        st = _lib.Layer()
-        st.hidden, st.inter, st.n_experts, st.top_k = self.hidden, self.inter, self.n_experts, self.top_k
-        st.has_shared = 1 if self.has_shared else 0
-        st.w_router, st.router_bias = _p(w_router), _p(router_bias)
-        st.w_gate, st.w_up, st.w_down = _p(gate), _p(up), _p(down)
-        st.s_gate, st.s_up, st.s_down = _p(s_gate), _p(s_up), _p(s_down)
-        if wfmt not in ("q4", "q8"):
-            raise ValueError("wfmt must be 'q4' or 'q8'")
         self.wfmt = wfmt
-        st.weight_format = _lib.WEIGHTS_Q8_0 if wfmt == "q8" else _lib.WEIGHTS_Q4_0
         self.tiles = None
         if tiles and self.hidden % 64 == 0 and self.inter % 64 == 0:
             tile = q8w_tile if wfmt == "q8" else q4_tile
             tl = lambda t: None if t is None else tile(t, stream=stream)  # noqa: E731
             self.tiles = dict(gate=tl(gate), up=tl(up), down=tl(down),
                               s_gate=tl(s_gate), s_up=tl(s_up), s_down=tl(s_down))
+        self._c = self._struct()
+        if self.tiles is not None and rowmajor is not True:
+            kept = (self.gate, self.up, self.down, self.s_gate, self.s_up, self.s_down)
+            self.gate = self.up = self.down = self.s_gate = self.s_up = self.s_down = None
+            st = self._struct()
+            if _lib.lib().moe_q4_check_layer(C.byref(st)) == _lib.MOE_Q4_OK:
+                self._c = st
+                # the tile kernels read the row-major copies on `stream`: the
+                # memory is reused only after them
+                s_ = stream if stream is not None else torch.cuda.current_stream()
+                for t in kept:
+                    if t is not None:
+                        t.record_stream(s_)
+            elif rowmajor is False:
+                raise RuntimeError("moe_q4_check_layer refused a layer without row-major matrices: %s"
+                                   % _lib.lib().moe_q4_last_error().decode(errors="replace"))
+            else:
+                self.gate, self.up, self.down, self.s_gate, self.s_up, self.s_down = kept
+
+    def _struct(self):
+        st = _lib.Layer()
+        st.hidden, st.inter, st.n_experts, st.top_k = self.hidden, self.inter, self.n_experts, self.top_k
+        st.has_shared = 1 if self.has_shared else 0
+        st.w_router, st.router_bias = _p(self.w_router), _p(self.router_bias)
+        st.w_gate, st.w_up, st.w_down = _p(self.gate), _p(self.up), _p(self.down)
+        st.s_gate, st.s_up, st.s_down = _p(self.s_gate), _p(self.s_up), _p(self.s_down)
+        st.weight_format = _lib.WEIGHTS_Q8_0 if self.wfmt == "q8" else _lib.WEIGHTS_Q4_0
+        if self.tiles is not None:
             T_ = self.tiles
             st.t_gate, st.t_up, st.t_down = _p(T_["gate"]), _p(T_["up"]), _p(T_["down"])
             st.ts_gate, st.ts_up, st.ts_down = _p(T_["s_gate"]), _p(T_["s_up"]), _p(T_["s_down"])
-        self._c = st
+        return st
 
     @classmethod
     def from_float(cls, w_router, gate, up, down, top_k, router_bias=None,
-                   s_gate=None, s_up=None, s_down=None, tiles=True, stream=None, wfmt="q4"):
+                   s_gate=None, s_up=None, s_down=None, tiles=True, stream=None, wfmt="q4", rowmajor=None):
         """Pack fp32 device weights with the library's q4_pack (or q8w_pack) kernel."""
         pack = q8w_pack if wfmt == "q8" else q4_pack
         pk = lambda t: None if t is None else pack(t, stream=stream)  # noqa: E731
         return cls(w_router, pk(gate), pk(up), pk(down), top_k, router_bias,
-                   pk(s_gate), pk(s_up), pk(s_down), tiles=tiles, stream=stream, wfmt=wfmt)
+                   pk(s_gate), pk(s_up), pk(s_down), tiles=tiles, stream=stream, wfmt=wfmt, rowmajor=rowmajor)
+
+    @property
+    def rowmajor(self) -> bool:
+        """Whether the layer holds the row-major matrices."""
+        return self.gate is not None
+
+    def clone(self) -> "MoELayer":
+        """A copy of the layer in new device memory (same layouts)."""
+        c = MoELayer.__new__(MoELayer)
+        c.__dict__.update(self.__dict__)
+        cl = lambda t: None if t is None else t.clone()  # noqa: E731
+        for n in ("w_router", "router_bias", "gate", "up", "down", "s_gate", "s_up", "s_down"):
+            setattr(c, n, cl(getattr(self, n)))
+        c.tiles = None if self.tiles is None else {n: cl(t) for n, t in self.tiles.items()}
+        c._c = c._struct()
+        return c
 
     def struct_ptr(self):
         return C.byref(self._c)

@@ -76,6 +76,7 @@ def _declare(lib):
         "moe_q4_prefill": (C.c_int, [P, P, I32, P, P, P, SZ, P]),
         "moe_q4_prefill_stage": (C.c_int, [P, P, I32, P, P, P, SZ, I32, P]),
         "moe_q4_prefill_status": (C.c_int, [P, I32, P, SZ, P, P]),
+        "moe_q4_check_layer": (C.c_int, [P]),
         "moe_q4_prefill_w4a8": (C.c_int, [P, P, I32, P, P, P, P, SZ, P]),
         "moe_q4_prefill_w4a8_stage": (C.c_int, [P, P, I32, P, P, P, P, SZ, I32, P]),
         "moe_q4_decode_workspace_bytes": (SZ, [P]),

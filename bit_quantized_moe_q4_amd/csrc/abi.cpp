@@ -54,10 +54,17 @@ int check_layer(const moe_q4_layer* L) {
     return fail(MOE_Q4_EINVAL, "top_k=%d must be in [1, min(n_experts, %d)]", L->top_k, kMaxTopK);
   if (L->has_shared != 0 && L->has_shared != 1)
     return fail(MOE_Q4_EINVAL, "has_shared=%d must be 0 or 1", L->has_shared);
-  if (!L->w_router || !L->w_gate || !L->w_up || !L->w_down)
-    return fail(MOE_Q4_EINVAL, "w_router, w_gate, w_up and w_down must be non-NULL");
-  if (L->has_shared && (!L->s_gate || !L->s_up || !L->s_down))
-    return fail(MOE_Q4_EINVAL, "has_shared=1 needs s_gate, s_up and s_down");
+  if (!L->w_router) return fail(MOE_Q4_EINVAL, "w_router must be non-NULL");
+  // the row-major matrices: all given, or (a tile-only layer) all NULL
+  const bool rm_any = L->w_gate || L->w_up || L->w_down || L->s_gate || L->s_up || L->s_down;
+  if (rm_any) {
+    if (!L->w_gate || !L->w_up || !L->w_down)
+      return fail(MOE_Q4_EINVAL, "w_gate, w_up and w_down are given together or not at all");
+    if (L->has_shared && (!L->s_gate || !L->s_up || !L->s_down))
+      return fail(MOE_Q4_EINVAL, "has_shared=1 needs s_gate, s_up and s_down");
+    if (!L->has_shared && (L->s_gate || L->s_up || L->s_down))
+      return fail(MOE_Q4_EINVAL, "s_gate, s_up and s_down are given only with has_shared=1");
+  }
   if (!aligned(L->w_router, 16) || !aligned(L->w_gate, 16) || !aligned(L->w_up, 16) ||
       !aligned(L->w_down, 16) || (L->router_bias && !aligned(L->router_bias, 4)))
     return fail(MOE_Q4_EINVAL, "layer pointers must be 16-byte aligned (router_bias 4-byte)");
@@ -80,8 +87,20 @@ int check_layer(const moe_q4_layer* L) {
         (L->has_shared && (!aligned(L->ts_gate, 16) || !aligned(L->ts_up, 16) || !aligned(L->ts_down, 16))))
       return fail(MOE_Q4_EINVAL, "tile-order matrices must be 16-byte aligned");
   }
+  if (!rm_any) {
+    // tile-only: every decode form must have its tile-order kernels for the
+    // shape (the one-launch step falls back to the three-launch kernels)
+    if (!any_t) return fail(MOE_Q4_EINVAL, "the layer needs its row-major matrices or their tile-order copies");
+    const moeq4::DecodeGeometry g =
+        moeq4::decode_geometry(L->hidden, L->inter, L->n_experts, L->top_k, L->has_shared);
+    if (g.gt_sp <= 0 || g.dt_sp <= 0)
+      return fail(MOE_Q4_EINVAL, "a layer without row-major matrices needs a shape the tile-order decode kernels "
+                                 "cover (H=%d I=%d E=%d k=%d)", L->hidden, L->inter, L->n_experts, L->top_k);
+  }
   return MOE_Q4_OK;
 }
+
+bool tile_only(const moe_q4_layer* L) { return !L->w_gate; }
 
 struct RouteWs {
   size_t partials, counts, rank, total;
@@ -407,6 +426,11 @@ int moe_q4_prefill_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int32_t 
       !routing->inv_perm)
     return fail(MOE_Q4_EINVAL, "moe_q4_prefill: NULL pointer");
   if (!aligned(x_bf16, 16) || !aligned(y, 16)) return fail(MOE_Q4_EINVAL, "moe_q4_prefill: x_bf16 and y must be 16-byte aligned");
+  // (the tile-order kernels address x through one 32-bit byte range; larger
+  // batches take the generic kernels, which read the row-major matrices)
+  if (tile_only(L) && (uint64_t)T * (uint64_t)L->hidden * 2u > 0xffffffffull)
+    return fail(MOE_Q4_EINVAL, "moe_q4_prefill: T=%d too large for a layer without row-major matrices "
+                               "(T * hidden * 2 must fit 32 bits)", T);
   const PrefillWs W = prefill_ws(L, T);
   rc = check_ws(ws, ws_bytes, W.total);
   if (rc) return rc;
@@ -521,6 +545,8 @@ int moe_q4_prefill_w4a8_stage(const moe_q4_layer* L, const uint16_t* x_bf16, int
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_prefill_w4a8/combine");
 }
 
+int moe_q4_check_layer(const moe_q4_layer* L) { return check_layer(L); }
+
 int moe_q4_prefill_status(const moe_q4_layer* L, int32_t T, const void* ws, size_t ws_bytes,
                           int32_t* failed_waits, hipStream_t stream) {
   int rc = check_layer(L);
@@ -602,6 +628,12 @@ int moe_q4_decode_batch(const moe_q4_layer* L, const float* x, int32_t M, float*
   a.s_gate = static_cast<const uint8_t*>(L->s_gate);
   a.s_up = static_cast<const uint8_t*>(L->s_up);
   a.s_down = static_cast<const uint8_t*>(L->s_down);
+  a.t_gate = static_cast<const uint8_t*>(L->t_gate);
+  a.t_up = static_cast<const uint8_t*>(L->t_up);
+  a.t_down = static_cast<const uint8_t*>(L->t_down);
+  a.ts_gate = static_cast<const uint8_t*>(L->ts_gate);
+  a.ts_up = static_cast<const uint8_t*>(L->ts_up);
+  a.ts_down = static_cast<const uint8_t*>(L->ts_down);
   a.partials = at<float>(ws, W.partials);
   a.qx = at<int8_t>(ws, W.qx);
   a.dx = at<float>(ws, W.dx);

@@ -30,6 +30,7 @@
 #include "launch.hpp"
 #include "w4a8.hpp"
 #include "decode_common.hpp"
+#include "decode_tile.hpp"
 
 namespace moeq4 {
 
@@ -147,12 +148,63 @@ __device__ __forceinline__ int expert_pairs(const DecodeBatchArgs& a, int e, int
 }
 
 // ---------------------------------------------------------------- gate/up
+// ---------------------------------------------------------------- tile order
+// A lane's blocks b0 .. b0+BPL-1 of row n (0..31) of a 32-row group in tile
+// order (`grp` = the group's first piece): block b is half b%2 of piece b/2,
+// the lane's codes at code * (n + 32 (b%2)), its scale at scale + 2 (n + 32
+// (b%2)).  Blocks >= nb are +0 leaves; the leaves and their pairwise tree are
+// those of wxa8_regs, so a row's value is the same bit for bit.
+template <int BPL, int FMT>
+struct TileSpan {
+  TileCodes<FMT> c[BPL];
+  uint32_t sc[BPL];
+};
+
+template <int BPL, int FMT, bool SCALES = true>
+__device__ __forceinline__ void tile_span_load(TileSpan<BPL, FMT>& t, const uint8_t* grp, int n, int nb, int b0) {
+  using TF = TileFmt<FMT>;
+#pragma unroll
+  for (int j = 0; j < BPL; j++) {
+    const int b = min(b0 + j, nb - 1);    // (loads past the row re-read its last block)
+    const uint8_t* pc = grp + (size_t)(b >> 1) * TF::piece;
+    const int l = n + 32 * (b & 1);
+    t.c[j] = tile_codes<FMT>(pc + TF::code * l);
+    if (SCALES) t.sc[j] = *reinterpret_cast<const uint16_t*>(pc + TF::scale + 2 * l);
+  }
+}
+
+// WHOLE: nb % BPL == 0, so a lane's span lies wholly inside or wholly past
+// the row and no block needs its own test.
+template <int BPL, int FMT, bool WHOLE, typename ActFn>
+__device__ __forceinline__ float tile_span_value(const TileSpan<BPL, FMT>& t, int nb, int b0, ActFn act) {
+  if (b0 >= nb) return 0.0f;              // a lane of padding leaves only
+  float p[BPL];
+#pragma unroll
+  for (int j = 0; j < BPL; j++) {
+    const int b = b0 + j;
+    p[j] = 0.0f;
+    if (WHOLE || b < nb) {
+      const ActBlock A = act(b);
+      const int32_t dot = tile_dot<FMT>(t.c[j], A.a, A.s);
+      const float sd = f16_bits_to_f32(t.sc[j]) * A.d;
+      p[j] = sd * (float)dot;
+    }
+  }
+  return reg_tree<BPL>(p);
+}
+
 constexpr int DBG_ROWS = 32;
 
 // tb: tokens whose codes fit the block's LDS at once; the expert's tokens are
 // taken tb at a time.
-template <int BPL, bool FAST, int FMT>
-__global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, int lpr, int tb) {
+// TILED: the weights are read from the tile-order copies (FAST then says
+// that nb % BPL == 0; the lane's span is held in registers when BPL <= 8,
+// else read per token from the caches).
+// sc_off (tile order, BPL <= 8): byte offset in LDS of a copy of the scale
+// sections of the block's two 32-row groups, staged by 16-byte loads (a
+// lane's scale loads would each touch a cache line for 2 bytes); 0: none.
+template <int BPL, bool FAST, int FMT, bool TILED>
+__global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, int lpr, int tb, int sc_off) {
   extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ int pairs_l[kDecodeBatchMax];
   __shared__ int n_l;
@@ -174,14 +226,49 @@ __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, 
   const size_t rb = (size_t)nbh * QB;
   const uint8_t* base = shared ? (is_up ? a.s_up : a.s_gate) + (size_t)i * rb
                                : (is_up ? a.w_up : a.w_gate) + ((size_t)e * I + i) * rb;
-  constexpr int NV = FAST ? QB * BPL / 16 : 1;
+  constexpr bool REGS = FAST && !TILED;
+  constexpr int NV = REGS ? QB * BPL / 16 : 1;
   uint32_t D[4 * NV + 1] = {};
-  if (FAST && lr * BPL < nbh) {
+  if (REGS && lr * BPL < nbh) {
     const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * QB);
 #pragma unroll
     for (int v = 0; v < NV; v++) {
       const uint4 q = src[v];
       D[4 * v] = q.x; D[4 * v + 1] = q.y; D[4 * v + 2] = q.z; D[4 * v + 3] = q.w;
+    }
+  }
+  // tile order: the row's 32-row group (matrix [E][I][H], groups of 32 rows)
+  constexpr bool TREGS = TILED && BPL <= 8;
+  const size_t gbytes = (size_t)(nbh / 2) * TileFmt<FMT>::piece;
+  const uint8_t* grp = nullptr;
+  if (TILED)
+    grp = shared ? (is_up ? a.ts_up : a.ts_gate) + (size_t)(i / 32) * gbytes
+                 : (is_up ? a.t_up : a.t_gate) + ((size_t)e * (I / 32) + i / 32) * gbytes;
+  TileSpan<(TILED ? BPL : 1), FMT> ts;
+  if constexpr (TREGS) {
+    using TF = TileFmt<FMT>;
+    if (sc_off) {                         // (uniform: a kernel argument)
+      uint8_t* sct = dyn + sc_off;         // [2][nbh / 2 pieces][64 scales]
+      const int nsec = nbh / 2;
+      const size_t g0 = shared ? (size_t)(i0 / 32) * gbytes : ((size_t)e * (I / 32) + i0 / 32) * gbytes;
+      const uint8_t* gg = (shared ? a.ts_gate : a.t_gate) + g0;
+      const uint8_t* gu = (shared ? a.ts_up : a.t_up) + g0;
+      for (int idx = tid; idx < 2 * nsec * 8; idx += blockDim.x) {
+        const int m = idx / (nsec * 8), rem = idx % (nsec * 8), sp = rem / 8, c = rem % 8;
+        const uint8_t* src = (m ? gu : gg) + (size_t)sp * TF::piece + TF::scale + 16 * c;
+        *reinterpret_cast<uint4*>(sct + ((size_t)m * nsec + sp) * 128 + 16 * c) =
+            *reinterpret_cast<const uint4*>(src);
+      }
+      tile_span_load<BPL, FMT, false>(ts, grp, i % 32, nbh, lr * BPL);
+      __syncthreads();
+      const uint16_t* sc16 = reinterpret_cast<const uint16_t*>(sct) + (size_t)(is_up ? nsec : 0) * 64;
+#pragma unroll
+      for (int j = 0; j < BPL; j++) {
+        const int b = min(lr * BPL + j, nbh - 1);
+        ts.sc[j] = sc16[(b >> 1) * 64 + (i % 32) + 32 * (b & 1)];
+      }
+    } else {
+      tile_span_load<BPL, FMT>(ts, grp, i % 32, nbh, lr * BPL);
     }
   }
   for (int u0 = 0; u0 < n; u0 += tb) {
@@ -209,8 +296,19 @@ __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, 
         return A;
       };
       float v;
-      if constexpr (FAST) v = wxa8_regs<BPL, FMT>(D, nbh, lr * BPL, act);
-      else v = wxa8_lane<BPL, false, FMT>(base, nbh, lr * BPL, act, nullptr);
+      if constexpr (TILED) {
+        if constexpr (TREGS) {
+          v = tile_span_value<BPL, FMT, FAST>(ts, nbh, lr * BPL, act);
+        } else {
+          TileSpan<BPL, FMT> tu;
+          tile_span_load<BPL, FMT>(tu, grp, i % 32, nbh, lr * BPL);
+          v = tile_span_value<BPL, FMT, FAST>(tu, nbh, lr * BPL, act);
+        }
+      } else if constexpr (FAST) {
+        v = wxa8_regs<BPL, FMT>(D, nbh, lr * BPL, act);
+      } else {
+        v = wxa8_lane<BPL, false, FMT>(base, nbh, lr * BPL, act, nullptr);
+      }
       v = wave_tree_sum(v, lpr);
       if (lr == 0) val[row * M + u0 + u] = v;
     }
@@ -240,7 +338,7 @@ __global__ void __launch_bounds__(1024) dbatch_gateup_kernel(DecodeBatchArgs a, 
 // ---------------------------------------------------------------- down
 // Block: `rows` (<= 128) output rows of one expert, lpr lanes per row, the
 // rows' weights in registers over the expert's pairs; o[pair][r] fp32.
-template <int BPL, bool FAST, int FMT>
+template <int BPL, bool FAST, int FMT, bool TILED>
 __global__ void __launch_bounds__(1024) dbatch_down_kernel(DecodeBatchArgs a, int lpr, int tb, int rows) {
   extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ int pairs_l[kDecodeBatchMax];
@@ -261,9 +359,10 @@ __global__ void __launch_bounds__(1024) dbatch_down_kernel(DecodeBatchArgs a, in
   const size_t rb = (size_t)nbi * QB;
   const uint8_t* base = shared ? a.s_down + (size_t)min(r, H - 1) * rb
                                : a.w_down + ((size_t)e * H + min(r, H - 1)) * rb;
-  constexpr int NV = FAST ? QB * BPL / 16 : 1;
+  constexpr bool REGS = FAST && !TILED;
+  constexpr int NV = REGS ? QB * BPL / 16 : 1;
   uint32_t D[4 * NV + 1] = {};
-  if (FAST && live && lr * BPL < nbi) {
+  if (REGS && live && lr * BPL < nbi) {
     const uint4* src = reinterpret_cast<const uint4*>(base + (size_t)lr * BPL * QB);
 #pragma unroll
     for (int v = 0; v < NV; v++) {
@@ -271,6 +370,15 @@ __global__ void __launch_bounds__(1024) dbatch_down_kernel(DecodeBatchArgs a, in
       D[4 * v] = q.x; D[4 * v + 1] = q.y; D[4 * v + 2] = q.z; D[4 * v + 3] = q.w;
     }
   }
+  // tile order: matrix [E][H][I], groups of 32 output rows
+  constexpr bool TREGS = TILED && BPL <= 8;
+  const int rr = min(r, H - 1);
+  const size_t gbytes = (size_t)(nbi / 2) * TileFmt<FMT>::piece;
+  const uint8_t* grp = nullptr;
+  if (TILED)
+    grp = shared ? a.ts_down + (size_t)(rr / 32) * gbytes : a.t_down + ((size_t)e * (H / 32) + rr / 32) * gbytes;
+  TileSpan<(TILED ? BPL : 1), FMT> ts;
+  if (TREGS) tile_span_load<(TILED ? BPL : 1), FMT>(ts, grp, rr % 32, nbi, lr * BPL);
   for (int u0 = 0; u0 < n; u0 += tb) {
     const int nu = min(tb, n - u0);
     if (u0 > 0) __syncthreads();          // the previous chunk's activations are read
@@ -296,8 +404,19 @@ __global__ void __launch_bounds__(1024) dbatch_down_kernel(DecodeBatchArgs a, in
         return A;
       };
       float v;
-      if constexpr (FAST) v = wxa8_regs<BPL, FMT>(D, nbi, lr * BPL, act);
-      else v = wxa8_lane<BPL, false, FMT>(base, nbi, lr * BPL, act, nullptr);
+      if constexpr (TILED) {
+        if constexpr (TREGS) {
+          v = tile_span_value<BPL, FMT, FAST>(ts, nbi, lr * BPL, act);
+        } else {
+          TileSpan<BPL, FMT> tu;
+          tile_span_load<BPL, FMT>(tu, grp, rr % 32, nbi, lr * BPL);
+          v = tile_span_value<BPL, FMT, FAST>(tu, nbi, lr * BPL, act);
+        }
+      } else if constexpr (FAST) {
+        v = wxa8_regs<BPL, FMT>(D, nbi, lr * BPL, act);
+      } else {
+        v = wxa8_lane<BPL, false, FMT>(base, nbi, lr * BPL, act, nullptr);
+      }
       v = wave_tree_sum(v, lpr);
       if (live && lr == 0) a.o[(size_t)pairs_l[u0 + u] * H + r] = v;
     }
@@ -364,12 +483,31 @@ template <int FMT>
 hipError_t launch_dbatch_experts(const DecodeBatchArgs& a, const DecodeBatchGeometry& g, int nexp,
                                  hipStream_t stream) {
   hipError_t err = hipSuccess;
+  // the tile-order copies when the layer carries them (H and I are then
+  // multiples of 64, so a lane's span covers whole pieces: bpl >= 2)
+  const bool tiled = a.t_gate && a.t_up && a.t_down && (!a.has_shared || (a.ts_gate && a.ts_up && a.ts_down)) &&
+                     g.gu_bpl >= 2 && g.dn_bpl >= 2;
   {
     dim3 grid(nexp * (a.I / DBG_ROWS));
     dim3 block(g.gu_threads);
+    // the tile-order kernel's LDS copy of the scale sections (2 groups x H/64
+    // pieces x 128 bytes) after the rest, when the lane spans are in registers
+    const int nbh = a.H / BLK;
+    const int sc_off = (tiled && g.gu_bpl <= 8 && nbh * 128 <= 16 * 1024) ? (int)((g.gu_lds + 15) / 16 * 16) : 0;
+    const size_t lds_t = sc_off ? (size_t)sc_off + (size_t)nbh * 128 : g.gu_lds;
 #define MOEQ4_GU(B, F) \
-  hipLaunchKernelGGL((dbatch_gateup_kernel<B, F, FMT>), grid, block, g.gu_lds, stream, a, g.gu_lpr, g.gu_tb)
-    if (g.gu_fast) {
+  hipLaunchKernelGGL((dbatch_gateup_kernel<B, F, FMT, false>), grid, block, g.gu_lds, stream, a, g.gu_lpr, g.gu_tb, 0)
+#define MOEQ4_GUT(B, W) \
+  hipLaunchKernelGGL((dbatch_gateup_kernel<B, W, FMT, true>), grid, block, lds_t, stream, a, g.gu_lpr, g.gu_tb, sc_off)
+#define MOEQ4_GUTW(B) \
+  if ((a.H / BLK) % B == 0) MOEQ4_GUT(B, true); else MOEQ4_GUT(B, false);
+    if (tiled) {
+      if (g.gu_bpl == 2) { MOEQ4_GUTW(2) }
+      else if (g.gu_bpl == 4) { MOEQ4_GUTW(4) }
+      else if (g.gu_bpl == 8) { MOEQ4_GUTW(8) }
+      else if (g.gu_bpl == 16) { MOEQ4_GUTW(16) }
+      else { MOEQ4_GUTW(32) }
+    } else if (g.gu_fast) {
       if (g.gu_bpl == 8) MOEQ4_GU(8, true);
       else if (g.gu_bpl == 16) MOEQ4_GU(16, true);
       else MOEQ4_GU(32, true);
@@ -381,6 +519,8 @@ hipError_t launch_dbatch_experts(const DecodeBatchArgs& a, const DecodeBatchGeom
       else if (g.gu_bpl == 16) MOEQ4_GU(16, false);
       else MOEQ4_GU(32, false);
     }
+#undef MOEQ4_GUTW
+#undef MOEQ4_GUT
 #undef MOEQ4_GU
     err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -389,8 +529,18 @@ hipError_t launch_dbatch_experts(const DecodeBatchArgs& a, const DecodeBatchGeom
     dim3 grid(nexp * ((a.H + g.dn_rows - 1) / g.dn_rows));
     dim3 block(g.dn_threads);
 #define MOEQ4_DN(B, F) \
-  hipLaunchKernelGGL((dbatch_down_kernel<B, F, FMT>), grid, block, g.dn_lds, stream, a, g.dn_lpr, g.dn_tb, g.dn_rows)
-    if (g.dn_fast) {
+  hipLaunchKernelGGL((dbatch_down_kernel<B, F, FMT, false>), grid, block, g.dn_lds, stream, a, g.dn_lpr, g.dn_tb, g.dn_rows)
+#define MOEQ4_DNT(B, W) \
+  hipLaunchKernelGGL((dbatch_down_kernel<B, W, FMT, true>), grid, block, g.dn_lds, stream, a, g.dn_lpr, g.dn_tb, g.dn_rows)
+#define MOEQ4_DNTW(B) \
+  if ((a.I / BLK) % B == 0) MOEQ4_DNT(B, true); else MOEQ4_DNT(B, false);
+    if (tiled) {
+      if (g.dn_bpl == 2) { MOEQ4_DNTW(2) }
+      else if (g.dn_bpl == 4) { MOEQ4_DNTW(4) }
+      else if (g.dn_bpl == 8) { MOEQ4_DNTW(8) }
+      else if (g.dn_bpl == 16) { MOEQ4_DNTW(16) }
+      else { MOEQ4_DNTW(32) }
+    } else if (g.dn_fast) {
       if (g.dn_bpl == 8) MOEQ4_DN(8, true);
       else if (g.dn_bpl == 16) MOEQ4_DN(16, true);
       else MOEQ4_DN(32, true);
@@ -402,6 +552,8 @@ hipError_t launch_dbatch_experts(const DecodeBatchArgs& a, const DecodeBatchGeom
       else if (g.dn_bpl == 16) MOEQ4_DN(16, false);
       else MOEQ4_DN(32, false);
     }
+#undef MOEQ4_DNTW
+#undef MOEQ4_DNT
 #undef MOEQ4_DN
     err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -204,6 +204,14 @@ struct DecodeBatchArgs {
   const uint8_t* s_gate;
   const uint8_t* s_up;
   const uint8_t* s_down;
+  // the same matrices in tile order (q4_tile / q8w_tile), or NULL: read in
+  // place of the row-major ones when given
+  const uint8_t* t_gate;
+  const uint8_t* t_up;
+  const uint8_t* t_down;
+  const uint8_t* ts_gate;
+  const uint8_t* ts_up;
+  const uint8_t* ts_down;
   // workspace
   float* partials;          // [M][H/32][E] router leaves
   int8_t* qx;               // [M][H]

@@ -22,10 +22,10 @@ def _pack_host(a: np.ndarray, device, wfmt="q4") -> torch.Tensor:
 
 
 def device_layer(cfg: moe_synth.Config, layer: int = 0, device="cuda", weights=None,
-                 threads: int = 16, tiles: bool = True, wfmt: str = "q4") -> MoELayer:
+                 threads: int = 16, tiles: bool = True, wfmt: str = "q4", rowmajor=None) -> MoELayer:
     """Pack layer `layer` of workload `cfg` on `device`.  `weights` (the dict
     from moe_synth.expert_weights) may be passed in to reuse a host copy;
-    `tiles` and `wfmt` as in MoELayer."""
+    `tiles`, `wfmt` and `rowmajor` as in MoELayer."""
     W = weights if weights is not None else moe_synth.expert_weights(cfg, layer, threads=threads)
     wr = torch.from_numpy(moe_synth.router(cfg, layer)).to(device)
     b = moe_synth.router_bias(cfg, layer)
@@ -33,7 +33,8 @@ def device_layer(cfg: moe_synth.Config, layer: int = 0, device="cuda", weights=N
     pk = {k: (None if W[k] is None else _pack_host(W[k], device, wfmt))
           for k in ("gate", "up", "down", "s_gate", "s_up", "s_down")}
     L = MoELayer(wr, pk["gate"], pk["up"], pk["down"], cfg.k, router_bias=bias,
-                 s_gate=pk["s_gate"], s_up=pk["s_up"], s_down=pk["s_down"], tiles=tiles, wfmt=wfmt)
+                 s_gate=pk["s_gate"], s_up=pk["s_up"], s_down=pk["s_down"], tiles=tiles, wfmt=wfmt,
+                 rowmajor=rowmajor)
     torch.cuda.synchronize(device)
     return L
 

@@ -12,14 +12,14 @@ import oracle
 from bit_quantized_moe_q4_amd.synth_layer import device_layer
 
 
-def both_layers(cfg, layer=0, threads=16, tiles=True, wfmt="q4"):
+def both_layers(cfg, layer=0, threads=16, tiles=True, wfmt="q4", rowmajor=True):
     W = moe_synth.expert_weights(cfg, layer, threads=threads)
     Wr = moe_synth.router(cfg, layer)
     bias = moe_synth.router_bias(cfg, layer)
     ol = oracle.PackedLayer.from_float(Wr, bias, W["gate"], W["up"], W["down"], W["s_gate"],
                                        W["s_up"], W["s_down"], k=cfg.k, threads=threads,
                                        wfmt=oracle.Q8_0 if wfmt == "q8" else oracle.Q4_0)
-    gl = device_layer(cfg, layer, weights=W, tiles=tiles, wfmt=wfmt)
+    gl = device_layer(cfg, layer, weights=W, tiles=tiles, wfmt=wfmt, rowmajor=rowmajor)
     return ol, gl
 
 

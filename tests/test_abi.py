@@ -39,7 +39,7 @@ def test_header_declares_the_api():
               "moe_q4_decode_stack", "moe_q4_decode_stack_workspace_bytes",
               "moe_q4_route_workspace_bytes", "moe_q4_prefill_workspace_bytes",
               "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm",
-              "moe_q4_prefill_status", "moe_q4_prefill_w4a8", "moe_q4_prefill_w4a8_stage",
+              "moe_q4_prefill_status", "moe_q4_prefill_w4a8", "moe_q4_prefill_w4a8_stage", "moe_q4_check_layer",
               "moe_q4_decode_status",
               "moe_q4_test_decode_wait_fail",
               "moe_q4_last_error"]:
@@ -299,6 +299,29 @@ def test_prefill_w4a8_checks(lib):
     for bad in (0, 8, 16, -1):
         assert lib.moe_q4_prefill_w4a8_stage(C.byref(L), x, 8, C.byref(R), y, None, ws, 1 << 30, bad, None) == -1
     assert lib.moe_q4_prefill_w4a8_stage(C.byref(L), None, 0, None, None, None, None, 0, 3, None) == 0
+
+
+def test_check_layer_tile_only(lib):
+    # one resident copy: the tile-order matrices without the row-major ones
+    L = _layer(hidden=2048, inter=512, E=128, k=8, shared=1)
+    assert lib.moe_q4_check_layer(C.byref(L)) == 0
+    L.t_gate = L.t_up = L.t_down = L.ts_gate = L.ts_up = L.ts_down = 0x20000
+    assert lib.moe_q4_check_layer(C.byref(L)) == 0                 # both copies
+    L.w_gate = L.w_up = L.w_down = L.s_gate = L.s_up = L.s_down = None
+    assert lib.moe_q4_check_layer(C.byref(L)) == 0                 # tile order only
+    L.w_gate = 0x10000                                             # a partial row-major set
+    assert lib.moe_q4_check_layer(C.byref(L)) == -1 and "together" in _err(lib)
+    L.w_gate = None
+    L.t_gate = L.t_up = L.t_down = L.ts_gate = L.ts_up = L.ts_down = None
+    assert lib.moe_q4_check_layer(C.byref(L)) == -1                # no matrices at all
+    # a shape the tile-order down kernel does not cover (I = 4096) keeps its rows
+    W = _layer(hidden=256, inter=4096, E=8, k=2)
+    W.w_gate = W.w_up = W.w_down = None
+    W.t_gate = W.t_up = W.t_down = 0x20000
+    assert lib.moe_q4_check_layer(C.byref(W)) == -1 and "cover" in _err(lib)
+    # and the entry points refuse such layers before any device access
+    assert lib.moe_q4_decode_workspace_bytes(C.byref(W)) == 0
+    assert lib.moe_q4_check_layer(None) == -1
 
 
 def test_decode_noalloc_checks(lib):

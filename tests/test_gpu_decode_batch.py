@@ -66,9 +66,21 @@ def decode_layers():
     return cfg, ol, gl
 
 
-@pytest.mark.parametrize("M", [1, 2, 5, 8, 17, 32])
-def test_decode_batch_full_layer(decode_layers, M):
+@pytest.fixture(scope="module")
+def decode_layers_tiled(decode_layers):
+    # the same packed matrices with their tile-order copies: the batched
+    # kernels then read the tile order
     cfg, ol, gl = decode_layers
+    return cfg, ol, mq.MoELayer(gl.w_router, gl.gate, gl.up, gl.down, gl.top_k, gl.router_bias,
+                                gl.s_gate, gl.s_up, gl.s_down, tiles=True)
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 17, 32])
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+def test_decode_batch_full_layer(decode_layers, decode_layers_tiled, M, layout):
+    cfg, ol, gl = decode_layers_tiled if layout == "tiled" else decode_layers
+    if layout == "tiled":
+        assert gl.tiles is not None
     X = _batch_tokens(cfg, M, 2000 + 40 * M)
     Y = _check_against_single(gl, X)
     worst = _check_against_oracle(ol, X, Y, sorted({0, M // 2, M - 1}))
@@ -99,11 +111,17 @@ def test_decode_batch_repeated_token(decode_layers):
     ("wide_hidden", 16384, 8, 64, 2, True, None, 32),
     # I = 8192: q8(h) staged a few pairs at a time; 16 lanes per down row
     ("wide_inter", 256, 16, 8192, 8, True, None, 32),
+    # H = I = 64: one tile piece per row (two blocks per lane span)
+    ("smallest_tiled", 64, 4, 64, 2, True, None, 5),
+    # H = 192, I = 320: 6 and 10 blocks per row, lane spans past the row
+    ("ragged_tiled", 192, 6, 320, 3, True, None, 11),
 ])
-def test_decode_batch_small(name, H, E, I, k, shared, bias, M):
-    say("decode batch", name, "M=%d" % M)
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+def test_decode_batch_small(name, H, E, I, k, shared, bias, M, layout):
+    say("decode batch", name, "M=%d" % M, layout)
     cfg = moe_synth.CONFIGS["tiny"].with_(name=name, H=H, E=E, I=I, k=k, shared=shared, bias=bias)
-    ol, gl = both_layers(cfg, tiles=False)
+    ol, gl = both_layers(cfg, tiles=(layout == "tiled"))
+    assert (gl.tiles is not None) == (layout == "tiled" and H % 64 == 0 and I % 64 == 0)
     X = _batch_tokens(cfg, M, 500)
     Y = _check_against_single(gl, X)
     _check_against_oracle(ol, X, Y, range(min(M, 4)))

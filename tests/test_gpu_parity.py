@@ -503,7 +503,7 @@ def test_decode_tied_logits():
     Wr[:, 1::2] = Wr[:, 0::2]
     ol = oracle.PackedLayer.from_float(Wr, None, W["gate"], W["up"], W["down"], W["s_gate"], W["s_up"],
                                        W["s_down"], k=cfg.k, threads=16)
-    g0 = device_layer(cfg, weights=W)
+    g0 = device_layer(cfg, weights=W, rowmajor=True)
     gl = mq.MoELayer(torch.from_numpy(Wr).cuda(), g0.gate, g0.up, g0.down, cfg.k, router_bias=None,
                      s_gate=g0.s_gate, s_up=g0.s_up, s_down=g0.s_down)
     _decode_steps(ol, gl, cfg, range(4))

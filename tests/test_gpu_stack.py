@@ -45,6 +45,12 @@ def test_stack_teacher_forced():
         layers.append(device_layer(cfg, layer=l, threads=16))
         if l % 5 == 4:
             say("packed layers 0..%d on the device" % l)
+    # one resident copy of the weights: 40 x (257 experts x 3 matrices of
+    # Q4_0 + the fp32 router) = 18.27 GB, the tile order only
+    assert all(not L.rowmajor for L in layers)
+    per = (cfg.E + 1) * 3 * cfg.I * (cfg.H // 32) * 18 + cfg.H * cfg.E * 4
+    assert sum(L.resident_bytes() for L in layers) == cfg.layers * per
+    say("resident: %.2f GB" % (cfg.layers * per / 1e9))
 
     # ---------------------------------------------------------------- prefill
     T = cfg.T
