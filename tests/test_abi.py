@@ -309,6 +309,9 @@ def test_check_layer_tile_only(lib):
     assert lib.moe_q4_check_layer(C.byref(L)) == 0                 # both copies
     L.w_gate = L.w_up = L.w_down = L.s_gate = L.s_up = L.s_down = None
     assert lib.moe_q4_check_layer(C.byref(L)) == 0                 # tile order only
+    L0 = _layer(hidden=2048, inter=512, E=128, k=8, shared=1)
+    L0.t_gate = L0.t_up = L0.t_down = L0.ts_gate = L0.ts_up = L0.ts_down = 0x20000
+    L0.w_gate = L0.w_up = L0.w_down = L0.s_gate = L0.s_up = L0.s_down = None
     L.w_gate = 0x10000                                             # a partial row-major set
     assert lib.moe_q4_check_layer(C.byref(L)) == -1 and "together" in _err(lib)
     L.w_gate = None
@@ -322,6 +325,15 @@ def test_check_layer_tile_only(lib):
     # and the entry points refuse such layers before any device access
     assert lib.moe_q4_decode_workspace_bytes(C.byref(W)) == 0
     assert lib.moe_q4_check_layer(None) == -1
+    # a batch whose bf16 tokens pass 2^32 bytes needs the generic GEMM, which
+    # reads the row-major matrices: refused for a tile-only layer
+    from bit_quantized_moe_q4_amd._lib import Routing
+    R = Routing()
+    R.topk_ids = R.topk_w = R.expert_offsets = R.perm = R.inv_perm = 0x3000
+    T = (1 << 20) + 1                                              # T * 2048 * 2 > 2^32 - 1
+    rc = lib.moe_q4_prefill(C.byref(L0), C.c_void_p(0x1000), T, C.byref(R), C.c_void_p(0x2000),
+                            C.c_void_p(0x100000), 1 << 45, None)
+    assert rc == -1 and "too large" in _err(lib)
 
 
 def test_decode_noalloc_checks(lib):
