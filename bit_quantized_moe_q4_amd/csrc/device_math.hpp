@@ -82,4 +82,28 @@ __device__ __forceinline__ float wave_tree_sum(float v, int width) {
   return v;
 }
 
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const int l2 = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xf, false);
+  const int h2 = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xf, false);
+  return ((uint64_t)(uint32_t)h2 << 32) | (uint32_t)l2;
+}
+
+// Maximum of v over the 64 lanes (all active), by DPP lane moves: xor 1 and
+// 2 inside quads, mirrors inside 8 and 16 lanes, then row broadcasts that
+// leave the maximum in lane 63; returned in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u64<0xb1, 0xf>(v));      // quad_perm [1,0,3,2]
+  v = mx(v, dpp_u64<0x4e, 0xf>(v));      // quad_perm [2,3,0,1]
+  v = mx(v, dpp_u64<0x141, 0xf>(v));     // row_half_mirror
+  v = mx(v, dpp_u64<0x140, 0xf>(v));     // row_mirror
+  v = mx(v, dpp_u64<0x142, 0xa>(v));     // row_bcast:15 into rows 1, 3
+  v = mx(v, dpp_u64<0x143, 0xc>(v));     // row_bcast:31 into rows 2, 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 }  // namespace moeq4

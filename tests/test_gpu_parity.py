@@ -417,6 +417,11 @@ def _decode_steps(ol, gl, cfg, steps):
     # the largest top-k on the fast row programs (33 slots; 264 gate/up
     # blocks and 33 rows per down block)
     ("many_slots", 512, 128, 256, 32, True, "zipf"),
+    # past 128 experts the one-launch step takes its top-k by wave rounds:
+    # 256 experts, a count that is not a power of two, and the 1024 limit
+    ("e256", 512, 256, 128, 8, True, None),
+    ("e200", 256, 200, 64, 6, False, "zipf"),
+    ("e1024_k4", 256, 1024, 64, 4, True, "zipf"),
 ])
 def test_decode_small(name, H, E, I, k, shared, bias):
     say("decode", name)
