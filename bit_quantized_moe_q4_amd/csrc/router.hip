@@ -47,74 +47,130 @@ struct Log2<1> { static constexpr int v = 0; };
 // chains on gfx950), so 32 instructions over k = 0..31 are the chunk's
 // sequential FMA chain, at twice the fp32 VALU rate.  A wave covers 32 tokens
 // x 64 experts: lane l supplies token t0 + l%32 (both lane halves) and
-// expert e0 + 32*(l/32) + l%32; block b's output (row i, column j) sits in
-// register 16b + 4*(i/8) + i%4 of lane 32*((i/4)%2) + j.  No LDS: a lane
-// reads its token's 32 chunk values and, per k, one dword of a W_r row that
-// the wave reads contiguously.  A chunk's operands are loaded two chunks
-// ahead, so the loads run under the previous chunks' MFMA chains.
-constexpr int RMW = 4;                    // waves (token tiles of 32) per block
+// expert e0 + l; block b's output (row i, column j) sits in register
+// 16b + 4*(i/8) + i%4 of lane 32*((i/4)%2) + j.
+//
+// Block = 4 waves = 2 token tiles x 2 halves of the grid z's aligned subtree
+// of CW chunks: half h computes the subtree of chunks h*CW/2 .. (h+1)*CW/2-1
+// and the two halves meet in LDS as (left + right), the subtree's own top
+// node.  The two waves of a half read the same router rows: the block stages
+// each chunk's 32 rows x 64 experts per half in LDS with direct
+// global->LDS loads (one 256-byte row per wave instruction), double
+// buffered, so a lane reads its weight per k with one conflict-free LDS
+// read.  A lane's token values come from global memory one chunk ahead.
+// Splitting the subtree over two waves keeps a wave's pending subtrees to
+// log2(CW/2) + 1 accumulators, so three waves fit on a SIMD.
+constexpr int RPW = 4;                    // waves per block
+constexpr int RPT = 2;                    // token tiles of 32 per block
+
+__device__ __forceinline__ void wait_vm_router() {
+  // s_waitcnt vmcnt(0), expcnt/lgkmcnt untouched (gfx9 encoding)
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
+template <int CW>
+struct RouterSmem {
+  static constexpr int NH = CW >= 2 ? 2 : 1;   // halves
+  float w[2][NH][BLK * 64];                     // [buffer][half][k][expert]
+};
 
 template <bool BF16, int CW>
-__global__ void __launch_bounds__(64 * RMW) router_partials_mfma_kernel(const void* __restrict__ xv, int T,
+__global__ void __launch_bounds__(64 * RPW) router_partials_mfma_kernel(const void* __restrict__ xv, int T,
                                                                          int H, const float* __restrict__ Wr,
                                                                          int E, int nc,
                                                                          float* __restrict__ partials) {
+#if defined(__HIP_DEVICE_COMPILE__)
   typedef float f32x32_t __attribute__((ext_vector_type(32)));
-  constexpr int L = Log2<CW>::v;
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  const int t0 = (blockIdx.y * RMW + wave) * 32, e0 = blockIdx.x * 64, split = blockIdx.z;
-  const int t = t0 + lane % 32, e = e0 + 32 * (lane / 32) + lane % 32;
-  const bool tv = t < T, ev = e < E;
-  const int tc = tv ? t : T - 1, ec = ev ? e : E - 1;       // clamped: loads stay in bounds
-  f32x32_t st[L + 1];
-  const int cbase = split * CW;
-  float xa[BLK], wa[BLK];
-  auto load = [&](int c) {
+  constexpr int NH = RouterSmem<CW>::NH;
+  constexpr int HC = CW / NH;                   // chunks per half
+  constexpr int L = Log2<HC>::v;
+  __shared__ RouterSmem<CW> sm;
+  const int lane = threadIdx.x % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int tt = wave % RPT, h = wave / RPT;
+  const int t0 = (blockIdx.y * RPT + tt) * 32, e0 = blockIdx.x * 64;
+  const int t = t0 + lane % 32, e = e0 + lane;
+  const int tc = t < T ? t : T - 1, ec = e < E ? e : E - 1;   // clamped: loads stay in bounds
+  const int cbase = blockIdx.z * CW + h * HC;   // this wave's first chunk (uniform)
+  const bool active = h < NH;                   // NH == 1: waves of half 1 only stage rows
+
+  // router rows: wave w stages rows k = tt + RPT*j of its half's chunk
+  // (readfirstlane returns int: each half goes through uint32_t, so the low
+  // word is not sign-extended into the high one)
+  const uint64_t wp = reinterpret_cast<uint64_t>(Wr);
+  const uint32_t wlo = __builtin_amdgcn_readfirstlane((uint32_t)wp);
+  const uint32_t whi = __builtin_amdgcn_readfirstlane((uint32_t)(wp >> 32));
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)whi << 32) | wlo), 0,
+      (int)__builtin_amdgcn_readfirstlane((uint32_t)((size_t)H * E * 4)), 0x00020000);
+  const uint32_t vw = 4u * (uint32_t)ec;
+  const int hs = h < NH ? h : 0;                // half whose rows this wave stages
+  constexpr int SW = NH == 2 ? RPT : RPW;       // waves staging one half's rows
+  const int sbase = blockIdx.z * CW + hs * HC;
+  auto stage_w = [&](int i, int buf) {
+    const int c = sbase + i;
+    if (c >= nc) return;                        // uniform
+#pragma unroll
+    for (int j = 0; j < BLK / SW; j++) {
+      const int k = (NH == 2 ? tt : wave) + SW * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (__attribute__((address_space(3))) void*)(&sm.w[buf][hs][k * 64]), 4, vw,
+          (uint32_t)((c * BLK + k) * E) * 4u, 0, 0);
+    }
+  };
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int XR = BF16 ? BLK / 2 : BLK;      // registers of one chunk of the lane's token
+  uint32_t xr[2][XR];
+  auto load_x = [&](int i, int slot) {
+    const int c = cbase + i;
+    if (!active || c >= nc) return;
     if (BF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + (size_t)tc * H + c * BLK);
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(xv) + (size_t)tc * H + c * BLK);
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const uint4 raw = src[q];
-        const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          xa[8 * q + 2 * i] = bf16_bits_to_f32(r[i] & 0xffffu);
-          xa[8 * q + 2 * i + 1] = bf16_bits_to_f32(r[i] >> 16);
-        }
+      for (int q = 0; q < XR / 4; q++) {
+        const u32x4_t v = src[q];
+        xr[slot][4 * q] = v.x; xr[slot][4 * q + 1] = v.y; xr[slot][4 * q + 2] = v.z; xr[slot][4 * q + 3] = v.w;
       }
     } else {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(xv) + (size_t)tc * H + c * BLK);
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(xv) + (size_t)tc * H + c * BLK);
 #pragma unroll
-      for (int q = 0; q < 8; q++) {
-        const float4 v = src[q];
-        xa[4 * q] = v.x; xa[4 * q + 1] = v.y; xa[4 * q + 2] = v.z; xa[4 * q + 3] = v.w;
+      for (int q = 0; q < XR / 4; q++) {
+        const u32x4_t v = src[q];
+        xr[slot][4 * q] = v.x; xr[slot][4 * q + 1] = v.y; xr[slot][4 * q + 2] = v.z; xr[slot][4 * q + 3] = v.w;
       }
     }
-    const float* wsrc = Wr + (size_t)c * BLK * E + ec;
-#pragma unroll
-    for (int k = 0; k < BLK; k++) wa[k] = wsrc[(size_t)k * E];
   };
-  float xb[3][BLK], wb[3][BLK];
-  auto stage = [&](int slot) {
-#pragma unroll
-    for (int k = 0; k < BLK; k++) { xb[slot][k] = xa[k]; wb[slot][k] = wa[k]; }
-  };
-  if (cbase < nc) { load(cbase); stage(0); }
-  if (CW > 1 && cbase + 1 < nc) { load(cbase + 1); stage(1); }
-#pragma unroll
-  for (int cl = 0; cl < CW; cl++) {
-    const int c = cbase + cl;
-    f32x32_t acc = {};
-    if (c < nc) {                         // padded leaves stay +0.0
-      if (cl + 2 < CW && c + 2 < nc) { load(c + 2); stage((cl + 2) % 3); }   // two chunks ahead
-#pragma unroll
-      for (int k = 0; k < BLK; k++) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xb[cl % 3][k], wb[cl % 3][k], acc, 0, 0, 0);
+  auto xval = [&](int slot, int k) -> float {
+    if (BF16) {
+      const uint32_t p = xr[slot][k / 2];
+      return __uint_as_float((k & 1) ? (p & 0xffff0000u) : (p << 16));
     }
-    // binary-counter merge: leaf cl joins the pending subtrees of equal size
+    return __uint_as_float(xr[slot][k]);
+  };
+
+  f32x32_t st[L + 1];
+  stage_w(0, 0);
+  load_x(0, 0);
+#pragma unroll
+  for (int i = 0; i < HC; i++) {
+    wait_vm_router();                           // own rows and token values of chunk i landed
+    __syncthreads();                            // every wave's rows of chunk i landed; chunk i-1 done
+    if (i + 1 < HC) {
+      stage_w(i + 1, (i + 1) & 1);
+      load_x(i + 1, (i + 1) & 1);
+    }
+    f32x32_t acc = {};
+    const int c = cbase + i;
+    if (active && c < nc) {                     // padded leaves stay +0.0
+      const float* wl = &sm.w[i & 1][h][lane];
+#pragma unroll
+      for (int k = 0; k < BLK; k++) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(xval(i & 1, k), wl[k * 64], acc, 0, 0, 0);
+    }
+    // binary-counter merge: leaf i joins the pending subtrees of equal size
     int lvl = 0;
 #pragma unroll
     for (int b = 0; b < L; b++) {
-      if (((cl >> b) & 1) == 0) break;
+      if (((i >> b) & 1) == 0) break;
       lvl = b + 1;
     }
 #pragma unroll
@@ -124,21 +180,38 @@ __global__ void __launch_bounds__(64 * RMW) router_partials_mfma_kernel(const vo
     for (int b = 0; b <= L; b++)
       if (b == lvl) st[b] = acc;
   }
-  float* out = partials + (size_t)split * T * E;
+  f32x32_t res = st[L];
+  if (NH == 2) {
+    // the right half's subtree meets the left one's: (left + right)
+    float* ex = &sm.w[0][0][0];                 // RPT waves x 32 registers x 64 lanes
+    __syncthreads();                            // every wave is done with the staged rows
+    if (h == 1) {
+#pragma unroll
+      for (int r = 0; r < 32; r++) ex[(tt * 32 + r) * 64 + lane] = res[r];
+    }
+    __syncthreads();
+    if (h == 1) return;
+#pragma unroll
+    for (int r = 0; r < 32; r++) res[r] = res[r] + ex[(tt * 32 + r) * 64 + lane];
+  } else if (h != 0) {
+    return;
+  }
+  float* out = partials + (size_t)blockIdx.z * T * E;
 #pragma unroll
   for (int r = 0; r < 32; r++) {
     const int blk = r / 16, i = 8 * ((r % 16) / 4) + 4 * (lane / 32) + (r % 4), j = lane % 32;
     const int to = t0 + i, eo = e0 + 32 * blk + j;
-    if (to < T && eo < E) out[(size_t)to * E + eo] = st[L][r];
+    if (to < T && eo < E) out[(size_t)to * E + eo] = res[r];
   }
+#endif
 }
 
 hipError_t launch_router_partials(const void* x, int x_bf16, int T, int H, const float* w_router,
                                   int E, const RouterSplit& sp, float* partials,
                                   hipStream_t stream) {
-  dim3 grid((E + 63) / 64, (T + 32 * RMW - 1) / (32 * RMW), sp.nsplit);
+  dim3 grid((E + 63) / 64, (T + 32 * RPT - 1) / (32 * RPT), sp.nsplit);
 #define MOEQ4_RP(BF, CWV)                                                                         \
-  hipLaunchKernelGGL((router_partials_mfma_kernel<BF, CWV>), grid, dim3(64 * RMW), 0, stream, x, T, H, \
+  hipLaunchKernelGGL((router_partials_mfma_kernel<BF, CWV>), grid, dim3(64 * RPW), 0, stream, x, T, H, \
                      w_router, E, sp.nc, partials)
 #define MOEQ4_RP_CW(BF)                      \
   switch (sp.cw) {                           \

@@ -173,6 +173,9 @@ def _check_route(ol, r, xw):
     ("wide", 130, 256, 8, 2048, None),
     ("k_equals_e", 33, 4, 4, 128, None),
     ("one_expert", 40, 1, 1, 64, None),
+    ("one_chunk", 40, 8, 2, 32, None),
+    ("e_not_mult_64", 100, 37, 6, 1024, None),
+    ("e256_long", 700, 256, 8, 2048, "zipf"),
 ])
 def test_route_bit_exact(name, T, E, k, H, bias):
     say("route", name, T, E, k, H, bias)
