@@ -77,7 +77,7 @@ struct RouterSmem {
 template <bool BF16, int CW>
 __global__ void __launch_bounds__(64 * RPW) router_partials_mfma_kernel(const void* __restrict__ xv, int T,
                                                                          int H, const float* __restrict__ Wr,
-                                                                         int E, int nc,
+                                                                         int E, int nc, int nsplit,
                                                                          float* __restrict__ partials) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef float f32x32_t __attribute__((ext_vector_type(32)));
@@ -85,13 +85,22 @@ __global__ void __launch_bounds__(64 * RPW) router_partials_mfma_kernel(const vo
   constexpr int HC = CW / NH;                   // chunks per half
   constexpr int L = Log2<HC>::v;
   __shared__ RouterSmem<CW> sm;
+  // Block b -> (expert tile ex, group g = token group * nsplit + split): the
+  // expert tiles of one group are 8 blocks apart, so they land on the same
+  // XCD (blocks are dealt to the 8 XCDs round robin) close in time, and the
+  // group's token rows are fetched into that XCD's L2 once.
+  const int nx = (E + 63) / 64;
+  const int q = blockIdx.x / 8;
+  const int ex = q % nx, g = 8 * (q / nx) + blockIdx.x % 8;
+  const int ty = g / nsplit, split = g % nsplit;
+  if (ty * RPT * 32 >= T) return;               // padding of the last 8 groups (uniform per block)
   const int lane = threadIdx.x % 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int tt = wave % RPT, h = wave / RPT;
-  const int t0 = (blockIdx.y * RPT + tt) * 32, e0 = blockIdx.x * 64;
+  const int t0 = (ty * RPT + tt) * 32, e0 = ex * 64;
   const int t = t0 + lane % 32, e = e0 + lane;
   const int tc = t < T ? t : T - 1, ec = e < E ? e : E - 1;   // clamped: loads stay in bounds
-  const int cbase = blockIdx.z * CW + h * HC;   // this wave's first chunk (uniform)
+  const int cbase = split * CW + h * HC;        // this wave's first chunk (uniform)
   const bool active = h < NH;                   // NH == 1: waves of half 1 only stage rows
 
   // router rows: wave w stages rows k = tt + RPT*j of its half's chunk
@@ -106,7 +115,7 @@ __global__ void __launch_bounds__(64 * RPW) router_partials_mfma_kernel(const vo
   const uint32_t vw = 4u * (uint32_t)ec;
   const int hs = h < NH ? h : 0;                // half whose rows this wave stages
   constexpr int SW = NH == 2 ? RPT : RPW;       // waves staging one half's rows
-  const int sbase = blockIdx.z * CW + hs * HC;
+  const int sbase = split * CW + hs * HC;
   auto stage_w = [&](int i, int buf) {
     const int c = sbase + i;
     if (c >= nc) return;                        // uniform
@@ -196,7 +205,7 @@ __global__ void __launch_bounds__(64 * RPW) router_partials_mfma_kernel(const vo
   } else if (h != 0) {
     return;
   }
-  float* out = partials + (size_t)blockIdx.z * T * E;
+  float* out = partials + (size_t)split * T * E;
 #pragma unroll
   for (int r = 0; r < 32; r++) {
     const int blk = r / 16, i = 8 * ((r % 16) / 4) + 4 * (lane / 32) + (r % 4), j = lane % 32;
@@ -209,10 +218,11 @@ __global__ void __launch_bounds__(64 * RPW) router_partials_mfma_kernel(const vo
 hipError_t launch_router_partials(const void* x, int x_bf16, int T, int H, const float* w_router,
                                   int E, const RouterSplit& sp, float* partials,
                                   hipStream_t stream) {
-  dim3 grid((E + 63) / 64, (T + 32 * RPT - 1) / (32 * RPT), sp.nsplit);
+  const int groups = (T + 32 * RPT - 1) / (32 * RPT) * sp.nsplit;
+  dim3 grid((uint32_t)(8 * ((groups + 7) / 8) * ((E + 63) / 64)));
 #define MOEQ4_RP(BF, CWV)                                                                         \
   hipLaunchKernelGGL((router_partials_mfma_kernel<BF, CWV>), grid, dim3(64 * RPW), 0, stream, x, T, H, \
-                     w_router, E, sp.nc, partials)
+                     w_router, E, sp.nc, sp.nsplit, partials)
 #define MOEQ4_RP_CW(BF)                      \
   switch (sp.cw) {                           \
     case 1: MOEQ4_RP(BF, 1); break;          \
