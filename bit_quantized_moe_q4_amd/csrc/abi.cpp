@@ -745,7 +745,16 @@ size_t moe_q4_decode_stack_workspace_bytes(const moe_q4_layer* layers, int32_t n
     const size_t w = decode_ws(&layers[l]).total;
     need = w > need ? w : need;
   }
-  return need + (n_layers > 0 ? 2 * up256((size_t)layers[0].hidden * 4) : 0);
+  // two y buffers between runs of layers, then the tagged words of a layer's y
+  return need + (n_layers > 0 ? 2 * up256((size_t)layers[0].hidden * 4) + up256((size_t)layers[0].hidden * 8) : 0);
+}
+
+// Layers that one stacked launch can run together: one shape, one weight
+// format, tile-order copies.
+static bool same_stack_shape(const moe_q4_layer* a, const moe_q4_layer* b) {
+  return a->hidden == b->hidden && a->inter == b->inter && a->n_experts == b->n_experts && a->top_k == b->top_k &&
+         a->has_shared == b->has_shared && a->weight_format == b->weight_format && b->t_gate && b->t_up &&
+         b->t_down && (!b->has_shared || (b->ts_gate && b->ts_up && b->ts_down));
 }
 
 int moe_q4_decode_stack(const moe_q4_layer* layers, int32_t n_layers, const float* x, float* y,
@@ -766,10 +775,45 @@ int moe_q4_decode_stack(const moe_q4_layer* layers, int32_t n_layers, const floa
   }
   if (!aligned(x, 16) || !aligned(y, 4)) return fail(MOE_Q4_EINVAL, "moe_q4_decode_stack: x must be 16-byte aligned");
   const size_t H = (size_t)layers[0].hidden;
-  const size_t need = dws + 2 * up256(H * 4);
+  const size_t need = dws + 2 * up256(H * 4) + up256(H * 8);
   int rc = check_ws(ws, ws_bytes, need);
   if (rc) return rc;
   float* ybuf[2] = {at<float>(ws, dws), at<float>(ws, dws + up256(H * 4))};
+  // one launch per run of up to kStackMaxLayers layers when every layer has
+  // the first one's shape and the one-launch step is available for it
+  bool same = true;
+  for (int32_t l = 0; l < n_layers; l++) same = same && same_stack_shape(&layers[0], &layers[l]);
+  if (same) {
+    moeq4::DecodeArgs a = decode_args(&layers[0], ws);
+    a.ll_y = at<uint64_t>(ws, dws + 2 * up256(H * 4));
+    a.test_wait_fail = g_test_decode_wait_fail.load();
+    // (a normal wait ends within microseconds; a shorter bound than one
+    // step's keeps a broken stack from waiting out 40 layers of bounds)
+    a.spin_max = a.test_wait_fail ? 16 : (1 << 16);
+    a.norm_eps = eps;
+    if (moeq4::stack_decode_available(a)) {
+      int run = 0;
+      for (int32_t c0 = 0; c0 < n_layers; c0 += moeq4::kStackMaxLayers, run++) {
+        const int32_t n = n_layers - c0 < moeq4::kStackMaxLayers ? n_layers - c0 : moeq4::kStackMaxLayers;
+        moeq4::StackTable t;
+        memset(&t, 0, sizeof t);
+        t.n = n;
+        for (int32_t i = 0; i < n; i++) {
+          const moe_q4_layer* L = &layers[c0 + i];
+          t.l[i] = {L->w_router, L->router_bias, static_cast<const uint8_t*>(L->t_gate),
+                    static_cast<const uint8_t*>(L->t_up), static_cast<const uint8_t*>(L->t_down),
+                    static_cast<const uint8_t*>(L->ts_gate), static_cast<const uint8_t*>(L->ts_up),
+                    static_cast<const uint8_t*>(L->ts_down)};
+        }
+        a.norm_in = c0 > 0;
+        a.x = c0 == 0 ? x : ybuf[(run - 1) & 1];
+        a.y = c0 + n == n_layers ? y : ybuf[run & 1];
+        hipError_t e = moeq4::launch_decode_stack(a, t, stream);
+        if (e != hipSuccess) return hip_fail(e, "moe_q4_decode_stack");
+      }
+      return MOE_Q4_OK;
+    }
+  }
   for (int32_t l = 0; l < n_layers; l++) {
     const moe_q4_layer* L = &layers[l];
     moeq4::DecodeArgs a = decode_args(L, ws);

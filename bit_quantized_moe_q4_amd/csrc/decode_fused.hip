@@ -58,6 +58,9 @@ constexpr int kFuWaves = kFuThreads / 64;
 constexpr int kFuSpinMax = 1 << 20;   // polls of one wait (about half a second) before it gives up
 constexpr int kFuQhWords = 10;        // words per published 32-group of q8(h): 8 code dwords, d, code sum
 constexpr int kFuMaxSlots = 12;       // slots (k + shared) the one-launch step covers
+// test only: waits look for tag + kFuTestTag, which no word of this or a
+// neighbouring call or layer carries
+constexpr uint32_t kFuTestTag = 0x40000000u;
 
 // A word's high half is the tag mixed with a multiplicative hash of its
 // payload, so bytes a workspace held before (other layers' or other paths'
@@ -111,6 +114,19 @@ __device__ __forceinline__ bool ll_wait(const uint64_t* base, size_t stride, int
   return all;
 }
 
+// x of a stacked layer after the first: the previous layer's y, handed over
+// as one tagged word per value, into LDS xl [H].  Whole block (H % 64 == 0).
+__device__ __forceinline__ void fu_stage_x(const uint64_t* llx, int H, uint32_t tag, float* xl, int spin_max,
+                                           bool& ok) {
+  for (int i0 = 4 * threadIdx.x; i0 < H; i0 += 4 * blockDim.x) {
+    uint32_t v[4];
+    ok = ll_wait<4>(llx + i0, 1, 4, tag, v, spin_max) && ok;
+#pragma unroll
+    for (int j = 0; j < 4; j++) xl[i0 + j] = __uint_as_float(v[j]);
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- router role
 // Router block r = (expert group eg, chunk group cg): experts e0 = eg * EB ..
 // e0 + EB - 1 over chunks c0 = cg * cpb .. c0 + cpb - 1 (chunks >= H/32 are
@@ -128,8 +144,11 @@ __device__ __forceinline__ float lds_subtree(const float* lf, int EB, int el) {
   return reg_tree<N>(v);
 }
 
-__device__ void fu_router(const DecodeArgs& a, const FusedGeometry& g, int r, const uint32_t* tag_s, uint8_t* dyn,
-                          float* part, float* tmp) {
+// (llx: x comes from the previous stacked layer's words with tag xtag, staged
+// in xl, after this block's first router weights are in flight)
+__device__ void fu_router(const DecodeArgs& a, const StackLayer& LW, int norm_in, const FusedGeometry& g, int r,
+                          const uint32_t* tag_s, uint8_t* dyn, float* part, float* tmp, const uint64_t* llx,
+                          uint32_t xtag, float* xl, bool& ok) {
   const int tid = threadIdx.x, E = a.E, nc = a.H / BLK, cpb = g.cpb, EB = g.eb;
   const int eg = r % g.n_eg, cg = r / g.n_eg;
   const int e0 = eg * EB, ne = min(EB, E - e0);
@@ -141,17 +160,22 @@ __device__ void fu_router(const DecodeArgs& a, const FusedGeometry& g, int r, co
   {
     const int p = min(tid, np - 1), cl = p / EB, el = min(p % EB, ne - 1);
     const int c = min(c0 + cl, nc - 1);
-    const float* w = a.w_router + (size_t)c * BLK * E + e0 + el;
+    const float* w = LW.w_router + (size_t)c * BLK * E + e0 + el;
 #pragma unroll
     for (int i = 0; i < BLK; i++) wv[i] = w[(size_t)i * E];
   }
-  if (a.norm_in) {
-    const float rr = rms_scale(a.x, a.H, a.norm_eps, part, tmp);
+  const float* X = a.x;
+  if (llx) {
+    fu_stage_x(llx, a.H, xtag, xl, a.spin_max, ok);
+    X = xl;
+  }
+  if (norm_in) {
+    const float rr = rms_scale(X, a.H, a.norm_eps, part, tmp);
     for (int i = tid; i < cpb * BLK; i += blockDim.x)
-      xs[i] = (c0 + i / BLK < nc) ? a.x[c0 * BLK + i] / rr : 0.0f;
+      xs[i] = (c0 + i / BLK < nc) ? X[c0 * BLK + i] / rr : 0.0f;
   } else {
     for (int i = tid; i < cpb * BLK; i += blockDim.x)
-      xs[i] = (c0 + i / BLK < nc) ? a.x[c0 * BLK + i] : 0.0f;
+      xs[i] = (c0 + i / BLK < nc) ? X[c0 * BLK + i] : 0.0f;
   }
   __syncthreads();
   const uint32_t tag = *tag_s;
@@ -159,7 +183,7 @@ __device__ void fu_router(const DecodeArgs& a, const FusedGeometry& g, int r, co
     const int cl = p / EB, el = min(p % EB, ne - 1);
     if (p != tid) {
       const int c = min(c0 + cl, nc - 1);
-      const float* w = a.w_router + (size_t)c * BLK * E + e0 + el;
+      const float* w = LW.w_router + (size_t)c * BLK * E + e0 + el;
 #pragma unroll
       for (int i = 0; i < BLK; i++) wv[i] = w[(size_t)i * E];
     }
@@ -311,8 +335,9 @@ __host__ __device__ inline size_t fu_gu_lds_bytes(int nbh, int E) {
 }
 
 template <int SP, int FMT>
-__device__ void fu_gateup(const DecodeArgs& a, const FusedGeometry& g, int jj, const uint32_t* tag_s, uint8_t* dyn,
-                          float* part, float* tmp, bool& ok) {
+__device__ void fu_gateup(const DecodeArgs& a, const StackLayer& LW, int norm_in, const FusedGeometry& g, int jj,
+                          const uint32_t* tag_s, uint8_t* dyn, float* part, float* tmp, const uint64_t* llx,
+                          uint32_t xtag, float* xl, bool& ok) {
   using TF = TileFmt<FMT>;
   constexpr int CHM = FMT == kQ4 ? 4 : 2;  // pieces whose loads are issued together
   constexpr int CH = SP < CHM ? SP : CHM;
@@ -345,13 +370,18 @@ __device__ void fu_gateup(const DecodeArgs& a, const FusedGeometry& g, int jj, c
   // q8 of x (x = y / r with the RMSNorm glue): 8 threads per 32-block, 4
   // elements each; amax and the code sum over the 8 threads by shuffles
   {
+    const float* X = a.x;
+    if (llx) {                            // (a stacked layer after the first)
+      fu_stage_x(llx, H, xtag, xl, a.spin_max, ok);
+      X = xl;
+    }
     float rr = 1.0f;
-    if (a.norm_in) rr = rms_scale(a.x, H, a.norm_eps, part, tmp);
+    if (norm_in) rr = rms_scale(X, H, a.norm_eps, part, tmp);
     for (int t = tid; t < nbh * 8; t += nt) {
       const int c = t / 8, s = t % 8;
-      const float4 v4 = *reinterpret_cast<const float4*>(a.x + c * BLK + 4 * s);
+      const float4 v4 = *reinterpret_cast<const float4*>(X + c * BLK + 4 * s);
       float v[4] = {v4.x, v4.y, v4.z, v4.w};
-      if (a.norm_in) {
+      if (norm_in) {
 #pragma unroll
         for (int i = 0; i < 4; i++) v[i] = v[i] / rr;
       }
@@ -380,7 +410,7 @@ __device__ void fu_gateup(const DecodeArgs& a, const FusedGeometry& g, int jj, c
   }
   __syncthreads();                        // x's codes and the tag
   const uint32_t tag = *tag_s;            // this call's words carry it
-  const uint32_t wtag = tag + (a.test_wait_fail ? 1u : 0u);     // waited for (test: a tag no word carries)
+  const uint32_t wtag = tag + (a.test_wait_fail ? kFuTestTag : 0u);   // waited for (test: a tag no word carries)
   if (routed) {
     // the published subtree values, polled directly: P lanes per expert, L
     // values per lane, then log2(P) shuffle levels of the tree
@@ -407,7 +437,7 @@ __device__ void fu_gateup(const DecodeArgs& a, const FusedGeometry& g, int jj, c
       }
       for (int o = 1; o < P; o <<= 1) lv = lv + __shfl_xor(lv, o, 64);
       if (in && p == 0) {
-        const float lg = a.bias ? lv + a.bias[e] : lv;
+        const float lg = LW.bias ? lv + LW.bias[e] : lv;
         logit[e] = lg;
         key[e] = rank_key(lg, e);
         if (publish && a.t_logits) a.t_logits[e] = lg;
@@ -441,11 +471,11 @@ __device__ void fu_gateup(const DecodeArgs& a, const FusedGeometry& g, int jj, c
   const uint8_t* ub;
   if (routed) {                           // (clamped: a NaN logit leaves ranks unfilled)
     const size_t G = (size_t)min(max(ids_l[slot], 0), E - 1) * ngrp + gx;
-    gb = a.t_gate + G * gbytes;
-    ub = a.t_up + G * gbytes;
+    gb = LW.t_gate + G * gbytes;
+    ub = LW.t_up + G * gbytes;
   } else {
-    gb = a.ts_gate + (size_t)gx * gbytes;
-    ub = a.ts_up + (size_t)gx * gbytes;
+    gb = LW.ts_gate + (size_t)gx * gbytes;
+    ub = LW.ts_up + (size_t)gx * gbytes;
   }
   const int half = lane >> 5;
   float cg[NCH], cu[NCH];
@@ -553,8 +583,8 @@ __host__ __device__ inline size_t fu_dn_lds_bytes(int ns, int nbi, int NH) {
 // pieces pairwise; with NH = 2 the two halves are the row's top subtrees,
 // added before the combine.  Then the fixed-order combine.
 template <int SPH, int FMT>
-__device__ void fu_down(const DecodeArgs& a, const FusedGeometry& g, int u, const uint32_t* tag_s, uint8_t* dyn,
-                        bool& ok) {
+__device__ void fu_down(const DecodeArgs& a, const StackLayer& LW, uint64_t* lly, const FusedGeometry& g, int u,
+                        const uint32_t* tag_s, uint8_t* dyn, bool& ok) {
   using TF = TileFmt<FMT>;
   __shared__ int ids_d[32];
   __shared__ float w_d[32];
@@ -571,7 +601,8 @@ __device__ void fu_down(const DecodeArgs& a, const FusedGeometry& g, int u, cons
   // XCDs round robin and base_dn % 8 == 0): their pieces share scale lines
   const int r0 = (H % 256 == 0) ? 32 * (8 * (u / 32) + u % 8) + kDtRows * ((u / 8) % 4) : u * kDtRows;
   __syncthreads();                        // the tag
-  const uint32_t tag = *tag_s + (a.test_wait_fail ? 1u : 0u);   // (test: a tag no word carries)
+  const uint32_t ptag = *tag_s;           // this call's words carry it
+  const uint32_t tag = ptag + (a.test_wait_fail ? kFuTestTag : 0u);   // waited for (test: a tag no word carries)
   // ids and weights
   if (tid < 2 * a.k) {
     uint32_t v[1];
@@ -592,7 +623,7 @@ __device__ void fu_down(const DecodeArgs& a, const FusedGeometry& g, int u, cons
   const int pl = 32 * half + (r0 % 32) + rr;                             // lane inside a piece
   const size_t G = (size_t)(r0 / 32);
   const int eid = min(max(ids_d[min(sl, a.k - 1)], 0), a.E - 1);
-  const uint8_t* base = (sl < a.k) ? a.t_down + ((size_t)eid * (H / 32) + G) * gbytes : a.ts_down + G * gbytes;
+  const uint8_t* base = (sl < a.k) ? LW.t_down + ((size_t)eid * (H / 32) + G) * gbytes : LW.ts_down + G * gbytes;
   const int s0 = hh * SPH;
   TileCodes<FMT> wn[SPH];
   uint32_t wsc[SPH];
@@ -668,7 +699,8 @@ __device__ void fu_down(const DecodeArgs& a, const FusedGeometry& g, int u, cons
       for (int s = 1; s < kFuMaxSlots; s++) osh = s == a.k ? row(s) : osh;
       acc = acc + osh;
     }
-    a.y[r0 + tid] = acc;
+    if (lly) ll_store(lly + r0 + tid, ptag, __float_as_uint(acc));   // (a stacked layer's y)
+    else a.y[r0 + tid] = acc;
   }
 }
 
@@ -684,6 +716,7 @@ __global__ void __launch_bounds__(kFuThreads, 2) decode_fused_kernel(DecodeArgs 
   __shared__ uint32_t tag_s;
   __shared__ float part[512], tmp[512];   // RMSNorm scale of the previous layer's y
   const int b = blockIdx.x;
+  const StackLayer LW = {a.w_router, a.bias, a.t_gate, a.t_up, a.t_down, a.ts_gate, a.ts_up, a.ts_down};
   uint32_t* slots = reinterpret_cast<uint32_t*>(a.hdr + 1);
   if (threadIdx.x == 0) {                 // read by each role after its first barrier
     const uint32_t ep = __hip_atomic_load(slots + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -695,22 +728,93 @@ __global__ void __launch_bounds__(kFuThreads, 2) decode_fused_kernel(DecodeArgs 
   if (b < rspan) {
     const int x = b % 8, r = 2 * (b / 8) + x;
     if (x < 2) {
-      if (r < g.nR) fu_router(a, g, r, &tag_s, dyn, part, tmp);
+      if (r < g.nR) fu_router(a, LW, a.norm_in, g, r, &tag_s, dyn, part, tmp, nullptr, 0u, nullptr, ok);
     } else {
       gu = 6 * (b / 8) + x - 2;
     }
   } else if (b < g.base_dn) {
     gu = 6 * (rspan / 8) + (b - rspan);
   } else if (b < g.base_dn + g.n_dn) {
-    fu_down<DSP, FMT>(a, g, b - g.base_dn, &tag_s, dyn, ok);
+    fu_down<DSP, FMT>(a, LW, nullptr, g, b - g.base_dn, &tag_s, dyn, ok);
   }
-  if (gu >= 0 && gu < g.n_gu) fu_gateup<GSP, FMT>(a, g, gu, &tag_s, dyn, part, tmp, ok);
+  if (gu >= 0 && gu < g.n_gu) fu_gateup<GSP, FMT>(a, LW, a.norm_in, g, gu, &tag_s, dyn, part, tmp, nullptr, 0u, nullptr, ok);
   if (!ok) fu_fail(a);
   // the next call's epoch, into this block's slots (read by no other block)
   __syncthreads();
   if (threadIdx.x == 0)
     for (int i = b; i < kFuSlots; i += g.nblocks)
       __hip_atomic_store(slots + i, tag_s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- stacked layers
+// The stacked decode (x_{l+1} = RMSNorm(y_l)) in one launch: every block keeps
+// its role of the one-launch step and runs it layer after layer.  Layer l's
+// words carry tag ep + 1 + l (ep: the block's epoch slot), so words of the
+// layer before never pass as this layer's.  A layer's y goes to the next
+// layer as one tagged word per value (ll_y): the next layer's router blocks
+// and gate/up units wait for all H of them, after issuing their own first
+// weight loads (the router's), then take the RMSNorm of y themselves.  The
+// last layer writes y.  One set of handoff words serves every layer: a
+// layer's producers only publish after reading the previous layer's y, which
+// is complete only after every reader of the previous layer's words is done.
+// What the launch boundary cost between layers (the drain, the next
+// kernel's start, the later start of XCDs 2-7) becomes one handoff.
+template <int GSP, int DSP, int FMT>
+__global__ void __launch_bounds__(kFuThreads, 4) decode_stack_kernel(DecodeArgs a0, FusedGeometry g, StackTable st) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  __shared__ uint32_t tag_s, ep_s;
+  __shared__ float part[512], tmp[512];   // RMSNorm scale of the previous layer's y
+  float* xl = reinterpret_cast<float*>(dyn + g.lds);     // [H] a stacked layer's x
+  const int b = blockIdx.x;
+  uint32_t* slots = reinterpret_cast<uint32_t*>(a0.hdr + 1);
+  if (threadIdx.x == 0) ep_s = __hip_atomic_load(slots + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bool ok = true;
+  const int rspan = 8 * ((g.nR + 1) / 2);
+  int role = 0, idx = -1;                 // 1 router, 2 gate/up, 3 down
+  if (b < rspan) {
+    const int x = b % 8, r = 2 * (b / 8) + x;
+    if (x < 2) {
+      if (r < g.nR) { role = 1; idx = r; }
+    } else {
+      role = 2;
+      idx = 6 * (b / 8) + x - 2;
+    }
+  } else if (b < g.base_dn) {
+    role = 2;
+    idx = 6 * (rspan / 8) + (b - rspan);
+  } else if (b < g.base_dn + g.n_dn) {
+    role = 3;
+    idx = b - g.base_dn;
+  }
+  if (role == 2 && idx >= g.n_gu) role = 0;
+  const uint32_t test = a0.test_wait_fail ? kFuTestTag : 0u;
+  // one layer loop per role (a loop around all three roles kept every
+  // role's loop-invariant values live at once and spilled)
+#define MOEQ4_LAYER_LOOP(CALL)                                                          \
+  for (int l = 0; l < st.n; l++) {                                                      \
+    __syncthreads();                      /* done with the previous layer's tag, LDS */ \
+    if (threadIdx.x == 0) tag_s = ep_s + 1u + (uint32_t)l;                              \
+    const StackLayer& LW = st.l[l];                                                     \
+    const int norm_in = l > 0 ? 1 : a0.norm_in;                                         \
+    const uint64_t* llx = l > 0 ? a0.ll_y : nullptr;                                    \
+    const uint32_t xtag = ep_s + (uint32_t)l + test;   /* the previous layer's words */ \
+    (void)norm_in; (void)llx; (void)xtag;                                               \
+    CALL;                                                                               \
+  }
+  if (role == 1) {
+    MOEQ4_LAYER_LOOP(fu_router(a0, LW, norm_in, g, idx, &tag_s, dyn, part, tmp, llx, xtag, xl, ok))
+  } else if (role == 2) {
+    MOEQ4_LAYER_LOOP((fu_gateup<GSP, FMT>(a0, LW, norm_in, g, idx, &tag_s, dyn, part, tmp, llx, xtag, xl, ok)))
+  } else if (role == 3) {
+    MOEQ4_LAYER_LOOP((fu_down<DSP, FMT>(a0, LW, l + 1 < st.n ? a0.ll_y : nullptr, g, idx, &tag_s, dyn, ok)))
+  }
+#undef MOEQ4_LAYER_LOOP
+  if (!ok) fu_fail(a0);
+  // the next call's epoch (this call's last tag), into this block's slots
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int i = b; i < kFuSlots; i += g.nblocks)
+      __hip_atomic_store(slots + i, ep_s + (uint32_t)st.n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- launch
@@ -805,6 +909,21 @@ static int fused_capacity(const void* fn, size_t lds) {
   return cap;
 }
 
+template <int FMT>
+static const void* stack_kernel_ptr(int gsp, int dsph) {
+#define MOEQ4_SK(G, D) reinterpret_cast<const void*>(&decode_stack_kernel<G, D, FMT>)
+#define MOEQ4_SKROW(G) \
+  switch (dsph) { case 1: return MOEQ4_SK(G, 1); case 2: return MOEQ4_SK(G, 2); case 4: return MOEQ4_SK(G, 4); default: return MOEQ4_SK(G, 8); }
+  switch (gsp) {
+    case 1: MOEQ4_SKROW(1);
+    case 2: MOEQ4_SKROW(2);
+    case 4: MOEQ4_SKROW(4);
+    default: MOEQ4_SKROW(8);
+  }
+#undef MOEQ4_SKROW
+#undef MOEQ4_SK
+}
+
 bool fused_decode_available(const DecodeArgs& a) {
   if (!a.hdr || !a.t_gate || !a.t_up || !a.t_down) return false;
   if (a.has_shared && (!a.ts_gate || !a.ts_up || !a.ts_down)) return false;
@@ -821,6 +940,28 @@ static hipError_t launch_fused(const DecodeArgs& a, const FusedGeometry& g, hipS
   FusedGeometry gg = g;
   void* args[] = {&aa, &gg};
   return hipLaunchKernel(fn, dim3(g.nblocks), dim3(kFuThreads), args, g.lds, stream);
+}
+
+bool stack_decode_available(const DecodeArgs& a) {
+  if (!a.hdr || !a.ll_y || !a.t_gate || !a.t_up || !a.t_down) return false;
+  if (a.has_shared && (!a.ts_gate || !a.ts_up || !a.ts_down)) return false;
+  const FusedGeometry g = fused_geometry(a.H, a.I, a.E, a.k, a.has_shared);
+  if (!g.ok) return false;
+  const size_t lds = g.lds + 4 * (size_t)a.H;
+  const void* fn = a.wfmt == kQ8 ? stack_kernel_ptr<kQ8>(g.gu_sp, g.dn_sp) : stack_kernel_ptr<kQ4>(g.gu_sp, g.dn_sp);
+  return lds <= 64 * 1024 && g.nblocks <= fused_capacity(fn, lds);
+}
+
+hipError_t launch_decode_stack(const DecodeArgs& a, const StackTable& t, hipStream_t stream) {
+  const FusedGeometry g = fused_geometry(a.H, a.I, a.E, a.k, a.has_shared);
+  const void* fn = a.wfmt == kQ8 ? stack_kernel_ptr<kQ8>(g.gu_sp, g.dn_sp) : stack_kernel_ptr<kQ4>(g.gu_sp, g.dn_sp);
+  DecodeArgs aa = a;
+  FusedGeometry gg = g;
+  StackTable tt = t;
+  void* args[] = {&aa, &gg, &tt};
+  hipError_t e = hipLaunchKernel(fn, dim3(g.nblocks), dim3(kFuThreads), args, g.lds + 4 * (size_t)a.H, stream);
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream) {

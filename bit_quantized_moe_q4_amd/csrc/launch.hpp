@@ -139,6 +139,7 @@ struct DecodeArgs {
   uint64_t* ll_leaf;        // [n_cg][E] router subtree values
   uint64_t* ll_route;       // [2k] ids, then weights
   uint64_t* ll_qh;          // [(k+S) * I/32][10] q8(h) groups: 8 code dwords, d, code sum
+  uint64_t* ll_y;           // [H] the stacked decode's y of a layer that is not the last, or NULL
   int spin_max;             // polls of one wait before it gives up
   int test_wait_fail;       // test only: every wait looks for a tag no word carries
   // optional trace
@@ -186,6 +187,30 @@ FusedGeometry fused_geometry(int H, int I, int E, int k, int has_shared);
 // count allow the one-launch decode with the given workspace words
 bool fused_decode_available(const DecodeArgs& a);
 hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream);
+
+// The stacked decode in one launch per run of up to kStackMaxLayers layers of
+// one shape (the table travels in the kernel arguments).
+constexpr int kStackMaxLayers = 40;
+struct StackLayer {
+  const float* w_router;
+  const float* bias;
+  const uint8_t* t_gate;
+  const uint8_t* t_up;
+  const uint8_t* t_down;
+  const uint8_t* ts_gate;
+  const uint8_t* ts_up;
+  const uint8_t* ts_down;
+};
+struct StackTable {
+  int n;
+  StackLayer l[kStackMaxLayers];
+};
+// true if the one-launch step is available for the shape of `a` with the
+// stacked kernel's extra LDS (the layer's x)
+bool stack_decode_available(const DecodeArgs& a);
+// a: layer 0's arguments with x, y, norm_in, norm_eps of the run and ll_y;
+// the layers' pointers come from t
+hipError_t launch_decode_stack(const DecodeArgs& a, const StackTable& t, hipStream_t stream);
 
 // Batched decode: M <= kDecodeBatchMax tokens, each through the single-token
 // program; the selected experts' weights are read once per call.
