@@ -116,8 +116,23 @@ __device__ __forceinline__ bool ll_wait(const uint64_t* base, size_t stride, int
 
 // x of a stacked layer after the first: the previous layer's y, handed over
 // as one tagged word per value, into LDS xl [H].  Whole block (H % 64 == 0).
+// Polls are device-scope loads that cross to memory, and every block of the
+// next layer needs all of y: so wave 0 alone polls one word per 8-row group
+// (a down unit stores its 8 words with one instruction) until all are there,
+// then every thread reads its words once (each checked again).  Every thread
+// polling all of its words took ~3 MB of loads per poll round over the grid
+// and slowed the producers.
 __device__ __forceinline__ void fu_stage_x(const uint64_t* llx, int H, uint32_t tag, float* xl, int spin_max,
                                            bool& ok) {
+  if (threadIdx.x < 64) {
+    const int ng = H / kDtRows, lane = threadIdx.x;
+    for (int g0 = 0; g0 < ng; g0 += 64 * 4) {
+      uint32_t v[4];
+      const int n = max(0, min(4, (ng - g0 - lane + 63) / 64));
+      ok = ll_wait<4>(llx + (size_t)(g0 + lane) * kDtRows, (size_t)64 * kDtRows, n, tag, v, spin_max) && ok;
+    }
+  }
+  __syncthreads();
   for (int i0 = 4 * threadIdx.x; i0 < H; i0 += 4 * blockDim.x) {
     uint32_t v[4];
     ok = ll_wait<4>(llx + i0, 1, 4, tag, v, spin_max) && ok;
