@@ -103,7 +103,7 @@ int check_layer(const moe_q4_layer* L) {
 bool tile_only(const moe_q4_layer* L) { return !L->w_gate; }
 
 struct RouteWs {
-  size_t partials, counts, rank, total;
+  size_t partials, counts, rank, tot, total;
 };
 RouteWs route_ws(const moe_q4_layer* L, int32_t T, const moeq4::RouterSplit& sp) {
   RouteWs w;
@@ -111,7 +111,8 @@ RouteWs route_ws(const moe_q4_layer* L, int32_t T, const moeq4::RouterSplit& sp)
   w.partials = 0;
   w.counts = w.partials + up256((size_t)sp.nsplit * T * L->n_experts * sizeof(float));
   w.rank = w.counts + up256(tiles * L->n_experts * sizeof(int32_t));
-  w.total = w.rank + up256((size_t)T * L->top_k * sizeof(int32_t));
+  w.tot = w.rank + up256((size_t)T * L->top_k * sizeof(int32_t));
+  w.total = w.tot + up256((size_t)L->n_experts * sizeof(int32_t));
   return w;
 }
 
@@ -369,7 +370,8 @@ int moe_q4_route(const moe_q4_layer* L, const void* x, int32_t x_dtype, int32_t 
   if (T == 0) {
     // only the offsets have content: all zero (the scan over no tiles)
     if (!out->expert_offsets) return fail(MOE_Q4_EINVAL, "moe_q4_route: expert_offsets is NULL");
-    hipError_t e = moeq4::launch_route_scan(nullptr, 0, L->n_experts, 0, out->expert_offsets, stream);
+    hipError_t e = moeq4::launch_route_scatter(nullptr, nullptr, nullptr, nullptr, 0, L->top_k, L->n_experts,
+                                               out->expert_offsets, nullptr, nullptr, stream);
     return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_route");
   }
   if (!x || !out->topk_ids || !out->topk_w || !out->expert_offsets || !out->perm || !out->inv_perm)
@@ -390,9 +392,11 @@ int moe_q4_route(const moe_q4_layer* L, const void* x, int32_t x_dtype, int32_t 
                               counts, rank, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_q4_route/topk");
   const int tiles = (T + moeq4::kTopkTokensPerBlock - 1) / moeq4::kTopkTokensPerBlock;
-  e = moeq4::launch_route_scan(counts, tiles, E, T * k, out->expert_offsets, stream);
+  int32_t* tot = at<int32_t>(ws, W.tot);
+  e = moeq4::launch_route_colscan(counts, tiles, E, tot, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_q4_route/scan");
-  e = moeq4::launch_route_scatter(out->topk_ids, rank, counts, T, k, E, out->perm, out->inv_perm, stream);
+  e = moeq4::launch_route_scatter(out->topk_ids, rank, counts, tot, T, k, E, out->expert_offsets, out->perm,
+                                  out->inv_perm, stream);
   if (e != hipSuccess) return hip_fail(e, "moe_q4_route/scatter");
   return MOE_Q4_OK;
 }

@@ -32,11 +32,11 @@ hipError_t launch_router_partials(const void* x, int x_bf16, int T, int H, const
 hipError_t launch_topk_hist(const float* partials, const RouterSplit& sp, const float* bias,
                             int T, int E, int k, float* logits_out, int32_t* ids, float* w,
                             int32_t* counts_w, int32_t* rank, hipStream_t stream);
-hipError_t launch_route_scan(int32_t* counts_w, int n_tiles, int E, int total,
-                             int32_t* offsets, hipStream_t stream);
+hipError_t launch_route_colscan(int32_t* counts_w, int n_tiles, int E, int32_t* tot, hipStream_t stream);
+// tot == nullptr: T == 0, offsets all zero
 hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* base_w,
-                                int T, int k, int E, int32_t* perm, int32_t* inv_perm,
-                                hipStream_t stream);
+                                const int32_t* tot, int T, int k, int E, int32_t* offsets, int32_t* perm,
+                                int32_t* inv_perm, hipStream_t stream);
 constexpr int kTopkTokensPerBlock = 16;   // tokens (= waves) per top-k block
 
 // Prefill expert FFN.

@@ -18,8 +18,9 @@
 //                    wave maximum over 64-bit order keys), weights, and a
 //                    wavefront-ballot histogram of the block's tokens with
 //                    each assignment's stable rank inside the block
-//   route_scan       per-expert prefix over blocks -> segment bases, offsets
-//   route_scatter    perm / inv_perm
+//   route_colscan    per expert (one block each): prefix of its counts over
+//                    the token tiles, and its total
+//   route_scatter    offsets from the totals (in every block), perm / inv_perm
 #include "launch.hpp"
 #include "device_math.hpp"
 
@@ -417,18 +418,19 @@ hipError_t launch_topk_hist(const float* partials, const RouterSplit& sp, const 
 }
 
 // ---------------------------------------------------------------- scan
-// counts_w [nt][E] (per block, per expert) -> in place: base of block b's
-// first assignment to expert e inside perm.  offsets [E+1].
-__global__ void __launch_bounds__(1024) route_scan_kernel(int32_t* __restrict__ counts_w, int nt,
-                                                          int E, int total,
-                                                          int32_t* __restrict__ offsets) {
-  __shared__ int32_t part[1024];
-  __shared__ int32_t tot[kMaxE + 1];
-  constexpr int CH = 16;                   // loads issued together
-  const int tpe = blockDim.x / E;          // threads per expert (>= 1)
-  const int e = threadIdx.x % E, g = threadIdx.x / E;
-  const int per = (nt + tpe - 1) / tpe;
-  const int b0 = g * per, b1 = min(nt, b0 + per);
+// Block e: the exclusive prefix of expert e's counts over the nt token tiles,
+// counts_w [nt][E] in place (tile b's first assignment to e is then
+// offsets[e] + counts_w[b][e] in perm), and the expert's total in tot[e].
+// One block per expert: the count matrix (512 KB at 8192 tokens and 256
+// experts) is read and rewritten by E blocks, not by one.  Thread i takes
+// tiles i*per .. (i+1)*per - 1, loads issued CH at a time.
+__global__ void __launch_bounds__(1024) route_colscan_kernel(int32_t* __restrict__ counts_w, int nt, int E,
+                                                             int32_t* __restrict__ tot) {
+  constexpr int CH = 16;
+  __shared__ int32_t wsum[16];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int per = (nt + blockDim.x - 1) / blockDim.x;
+  const int b0 = tid * per, b1 = min(nt, b0 + per);
   int run = 0;
   for (int b = b0; b < b1; b += CH) {
     int c[CH];
@@ -437,31 +439,25 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < CH; i++) run += c[i];
   }
-  part[threadIdx.x] = run;
-  __syncthreads();
-  // exclusive prefix of the groups of one expert; expert totals
-  int before = 0;
-  for (int q = 0; q < g; q++) before += part[q * E + e];
-  if (g == tpe - 1) tot[e] = before + run;
-  __syncthreads();
-  if (threadIdx.x < 64) {                  // exclusive scan of the E totals by one wave
-    int carry = 0;
-    for (int base = 0; base < E; base += 64) {
-      const int i = base + threadIdx.x;
-      const int v = (i < E) ? tot[i] : 0;
-      int incl = v;
+  // exclusive prefix of the thread sums: inside each wave, then over waves
+  int incl = run;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d, 64);
-        if ((int)threadIdx.x >= d) incl += o;
-      }
-      if (i < E) tot[i] = carry + incl - v;
-      carry += __shfl(incl, 63, 64);
-    }
-    if (threadIdx.x == 0) tot[E] = carry;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
   }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  int acc = tot[e] + before;
+  int before = incl - run;
+  const int nw = blockDim.x / 64;
+  int total = 0;
+  for (int w = 0; w < nw; w++) {
+    const int v = wsum[w];
+    if (w < wave) before += v;
+    total += v;
+  }
+  if (tid == 0) tot[e] = total;
+  int acc = before;
   for (int b = b0; b < b1; b += CH) {
     int c[CH];
 #pragma unroll
@@ -473,40 +469,76 @@ __global__ void __launch_bounds__(1024) route_scan_kernel(int32_t* __restrict__ 
         acc += c[i];
       }
   }
-  for (int i = threadIdx.x; i <= E; i += blockDim.x) offsets[i] = (i == E) ? total : tot[i];
 }
 
-hipError_t launch_route_scan(int32_t* counts_w, int n_tiles, int E, int total, int32_t* offsets,
-                             hipStream_t stream) {
-  const int threads = (1024 / E) * E;
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(threads), 0, stream, counts_w, n_tiles, E,
-                     total, offsets);
+hipError_t launch_route_colscan(int32_t* counts_w, int n_tiles, int E, int32_t* tot, hipStream_t stream) {
+  hipLaunchKernelGGL(route_colscan_kernel, dim3(E), dim3(1024), 0, stream, counts_w, n_tiles, E, tot);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- scatter
+// Every block first turns the E expert totals into segment offsets in LDS
+// (exclusive scan; block 0 also writes offsets [E+1]), then places its
+// assignments: perm[pos] = f, inv_perm[f] = pos with pos = offsets[e] +
+// (tile prefix of e) + (rank of f among the tile's assignments to e).
+// tot == nullptr: no assignments (T == 0), every offset 0.
 __global__ void __launch_bounds__(256) route_scatter_kernel(const int32_t* __restrict__ ids,
                                                             const int32_t* __restrict__ rank,
                                                             const int32_t* __restrict__ base_w,
-                                                            int T, int k, int E,
+                                                            const int32_t* __restrict__ tot, int T, int k, int E,
+                                                            int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ perm,
                                                             int32_t* __restrict__ inv_perm) {
-  const int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ int32_t off_l[kMaxE];
+  __shared__ int32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  // exclusive scan of tot: thread t takes experts 4t .. 4t+3
+  int v[4], run = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = 4 * tid + i;
+    v[i] = (tot && e < E) ? tot[e] : 0;
+    run += v[i];
+  }
+  int incl = run;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int acc = incl - run;
+  for (int w = 0; w < wave; w++) acc += wsum[w];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = 4 * tid + i;
+    if (e < E) {
+      off_l[e] = acc;
+      if (blockIdx.x == 0) offsets[e] = acc;
+    }
+    acc += v[i];
+  }
+  if (blockIdx.x == 0 && tid == 0) offsets[E] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  const int64_t f = (int64_t)blockIdx.x * blockDim.x + tid;
   if (f >= (int64_t)T * k) return;
   const int t = (int)(f / k);
   const int e = ids[f];
-  const int pos = base_w[(size_t)(t / kTopkTokensPerBlock) * E + e] + rank[f];
+  if (e < 0 || e >= E) return;            // unreachable for the ids the top-k writes
+  const int pos = off_l[e] + base_w[(size_t)(t / kTopkTokensPerBlock) * E + e] + rank[f];
   if (pos < 0 || (int64_t)pos >= (int64_t)T * k) return;   // unreachable for valid ranks
   perm[pos] = (int32_t)f;
   inv_perm[f] = pos;
 }
 
 hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const int32_t* base_w,
-                                int T, int k, int E, int32_t* perm, int32_t* inv_perm,
-                                hipStream_t stream) {
+                                const int32_t* tot, int T, int k, int E, int32_t* offsets, int32_t* perm,
+                                int32_t* inv_perm, hipStream_t stream) {
   const int64_t n = (int64_t)T * k;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream,
-                     ids, rank, base_w, T, k, E, perm, inv_perm);
+  const uint32_t blocks = n > 0 ? (uint32_t)((n + 255) / 256) : 1u;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(blocks), dim3(256), 0, stream, ids, rank, base_w, tot, T, k, E,
+                     offsets, perm, inv_perm);
   return hipGetLastError();
 }
 
