@@ -437,7 +437,8 @@ def bench_full_depth(args, torch, mq, moe_synth):
         "total_s": round(t_pre + cfg.steps * t_dec, 4),
         "resident_bytes": resident,
         "note": "prefill: route + fused grouped GEMM + combine + RMSNorm per layer, eager launches, "
-                "mean of 3 passes; decode: moe_q4_decode_stack, HIP graph of 32 steps replayed 8 times; "
+                "mean of 3 passes; decode: moe_q4_decode_stack (one persistent launch per token for the "
+                "40 layers), HIP graph of 32 steps replayed 8 times; "
                 "every step streams its 9 experts per layer from HBM (40 layers x 17 MB > the 256 MB "
                 "last-level cache)",
     }
@@ -548,8 +549,8 @@ def bench_stack(args, torch, mq, moe_synth, dec):
             "us_per_token_fused_norm": round(t_f * 1e6, 2), "us_per_token_chain": round(t_c * 1e6, 2),
             "us_per_layer_fused_norm": round(t_f * 1e6 / STACK_LAYERS, 3),
             "note": "one decode token through 40 layers of the decode layer's shape, graph replay: "
-                    "moe_q4_decode_stack (RMSNorm fused into each next layer, 3 launches per layer) vs "
-                    "moe_q4_decode + moe_q4_rmsnorm per layer (4 launches)"}
+                    "moe_q4_decode_stack (one persistent launch for the 40 layers, RMSNorm fused into "
+                    "each next layer) vs moe_q4_decode + moe_q4_rmsnorm per layer (2 launches per layer)"}
 
 
 def _graph_time(torch, calls, reps):
