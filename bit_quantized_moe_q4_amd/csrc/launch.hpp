@@ -96,7 +96,8 @@ hipError_t launch_prefill_w4a8(const W4A8PrefillArgs& a, int32_t* gate_dots, int
 // ceil(c / kPrefillTileRows) tiles) and an upper bound of the tile count.
 constexpr int kPrefillTileRows = 160;
 inline int64_t prefill_tile_bound(int64_t T, int k, int E, int has_shared) {
-  return T * k / kPrefillTileRows + E + (has_shared ? (T + kPrefillTileRows - 1) / kPrefillTileRows : 0);
+  // (+ 7: the shared expert's tile count is rounded up to a multiple of 8)
+  return T * k / kPrefillTileRows + E + (has_shared ? (T + kPrefillTileRows - 1) / kPrefillTileRows + 7 : 0);
 }
 
 // Decode.

@@ -34,7 +34,11 @@ __device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offset
   t.expert = -1;
   t.m0 = 0;
   int c = -1, q = 0;
-  const int n_sh = has_shared ? (T + FMAXR - 1) / FMAXR : 0;
+  // the shared expert's tiles, the largest units, come in a multiple of 8
+  // once there are 8 or more (balanced: tiles are dealt to the 8 XCDs by
+  // index, and 13 tiles at 2048 tokens gave five XCDs one heavy tile more)
+  int n_sh = has_shared ? (T + FMAXR - 1) / FMAXR : 0;
+  if (BAL && n_sh >= 8) n_sh = (n_sh + 7) / 8 * 8;
   if (mt < n_sh) {                        // (uniform per wave)
     c = T;
     q = mt;
