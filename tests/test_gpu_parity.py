@@ -316,6 +316,46 @@ def test_prefill_2k_sampled_generic_kernels(prefill_layer):
     assert rel <= PREFILL_TOL
 
 
+def _fused_vs_stages(gl, xbd):
+    """moe_q4_prefill (all stages in one call) against the stages run apart
+    (gate/up + down, then the combine)."""
+    T = xbd.shape[0]
+    r = mq.moe_q4_route(gl, xbd)
+    y_all = mq.moe_q4_prefill(gl, xbd, r)
+    ws = torch.empty(mq.moe_q4_prefill_workspace_bytes(gl, T), dtype=torch.uint8, device="cuda")
+    y_st = torch.empty_like(y_all)
+    S = mq._lib
+    mq.moe_q4_prefill_stage(gl, xbd, r, y_st, ws, S.STAGE_GATEUP | S.STAGE_DOWN)
+    mq.moe_q4_prefill_stage(gl, xbd, r, y_st, ws, S.STAGE_COMBINE)
+    return y_all, y_st
+
+
+def test_prefill_all_stages_match_stages_apart(prefill_layer):
+    # the same y bit for bit, whichever way the call is split
+    cfg, (ol, gl) = prefill_layer
+    x, bits, xw, xd, xbd = tokens(cfg, T=cfg.T, step=11)
+    y_all, y_st = _fused_vs_stages(gl, xbd)
+    assert torch.equal(y_all, y_st)
+
+
+@pytest.mark.parametrize("name,T,H,E,I,k,shared", [
+    ("no_shared", 300, 512, 16, 256, 4, False),
+    ("ragged_cols", 77, 192, 5, 64, 2, True),
+    ("k8_many_tiles", 700, 256, 64, 128, 8, True),
+])
+def test_prefill_all_stages_small(name, T, H, E, I, k, shared):
+    cfg = moe_synth.CONFIGS["tiny"].with_(name=name, H=H, E=E, I=I, k=k, shared=shared)
+    ol, gl = both_layers(cfg)
+    x, bits, xw, xd, xbd = tokens(cfg, T=T)
+    y_all, y_st = _fused_vs_stages(gl, xbd)
+    assert torch.equal(y_all, y_st)
+    # and against the binary64 reference
+    ref_route = oracle.route(ol, xw)
+    yref = oracle.prefill_ref(ol, xw, ref_route["ids"], ref_route["w64"], threads=8)
+    rel = np.linalg.norm(y_all.cpu().numpy().astype(np.float64) - yref) / np.linalg.norm(yref)
+    assert rel <= PREFILL_TOL, rel
+
+
 def test_prefill_2k_token_permutation_equivariance(prefill_layer):
     cfg, (ol, gl) = prefill_layer
     x, bits, xw, xd, xbd = tokens(cfg, T=512, step=5)
