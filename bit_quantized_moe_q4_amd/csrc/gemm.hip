@@ -435,20 +435,28 @@ __device__ __forceinline__ void g2_load_w(__amdgpu_buffer_rsrc_t r, uint32_t vn,
 
 #endif
 
-// 8 bf16 weights of element group Q of the lane's block: scale bits `sc`,
-// nibble dwords nib[0..3] (byte j of the 16 holds element j low, j+16 high).
+// 8 bf16 weights of element group Q of the lane's block: scale d, nibble
+// dwords nib[0..3] (byte j of the 16 holds element j low, j+16 high).
+// A byte holding one nibble q, read as an OCP fp8 e4m3 value, is exactly
+// q * 2^-9 (q < 8: the subnormals m * 2^-9; q >= 8: (8 + m) * 2^-9), so one
+// v_cvt_pk_f32_fp8 turns two nibbles into fp32 (a high nibble is shifted
+// down first).  Then (q - 8) * d = fma(q * 2^-9, d * 2^9, -8 d), exact in
+// fp32, rounded once to bf16: the same bits as a byte-by-byte conversion,
+// in 19 VALU instructions per 8 weights instead of 22.
 template <int Q>
 __device__ __forceinline__ bf16x8_t g2_deq(const uint32_t* nib, float d) {
   const float off = -8.0f * d;
-  const float mul = (Q >> 1) ? d * 0.0625f : d;
-  const uint32_t mask = (Q >> 1) ? 0xf0f0f0f0u : 0x0f0f0f0fu;
-  const uint32_t v0 = opaque_and(nib[2 * (Q & 1)], mask);
-  const uint32_t v1 = opaque_and(nib[2 * (Q & 1) + 1], mask);
+  const float mul = d * 512.0f;
+  const uint32_t w0 = nib[2 * (Q & 1)], w1 = nib[2 * (Q & 1) + 1];
+  const uint32_t v0 = ((Q >> 1) ? (w0 >> 4) : w0) & 0x0f0f0f0fu;
+  const uint32_t v1 = ((Q >> 1) ? (w1 >> 4) : w1) & 0x0f0f0f0fu;
+  const f32x2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8((int)v0, false), __builtin_amdgcn_cvt_pk_f32_fp8((int)v0, true),
+                        __builtin_amdgcn_cvt_pk_f32_fp8((int)v1, false), __builtin_amdgcn_cvt_pk_f32_fp8((int)v1, true)};
   float f[8];
 #pragma unroll
   for (int b = 0; b < 4; b++) {
-    f[b] = __builtin_fmaf((float)((v0 >> (8 * b)) & 0xffu), mul, off);
-    f[4 + b] = __builtin_fmaf((float)((v1 >> (8 * b)) & 0xffu), mul, off);
+    f[2 * b] = __builtin_fmaf(p[b].x, mul, off);
+    f[2 * b + 1] = __builtin_fmaf(p[b].y, mul, off);
   }
   uint32_t w[4];
 #pragma unroll
@@ -463,7 +471,7 @@ __device__ __forceinline__ void g2_interleave() {
 #pragma unroll
   for (int j = 0; j < 2 * MS; j++) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, (44 + 2 * MS - 1) / (2 * MS), 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x002, (40 + 2 * MS - 1) / (2 * MS), 0);  // VALU
     if (j & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // DS read
   }
 }
