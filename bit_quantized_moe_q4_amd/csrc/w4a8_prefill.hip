@@ -27,16 +27,21 @@
 //
 // Kernels (all on the caller's stream):
 //   q8x   x bf16 [T][H] -> codes [T][H] int8, scales [T][H/32] fp32
-//   gate/up   unit = (tile of <= 128 rows of one expert segment, 32 columns
-//         of I); wave w of 4: rows 32w .. 32w+31, gate and up of the 32
-//         columns (a wave past the tile's rows idles);
+//   gate/up   unit = one wave: (tile of <= 32 rows of one expert segment,
+//         32 columns of I), gate and up of the 32 columns;
 //         h = silu(g) * u and its q8 (the unit holds whole 32-groups of I)
-//   down  unit = (tile, 64 columns of H); wave w: rows 32w .. +31, two
-//         groups of 32 columns; routed rows -> bf16 expert outputs in segment
-//         order, the shared expert -> y
+//   down  unit = one wave: (tile, 64 columns of H), two groups of 32
+//         columns; routed rows -> bf16 expert outputs in segment order, the
+//         shared expert -> y
 //   combine  (gemm.hip) y[t] += sum_s w[t,s] * O[inv_perm[t*k+s]]
-// A tile's column blocks run on one XCD (blocks are dealt to the 8 XCDs round
-// robin), so its activation rows are fetched into that XCD's L2 once.
+// Tiles are greedy 32-row groups of a segment (an expert of c rows costs
+// ceil(c/32) units per column block, no idle rows past the last group).
+// Blocks are dealt to the 8 XCDs round robin; each aligned group of four
+// consecutive tiles (mostly one expert's rows) runs on one XCD with all its
+// column blocks, so the expert's weight columns and the tiles' activation
+// rows are fetched into that XCD's L2 once.  One-wave units schedule finer
+// than the four-wave units of 128-row tiles that came before (342 -> 405
+// TOPS for gate/up + down at 2048 tokens, same bits).
 #include "launch.hpp"
 #include "device_math.hpp"
 #include "tiles.hpp"
@@ -46,10 +51,21 @@ namespace moeq4 {
 typedef int w8v4 __attribute__((ext_vector_type(4)));
 typedef int w8v16 __attribute__((ext_vector_type(16)));
 
-constexpr int kW8Rows = 128;           // rows per tile (4 waves x 32), greedy tiles
-constexpr int kW8Waves = kW8Rows / 32;
-constexpr int kW8Threads = 64 * kW8Waves;
+constexpr int kW8Rows = 32;            // rows per tile, greedy tiles
+constexpr int kW8Threads = 64;         // one wave per unit
+constexpr int kW8Group = 4;            // consecutive tiles dealt to one XCD
+constexpr int kW8WavesPerSimd = 4;     // occupancy asked of the compiler: at most 128 VGPRs
 constexpr int kW8DnCols = 64;          // columns of H per down unit
+static_assert(kW8Threads == 2 * kW8Rows, "the scale staging takes two threads per tile row");
+
+// Block b -> (tile, column block cb) out of ncb: tiles 8G*m + G*x .. + G-1
+// (G = kW8Group) run on XCD slot x = b % 8, the G tiles of a column block
+// next to each other in dispatch order.
+__device__ __forceinline__ void w8_unit(int b, int ncb, int& tile, int& cb) {
+  const int x = b % 8, q = b / 8;
+  tile = 8 * kW8Group * (q / (kW8Group * ncb)) + kW8Group * x + q % kW8Group;
+  cb = (q / kW8Group) % ncb;
+}
 
 // ---------------------------------------------------------------- q8 of x
 // 8 threads per 32-block, 4 elements each: d = amax / 127, q = round(x / d)
@@ -113,21 +129,20 @@ __device__ __forceinline__ void w8_accumulate(float (&acc)[16], const w8v16& dot
 }
 
 // ---------------------------------------------------------------- gate/up
-// LDS: activation scales of the tile's rows [nb][kW8Rows], the wave's q8(h)
-// codes [waves][32][32] for the coalesced store, the tile rows' tokens.
+// LDS: activation scales of the tile's rows [nb][kW8Rows], the q8(h) codes
+// [32][32] for the coalesced store, the tile rows' tokens.
 template <bool DOTS>
-__global__ void __launch_bounds__(kW8Threads, 2) w8_gateup_kernel(W4A8PrefillArgs a, int32_t* __restrict__ gate_dots) {
+__global__ void __launch_bounds__(kW8Threads) __attribute__((amdgpu_waves_per_eu(DOTS ? 1 : kW8WavesPerSimd))) w8_gateup_kernel(W4A8PrefillArgs a, int32_t* __restrict__ gate_dots) {
   extern __shared__ __align__(16) uint8_t dyn[];
   const int H = a.H, I = a.I, nb = H / BLK, nsteps = H / 64, ncb = I / 32;
   float* da_l = reinterpret_cast<float*>(dyn);                              // [nb][kW8Rows]
-  uint8_t* qo_l = dyn + (size_t)nb * kW8Rows * 4;                           // [waves][32][32]
-  int* tok_l = reinterpret_cast<int*>(qo_l + 1024 * kW8Waves);              // [kW8Rows]
-  const int b = blockIdx.x, qq = b / 8;
-  const int tile = 8 * (qq / ncb) + b % 8, cb = qq % ncb;
+  uint8_t* qo_l = dyn + (size_t)nb * kW8Rows * 4;                           // [32][32]
+  int* tok_l = reinterpret_cast<int*>(qo_l + 1024);                         // [kW8Rows]
+  int tile, cb;
+  w8_unit(blockIdx.x, ncb, tile, cb);
   const Tile t = find_tile_bal<kW8Rows, false>(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
   if (!t.valid) return;
   const int tid = threadIdx.x, lane = tid % 64;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   // token of each tile row (rows past the tile repeat its first row)
   if (tid < kW8Rows) {
     const int r = tid < t.rows ? tid : 0;
@@ -135,7 +150,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_gateup_kernel(W4A8PrefillArg
   }
   __syncthreads();
   {                                                          // da_l[bb][row], 4 independent loads per round
-    const int row = tid % kW8Rows, b0 = tid / kW8Rows;       // (2 x kW8Rows threads: 2 blocks per round)
+    const int row = tid % kW8Rows, b0 = tid / kW8Rows;       // (two threads per row: 2 blocks per round)
     const float* src = a.dx + (size_t)tok_l[row] * nb;
     for (int bb = b0; bb < nb; bb += 8) {
       float v[4];
@@ -147,8 +162,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_gateup_kernel(W4A8PrefillArg
     }
   }
   const int n = lane % 32, h = lane / 32, shl = 4 * (1 - h);
-  const int row_a = 32 * wave + n;                          // the lane's A row (token)
-  const int8_t* arow = a.qx + (size_t)tok_l[row_a] * H + 16 * h;
+  const int8_t* arow = a.qx + (size_t)tok_l[n] * H + 16 * h;   // the lane's A row (token)
   const size_t gbytes = (size_t)nsteps * 1152;              // one 32-row group of a matrix
   const uint8_t* gw = (t.expert >= 0 ? a.t_gate + ((size_t)t.expert * ncb + cb) * gbytes : a.ts_gate + cb * gbytes);
   const uint8_t* uw = (t.expert >= 0 ? a.t_up + ((size_t)t.expert * ncb + cb) * gbytes : a.ts_up + cb * gbytes);
@@ -157,10 +171,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_gateup_kernel(W4A8PrefillArg
 #pragma unroll
   for (int r = 0; r < 16; r++) accg[r] = accu[r] = 0.0f;
   const w8v16 zero = {};
-  const float* da_w = da_l + 32 * wave + 4 * h;             // + bb * kW8Rows + 8 q
-  // a wave whose 32 rows all lie past the tile computes nothing (it still
-  // takes part in the barriers)
-  const int nsteps_w = __builtin_amdgcn_readfirstlane((32 * wave < t.rows) ? nsteps : 0);
+  const float* da_w = da_l + 4 * h;                         // + bb * kW8Rows + 8 q
   // operands of a step (blocks 2s, 2s+1), one step ahead in registers
   auto load = [&](int s, uint4 (&A)[2], uint4 (&G)[2], uint4 (&U)[2], uint32_t (&sg)[2], uint32_t (&su)[2]) {
     const uint8_t* gp = gw + (size_t)s * 1152;
@@ -191,7 +202,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_gateup_kernel(W4A8PrefillArg
       if (DOTS) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          const int row = 32 * wave + 8 * (r / 4) + 4 * h + (r % 4);
+          const int row = 8 * (r / 4) + 4 * h + (r % 4);
           if (row < t.rows)
             gate_dots[((size_t)(t.pos0 + row) * I + 32 * cb + n) * nb + bb] = dg[r] >> 4;
         }
@@ -203,7 +214,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_gateup_kernel(W4A8PrefillArg
   uint4 A[2], G[2], U[2];
   uint32_t sg[2], su[2];
   load(0, A, G, U, sg, su);
-  for (int s = 0; s < nsteps_w; s++) {
+  for (int s = 0; s < nsteps; s++) {
     uint4 An[2], Gn[2], Un[2];
     uint32_t sgn[2], sun[2];
     load(min(s + 1, nsteps - 1), An, Gn, Un, sgn, sun);
@@ -216,7 +227,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_gateup_kernel(W4A8PrefillArg
   // h = silu(g) * u, then q8 of each row's 32 values (lanes of one half hold
   // a row's 32 columns): amax by a butterfly over the half, d = amax / 127,
   // q = round(h / d)
-  uint8_t* qw = qo_l + 1024 * wave;
+  uint8_t* qw = qo_l;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const float g = accg[r], u = accu[r];
@@ -226,32 +237,30 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_gateup_kernel(W4A8PrefillArg
     for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
     const float d = amax / 127.0f;
     const int qv = (d == 0.0f) ? 0 : (int)roundf(hv / d);
-    const int rw = 8 * (r / 4) + 4 * h + (r % 4);           // the row inside the wave's 32
-    qw[32 * rw + n] = (uint8_t)qv;
-    const int row = 32 * wave + rw;
+    const int row = 8 * (r / 4) + 4 * h + (r % 4);          // the row inside the tile
+    qw[32 * row + n] = (uint8_t)qv;
     if (n == 0 && row < t.rows) a.dh[(size_t)(t.pos0 + row) * ncb + cb] = d;
   }
   __syncthreads();
   {                                                          // 32 rows x 32 bytes: 16 bytes per lane
-    const int rw = lane / 2, row = 32 * wave + rw;
+    const int row = lane / 2;
     if (row < t.rows)
       *reinterpret_cast<uint4*>(a.qh + (size_t)(t.pos0 + row) * I + 32 * cb + 16 * (lane % 2)) =
-          *reinterpret_cast<const uint4*>(qw + 32 * rw + 16 * (lane % 2));
+          *reinterpret_cast<const uint4*>(qw + 32 * row + 16 * (lane % 2));
   }
 }
 
 // ---------------------------------------------------------------- down
 // LDS: q8(h) scales of the tile's rows [I/32][kW8Rows].
-__global__ void __launch_bounds__(kW8Threads, 2) w8_down_kernel(W4A8PrefillArgs a) {
+__global__ void __launch_bounds__(kW8Threads) __attribute__((amdgpu_waves_per_eu(kW8WavesPerSimd))) w8_down_kernel(W4A8PrefillArgs a) {
   extern __shared__ __align__(16) uint8_t dyn[];
   const int H = a.H, I = a.I, nb = I / BLK, nsteps = I / 64, ncb = H / kW8DnCols;
   float* da_l = reinterpret_cast<float*>(dyn);                              // [nb][kW8Rows]
-  const int b = blockIdx.x, qq = b / 8;
-  const int tile = 8 * (qq / ncb) + b % 8, cb = qq % ncb;
+  int tile, cb;
+  w8_unit(blockIdx.x, ncb, tile, cb);
   const Tile t = find_tile_bal<kW8Rows, false>(a.offsets, a.E, a.T, a.k, a.has_shared, tile);
   if (!t.valid) return;
   const int tid = threadIdx.x, lane = tid % 64;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   {                                                          // da_l[bb][row], 4 independent loads per round
     const int row = tid % kW8Rows, b0 = tid / kW8Rows;
     const float* src = a.dh + (size_t)(t.pos0 + (row < t.rows ? row : 0)) * nb;
@@ -265,8 +274,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_down_kernel(W4A8PrefillArgs 
     }
   }
   const int n = lane % 32, h = lane / 32, shl = 4 * (1 - h);
-  const int row_a = 32 * wave + n;
-  const int8_t* arow = a.qh + (size_t)(t.pos0 + (row_a < t.rows ? row_a : 0)) * I + 16 * h;
+  const int8_t* arow = a.qh + (size_t)(t.pos0 + (n < t.rows ? n : 0)) * I + 16 * h;   // the lane's A row
   const size_t gbytes = (size_t)nsteps * 1152;
   const int G0 = 2 * cb;                                     // the unit's two 32-column groups of H
   const uint8_t* w0 = (t.expert >= 0 ? a.t_down + ((size_t)t.expert * (H / 32) + G0) * gbytes : a.ts_down + G0 * gbytes);
@@ -276,9 +284,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_down_kernel(W4A8PrefillArgs 
 #pragma unroll
   for (int r = 0; r < 16; r++) acc0[r] = acc1[r] = 0.0f;
   const w8v16 zero = {};
-  const float* da_w = da_l + 32 * wave + 4 * h;
-  // (waves past the tile compute nothing)
-  const int nsteps_w = __builtin_amdgcn_readfirstlane((32 * wave < t.rows) ? nsteps : 0);
+  const float* da_w = da_l + 4 * h;
   auto load = [&](int s, uint4 (&A)[2], uint4 (&B0)[2], uint4 (&B1)[2], uint32_t (&s0)[2], uint32_t (&s1)[2]) {
     const uint8_t* p0 = w0 + (size_t)s * 1152;
     const uint8_t* p1 = w1 + (size_t)s * 1152;
@@ -309,7 +315,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_down_kernel(W4A8PrefillArgs 
   uint4 A[2], B0[2], B1[2];
   uint32_t s0[2], s1[2];
   load(0, A, B0, B1, s0, s1);
-  for (int s = 0; s < nsteps_w; s++) {
+  for (int s = 0; s < nsteps; s++) {
     uint4 An[2], B0n[2], B1n[2];
     uint32_t s0n[2], s1n[2];
     load(min(s + 1, nsteps - 1), An, B0n, B1n, s0n, s1n);
@@ -322,7 +328,7 @@ __global__ void __launch_bounds__(kW8Threads, 2) w8_down_kernel(W4A8PrefillArgs 
   const int c0 = kW8DnCols * cb + n, c1 = c0 + 32;
 #pragma unroll
   for (int r = 0; r < 16; r++) {
-    const int row = 32 * wave + 8 * (r / 4) + 4 * h + (r % 4);
+    const int row = 8 * (r / 4) + 4 * h + (r % 4);
     if (row >= t.rows) continue;
     if (t.expert >= 0) {
       a.o_perm[(size_t)(t.pos0 + row) * H + c0] = f32_to_bf16_bits(acc0[r]);
@@ -341,7 +347,8 @@ int64_t w4a8_prefill_tile_bound(int64_t T, int k, int E, int has_shared) {
 }
 
 hipError_t launch_prefill_w4a8(const W4A8PrefillArgs& a, int32_t* gate_dots, int stages, hipStream_t stream) {
-  const int groups = (int)((w4a8_prefill_tile_bound(a.T, a.k, a.E, a.has_shared) + 7) / 8);
+  // w8_unit covers tiles [0, 8 * kW8Group * supers)
+  const int supers = (int)((w4a8_prefill_tile_bound(a.T, a.k, a.E, a.has_shared) + 8 * kW8Group - 1) / (8 * kW8Group));
   const int ncb_gu = a.I / 32, ncb_dn = a.H / kW8DnCols;
   hipError_t err = hipSuccess;
   if (stages & 1) {                      // q8(x), then gate/up + SwiGLU + q8(h)
@@ -350,17 +357,17 @@ hipError_t launch_prefill_w4a8(const W4A8PrefillArgs& a, int32_t* gate_dots, int
                        a.qx, a.dx);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t lds_gu = (size_t)(a.H / BLK) * kW8Rows * 4 + 1024 * kW8Waves + kW8Rows * 4;
+    const size_t lds_gu = (size_t)(a.H / BLK) * kW8Rows * 4 + 1024 + kW8Rows * 4;
     if (gate_dots)
-      hipLaunchKernelGGL(w8_gateup_kernel<true>, dim3(groups * 8 * ncb_gu), dim3(kW8Threads), lds_gu, stream, a, gate_dots);
+      hipLaunchKernelGGL(w8_gateup_kernel<true>, dim3(supers * 8 * kW8Group * ncb_gu), dim3(kW8Threads), lds_gu, stream, a, gate_dots);
     else
-      hipLaunchKernelGGL(w8_gateup_kernel<false>, dim3(groups * 8 * ncb_gu), dim3(kW8Threads), lds_gu, stream, a, gate_dots);
+      hipLaunchKernelGGL(w8_gateup_kernel<false>, dim3(supers * 8 * kW8Group * ncb_gu), dim3(kW8Threads), lds_gu, stream, a, gate_dots);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (stages & 2) {
     const size_t lds_dn = (size_t)(a.I / BLK) * kW8Rows * 4;
-    hipLaunchKernelGGL(w8_down_kernel, dim3(groups * 8 * ncb_dn), dim3(kW8Threads), lds_dn, stream, a);
+    hipLaunchKernelGGL(w8_down_kernel, dim3(supers * 8 * kW8Group * ncb_dn), dim3(kW8Threads), lds_dn, stream, a);
     err = hipGetLastError();
   }
   return err;
