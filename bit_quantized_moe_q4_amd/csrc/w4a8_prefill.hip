@@ -36,12 +36,13 @@
 //   combine  (gemm.hip) y[t] += sum_s w[t,s] * O[inv_perm[t*k+s]]
 // Tiles are greedy 32-row groups of a segment (an expert of c rows costs
 // ceil(c/32) units per column block, no idle rows past the last group).
-// Blocks are dealt to the 8 XCDs round robin; each aligned group of four
-// consecutive tiles (mostly one expert's rows) runs on one XCD with all its
-// column blocks, so the expert's weight columns and the tiles' activation
-// rows are fetched into that XCD's L2 once.  One-wave units schedule finer
-// than the four-wave units of 128-row tiles that came before (342 -> 405
-// TOPS for gate/up + down at 2048 tokens, same bits).
+// Blocks are dealt to the 8 XCDs round robin; each aligned group of eight
+// consecutive tiles runs on one XCD with all its column blocks, so an
+// expert's weight columns are mostly fetched into one XCD's L2 (groups of
+// four split most ~128-row experts over two XCDs: 1.2x the HBM reads at the
+// same speed).  One-wave units schedule finer than the four-wave units of
+// 128-row tiles that came before (342 -> 405 TOPS for gate/up + down at 2048
+// tokens, same bits).
 #include "launch.hpp"
 #include "device_math.hpp"
 #include "tiles.hpp"
@@ -53,7 +54,7 @@ typedef int w8v16 __attribute__((ext_vector_type(16)));
 
 constexpr int kW8Rows = 32;            // rows per tile, greedy tiles
 constexpr int kW8Threads = 64;         // one wave per unit
-constexpr int kW8Group = 4;            // consecutive tiles dealt to one XCD
+constexpr int kW8Group = 8;            // consecutive tiles dealt to one XCD
 constexpr int kW8WavesPerSimd = 4;     // occupancy asked of the compiler: at most 128 VGPRs
 constexpr int kW8DnCols = 64;          // columns of H per down unit
 static_assert(kW8Threads == 2 * kW8Rows, "the scale staging takes two threads per tile row");
