@@ -87,6 +87,9 @@ def _declare(lib):
         "orc_topk": (None, [P, I64, I64, I32, P, P, P]),
         "orc_route_permutation": (None, [P, I64, I32, I64, P, P, P, P]),
         "orc_prefill_ref": (None, [P, P, P, P, P, I64, P]),
+        "orc_bf16_round": (F, [F]),
+        "orc_bf16_round_n": (None, [P, I64, P]),
+        "orc_prefill_bf16": (None, [P, P, P, P, P, I64, P]),
         "orc_w4a8_gemv": (None, [P, I64, I64, P, P, P, P]),
         "orc_decode": (None, [P, P, P, P]),
         "orc_rmsnorm": (None, [P, I64, I64, F, P]),
@@ -366,6 +369,43 @@ def prefill_ref(layer: PackedLayer, x, ids, w64, tokens=None, lib=None, threads:
     def run(lo, hi):
         if hi > lo:
             lib.orc_prefill_ref(C.byref(L), _p(x), _p(ids), _p(w64), _p(tok[lo:hi]), hi - lo, _p(y[lo:hi]))
+    if threads <= 1 or n < 2 * threads:
+        run(0, n)
+        return y
+    step = (n + threads - 1) // threads
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda i: run(i, min(i + step, n)), range(0, n, step)))
+    return y
+
+
+def bf16_round(x, lib=None) -> np.ndarray:
+    """``orc_bf16_round`` of each element: the nearest bfloat16 (ties to
+    even), widened back to float32."""
+    lib = lib or load()
+    x = _c(np.atleast_1d(x), np.float32)
+    out = np.empty_like(x)
+    lib.orc_bf16_round_n(_p(x), x.size, _p(out))
+    return out
+
+
+def prefill_bf16(layer: PackedLayer, x, ids, w32, tokens=None, lib=None, threads: int = 1) -> np.ndarray:
+    """``orc_prefill_bf16``: the bf16 prefill program for the listed tokens ->
+    [n, H] float32 (x: bf16 values widened to float32; w32: the float32
+    routing weights).  ``threads`` as in ``prefill_ref``."""
+    assert layer.wfmt == Q4_0, "the prefill program is defined for Q4_0 layers"
+    lib = lib or load()
+    x = _c(x, np.float32)
+    ids = _c(ids, np.int32)
+    w32 = _c(w32, np.float32)
+    T = x.shape[0]
+    tok = np.arange(T, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    n = tok.size
+    y = np.empty((n, layer.H), dtype=np.float32)
+    L = layer.cstruct()
+
+    def run(lo, hi):
+        if hi > lo:
+            lib.orc_prefill_bf16(C.byref(L), _p(x), _p(ids), _p(w32), _p(tok[lo:hi]), hi - lo, _p(y[lo:hi]))
     if threads <= 1 or n < 2 * threads:
         run(0, n)
         return y

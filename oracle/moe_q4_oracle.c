@@ -42,6 +42,10 @@
  *     the activations) both the oracle and the GPU evaluate the same fp32
  *     program, defined here: see tree_sum(), router_logit(), exp_p(),
  *     w4a8_row(), rmsnorm_row().
+ *   - The prefill's float path has two statements here: the exact layer in
+ *     binary64 (orc_prefill_ref), and the library's rounding points of the
+ *     grouped GEMM -- weights, h and routed outputs in bf16, the float32
+ *     combine in slot order -- with sums in binary64 (orc_prefill_bf16).
  *
  * Every function works on host memory owned by the caller; no allocation
  * survives a call.
@@ -509,6 +513,106 @@ void orc_prefill_ref(const orc_layer *L, const float *x, const int32_t *ids,
         if (L->has_shared) {
             expert_ffn_f64(L->s_gate, L->s_up, L->s_down, H, I, xd, hb, o);
             for (int64_t h = 0; h < H; h++) yt[h] += o[h];
+        }
+    }
+    free(xd); free(hb); free(o);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The bf16 prefill program [FERMI Methodology 1: grouped 4-bit GEMM]         */
+/* ------------------------------------------------------------------------ */
+
+/* binary32 -> nearest bfloat16 (the top 16 bits of a binary32; ties to even),
+ * returned widened back to binary32.  Infinities, zeros and subnormals follow
+ * the same bit rule; a NaN stays a (quiet) NaN. */
+float orc_bf16_round(float f)
+{
+    uint32_t u = f32_bits(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+        return bits_f32((u | 0x00400000u) & 0xffff0000u);
+    uint32_t base = u & 0xffff0000u, rem = u & 0x0000ffffu;
+    if (rem > 0x8000u || (rem == 0x8000u && (base & 0x00010000u)))
+        base += 0x00010000u;               /* a carry into the exponent is the next binade */
+    return bits_f32(base);
+}
+
+void orc_bf16_round_n(const float *x, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = orc_bf16_round(x[i]);
+}
+
+/* binary64 dot of one Q4 row, each weight (q - 8) * d (exact in binary32)
+ * rounded once to bf16, with a binary64 vector. */
+static double q4_row_dot_bf16w(const uint8_t *row, int64_t K, const double *v)
+{
+    double acc = 0.0;
+    for (int64_t b = 0; b < K / ORC_BLK; b++) {
+        const uint8_t *blk = row + b * ORC_Q4_BYTES;
+        float d = q4_scale(blk);
+        for (int j = 0; j < ORC_BLK; j++) {
+            float w = orc_bf16_round((float)(q4_code(blk, j) - 8) * d);
+            acc += (double)w * v[b * ORC_BLK + j];
+        }
+    }
+    return acc;
+}
+
+/* One SwiGLU expert of the bf16 program: gate and up over bf16 weights,
+ * h = bf16(silu(g) * u), o = down over bf16 weights and h, rounded to
+ * binary32 and, for a routed expert (round_o), on to bf16. */
+static void expert_ffn_bf16(const uint8_t *g, const uint8_t *u, const uint8_t *dn,
+                            int64_t H, int64_t I, const double *x, double *hbuf,
+                            float *o, int round_o)
+{
+    size_t rg = orc_q4_row_bytes(H), rd = orc_q4_row_bytes(I);
+    for (int64_t i = 0; i < I; i++) {
+        double gi = q4_row_dot_bf16w(g + i * rg, H, x);
+        double ui = q4_row_dot_bf16w(u + i * rg, H, x);
+        hbuf[i] = (double)orc_bf16_round((float)(gi / (1.0 + exp(-gi)) * ui));
+    }
+    for (int64_t r = 0; r < H; r++) {
+        float v = (float)q4_row_dot_bf16w(dn + r * rd, I, hbuf);
+        o[r] = round_o ? orc_bf16_round(v) : v;
+    }
+}
+
+/* The library's bf16 prefill program (the rounding points of the grouped
+ * GEMM; the pages give the GEMM and no precision).  For each listed token t,
+ * x_t already bf16 (widened): every weight is (q - 8) * d rounded once to
+ * bf16; gate, up and down sums are exact-ish (binary64 here, any order on
+ * the GPU); h = bf16(silu(g) * u); a routed expert's output is rounded to
+ * bf16, the shared expert's to binary32; then, in binary32 and in this order,
+ *   y_t = (((o_shared + w[t,0] * o_0) + w[t,1] * o_1) + ...)
+ * with w the binary32 routing weights (o_shared = 0 without a shared expert).
+ * x: [T][H]; ids, w32: [T][k]; tokens: indices into x (NULL: 0..n_tok-1);
+ * y: [n_tok][H] binary32. */
+void orc_prefill_bf16(const orc_layer *L, const float *x, const int32_t *ids,
+                      const float *w32, const int64_t *tokens, int64_t n_tok,
+                      float *y)
+{
+    int64_t H = L->H, I = L->I;
+    double *xd = (double *)malloc((size_t)H * sizeof(double));
+    double *hb = (double *)malloc((size_t)I * sizeof(double));
+    float *o = (float *)malloc((size_t)H * sizeof(float));
+    for (int64_t n = 0; n < n_tok; n++) {
+        int64_t t = tokens ? tokens[n] : n;
+        float *yt = y + n * H;
+        for (int64_t h = 0; h < H; h++) xd[h] = (double)x[t * H + h];
+        if (L->has_shared) {
+            expert_ffn_bf16(L->s_gate, L->s_up, L->s_down, H, I, xd, hb, o, 0);
+            for (int64_t h = 0; h < H; h++) yt[h] = o[h];
+        } else {
+            for (int64_t h = 0; h < H; h++) yt[h] = 0.0f;
+        }
+        for (int32_t s = 0; s < L->k; s++) {
+            int64_t e = ids[t * L->k + s];
+            float ws = w32[t * L->k + s];
+            expert_ffn_bf16(expert_mat(L->gate, e, I, H), expert_mat(L->up, e, I, H),
+                            expert_mat(L->down, e, H, I), H, I, xd, hb, o, 1);
+            for (int64_t h = 0; h < H; h++) {
+                float p = ws * o[h];
+                yt[h] = yt[h] + p;
+            }
         }
     }
     free(xd); free(hb); free(o);

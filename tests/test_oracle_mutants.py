@@ -17,7 +17,8 @@ import oracle
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-PINS = ["test_oracle_formats.py", "test_oracle_routing.py", "test_oracle_layer.py"]
+PINS = ["test_oracle_formats.py", "test_oracle_routing.py", "test_oracle_layer.py",
+        "test_oracle_prefill_bf16.py"]
 
 # (name, exact text in moe_q4_oracle.c, replacement)
 MUTANTS = [
@@ -65,6 +66,17 @@ MUTANTS = [
      "return w4a8_row(row, K, qa, da, NULL, buf);"),
     ("rmsnorm_mean_h_minus_1", "float r = sqrtf(ss / (float)H + eps);",
      "float r = sqrtf(ss / (float)(H - 1) + eps);"),
+    ("bf16_ties_away", "if (rem > 0x8000u || (rem == 0x8000u && (base & 0x00010000u)))",
+     "if (rem >= 0x8000u)"),
+    ("prefill_bf16_w_unrounded", "float w = orc_bf16_round((float)(q4_code(blk, j) - 8) * d);",
+     "float w = (float)(q4_code(blk, j) - 8) * d;"),
+    ("prefill_bf16_h_unrounded", "hbuf[i] = (double)orc_bf16_round((float)(gi / (1.0 + exp(-gi)) * ui));",
+     "hbuf[i] = gi / (1.0 + exp(-gi)) * ui;"),
+    ("prefill_bf16_o_unrounded", "o[r] = round_o ? orc_bf16_round(v) : v;", "o[r] = v;"),
+    ("prefill_bf16_shared_rounded", "expert_ffn_bf16(L->s_gate, L->s_up, L->s_down, H, I, xd, hb, o, 0);",
+     "expert_ffn_bf16(L->s_gate, L->s_up, L->s_down, H, I, xd, hb, o, 1);"),
+    ("prefill_bf16_combine_in_double", "float p = ws * o[h];\n                yt[h] = yt[h] + p;",
+     "yt[h] = (float)((double)yt[h] + (double)ws * (double)o[h]);"),
 ]
 
 
