@@ -156,6 +156,35 @@ def hbm_copy_gbps(torch, nbytes=1 << 30, reps=5):
     return 2.0 * nbytes / ts[len(ts) // 2] / 1e9
 
 
+def mfma_probe(torch, mq, blocks=512, iters=12000, reps=5):
+    """Matrix-core rates this GPU sustains (moe_q4_probe_mfma): independent
+    MFMA chains on register operands, 2 waves per SIMD like the grouped GEMM;
+    each shape's launch timed with events on the launch stream, median of
+    `reps` after one warm launch."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for kind, key in ((mq.PROBE_BF16, "bf16_32x32x16_tflops"), (mq.PROBE_I8, "i8_32x32x32_tops"),
+                      (mq.PROBE_F32_K1, "f32_32x32x1_tflops")):
+        ops = mq.moe_q4_probe_mfma(kind, blocks, iters, out)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            mq.moe_q4_probe_mfma(kind, blocks, iters, out)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        ts.sort()
+        res[key] = round(ops / ts[len(ts) // 2] / 1e12, 1)
+    assert torch.isfinite(out).all().item()
+    res["blocks"] = blocks
+    res["waves_per_simd"] = blocks * 4 // 1024
+    res["note"] = ("what the matrix cores sustain for each MFMA shape the kernels issue (no memory "
+                   "traffic); the published peaks are 2500 (bf16), 5000 (int8) and 157.3 (fp32)")
+    return res
+
+
 def copy_probe(torch):
     """One plain device-to-device copy of COPY_PROBE_BYTES (counter calibration)."""
     a = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -757,6 +786,7 @@ def main():
     ap.add_argument("--no-w4a8-prefill", action="store_true", help="skip the W4A8-form prefill leg")
     ap.add_argument("--no-skew", action="store_true", help="skip the 10240-token skewed prefill leg")
     ap.add_argument("--no-full-depth", action="store_true", help="skip the 40-layer full-depth leg")
+    ap.add_argument("--no-mfma-probe", action="store_true", help="skip the matrix-core rate probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with one 1 GiB device copy (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -800,6 +830,7 @@ def main():
     torch.cuda.empty_cache()
     w8gemm = None if args.no_w4a8_gemm else bench_w4a8_gemm(args, torch, mq)
     copy_gbps = hbm_copy_gbps(torch)
+    probe = None if args.no_mfma_probe else mfma_probe(torch, mq)
     w8 = None if args.no_w4a8_prefill else bench_prefill_w4a8(args, torch, mq, pre)
     pre = bench_prefill(args, torch, mq, pre)
     for k_ in ("xb", "y", "routing", "rws", "pws"):
@@ -842,6 +873,8 @@ def main():
             "traffic_over_algorithmic": None if _traffic("gemm") is None else round(_traffic("gemm") / alg_gemm, 3),
             "flop_per_launch": fl_gemm,
             "avg_launch_us": round(pre["t_gemm"] * 1e6, 2),
+            "achievable": None if probe is None else probe["bf16_32x32x16_tflops"],
+            "frac_of_achievable": None if probe is None else round(ach / probe["bf16_32x32x16_tflops"], 4),
             "timing": "%d back-to-back fused GEMM calls (counter fill + gemm_ffn_kernel) between two "
                       "events on the launch stream" % args.steps,
         },
@@ -892,11 +925,13 @@ def main():
                          "bound": "mfma", "achieved": round(ops8 / t8 / 1e12, 2), "peak": PEAK_INT8_TOPS,
                          "unit": "TOPS", "frac": round(ops8 / t8 / 1e12 / PEAK_INT8_TOPS, 4),
                          "ops_per_step": ops8, "traffic": tr8, "algorithmic_bytes": alg8,
+                         "achievable": None if probe is None else probe["i8_32x32x32_tops"],
                          "traffic_over_algorithmic": None if tr8 is None else round(tr8 / alg8, 3),
                          "note": "int8 matrix-core peak; each block dot needs its own fp32 rescale, so "
                                  "the kernels are bound by VALU issue well below it"},
             "bf16_form_gemm_tflops": round(ach, 2),
         }
+    out["mfma_probe"] = probe
     out["prefill_skewed_10k"] = skew
     out["full_depth_40_layers"] = full
     out["small_batch_decode"] = small

@@ -531,6 +531,22 @@ def moe_q4_w4a8_gemm(Wt: torch.Tensor, N: int, K: int, qa: torch.Tensor, da: tor
     return dots, out
 
 
+PROBE_BF16, PROBE_I8, PROBE_F32_K1 = 0, 1, 2
+
+
+def moe_q4_probe_mfma(kind: int, blocks: int, iters: int, out: torch.Tensor, stream=None) -> int:
+    """One launch of the matrix-core rate probe (kind PROBE_BF16 / PROBE_I8 /
+    PROBE_F32_K1) into `out` (device float32, blocks * 256 elements); returns
+    the operation count of the launch (time it on `stream`)."""
+    _dev(out, "out")
+    if out.dtype != torch.float32 or out.numel() < blocks * 256:
+        raise ValueError("out must be float32 with blocks * 256 elements")
+    ops = C.c_int64(0)
+    _lib.check(_lib.lib().moe_q4_probe_mfma(int(kind), int(blocks), int(iters), _p(out), C.byref(ops),
+                                            _s(stream)), "moe_q4_probe_mfma")
+    return int(ops.value)
+
+
 def moe_q4_rmsnorm(y: torch.Tensor, eps: float = 1e-6, f32: bool = True, bf16: bool = False,
                    stream=None, out_f32: torch.Tensor | None = None, out_bf16: torch.Tensor | None = None):
     """Unit-gain RMSNorm of y [T, H] fp32 -> (fp32 | None, bf16 | None); out_f32 /

@@ -91,6 +91,7 @@ def _declare(lib):
         "moe_q4_w4a8_gemv": (C.c_int, [P, I32, I32, P, P, P, P, P]),
         "moe_q4_w4a8_gemm": (C.c_int, [P, I32, I32, P, P, I32, P, P, P]),
         "moe_q4_rmsnorm": (C.c_int, [P, I32, I32, C.c_float, P, P, P]),
+        "moe_q4_probe_mfma": (C.c_int, [I32, I32, I32, P, P, P]),
         "moe_q4_last_error": (C.c_char_p, []),
     }
     for name, (res, args) in sig.items():

@@ -36,7 +36,7 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-SOURCES = ["abi.cpp", "pack.hip", "router.hip", "gemm.hip", "decode.hip", "decode_fused.hip", "decode_batch.hip",
+SOURCES = ["abi.cpp", "probe.hip", "pack.hip", "router.hip", "gemm.hip", "decode.hip", "decode_fused.hip", "decode_batch.hip",
            "rmsnorm.hip", "w4a8_gemm.hip", "w4a8_prefill.hip"]
 
 

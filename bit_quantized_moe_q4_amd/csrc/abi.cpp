@@ -857,6 +857,16 @@ int moe_q4_w4a8_gemm(const void* Wt, int32_t N, int32_t K, const int8_t* qa, con
   return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_w4a8_gemm");
 }
 
+int moe_q4_probe_mfma(int32_t kind, int32_t blocks, int32_t iters, float* out, int64_t* ops, hipStream_t stream) {
+  if (kind < 0 || kind > 2 || blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 22) || !out || !ops)
+    return fail(MOE_Q4_EINVAL, "moe_q4_probe_mfma: kind=%d (0..2) blocks=%d (1..65536) iters=%d (1..2^22), "
+                               "out and ops non-NULL", kind, blocks, iters);
+  static const int64_t kOpsPerMfma[3] = {32 * 32 * 16 * 2, 32 * 32 * 32 * 2, 2 * 32 * 32 * 1 * 2};
+  *ops = moeq4::probe_mfma_count(kind, blocks, iters) * kOpsPerMfma[kind];
+  const hipError_t e = moeq4::launch_probe_mfma(kind, blocks, iters, out, stream);
+  return e == hipSuccess ? MOE_Q4_OK : hip_fail(e, "moe_q4_probe_mfma");
+}
+
 int moe_q4_rmsnorm(const float* y, int32_t T, int32_t H, float eps, float* out_f32,
                    uint16_t* out_bf16, hipStream_t stream) {
   if (T < 0 || H <= 0 || H % 32 || H > kMaxDim)

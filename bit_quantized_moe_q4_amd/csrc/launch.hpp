@@ -39,6 +39,11 @@ hipError_t launch_route_scatter(const int32_t* ids, const int32_t* rank, const i
                                 int32_t* inv_perm, hipStream_t stream);
 constexpr int kTopkTokensPerBlock = 16;   // tokens (= waves) per top-k block
 
+// Matrix-core rate probes (probe.hip): kind 0 bf16 32x32x16, 1 int8
+// 32x32x32, 2 fp32 32x32x1 (two blocks); MFMA instructions a launch issues.
+int64_t probe_mfma_count(int kind, int blocks, int iters);
+hipError_t launch_probe_mfma(int kind, int blocks, int iters, float* out, hipStream_t stream);
+
 // Prefill expert FFN.
 struct PrefillArgs {
   const uint16_t* x;        // [T][H] bf16

@@ -41,7 +41,7 @@ def test_header_declares_the_api():
               "moe_q4_decode_workspace_bytes", "moe_q4_w4a8_gemv", "moe_q4_w4a8_gemm", "moe_q4_rmsnorm",
               "moe_q4_prefill_status", "moe_q4_prefill_w4a8", "moe_q4_prefill_w4a8_stage", "moe_q4_check_layer",
               "moe_q4_decode_status",
-              "moe_q4_test_decode_wait_fail",
+              "moe_q4_test_decode_wait_fail", "moe_q4_probe_mfma",
               "moe_q4_last_error"]:
         assert n in names, n
 
@@ -354,6 +354,18 @@ def test_gemv_and_rmsnorm_checks(lib):
     assert lib.moe_q4_rmsnorm(C.c_void_p(0x1000), 4, 40, 1e-6, C.c_void_p(0x2000), None, None) == -1
     assert lib.moe_q4_rmsnorm(C.c_void_p(0x1000), 4, 64, 1e-6, None, None, None) == -1
     assert lib.moe_q4_rmsnorm(None, 0, 64, 1e-6, None, None, None) == 0
+
+
+def test_probe_mfma_checks(lib):
+    ops = C.c_int64(-1)
+    out = C.c_void_p(0x1000)
+    assert lib.moe_q4_probe_mfma(3, 512, 100, out, C.byref(ops), None) == -1
+    assert "kind" in _err(lib)
+    assert lib.moe_q4_probe_mfma(0, 0, 100, out, C.byref(ops), None) == -1
+    assert lib.moe_q4_probe_mfma(0, 512, 0, out, C.byref(ops), None) == -1
+    assert lib.moe_q4_probe_mfma(0, 512, 100, None, C.byref(ops), None) == -1
+    assert lib.moe_q4_probe_mfma(1, 512, 100, out, None, None) == -1
+    assert ops.value == -1                   # nothing launched, nothing written
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
