@@ -16,7 +16,8 @@ Bars:
     form does not apply to 8-bit activations).
 Sizes: small shapes over several tiles with ragged tails (every token
 checked), the 2048-token prefill layer and the 10240-token skewed layer on
-sampled tokens that cover every 32-row subtile of every expert segment.
+sampled tokens that cover every 32-row subtile of every expert segment, and
+one 8192-token layer of 256 experts on a quarter of such a cover.
 """
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -199,6 +200,17 @@ def test_w4a8_prefill_matches_bf16_form(prefill_layer):
     rel = (torch.linalg.norm(y8 - y16) / torch.linalg.norm(y16)).item()
     say("W4A8 form vs bf16 form: rel-L2 %.3e" % rel)
     assert rel <= REF_TOL
+
+
+def test_w4a8_prefill_8k_256_experts_sampled():
+    # the full-depth layer shape (one layer of it): 2,304+ tiles of 32 rows,
+    # 40 groups of 64 tiles dealt to the XCDs
+    cfg = moe_synth.CONFIGS["stack"].with_(layers=1)
+    say("building 256-expert layer")
+    ol, gl = both_layers(cfg)
+    _run(ol, gl, cfg, cfg.T,
+         dots_positions=lambda rr: _segment_cover(rr, cfg.T, cfg.k, True, extra=20, seed=6)[::4],
+         sample=lambda rr: _token_cover(rr, cfg.T, cfg.k, extra=10, seed=5)[::4])
 
 
 def test_w4a8_prefill_skewed_10k_sampled():
