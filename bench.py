@@ -156,6 +156,13 @@ def hbm_copy_gbps(torch, nbytes=1 << 30, reps=5):
     return 2.0 * nbytes / ts[len(ts) // 2] / 1e9
 
 
+# The W4A8 kernels' ceiling from instruction issue: the gate/up loop issues
+# 4 int8 MFMAs (262,144 ops) and 242 VALU instructions per step; one SIMD
+# issues a wave64 VALU instruction every 4 cycles, so 968 cycles per step,
+# 262,144 / 968 ops per cycle per SIMD x 1024 SIMDs x 2.4 GHz.
+W4A8_VALU_CEILING_TOPS = 665.0
+
+
 def mfma_probe(torch, mq, blocks=512, iters=12000, reps=5):
     """Matrix-core rates this GPU sustains (moe_q4_probe_mfma): independent
     MFMA chains on register operands, 2 waves per SIMD like the grouped GEMM;
@@ -926,6 +933,8 @@ def main():
                          "unit": "TOPS", "frac": round(ops8 / t8 / 1e12 / PEAK_INT8_TOPS, 4),
                          "ops_per_step": ops8, "traffic": tr8, "algorithmic_bytes": alg8,
                          "achievable": None if probe is None else probe["i8_32x32x32_tops"],
+                         "valu_issue_ceiling": W4A8_VALU_CEILING_TOPS,
+                         "frac_of_valu_ceiling": round(ops8 / t8 / 1e12 / W4A8_VALU_CEILING_TOPS, 4),
                          "traffic_over_algorithmic": None if tr8 is None else round(tr8 / alg8, 3),
                          "note": "int8 matrix-core peak; each block dot needs its own fp32 rescale, so "
                                  "the kernels are bound by VALU issue well below it"},
