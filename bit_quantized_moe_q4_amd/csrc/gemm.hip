@@ -420,6 +420,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t g2_rsrc(const void* base, uint
   return __builtin_amdgcn_make_buffer_rsrc(u, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// Two floats rounded to bf16 (nearest, ties to even) by one packed
+// conversion: a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t g2_bf16x2_bits(float a, float b) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const f32x2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
 typedef uint32_t g2_u32x4 __attribute__((ext_vector_type(4)));
 
 // Step s of the lane's weights from a group's pieces: nibble dwords D[0..3]
@@ -598,26 +607,72 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
   }
   }
   wait_vm<0>();                                  // the repeated last fetch has landed in LDS
-  const int n0c = c0 + ln, n1c = c1 + ln;
+  // Stores through a buffer descriptor over the tile's output rows (h, o_perm
+  // or, for the shared expert, y): a row past t.rows lies past the
+  // descriptor's end and its store is dropped, so the padding rows need no
+  // test, and each store adds one wave-uniform row offset to the lane's
+  // offset instead of forming a 64-bit address.  (Per-element 64-bit
+  // addresses and row tests made the epilogue of a down unit about a third
+  // of its time.)  Pairs of values are rounded to bf16 by one conversion.
+  const int Nout = GATEUP ? I : H;
+  // (wave-uniform values made visibly so: scalar row strides and branches)
+  const int routed = __builtin_amdgcn_readfirstlane(t.expert >= 0 ? 1 : 0);
+  const int l0 = __builtin_amdgcn_readfirstlane(live0 ? 1 : 0), l1 = __builtin_amdgcn_readfirstlane(live1 ? 1 : 0);
+  const int esz = (!GATEUP && !routed) ? 4 : 2;
+  const void* obase = GATEUP ? static_cast<const void*>(a.h + (size_t)t.pos0 * I)
+                    : routed ? static_cast<const void*>(a.o_perm + (size_t)t.pos0 * H)
+                             : static_cast<const void*>(a.y + (size_t)t.m0 * H);
+  const __amdgpu_buffer_rsrc_t ro = g2_rsrc(obase, (uint32_t)t.rows * (uint32_t)Nout * (uint32_t)esz);
+  const uint32_t rstride = __builtin_amdgcn_readfirstlane((uint32_t)(Nout * esz));   // bytes per output row
+  const uint32_t vb0 = (uint32_t)((4 * g * Nout + c0 + ln) * esz);
+  const uint32_t vb1 = (uint32_t)((4 * g * Nout + c1 + ln) * esz);
+  auto off = [&](uint32_t vb, int sub, int r) { return vb + (uint32_t)(32 * sub + 8 * (r / 4) + (r % 4)) * rstride; };
+  if (GATEUP) {
+    if (l0) {
 #pragma unroll
-  for (int sub = 0; sub < MS; sub++)
+      for (int sub = 0; sub < MS; sub++)
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int rr = 32 * sub + 8 * (r / 4) + 4 * g + (r % 4);
-      if (rr >= t.rows) continue;
-      if (GATEUP) {
-        if (!live0) continue;
-        const float gv = acc0[sub][r], uv = acc1[sub][r];
-        const float hv = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
-        a.h[(size_t)(t.pos0 + rr) * I + n0c] = f32_to_bf16_bits(hv);
-      } else if (t.expert >= 0) {
-        if (live0) a.o_perm[(size_t)(t.pos0 + rr) * H + n0c] = f32_to_bf16_bits(acc0[sub][r]);
-        if (live1) a.o_perm[(size_t)(t.pos0 + rr) * H + n1c] = f32_to_bf16_bits(acc1[sub][r]);
-      } else {
-        if (live0) a.y[(size_t)(t.m0 + rr) * H + n0c] = acc0[sub][r];
-        if (live1) a.y[(size_t)(t.m0 + rr) * H + n1c] = acc1[sub][r];
-      }
+        for (int r = 0; r < 16; r += 2) {
+          float hv[2];
+#pragma unroll
+          for (int i = 0; i < 2; i++) {
+            const float gv = acc0[sub][r + i], uv = acc1[sub][r + i];
+            hv[i] = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
+          }
+          const uint32_t hb = g2_bf16x2_bits(hv[0], hv[1]);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb, ro, off(vb0, sub, r), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hb >> 16), ro, off(vb0, sub, r + 1), 0, 0);
+        }
     }
+  } else if (routed) {
+    if (l0 && l1) {
+#pragma unroll
+      for (int sub = 0; sub < MS; sub++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const uint32_t ob = g2_bf16x2_bits(acc0[sub][r], acc1[sub][r]);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ob, ro, off(vb0, sub, r), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(ob >> 16), ro, off(vb1, sub, r), 0, 0);
+        }
+    } else if (l0) {
+#pragma unroll
+      for (int sub = 0; sub < MS; sub++)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const uint32_t ob = g2_bf16x2_bits(acc0[sub][r], acc0[sub][r + 1]);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ob, ro, off(vb0, sub, r), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(ob >> 16), ro, off(vb0, sub, r + 1), 0, 0);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int sub = 0; sub < MS; sub++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        if (l0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc0[sub][r]), ro, off(vb0, sub, r), 0, 0);
+        if (l1) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc1[sub][r]), ro, off(vb1, sub, r), 0, 0);
+      }
+  }
 #endif
 }
 
