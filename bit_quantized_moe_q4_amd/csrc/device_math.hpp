@@ -38,6 +38,28 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return b;
 }
 
+// Two floats rounded to bf16 (nearest, ties to even) by one packed
+// conversion: a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  const f32x2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer descriptors exist only in the device pass
+// Buffer resource of a wave-uniform byte range; readfirstlane makes its
+// uniformity explicit so the descriptor lives in scalar registers.  Raw
+// accesses at offsets past `bytes` read zeros and drop stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+#endif
+
 // Fixed fp32 exponential.  Cody & Waite range reduction (Software Manual for
 // the Elementary Functions, 1980): n = rint(x*log2 e), r = x - n*ln2 with ln2
 // split into a 15-bit-significand head (n*head exact for |n| < 2^9) and a

@@ -410,25 +410,6 @@ struct G2Smem {
 __device__ __forceinline__ int g2_slot(int cc, int m) { return cc ^ (m & 7) ^ ((m >> 3) & 1); }
 
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer descriptors exist only in the device pass
-// Buffer resource of a wave-uniform range; readfirstlane makes its
-// uniformity explicit so the descriptor lives in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t g2_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
-  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(u, 0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-
-// Two floats rounded to bf16 (nearest, ties to even) by one packed
-// conversion: a in the low half, b in the high half.
-__device__ __forceinline__ uint32_t g2_bf16x2_bits(float a, float b) {
-  typedef float f32x2v __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-  const f32x2v v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
-}
-
 typedef uint32_t g2_u32x4 __attribute__((ext_vector_type(4)));
 
 // Step s of the lane's weights from a group's pieces: nibble dwords D[0..3]
@@ -513,14 +494,14 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
   // Raw buffer resources: the wave's two 32-row groups (their tile-order
   // pieces) and the activation rows.  The per-step offset is a scalar, so the
   // loop computes no addresses; an offset past num_records would read zeros.
-  const __amdgpu_buffer_rsrc_t rw0 = g2_rsrc(w0, (uint32_t)(32 * rb));
-  const __amdgpu_buffer_rsrc_t rw1 = g2_rsrc(w1, (uint32_t)(32 * rb));
+  const __amdgpu_buffer_rsrc_t rw0 = uniform_buffer_rsrc(w0, (uint32_t)(32 * rb));
+  const __amdgpu_buffer_rsrc_t rw1 = uniform_buffer_rsrc(w1, (uint32_t)(32 * rb));
   const uint32_t vn = 16u * (uint32_t)lane;                   // the lane's nibbles in a piece (scale: 1024 + 2 * lane)
 
   // activation rows: wave-load j = wave + 4q covers tile rows 8j..8j+7
   const uint16_t* abase = GATEUP ? a.x : a.h + (size_t)t.pos0 * I;
   const __amdgpu_buffer_rsrc_t ra =
-      g2_rsrc(abase, GATEUP ? (uint32_t)a.T * (uint32_t)H * 2u : (uint32_t)t.rows * (uint32_t)I * 2u);
+      uniform_buffer_rsrc(abase, GATEUP ? (uint32_t)a.T * (uint32_t)H * 2u : (uint32_t)t.rows * (uint32_t)I * 2u);
   uint32_t voff[MS];                                          // byte offset of the lane's 16-byte chunk, step 0
 #pragma unroll
   for (int q = 0; q < MS; q++) {
@@ -622,7 +603,7 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
   const void* obase = GATEUP ? static_cast<const void*>(a.h + (size_t)t.pos0 * I)
                     : routed ? static_cast<const void*>(a.o_perm + (size_t)t.pos0 * H)
                              : static_cast<const void*>(a.y + (size_t)t.m0 * H);
-  const __amdgpu_buffer_rsrc_t ro = g2_rsrc(obase, (uint32_t)t.rows * (uint32_t)Nout * (uint32_t)esz);
+  const __amdgpu_buffer_rsrc_t ro = uniform_buffer_rsrc(obase, (uint32_t)t.rows * (uint32_t)Nout * (uint32_t)esz);
   const uint32_t rstride = __builtin_amdgcn_readfirstlane((uint32_t)(Nout * esz));   // bytes per output row
   const uint32_t vb0 = (uint32_t)((4 * g * Nout + c0 + ln) * esz);
   const uint32_t vb1 = (uint32_t)((4 * g * Nout + c1 + ln) * esz);
@@ -639,7 +620,7 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
             const float gv = acc0[sub][r + i], uv = acc1[sub][r + i];
             hv[i] = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
           }
-          const uint32_t hb = g2_bf16x2_bits(hv[0], hv[1]);
+          const uint32_t hb = bf16x2_bits(hv[0], hv[1]);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)hb, ro, off(vb0, sub, r), 0, 0);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hb >> 16), ro, off(vb0, sub, r + 1), 0, 0);
         }
@@ -650,7 +631,7 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
       for (int sub = 0; sub < MS; sub++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          const uint32_t ob = g2_bf16x2_bits(acc0[sub][r], acc1[sub][r]);
+          const uint32_t ob = bf16x2_bits(acc0[sub][r], acc1[sub][r]);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ob, ro, off(vb0, sub, r), 0, 0);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(ob >> 16), ro, off(vb1, sub, r), 0, 0);
         }
@@ -659,7 +640,7 @@ __device__ __forceinline__ void g2_tile(const PrefillArgs& a, const Tile& t, int
       for (int sub = 0; sub < MS; sub++)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const uint32_t ob = g2_bf16x2_bits(acc0[sub][r], acc0[sub][r + 1]);
+          const uint32_t ob = bf16x2_bits(acc0[sub][r], acc0[sub][r + 1]);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ob, ro, off(vb0, sub, r), 0, 0);
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(ob >> 16), ro, off(vb0, sub, r + 1), 0, 0);
         }

@@ -33,7 +33,7 @@ __device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offset
   t.pos0 = 0;
   t.expert = -1;
   t.m0 = 0;
-  int c = -1, q = 0;
+  int c = -1, q = 0, seg0 = 0;
   // the shared expert's tiles, the largest units, come in a multiple of 8
   // once there are 8 or more (balanced: tiles are dealt to the 8 XCDs by
   // index, and 13 tiles at 2048 tokens gave five XCDs one heavy tile more)
@@ -47,8 +47,11 @@ __device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offset
     int carry = 0;
     for (int base = 0; base < E; base += 64) {
       const int e = base + lane;
-      int ce = 0;
-      if (e < E) ce = offsets[e + 1] - offsets[e];
+      int ce = 0, o0 = 0;
+      if (e < E) {
+        o0 = offsets[e];
+        ce = offsets[e + 1] - o0;
+      }
       const int nt = (ce + FMAXR - 1) / FMAXR;
       int incl = nt;
 #pragma unroll
@@ -61,6 +64,7 @@ __device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offset
         const int f = __builtin_ctzll(hit);
         t.expert = base + f;
         c = __shfl(ce, f, 64);
+        seg0 = __shfl(o0, f, 64);          // the segment's start, already loaded
         q = mr - (carry + __shfl(incl, f, 64) - __shfl(nt, f, 64));
         break;
       }
@@ -75,7 +79,7 @@ __device__ __forceinline__ Tile find_tile_bal(const int32_t* __restrict__ offset
   t.rows = min(tr, c - t.m0);
   if (t.rows <= 0) return t;
   t.valid = 1;
-  t.pos0 = (t.expert >= 0) ? offsets[t.expert] + t.m0 : T * k + t.m0;
+  t.pos0 = (t.expert >= 0) ? seg0 + t.m0 : T * k + t.m0;
   return t;
 }
 

@@ -326,19 +326,34 @@ __global__ void __launch_bounds__(kW8Threads) __attribute__((amdgpu_waves_per_eu
       A[j] = An[j]; B0[j] = B0n[j]; B1[j] = B1n[j]; s0[j] = s0n[j]; s1[j] = s1n[j];
     }
   }
-  const int c0 = kW8DnCols * cb + n, c1 = c0 + 32;
+#if defined(__HIP_DEVICE_COMPILE__)   // (buffer descriptors exist only in the device pass)
+  // Stores through a descriptor over the tile's output rows (o_perm, or y for
+  // the shared expert): rows past t.rows fall past its end and are dropped,
+  // and each store adds a scalar row offset to the lane's offset.
+  const int routed = __builtin_amdgcn_readfirstlane(t.expert >= 0 ? 1 : 0);
+  const int esz = routed ? 2 : 4;
+  const void* obase = routed ? static_cast<const void*>(a.o_perm + (size_t)t.pos0 * H)
+                             : static_cast<const void*>(a.y + (size_t)t.m0 * H);
+  const __amdgpu_buffer_rsrc_t ro = uniform_buffer_rsrc(obase, (uint32_t)t.rows * (uint32_t)H * (uint32_t)esz);
+  const uint32_t rstride = __builtin_amdgcn_readfirstlane((uint32_t)(H * esz));
+  const uint32_t vb0 = (uint32_t)((4 * h * H + kW8DnCols * cb + n) * esz), vb1 = vb0 + 32u * (uint32_t)esz;
+  if (routed) {
 #pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int row = 8 * (r / 4) + 4 * h + (r % 4);
-    if (row >= t.rows) continue;
-    if (t.expert >= 0) {
-      a.o_perm[(size_t)(t.pos0 + row) * H + c0] = f32_to_bf16_bits(acc0[r]);
-      a.o_perm[(size_t)(t.pos0 + row) * H + c1] = f32_to_bf16_bits(acc1[r]);
-    } else {
-      a.y[(size_t)(t.m0 + row) * H + c0] = acc0[r];
-      a.y[(size_t)(t.m0 + row) * H + c1] = acc1[r];
+    for (int r = 0; r < 16; r++) {
+      const uint32_t ro_r = (uint32_t)(8 * (r / 4) + (r % 4)) * rstride;
+      const uint32_t ob = bf16x2_bits(acc0[r], acc1[r]);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)ob, ro, vb0 + ro_r, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(ob >> 16), ro, vb1 + ro_r, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const uint32_t ro_r = (uint32_t)(8 * (r / 4) + (r % 4)) * rstride;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc0[r]), ro, vb0 + ro_r, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc1[r]), ro, vb1 + ro_r, 0, 0);
     }
   }
+#endif
 }
 
 // ---------------------------------------------------------------- launch
