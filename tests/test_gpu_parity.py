@@ -358,6 +358,50 @@ def _fused_vs_stages(gl, xbd):
     return y_all, y_st
 
 
+@pytest.mark.parametrize("k", [3, 4])
+def test_prefill_stores_stay_inside_tile_rows(k):
+    """The grouped GEMM stores through buffer descriptors bounded by each
+    tile's row count, so a partial tile's padding rows are never stored.
+    With 77 tokens the shared expert's last tile and the last expert's
+    segment end inside a 32-row group: y sits at the start of a larger
+    buffer whose tail holds a sentinel, and the workspace is filled with a
+    sentinel byte first.  After gate/up + down, the tail past y and the
+    alignment padding after h (k = 4) or after the expert outputs (k = 3)
+    are unchanged, and after the combine y equals a one-call prefill's bit
+    for bit."""
+    cfg = moe_synth.CONFIGS["tiny"].with_(name="pad_rows", T=77, H=320, E=16, I=64, k=k, shared=True)
+    ol, gl = both_layers(cfg)
+    assert gl.tiles is not None
+    x, bits, xw, xd, xbd = tokens(cfg, T=cfg.T)
+    T, H, I = cfg.T, cfg.H, cfg.I
+    r = mq.moe_q4_route(gl, xbd)
+    say("padding rows: T=%d k=%d H=%d I=%d" % (T, k, H, I))
+    sentinel = -12345.0
+    big = torch.full(((T + 64) * H,), sentinel, dtype=torch.float32, device="cuda")
+    y = big[:T * H].view(T, H)
+    ws = torch.full((mq.moe_q4_prefill_workspace_bytes(gl, T),), 0xA5, dtype=torch.uint8, device="cuda")
+    S = mq._lib
+    mq.moe_q4_prefill_stage(gl, xbd, r, y, ws, S.STAGE_GATEUP | S.STAGE_DOWN)
+    torch.cuda.synchronize()
+    assert torch.all(big[T * H:] == sentinel)
+    # workspace: h [(T*k + T) rows][I] bf16, then the expert outputs [T*k][H]
+    # bf16, each region rounded up to 256 bytes
+    up256 = lambda n: (n + 255) // 256 * 256
+    h_end = (T * k + T) * I * 2
+    o0 = up256(h_end)
+    o_end = o0 + T * k * H * 2
+    pads = [(h_end, o0), (o_end, up256(o_end))]
+    pads = [(a, b) for a, b in pads if b > a]
+    assert pads, "the shape leaves no padding to check"
+    wsc = ws.cpu().numpy()
+    for a, b in pads:
+        assert np.all(wsc[a:b] == 0xA5), (a, b)
+    mq.moe_q4_prefill_stage(gl, xbd, r, y, ws, S.STAGE_COMBINE)
+    y_one = mq.moe_q4_prefill(gl, xbd, r)
+    assert torch.equal(y, y_one)
+    assert torch.all(big[T * H:] == sentinel)
+
+
 def test_prefill_all_stages_match_stages_apart(prefill_layer):
     # the same y bit for bit, whichever way the call is split
     cfg, (ol, gl) = prefill_layer
