@@ -158,6 +158,38 @@ def test_w4a8_prefill_small(name, T, H, E, I, k, shared):
     _run(ol, gl, cfg, T)
 
 
+def test_w4a8_prefill_stores_stay_inside_tile_rows():
+    """The int8 down stage stores through a buffer descriptor bounded by the
+    tile's row count: with 77 tokens the shared expert's last 32-row tile
+    holds 13 rows, and the last expert's segment ends inside one.  y sits at
+    the start of a larger buffer whose tail holds a sentinel and the
+    workspace is pre-filled with a sentinel byte: after gate/up + down the
+    tail past y and the alignment padding after the expert outputs are
+    unchanged, and after the combine y equals a one-call W4A8 prefill's bit
+    for bit."""
+    cfg = moe_synth.CONFIGS["tiny"].with_(name="w8_pad_rows", T=77, H=192, E=5, I=64, k=3, shared=True)
+    ol, gl = both_layers(cfg)
+    x, bits, xw, xd, xbd = tokens(cfg, T=cfg.T)
+    T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
+    r = mq.moe_q4_route(gl, xbd)
+    sentinel = -12345.0
+    big = torch.full(((T + 64) * H,), sentinel, dtype=torch.float32, device="cuda")
+    y = big[:T * H].view(T, H)
+    ws = torch.full((mq.moe_q4_prefill_workspace_bytes(gl, T),), 0xA5, dtype=torch.uint8, device="cuda")
+    S = mq._lib
+    mq.moe_q4_prefill_w4a8_stage(gl, xbd, r, y, ws, S.STAGE_GATEUP | S.STAGE_DOWN)
+    torch.cuda.synchronize()
+    assert torch.all(big[T * H:] == sentinel)
+    up256 = lambda n: (n + 255) // 256 * 256
+    o_end = up256((T * k + T) * I * 2) + T * k * H * 2     # the expert outputs follow h
+    assert up256(o_end) > o_end
+    assert np.all(ws[o_end:up256(o_end)].cpu().numpy() == 0xA5)
+    mq.moe_q4_prefill_w4a8_stage(gl, xbd, r, y, ws, S.STAGE_COMBINE)
+    y_one = mq.moe_q4_prefill_w4a8(gl, xbd, r)
+    assert torch.equal(y, y_one)
+    assert torch.all(big[T * H:] == sentinel)
+
+
 def test_w4a8_prefill_empty_batch():
     cfg = moe_synth.CONFIGS["tiny"]
     ol, gl = both_layers(cfg)
